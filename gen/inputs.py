@@ -1,0 +1,137 @@
+"""Seeded synthetic inputs for the selective scan (S6).
+
+This module is shared by the CPU oracle and the GPU path and holds none of the
+scan's arithmetic: only random draws, the round-to-nearest-even narrowing of
+those draws to bfloat16, and the recipe's parameter transforms (the per-channel
+log-uniform step size turned into its bias, the perturbation of A).
+
+Every tensor has its own child stream of ``numpy.random.SeedSequence(seed)``,
+spawned in the fixed order of ``STREAMS``, so a tensor's values do not depend on
+which other tensors a case draws.  bf16 tensors are returned as float32 arrays
+whose values are exactly representable in bf16 (the low 16 bits are zero): the
+GPU receives those bits, the oracle widens the same values exactly.
+
+Layouts (dense, row-major): x, dt_raw, z, dy: [B, D, L]; Bm, Cm: [B, N, L];
+A: [D, N]; dt_bias, Dskip: [D]; h0, dh_final: [B, D, N].
+"""
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+
+from .configs import Workload, seed_of
+
+STREAMS = ("x", "z", "dt_raw", "dt", "eps", "B", "C", "D", "dy", "h0", "dh_final", "spare")
+
+_CHUNK = 1 << 24  # elements per narrowing pass, bounds temporaries for the 268M-element tensors
+
+
+def bf16_bits(a: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns (uint16), round to nearest, ties to even.
+
+    Integer arithmetic on the float32 bits: add 0x7FFF plus the lowest kept bit,
+    then drop the low 16 bits.  Inputs are finite.
+    """
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    flat = a.reshape(-1)
+    out = np.empty(flat.shape, dtype=np.uint16)
+    for s in range(0, flat.size, _CHUNK):
+        u = flat[s:s + _CHUNK].view(np.uint32)
+        r = u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))
+        out[s:s + _CHUNK] = (r >> np.uint32(16)).astype(np.uint16)
+    return out.reshape(a.shape)
+
+
+def bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns -> float32 values (exact widening)."""
+    return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def round_bf16(a: np.ndarray) -> np.ndarray:
+    """float32 values rounded to the nearest bfloat16, kept as float32."""
+    return bits_to_f32(bf16_bits(a))
+
+
+def _normal(rng: np.random.Generator, shape, scale: float = 1.0) -> np.ndarray:
+    v = rng.standard_normal(shape, dtype=np.float32)
+    if scale != 1.0:
+        v *= np.float32(scale)
+    return v
+
+
+@dataclass
+class S6Inputs:
+    """One case of the scan's inputs (all float32 numpy arrays, C-contiguous)."""
+    batch: int
+    seqlen: int
+    dim: int
+    dstate: int
+    dtype: str                       # "f32" | "bf16" (x, dt_raw, z, Bm, Cm hold bf16-exact values)
+    x: np.ndarray
+    dt_raw: np.ndarray
+    dt_bias: np.ndarray
+    A: np.ndarray
+    Bm: np.ndarray
+    Cm: np.ndarray
+    Dskip: np.ndarray
+    z: Optional[np.ndarray] = None
+    h0: Optional[np.ndarray] = None
+    dy: Optional[np.ndarray] = None
+    dh_final: Optional[np.ndarray] = None
+    meta: dict = field(default_factory=dict)
+
+    def oracle_args(self):
+        """Positional inputs in the order the oracles take them."""
+        return (self.x, self.dt_raw, self.dt_bias, self.A, self.Bm, self.Cm, self.Dskip)
+
+
+def make_inputs(batch: int, seqlen: int, dim: int, dstate: int, *, dtype: str = "f32",
+                seed: int = 0, gate: bool = False, a_perturb: bool = False,
+                with_h0: bool = False, with_dy: bool = False, with_dh_final: bool = False,
+                dt_min: float = 1e-3, dt_max: float = 1e-1) -> S6Inputs:
+    """Draw one seeded case with the benchmark recipe.
+
+    x, z ~ N(0,1); dt_raw ~ 0.5*N(0,1); dt ~ logU[dt_min, dt_max] per channel and
+    dt_bias = log(expm1(dt)); A[d,n] = -(n+1), times exp(eps) with eps ~ N(0, 0.1^2)
+    per (d,n) when a_perturb; B, C, D ~ N(0,1); h0, dy, dh_final ~ N(0,1).
+    """
+    if dtype not in ("f32", "bf16"):
+        raise ValueError(f"dtype must be 'f32' or 'bf16', got {dtype!r}")
+    kids = np.random.SeedSequence(seed).spawn(len(STREAMS))
+    rng = {name: np.random.Generator(np.random.PCG64(k)) for name, k in zip(STREAMS, kids)}
+    Bn, L, D, N = batch, seqlen, dim, dstate
+    narrow = round_bf16 if dtype == "bf16" else (lambda a: a)
+
+    x = narrow(_normal(rng["x"], (Bn, D, L)))
+    dt_raw = narrow(_normal(rng["dt_raw"], (Bn, D, L), 0.5))
+    z = narrow(_normal(rng["z"], (Bn, D, L))) if gate else None
+
+    log_dt = rng["dt"].uniform(np.log(dt_min), np.log(dt_max), size=D)
+    dt = np.exp(log_dt)
+    dt_bias = np.log(np.expm1(dt)).astype(np.float32)
+
+    base = -np.arange(1, N + 1, dtype=np.float64)[None, :].repeat(D, axis=0)
+    if a_perturb:
+        eps = rng["eps"].normal(0.0, 0.1, size=(D, N))
+        base = base * np.exp(eps)
+    A = base.astype(np.float32)
+
+    Bm = narrow(_normal(rng["B"], (Bn, N, L)))
+    Cm = narrow(_normal(rng["C"], (Bn, N, L)))
+    Dskip = _normal(rng["D"], (D,))
+
+    h0 = _normal(rng["h0"], (Bn, D, N)) if with_h0 else None
+    dy = _normal(rng["dy"], (Bn, D, L)) if with_dy else None
+    dh_final = _normal(rng["dh_final"], (Bn, D, N)) if with_dh_final else None
+
+    return S6Inputs(Bn, L, D, N, dtype, x, dt_raw, dt_bias, A, Bm, Cm, Dskip,
+                    z=z, h0=h0, dy=dy, dh_final=dh_final,
+                    meta=dict(seed=seed, gate=gate, a_perturb=a_perturb))
+
+
+def workload_inputs(w: Workload, **overrides) -> S6Inputs:
+    """Inputs of a named workload, seeded with its index."""
+    kw = dict(dtype=w.dtype, seed=seed_of(w), gate=w.gate, a_perturb=w.a_perturb,
+              with_dy=w.backward)
+    kw.update(overrides)
+    return make_inputs(w.batch, w.seqlen, w.dim, w.dstate, **kw)
