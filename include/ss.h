@@ -1,0 +1,135 @@
+/*
+ * ss.h — C ABI of the MI355X (gfx950) selective-scan (S6) library.
+ *
+ * The operation (sources cited by page title and section):
+ *   Page "3.2 선택적 스캔(Selective Scan) 알고리즘과 정보의 압축 및 선별"
+ *   (booiljung.github.io) — §1.2 selection: Δ_t = softplus(parameter + per-token
+ *   input); §2.1 ZOH discretisation Ā_t = exp(Δ_t A) with A diagonal; §2.2 the
+ *   recurrence h_t = Ā_t h_{t-1} + B̄_t x_t as an associative scan; §1.1 readout
+ *   y_t = C_t h_t; §3.2 kernel fusion (inputs in, only y out; the state never
+ *   reaches HBM); §3.3 recomputation of states in the backward pass.
+ *   Note "상태공간 모델(SSM)과 Mamba 아키텍처", §3: the SiLU gate branch that
+ *   multiplies the scan's output.
+ *
+ * Per batch row b, channel d and time t (n indexes the N states):
+ *   δ      = softplus(dt_bias[d] + dt_raw[b,d,t])
+ *   h[n]   = exp(δ·A[d,n])·h[n] + δ·B[b,n,t]·x[b,d,t]      (first-order B̄ = Δ·B)
+ *   y[b,d,t] = (Σ_n C[b,n,t]·h[n] + Dskip[d]·x[b,d,t]) · silu(z[b,d,t])   (gate optional)
+ * with h = h0[b,d,:] (or 0) before t = 0 and h_final[b,d,:] = h after t = L-1.
+ *
+ * Layouts (dense, row-major, element strides implied by the dims):
+ *   x, dt_raw, z, y, dy, dx, ddt_raw, dz : [B, D, L]
+ *   Bm, Cm, dB, dC                        : [B, N, L]
+ *   A, dA                                 : [D, N]
+ *   dt_bias, Dskip, ddt_bias, dD          : [D]
+ *   h0, h_final, dh_final, dh0            : [B, D, N]
+ * x, dt_raw, z, Bm, Cm have the dtype ss_dims.in_dtype (float32 or bfloat16);
+ * every other array, including all outputs and all gradients, is float32.
+ *
+ * Conventions:
+ *   - All pointers are device pointers (hipMalloc'd or equivalent) except the
+ *     ss_dims pointer, which is a host pointer read during the call only.
+ *   - The caller owns every buffer and the workspace; the library never
+ *     allocates, frees or synchronises.  All work is enqueued on `stream`
+ *     (0 = the null stream) and the call returns without waiting.
+ *   - Outputs are overwritten, never accumulated into (the reduced gradients
+ *     dA, dB, dC, dD, ddt_bias included).  Inputs and outputs must not alias.
+ *   - The library keeps no state between calls and is re-entrant; concurrent
+ *     calls need distinct workspaces.
+ *   - Arguments are validated before anything is launched; on an error code
+ *     nothing has been enqueued.
+ *   - All base pointers must be 16-byte aligned.
+ */
+#ifndef SS_H_
+#define SS_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SS_VERSION_MAJOR 0
+#define SS_VERSION_MINOR 1
+
+/* dtype of x, dt_raw, z, Bm, Cm */
+typedef enum { SS_F32 = 0, SS_BF16 = 1 } ss_dtype;
+
+/* Execution plan.
+ *   SS_PLAN_AUTO    — chosen from the dims.
+ *   SS_PLAN_SINGLE  — one pass, each channel's whole sequence on one lane.
+ *   SS_PLAN_CHUNKED — sequence split into chunks: per-chunk aggregates, a carry
+ *                     scan of the affine pairs across chunks (§2.2 operator),
+ *                     then the output pass from each chunk's true start state.
+ * The backward always runs chunked. */
+typedef enum { SS_PLAN_AUTO = 0, SS_PLAN_SINGLE = 1, SS_PLAN_CHUNKED = 2 } ss_plan;
+
+typedef struct ss_dims {
+    int64_t batch;    /* B  >= 1 */
+    int64_t seqlen;   /* L  >= 1 */
+    int64_t dim;      /* D  >= 1 */
+    int64_t dstate;   /* N, one of 1, 2, 4, 8, 16, 32 */
+    int32_t in_dtype; /* ss_dtype */
+    int32_t plan;     /* ss_plan */
+    int64_t chunk;    /* chunk length of the chunked plan (multiple of 8); 0 = automatic */
+} ss_dims;
+
+/* Return codes: 0 on success, negative on error. */
+enum {
+    SS_OK = 0,
+    SS_ERR_NULL = -1,        /* a required pointer is NULL */
+    SS_ERR_DIMS = -2,        /* a dim <= 0, N unsupported, sizes overflow, or bad chunk */
+    SS_ERR_DTYPE = -3,       /* in_dtype or plan not one of the enums */
+    SS_ERR_ALIGN = -4,       /* a base pointer is not 16-byte aligned */
+    SS_ERR_WORKSPACE = -5,   /* workspace NULL while needed, or workspace_bytes too small */
+    SS_ERR_HIP = -6,         /* a HIP call failed; see ss_last_hip_error() */
+    SS_ERR_UNSUPPORTED = -7  /* valid arguments this build does not handle */
+};
+
+/* Workspace bytes ss_fwd / ss_bwd need for these dims (written to *bytes).
+ * Returns SS_OK, SS_ERR_NULL, SS_ERR_DIMS or SS_ERR_DTYPE. */
+int ss_fwd_workspace_size(const ss_dims* dims, size_t* bytes);
+int ss_bwd_workspace_size(const ss_dims* dims, size_t* bytes);
+
+/* Forward scan.
+ *   x, dt_raw, Bm, Cm, dt_bias, A, Dskip, y : required.
+ *   z       : NULL = no gate.
+ *   h0      : NULL = zero initial state.
+ *   h_final : NULL = final state not written.
+ *   workspace / workspace_bytes : at least ss_fwd_workspace_size bytes of device memory. */
+int ss_fwd(const ss_dims* dims,
+           const void* x, const void* dt_raw, const float* dt_bias, const float* A,
+           const void* Bm, const void* Cm, const float* Dskip, const void* z, const float* h0,
+           float* y, float* h_final,
+           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Backward: gradients of sum(dy·y) + sum(dh_final·h_final) with respect to every
+ * input, recomputing the states from the inputs (§3.3) instead of storing them.
+ *   Inputs as ss_fwd; dy required; dh_final NULL = zero.
+ *   dx, ddt_raw, ddt_bias, dA, dB, dC, dD : required outputs.
+ *   dz  : required iff z is given (else must be NULL).
+ *   dh0 : required iff h0 is given (else must be NULL). */
+int ss_bwd(const ss_dims* dims,
+           const void* x, const void* dt_raw, const float* dt_bias, const float* A,
+           const void* Bm, const void* Cm, const float* Dskip, const void* z, const float* h0,
+           const float* dy, const float* dh_final,
+           float* dx, float* ddt_raw, float* ddt_bias, float* dA, float* dB, float* dC,
+           float* dD, float* dz, float* dh0,
+           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Static description of a return code. */
+const char* ss_strerror(int code);
+
+/* hipError_t of the last failing HIP call made by this thread inside the library. */
+int ss_last_hip_error(void);
+
+/* (SS_VERSION_MAJOR << 16) | SS_VERSION_MINOR */
+int ss_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SS_H_ */

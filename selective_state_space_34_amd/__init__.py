@@ -1,0 +1,208 @@
+"""Python binding of the MI355X selective-scan (S6) library (include/ss.h).
+
+Argument marshalling only: torch supplies device memory and the current stream,
+every step of the scan runs in the library's HIP kernels.  There is no CPU or
+PyTorch fallback: if the compiled library is missing, ``load()`` raises.
+
+    y = ss_fwd(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, z=None, h0=None)
+    y, h_final = ss_fwd(..., return_final=True)
+    grads = ss_bwd(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, dy, z=None, h0=None, dh_final=None)
+
+Layouts: x, dt_raw, z, y [B, D, L]; Bm, Cm [B, N, L]; A [D, N]; dt_bias, Dskip [D];
+h0, h_final [B, D, N].  x, dt_raw, z, Bm, Cm are float32 or bfloat16 (all the same);
+everything else is float32.
+"""
+import ctypes
+import os
+
+from ._build import LIB, build, stale  # noqa: F401
+
+SS_F32, SS_BF16 = 0, 1
+SS_PLAN_AUTO, SS_PLAN_SINGLE, SS_PLAN_CHUNKED = 0, 1, 2
+
+ERRORS = {0: "SS_OK", -1: "SS_ERR_NULL", -2: "SS_ERR_DIMS", -3: "SS_ERR_DTYPE", -4: "SS_ERR_ALIGN",
+          -5: "SS_ERR_WORKSPACE", -6: "SS_ERR_HIP", -7: "SS_ERR_UNSUPPORTED"}
+
+EXPORTS = ("ss_fwd", "ss_bwd", "ss_fwd_workspace_size", "ss_bwd_workspace_size", "ss_strerror",
+           "ss_last_hip_error", "ss_version")
+
+
+class ss_dims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("dim", ctypes.c_int64),
+                ("dstate", ctypes.c_int64), ("in_dtype", ctypes.c_int32), ("plan", ctypes.c_int32),
+                ("chunk", ctypes.c_int64)]
+
+
+class SSError(RuntimeError):
+    def __init__(self, code, lib=None):
+        msg = ERRORS.get(code, str(code))
+        if lib is not None:
+            msg += ": " + lib.ss_strerror(code).decode()
+            if code == -6:
+                msg += f" (hipError {lib.ss_last_hip_error()})"
+        super().__init__(msg)
+        self.code = code
+
+
+_lib = None
+
+
+def load(path: str = LIB):
+    """Load libss.so (built in-tree by ``build()``).  Raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"HIP library not built: {path} (run selective_state_space_34_amd.build())")
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    D = ctypes.POINTER(ss_dims)
+    lib.ss_fwd.argtypes = [D] + [P] * 11 + [P, ctypes.c_size_t, P]
+    lib.ss_fwd.restype = ctypes.c_int
+    lib.ss_bwd.argtypes = [D] + [P] * 9 + [P, P] + [P] * 9 + [P, ctypes.c_size_t, P]
+    lib.ss_bwd.restype = ctypes.c_int
+    for f in ("ss_fwd_workspace_size", "ss_bwd_workspace_size"):
+        getattr(lib, f).argtypes = [D, ctypes.POINTER(ctypes.c_size_t)]
+        getattr(lib, f).restype = ctypes.c_int
+    lib.ss_strerror.argtypes = [ctypes.c_int]
+    lib.ss_strerror.restype = ctypes.c_char_p
+    lib.ss_last_hip_error.restype = ctypes.c_int
+    lib.ss_version.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def make_dims(batch, seqlen, dim, dstate, in_dtype=SS_F32, plan=SS_PLAN_AUTO, chunk=0):
+    return ss_dims(batch, seqlen, dim, dstate, in_dtype, plan, chunk)
+
+
+def workspace_size(dims, backward=False) -> int:
+    lib = load()
+    n = ctypes.c_size_t(0)
+    fn = lib.ss_bwd_workspace_size if backward else lib.ss_fwd_workspace_size
+    rc = fn(ctypes.byref(dims), ctypes.byref(n))
+    if rc != 0:
+        raise SSError(rc, lib)
+    return n.value
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(t, name, shape, dtype, device):
+    import torch
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _dims_of(x, A, Bm, plan, chunk):
+    import torch
+    Bn, D, L = x.shape
+    N = A.shape[1]
+    if x.dtype == torch.float32:
+        dt = SS_F32
+    elif x.dtype == torch.bfloat16:
+        dt = SS_BF16
+    else:
+        raise ValueError(f"x dtype must be float32 or bfloat16, got {x.dtype}")
+    return make_dims(Bn, L, D, N, dt, plan, chunk)
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check_inputs(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, z, h0):
+    import torch
+    Bn, D, L = x.shape
+    N = A.shape[1]
+    dev = x.device
+    f32 = torch.float32
+    _check(dt_raw, "dt_raw", (Bn, D, L), x.dtype, dev)
+    _check(z, "z", (Bn, D, L), x.dtype, dev)
+    _check(Bm, "Bm", (Bn, N, L), x.dtype, dev)
+    _check(Cm, "Cm", (Bn, N, L), x.dtype, dev)
+    _check(A, "A", (D, N), f32, dev)
+    _check(dt_bias, "dt_bias", (D,), f32, dev)
+    _check(Dskip, "Dskip", (D,), f32, dev)
+    _check(h0, "h0", (Bn, D, N), f32, dev)
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+
+
+def ss_fwd(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, z=None, h0=None, *, return_final=False,
+           y=None, h_final=None, workspace=None, plan=SS_PLAN_AUTO, chunk=0, stream=None):
+    """Forward scan through the C ABI.  Returns y, or (y, h_final) with return_final."""
+    import torch
+    lib = load()
+    _check_inputs(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, z, h0)
+    dims = _dims_of(x, A, Bm, plan, chunk)
+    Bn, D, L = x.shape
+    N = A.shape[1]
+    if y is None:
+        y = torch.empty((Bn, D, L), dtype=torch.float32, device=x.device)
+    _check(y, "y", (Bn, D, L), torch.float32, x.device)
+    if return_final and h_final is None:
+        h_final = torch.empty((Bn, D, N), dtype=torch.float32, device=x.device)
+    _check(h_final, "h_final", (Bn, D, N), torch.float32, x.device)
+    need = workspace_size(dims)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib.ss_fwd(ctypes.byref(dims), _ptr(x), _ptr(dt_raw), _ptr(dt_bias), _ptr(A), _ptr(Bm),
+                    _ptr(Cm), _ptr(Dskip), _ptr(z), _ptr(h0), _ptr(y), _ptr(h_final),
+                    _ptr(workspace), wbytes, _stream(stream))
+    if rc != 0:
+        raise SSError(rc, lib)
+    return (y, h_final) if (return_final or h_final is not None) else y
+
+
+def ss_bwd(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, dy, z=None, h0=None, dh_final=None, *,
+           workspace=None, chunk=0, out=None, stream=None):
+    """Backward through the C ABI.  Returns a dict dx, ddt_raw, ddt_bias, dA, dB, dC, dD,
+    dz (None without gate), dh0 (None without h0); all float32."""
+    import torch
+    lib = load()
+    _check_inputs(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, z, h0)
+    dims = _dims_of(x, A, Bm, SS_PLAN_CHUNKED, chunk)
+    Bn, D, L = x.shape
+    N = A.shape[1]
+    dev = x.device
+    f32 = torch.float32
+    _check(dy, "dy", (Bn, D, L), f32, dev)
+    _check(dh_final, "dh_final", (Bn, D, N), f32, dev)
+    shapes = dict(dx=(Bn, D, L), ddt_raw=(Bn, D, L), ddt_bias=(D,), dA=(D, N), dB=(Bn, N, L),
+                  dC=(Bn, N, L), dD=(D,), dz=(Bn, D, L), dh0=(Bn, D, N))
+    g = {} if out is None else dict(out)
+    for k, shp in shapes.items():
+        if (k == "dz" and z is None) or (k == "dh0" and h0 is None):
+            g[k] = None
+            continue
+        if g.get(k) is None:
+            g[k] = torch.empty(shp, dtype=f32, device=dev)
+        _check(g[k], k, shp, f32, dev)
+    need = workspace_size(dims, backward=True)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib.ss_bwd(ctypes.byref(dims), _ptr(x), _ptr(dt_raw), _ptr(dt_bias), _ptr(A), _ptr(Bm),
+                    _ptr(Cm), _ptr(Dskip), _ptr(z), _ptr(h0), _ptr(dy), _ptr(dh_final),
+                    _ptr(g["dx"]), _ptr(g["ddt_raw"]), _ptr(g["ddt_bias"]), _ptr(g["dA"]),
+                    _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]), _ptr(g["dh0"]),
+                    _ptr(workspace), wbytes, _stream(stream))
+    if rc != 0:
+        raise SSError(rc, lib)
+    return g

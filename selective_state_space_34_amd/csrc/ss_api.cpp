@@ -1,0 +1,120 @@
+// C ABI of the selective-scan library: validation, plan choice, workspace carving
+// and kernel launches on the caller's stream.  Declared in include/ss.h.
+//
+// Every argument check happens before the first HIP call, so an error return
+// means nothing was enqueued.  The library allocates nothing: all scratch memory
+// comes from the caller's workspace.
+#include "ss.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "ss_kernels.h"
+#include "ss_plan.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_fail(hipError_t e) {
+    g_last_hip_error = int(e);
+    return SS_ERR_HIP;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+int ss_version(void) { return (SS_VERSION_MAJOR << 16) | SS_VERSION_MINOR; }
+
+int ss_last_hip_error(void) { return g_last_hip_error; }
+
+const char* ss_strerror(int code) {
+    switch (code) {
+        case SS_OK: return "success";
+        case SS_ERR_NULL: return "a required pointer is NULL";
+        case SS_ERR_DIMS: return "invalid dimensions (dim <= 0, unsupported dstate, overflow or bad chunk)";
+        case SS_ERR_DTYPE: return "invalid dtype or plan";
+        case SS_ERR_ALIGN: return "a base pointer is not 16-byte aligned";
+        case SS_ERR_WORKSPACE: return "workspace missing or too small";
+        case SS_ERR_HIP: return "a HIP runtime call failed";
+        case SS_ERR_UNSUPPORTED: return "unsupported by this build";
+        default: return "unknown error code";
+    }
+}
+
+int ss_fwd_workspace_size(const ss_dims* dims, size_t* bytes) {
+    if (!dims || !bytes) return SS_ERR_NULL;
+    ss::Plan p;
+    const int rc = ss::make_plan(*dims, /*backward=*/false, &p);
+    if (rc != SS_OK) return rc;
+    *bytes = p.ws_total;
+    return SS_OK;
+}
+
+int ss_bwd_workspace_size(const ss_dims* dims, size_t* bytes) {
+    if (!dims || !bytes) return SS_ERR_NULL;
+    ss::Plan p;
+    const int rc = ss::make_plan(*dims, /*backward=*/true, &p);
+    if (rc != SS_OK) return rc;
+    *bytes = p.ws_total;
+    return SS_OK;
+}
+
+int ss_fwd(const ss_dims* dims, const void* x, const void* dt_raw, const float* dt_bias,
+           const float* A, const void* Bm, const void* Cm, const float* Dskip, const void* z,
+           const float* h0, float* y, float* h_final, void* workspace, size_t workspace_bytes,
+           hipStream_t stream) {
+    if (!dims) return SS_ERR_NULL;
+    ss::Plan p;
+    int rc = ss::make_plan(*dims, false, &p);
+    if (rc != SS_OK) return rc;
+    if (!x || !dt_raw || !dt_bias || !A || !Bm || !Cm || !Dskip || !y) return SS_ERR_NULL;
+    const void* ptrs[] = {x, dt_raw, dt_bias, A, Bm, Cm, Dskip, y};
+    for (const void* q : ptrs)
+        if (!aligned16(q)) return SS_ERR_ALIGN;
+    if ((z && !aligned16(z)) || (h0 && !aligned16(h0)) || (h_final && !aligned16(h_final)))
+        return SS_ERR_ALIGN;
+    if (p.ws_total > 0 && (!workspace || workspace_bytes < p.ws_total)) return SS_ERR_WORKSPACE;
+    if (workspace && !aligned16(workspace)) return SS_ERR_ALIGN;
+
+    char* ws = static_cast<char*>(workspace);
+    float* BC = reinterpret_cast<float*>(ws + p.off_bc);
+    const int bf16 = p.in_dtype == SS_BF16;
+    hipError_t e = ss::launch_bc_stage(bf16, int(p.N), Bm, Cm, BC, p.B, p.L, stream);
+    if (e != hipSuccess) return hip_fail(e);
+
+    ss::ScanLaunch s{};
+    s.x = x; s.dt_raw = dt_raw; s.z = z; s.dt_bias = dt_bias; s.A = A; s.Dskip = Dskip; s.BC = BC;
+    s.B = p.B; s.L = p.L; s.D = p.D; s.vec = p.vec;
+    if (!p.chunked) {
+        s.chunk = p.L; s.K = 1; s.h_init = h0; s.y = y; s.h_last = h_final; s.agg = 0;
+        e = ss::launch_scan(bf16, int(p.N), s, stream);
+        if (e != hipSuccess) return hip_fail(e);
+        return SS_OK;
+    }
+    float* h_end = reinterpret_cast<float*>(ws + p.off_hend);
+    float* dsum = reinterpret_cast<float*>(ws + p.off_dsum);
+    float* h_start = reinterpret_cast<float*>(ws + p.off_hstart);
+    s.chunk = p.chunk; s.K = int(p.K);
+    // 1. per-chunk aggregates
+    s.h_init = nullptr; s.y = nullptr; s.h_last = h_end; s.dsum = dsum; s.agg = 1; s.z = nullptr;
+    e = ss::launch_scan(bf16, int(p.N), s, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    // 2. carry across chunks
+    ss::CarryLaunch c{};
+    c.h_end = h_end; c.dsum = dsum; c.A = A; c.h_in = h0; c.h_start = h_start; c.h_out = nullptr;
+    c.B = p.B; c.D = p.D; c.K = int(p.K); c.reverse = 0;
+    e = ss::launch_carry(int(p.N), c, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    // 3. output pass from each chunk's true start state
+    s.z = z; s.h_init = h_start; s.y = y; s.h_last = h_final; s.dsum = nullptr; s.agg = 0;
+    e = ss::launch_scan(bf16, int(p.N), s, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    return SS_OK;
+}
+
+}  // extern "C"

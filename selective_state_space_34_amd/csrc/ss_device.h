@@ -1,0 +1,71 @@
+// Device helpers shared by the gfx950 selective-scan kernels.
+//
+// Numerics of the per-token step (page "3.2 선택적 스캔(Selective Scan) 알고리즘과
+// 정보의 압축 및 선별", §1.2 softplus step size, §2.1 exp discretisation) and of
+// the SiLU gate (note "상태공간 모델(SSM)과 Mamba 아키텍처", §3), written for the
+// CDNA4 transcendental unit: exp and log are the hardware base-2 instructions,
+// with natural-base constants folded into their operands.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ss {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Hardware 2^x (v_exp_f32).  Arguments here are <= 0 or moderate, results normal or 0.
+__device__ __forceinline__ float exp2_hw(float v) { return __builtin_amdgcn_exp2f(v); }
+// Hardware log2 (v_log_f32), used only for arguments in [1+1/32, 2].
+__device__ __forceinline__ float log2_hw(float v) { return __builtin_amdgcn_logf(v); }
+__device__ __forceinline__ float rcp_hw(float v) { return __builtin_amdgcn_rcpf(v); }
+
+// softplus(u) = log(1 + e^u) = max(u, 0) + log1p(w), w = e^{-|u|} in (0, 1].
+// log1p(w): for w < 1/32 a 4-term series (truncation < w^5/5, i.e. < 3e-8 relative);
+// otherwise log(1+w) from the hardware log2 of v = fl(1+w) plus the rounding
+// error w - (v - 1) of v (first-order correction, exact subtraction since v in [1,2]).
+__device__ __forceinline__ float softplus(float u) {
+    const float w = exp2_hw(-fabsf(u) * kLog2e);
+    const float ser = w * fmaf(w, fmaf(w, fmaf(w, -0.25f, 0.33333334f), -0.5f), 1.0f);
+    const float v = 1.0f + w;
+    const float lg = fmaf(log2_hw(v), kLn2, w - (v - 1.0f));
+    return fmaxf(u, 0.0f) + (w < 0.03125f ? ser : lg);
+}
+
+// sigmoid(z) = 1 / (1 + e^{-z}); e^{-z} = inf for z << 0 gives exactly 0.
+__device__ __forceinline__ float sigmoid(float z) { return rcp_hw(1.0f + exp2_hw(-z * kLog2e)); }
+
+// silu(z) = z * sigmoid(z): the gate of the output branch.
+__device__ __forceinline__ float silu(float z) { return z * sigmoid(z); }
+
+// ---- input element types -------------------------------------------------------------
+struct bf16_t {
+    uint16_t bits;
+};
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16_t v) { return __uint_as_float(uint32_t(v.bits) << 16); }
+
+// Load 8 consecutive elements (16-byte aligned for bf16, 32-byte for f32) as float.
+__device__ __forceinline__ void load8(const float* __restrict__ p, float (&o)[8]) {
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    const float4 b = *reinterpret_cast<const float4*>(p + 4);
+    o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
+    o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+}
+__device__ __forceinline__ void load8(const bf16_t* __restrict__ p, float (&o)[8]) {
+    const uint4 a = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        o[2 * i] = __uint_as_float(w[i] << 16);
+        o[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+}
+__device__ __forceinline__ void store8(float* __restrict__ p, const float (&v)[8]) {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+}
+
+}  // namespace ss

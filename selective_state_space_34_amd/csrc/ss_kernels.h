@@ -1,0 +1,48 @@
+// Internal launch interface between the C-ABI layer (ss_api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ss {
+
+struct ScanLaunch {
+    const void* x;
+    const void* dt_raw;
+    const void* z;          // nullable (no gate); ignored in AGG mode
+    const float* dt_bias;
+    const float* A;
+    const float* Dskip;
+    const float* BC;        // [B, L, 2N] float32 staging copy of B and C
+    const float* h_init;    // nullable; [B, K, D, N]
+    float* y;               // OUT mode
+    float* h_last;          // OUT: h_final (nullable); AGG: h_end [B, K, D, N]
+    float* dsum;            // AGG: Σδ per chunk [B, K, D]
+    int64_t B, L, D, chunk;
+    int K;
+    int vec;                // 1: L % 8 == 0, 8-step vector loads
+    int agg;                // 1: AGG mode
+};
+
+// Affine-pair carry across chunks (one workgroup per channel).  Chunk c's pair is
+// (exp(A Σδ_c), h_end_c); h_start_c is the state entering chunk c in scan order
+// (reverse = 1 scans chunks from last to first, for the adjoint), h_out the state
+// after the last one.  h_in, h_out nullable.
+struct CarryLaunch {
+    const float* h_end;     // [B, K, D, N]
+    const float* dsum;      // [B, K, D]
+    const float* A;         // [D, N]
+    const float* h_in;      // [B, D, N]
+    float* h_start;         // [B, K, D, N]
+    float* h_out;           // [B, D, N]
+    int64_t B, D;
+    int K;
+    int reverse;
+};
+
+hipError_t launch_bc_stage(int bf16, int N, const void* Bm, const void* Cm, float* BC, int64_t B,
+                           int64_t L, hipStream_t s);
+hipError_t launch_scan(int bf16, int N, const ScanLaunch& p, hipStream_t s);
+hipError_t launch_carry(int N, const CarryLaunch& p, hipStream_t s);
+
+}  // namespace ss

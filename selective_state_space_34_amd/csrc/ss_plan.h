@@ -1,0 +1,108 @@
+// Plan choice and workspace layout of the selective-scan library.  Host-only,
+// HIP-free: everything here depends on the dims alone, so the same dims always
+// give the same plan and the same workspace size.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "ss.h"
+
+namespace ss {
+
+struct Plan {
+    int64_t B, L, D, N;
+    int in_dtype;
+    int chunked;     // forward: 0 = single pass, 1 = chunked; backward: always 1
+    int64_t chunk;   // steps per chunk (multiple of 8 unless chunk == L)
+    int64_t K;       // number of chunks
+    int vec;         // L % 8 == 0: 8-step vector loads
+    // workspace carving (byte offsets, 256-aligned)
+    size_t off_bc, off_hend, off_dsum, off_hstart, off_gend, off_gstart, off_red;
+    size_t red_bytes;
+    size_t ws_total;
+};
+
+constexpr int64_t kMaxGridYZ = 65535;
+
+inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+inline bool mul_ok(int64_t a, int64_t b, int64_t lim) { return a > 0 && b > 0 && a <= lim / b; }
+
+// Target number of 64-lane waves for the sequence-parallel plans: four per SIMD
+// of a 256-CU, 4-SIMD part.
+constexpr int64_t kTargetWaves = 4096;
+// Channel-parallel forward alone when it already yields this many waves.
+constexpr int64_t kSingleWaves = 512;
+
+// Number of workgroups the reduction of the backward's per-block partials uses
+// (see ss_bwd.hip); the partial buffers are sized from it.
+int64_t bwd_reduce_blocks(const Plan& p);
+size_t bwd_partial_bytes(const Plan& p);
+
+inline int make_plan(const ss_dims& d, bool backward, Plan* out) {
+    Plan p{};
+    if (d.in_dtype != SS_F32 && d.in_dtype != SS_BF16) return SS_ERR_DTYPE;
+    if (d.plan != SS_PLAN_AUTO && d.plan != SS_PLAN_SINGLE && d.plan != SS_PLAN_CHUNKED)
+        return SS_ERR_DTYPE;
+    if (d.batch <= 0 || d.seqlen <= 0 || d.dim <= 0 || d.dstate <= 0) return SS_ERR_DIMS;
+    const int64_t N = d.dstate;
+    if (N != 1 && N != 2 && N != 4 && N != 8 && N != 16 && N != 32) return SS_ERR_DIMS;
+    if (d.chunk < 0 || (d.chunk % 8) != 0) return SS_ERR_DIMS;
+    const int64_t lim = int64_t(1) << 40;  // element count bound of any one array
+    if (!mul_ok(d.batch, d.dim, lim) || !mul_ok(d.batch * d.dim, d.seqlen, lim) ||
+        !mul_ok(d.batch * d.dstate, d.seqlen, lim) || !mul_ok(d.batch * d.dim, N, lim))
+        return SS_ERR_DIMS;
+    if (d.batch > kMaxGridYZ) return SS_ERR_DIMS;
+    p.B = d.batch; p.L = d.seqlen; p.D = d.dim; p.N = N; p.in_dtype = d.in_dtype;
+    p.vec = (p.L % 8) == 0;
+
+    const int64_t waves = (p.B * p.D + 63) / 64;
+    int chunked = backward ? 1 : 0;
+    if (!backward) {
+        if (d.plan == SS_PLAN_CHUNKED) chunked = 1;
+        else if (d.plan == SS_PLAN_SINGLE) chunked = 0;
+        else chunked = (waves < kSingleWaves && p.L > 512) ? 1 : 0;
+    }
+    int64_t chunk = p.L;
+    if (chunked) {
+        if (d.chunk > 0) {
+            chunk = d.chunk;
+        } else {
+            int64_t K = (kTargetWaves + waves - 1) / waves;
+            int64_t c = (p.L + K - 1) / K;
+            const int64_t cmin = backward ? 64 : 128;
+            if (c < cmin) c = cmin;
+            chunk = (c + 7) / 8 * 8;
+        }
+        if (chunk > p.L) chunk = (p.L + 7) / 8 * 8;
+    }
+    p.chunked = chunked;
+    p.chunk = chunk;
+    p.K = (p.L + chunk - 1) / chunk;
+    if (p.K > kMaxGridYZ) return SS_ERR_DIMS;
+
+    size_t off = 0;
+    p.off_bc = off;
+    off = align256(off + size_t(p.B) * size_t(p.L) * size_t(2 * N) * sizeof(float));
+    p.off_hend = p.off_dsum = p.off_hstart = p.off_gend = p.off_gstart = p.off_red = 0;
+    p.red_bytes = 0;
+    if (chunked) {
+        const size_t st = size_t(p.B) * size_t(p.K) * size_t(p.D) * size_t(N) * sizeof(float);
+        const size_t sm = size_t(p.B) * size_t(p.K) * size_t(p.D) * sizeof(float);
+        p.off_hend = off; off = align256(off + st);
+        p.off_dsum = off; off = align256(off + sm);
+        p.off_hstart = off; off = align256(off + st);
+        if (backward) {
+            p.off_gend = off; off = align256(off + st);
+            p.off_gstart = off; off = align256(off + st);
+            p.red_bytes = bwd_partial_bytes(p);
+            p.off_red = off; off = align256(off + p.red_bytes);
+        }
+    }
+    p.ws_total = off;
+    *out = p;
+    return SS_OK;
+}
+
+}  // namespace ss

@@ -1,0 +1,129 @@
+"""C-ABI library: it loads, exports every symbol include/ss.h declares, and rejects
+bad arguments with the documented codes before launching anything.
+
+These run without a GPU: every call here fails validation, which happens before
+the library's first HIP call.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import selective_state_space_34_amd as ss
+from selective_state_space_34_amd import _build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if _build.stale():
+        _build.build()
+    return ss.load()
+
+
+def header_functions():
+    txt = open(os.path.join(ROOT, "include", "ss.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(ss_\w+)\s*\(", txt, flags=re.M)))
+
+
+def test_exports_match_header(lib):
+    names = header_functions()
+    assert set(names) == set(ss.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), f"missing export {n}"
+
+
+def test_version_and_strerror(lib):
+    assert lib.ss_version() == (0 << 16) | 1
+    for code in ss.ERRORS:
+        assert len(lib.ss_strerror(code)) > 0
+    assert b"unknown" in lib.ss_strerror(12345)
+
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: every call below fails validation first
+
+
+def _fwd(lib, dims, ptrs=None, ws=None, wbytes=0):
+    p = [ctypes.c_void_p(FAKE)] * 11 if ptrs is None else ptrs
+    return lib.ss_fwd(None if dims is None else ctypes.byref(dims), *p,
+                      ws, ctypes.c_size_t(wbytes), None)
+
+
+def test_fwd_validation(lib):
+    good = ss.make_dims(2, 64, 32, 16, ss.SS_F32)
+    assert _fwd(lib, None) == -1
+    for bad in (ss.make_dims(0, 64, 32, 16), ss.make_dims(2, 0, 32, 16), ss.make_dims(2, 64, -1, 16),
+                ss.make_dims(2, 64, 32, 3), ss.make_dims(2, 64, 32, 64), ss.make_dims(2, 64, 32, 0),
+                ss.make_dims(2, 64, 32, 16, chunk=12), ss.make_dims(2, 64, 32, 16, chunk=-8),
+                ss.make_dims(1 << 20, 1 << 20, 1 << 20, 16)):
+        assert _fwd(lib, bad) == -2
+    assert _fwd(lib, ss.make_dims(2, 64, 32, 16, in_dtype=7)) == -3
+    assert _fwd(lib, ss.make_dims(2, 64, 32, 16, plan=9)) == -3
+    # required pointers
+    for i in (0, 1, 2, 3, 4, 5, 6, 9):
+        p = [ctypes.c_void_p(FAKE)] * 11
+        p[i] = None
+        assert _fwd(lib, good, p) == -1, i
+    # optional pointers (z, h0, h_final) may be NULL: the call then reaches the workspace check
+    p = [ctypes.c_void_p(FAKE)] * 11
+    p[7] = p[8] = p[10] = None
+    assert _fwd(lib, good, p) == -5
+    # alignment
+    for i in range(11):
+        p = [ctypes.c_void_p(FAKE)] * 11
+        p[i] = ctypes.c_void_p(FAKE + 4)
+        assert _fwd(lib, good, p) == -4, i
+    # workspace
+    need = ss.workspace_size(good)
+    assert need > 0
+    assert _fwd(lib, good, ws=None, wbytes=0) == -5
+    assert _fwd(lib, good, ws=ctypes.c_void_p(FAKE), wbytes=need - 1) == -5
+    assert _fwd(lib, good, ws=ctypes.c_void_p(FAKE + 8), wbytes=need) == -4
+
+
+def test_workspace_sizes(lib):
+    # single pass: staging copy of B and C only
+    d = ss.make_dims(8, 2048, 5120, 16, ss.SS_BF16, ss.SS_PLAN_SINGLE)
+    assert ss.workspace_size(d) == 8 * 2048 * 32 * 4
+    # chunked: staging + two state buffers + chunk sums, deterministic for the dims
+    d = ss.make_dims(1, 1 << 20, 256, 16, ss.SS_BF16, ss.SS_PLAN_CHUNKED, 1024)
+    K = 1024
+    st = 1 * K * 256 * 16 * 4
+    assert ss.workspace_size(d) == (1 << 20) * 32 * 4 + 2 * st + K * 256 * 4
+    assert ss.workspace_size(d) == ss.workspace_size(d)
+    n = ctypes.c_size_t()
+    assert lib.ss_fwd_workspace_size(None, ctypes.byref(n)) == -1
+    assert lib.ss_fwd_workspace_size(ctypes.byref(d), None) == -1
+    assert lib.ss_bwd_workspace_size(ctypes.byref(ss.make_dims(1, 1, 1, 5)), ctypes.byref(n)) == -2
+
+
+def test_bwd_validation(lib):
+    good = ss.make_dims(2, 64, 32, 16, ss.SS_F32)
+    F = ctypes.c_void_p(FAKE)
+    # x dt_raw dt_bias A Bm Cm Dskip | z h0 | dy dh_final | dx ddt_raw ddt_bias dA dB dC dD | dz dh0
+    args = [F] * 7 + [None, None] + [F, None] + [F] * 7 + [None, None]
+
+    def call(dims, a, ws=None, wbytes=0):
+        return lib.ss_bwd(None if dims is None else ctypes.byref(dims), *a, ws,
+                          ctypes.c_size_t(wbytes), None)
+    assert call(None, args) == -1
+    assert call(ss.make_dims(2, 64, 32, 7), args) == -2
+    a = list(args)
+    a[9] = None  # dy
+    assert call(good, a) == -1
+    # z given but dz missing; h0 given but dh0 missing
+    a = list(args)
+    a[7] = F
+    assert call(good, a) == -1
+    a = list(args)
+    a[8] = F
+    assert call(good, a) == -1
+    # dz given without z
+    a = list(args)
+    a[7] = None
+    a[18] = F
+    assert call(good, a) == -1
+    assert call(good, args) == -5
