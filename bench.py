@@ -1,0 +1,205 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X selective-scan forward (one GPU).
+
+One step = one ss_fwd call over one batch of synthetic input already resident in
+HBM: B/C staging + the fused scan (softplus step size, exp discretisation,
+recurrence, readout, D skip, SiLU gate), i.e. every forward row of the hot path.
+Default workload: S6 fwd + gate, bf16 x/z/dt_raw/B/C, fp32 A/D/dt_bias/state/y,
+B=8 L=2048 D=5120 N=16.
+
+Prints ONE JSON line on stdout (everything else goes to stderr):
+  value        B·L·D elements/s over the timed steps
+  roofline     the scan kernel against its binding roof (ALU), with the
+               HBM view (minimum bytes / time vs 8 TB/s) beside it
+  cpu_baseline the fp64 C oracle on a bounded sample of the same workload, host cores
+"""
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+# ALU roof: 256 CUs x 4 SIMDs x 16 fp32 lanes x 2.4 GHz = 39.32e12 VALU lane-slots/s
+# (packed fp32 is not used; transcendentals issue at half rate = 2 slots each).
+ALU_PEAK_TSLOTS = 256 * 4 * 16 * 2.4e9 / 1e12
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def min_bytes(w, s_in):
+    """Algorithmic HBM bytes of one forward: read x, dt_raw (, z), B, C and parameters,
+    write y (the (B,L,D,N) state and Ā/B̄ are never materialised)."""
+    BLD = w.batch * w.seqlen * w.dim
+    n_in = 3 if w.gate else 2
+    rd = n_in * BLD * s_in + 2 * w.batch * w.dstate * w.seqlen * s_in
+    rd += w.dim * w.dstate * 4 + 2 * w.dim * 4
+    wr = BLD * 4 + (w.batch * w.dim * w.dstate * 4 if w.h_final else 0)
+    return rd + wr
+
+
+def alu_slots_per_elem(w):
+    """Algorithmic VALU lane-slots per (b,t,d) element (transcendental = 2 slots).
+    Per state: exp (2) + δ·A, δx·B, state fma, readout fma (4)  -> 6 x N.
+    Per element: softplus 5 VALU + 2 trans; δ·x 1; D·x fma 1; gate 4 VALU + 2 trans (if any);
+    bf16 widening 1 per bf16 input tensor."""
+    per_state = 6 * w.dstate
+    elem = 5 + 2 * 2 + 1 + 1
+    if w.gate:
+        elem += 4 + 2 * 2
+    if w.dtype == "bf16":
+        elem += 3 if w.gate else 2
+    return per_state + elem
+
+
+def cpu_baseline(w, inp, budget_s=4.0):
+    """Time the fp64 C oracle (as it stands) on a growing sample of channels until
+    one run takes about budget_s seconds of wall time on all host threads."""
+    from oracle import cref
+    threads = cref.threads(0)
+    C = w.batch * w.dim
+    n = max(1, min(C, 64))
+    rng = np.random.default_rng(0)
+    args = (inp.x, inp.dt_raw, inp.dt_bias, inp.A, inp.Bm, inp.Cm, inp.Dskip)
+    while True:
+        chans = np.sort(rng.choice(C, n, replace=False))
+        t0 = time.perf_counter()
+        cref.fwd(*args, z=inp.z if w.gate else None, chans=chans, want_h_final=False)
+        dt = time.perf_counter() - t0
+        if dt >= budget_s / 4 or n == C:
+            break
+        n = min(C, int(n * max(2.0, budget_s / max(dt, 1e-3) / 2)))
+    elems = n * w.seqlen
+    return {"value": elems / dt, "unit": "elem/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n} of {C} channels x full L={w.seqlen} (B*L*D elements {elems}), "
+                      f"{dt:.2f} s wall on {threads} OpenMP threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c2", help="c0..c4 (default c2, D=5120 forward)")
+    ap.add_argument("--plan", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also launch one device copy of this many MiB (HBM counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the scan shards by batch/channel with no exchange in the forward; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import selective_state_space_34_amd as ss
+    from gen import workload, workload_inputs
+
+    w = workload(args.workload)
+    log(f"[bench] workload {w.name}: {w.label}")
+    t0 = time.perf_counter()
+    inp = workload_inputs(w, with_dy=False)
+    log(f"[bench] inputs generated in {time.perf_counter() - t0:.1f}s")
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    dev = torch.device("cuda:0")
+    t_in = lambda a: torch.from_numpy(a).to(dt).to(dev)
+    t32 = lambda a: torch.from_numpy(a).to(dev)
+    x, dtr, Bm, Cm = t_in(inp.x), t_in(inp.dt_raw), t_in(inp.Bm), t_in(inp.Cm)
+    z = t_in(inp.z) if w.gate else None
+    dtb, A, Dk = t32(inp.dt_bias), t32(inp.A), t32(inp.Dskip)
+    y = torch.empty((w.batch, w.dim, w.seqlen), dtype=torch.float32, device=dev)
+    hf = torch.empty((w.batch, w.dim, w.dstate), dtype=torch.float32, device=dev) if w.h_final else None
+    dims = ss.make_dims(w.batch, w.seqlen, w.dim, w.dstate,
+                        ss.SS_BF16 if w.dtype == "bf16" else ss.SS_F32, args.plan, 0)
+    ws = torch.empty(max(ss.workspace_size(dims), 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        ss.ss_fwd(x, dtr, dtb, A, Bm, Cm, Dk, z=z, y=y, h_final=hf, workspace=ws,
+                  plan=args.plan, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if args.calib_copy_mib:
+        nb = args.calib_copy_mib << 20
+        a = torch.empty(nb, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy of {nb} bytes done")
+
+    # timed region: K steps, HIP events around every step on the stream the kernels run on
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for e0, e1 in evs:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    per = np.array([e0.elapsed_time(e1) for e0, e1 in evs]) * 1e-3  # seconds per launch
+
+    elems = w.batch * w.seqlen * w.dim
+    s_in = 2 if w.dtype == "bf16" else 4
+    mb = min_bytes(w, s_in)
+    t_avg = float(per.mean())
+    value = elems * args.steps / wall
+    slots = elems * alu_slots_per_elem(w)
+    alu_achieved = slots / t_avg / 1e12
+    hbm_achieved = mb / t_avg / 1e9
+    log(f"[bench] per-step event time avg {t_avg * 1e6:.1f} us (min {per.min() * 1e6:.1f}, "
+        f"max {per.max() * 1e6:.1f}); wall {wall / args.steps * 1e6:.1f} us/step")
+    log(f"[bench] HBM view: {mb / 1e6:.1f} MB min bytes -> {hbm_achieved:.0f} GB/s "
+        f"({hbm_achieved / HBM_PEAK_GBPS:.3f} of 8 TB/s)")
+    log(f"[bench] ALU view: {alu_slots_per_elem(w)} slots/elem -> {alu_achieved:.2f} T slots/s "
+        f"({alu_achieved / ALU_PEAK_TSLOTS:.3f} of {ALU_PEAK_TSLOTS:.2f})")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle baseline ...")
+        cpu = cpu_baseline(w, inp)
+        log(f"[bench] cpu baseline {cpu['value']:.3e} elem/s ({cpu['sample']})")
+
+    out = {
+        "metric": "selective-scan fwd B·L·D elements/s; achieved HBM GB/s vs MI355X peak",
+        "value": value,
+        "unit": "elem/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: {w.label}", "batch": w.batch, "seqlen": w.seqlen,
+                   "dim": w.dim, "dstate": w.dstate, "in_dtype": w.dtype, "gate": w.gate,
+                   "plan": args.plan},
+        "roofline": {"bound": "alu", "achieved": alu_achieved, "peak": ALU_PEAK_TSLOTS,
+                     "unit": "T VALU-slot/s", "frac": alu_achieved / ALU_PEAK_TSLOTS,
+                     "traffic": None,
+                     "kernel": "ss_fwd (bc_stage + scan)", "launch_us": t_avg * 1e6,
+                     "slots_per_elem": alu_slots_per_elem(w)},
+        "hbm": {"min_bytes": mb, "achieved_gbps": hbm_achieved, "peak_gbps": HBM_PEAK_GBPS,
+                "frac": hbm_achieved / HBM_PEAK_GBPS},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
