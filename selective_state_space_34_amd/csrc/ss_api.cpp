@@ -92,7 +92,7 @@ int ss_fwd(const ss_dims* dims, const void* x, const void* dt_raw, const float* 
     s.B = p.B; s.L = p.L; s.D = p.D; s.vec = p.vec;
     if (!p.chunked) {
         s.chunk = p.L; s.K = 1; s.h_init = h0; s.y = y; s.h_last = h_final; s.agg = 0;
-        e = ss::launch_scan(bf16, int(p.N), s, stream);
+        e = p.quad ? ss::launch_scanq(bf16, int(p.N), s, stream) : ss::launch_scan(bf16, int(p.N), s, stream);
         if (e != hipSuccess) return hip_fail(e);
         return SS_OK;
     }
@@ -102,7 +102,7 @@ int ss_fwd(const ss_dims* dims, const void* x, const void* dt_raw, const float* 
     s.chunk = p.chunk; s.K = int(p.K);
     // 1. per-chunk aggregates
     s.h_init = nullptr; s.y = nullptr; s.h_last = h_end; s.dsum = dsum; s.agg = 1; s.z = nullptr;
-    e = ss::launch_scan(bf16, int(p.N), s, stream);
+    e = p.quad ? ss::launch_scanq(bf16, int(p.N), s, stream) : ss::launch_scan(bf16, int(p.N), s, stream);
     if (e != hipSuccess) return hip_fail(e);
     // 2. carry across chunks
     ss::CarryLaunch c{};
@@ -112,7 +112,7 @@ int ss_fwd(const ss_dims* dims, const void* x, const void* dt_raw, const float* 
     if (e != hipSuccess) return hip_fail(e);
     // 3. output pass from each chunk's true start state
     s.z = z; s.h_init = h_start; s.y = y; s.h_last = h_final; s.dsum = nullptr; s.agg = 0;
-    e = ss::launch_scan(bf16, int(p.N), s, stream);
+    e = p.quad ? ss::launch_scanq(bf16, int(p.N), s, stream) : ss::launch_scan(bf16, int(p.N), s, stream);
     if (e != hipSuccess) return hip_fail(e);
     return SS_OK;
 }

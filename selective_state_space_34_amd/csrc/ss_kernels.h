@@ -43,6 +43,8 @@ struct CarryLaunch {
 hipError_t launch_bc_stage(int bf16, int N, const void* Bm, const void* Cm, float* BC, int64_t B,
                            int64_t L, hipStream_t s);
 hipError_t launch_scan(int bf16, int N, const ScanLaunch& p, hipStream_t s);
+// quad-split layout (N in {4, 8, 16, 32}, L % 8 == 0)
+hipError_t launch_scanq(int bf16, int N, const ScanLaunch& p, hipStream_t s);
 hipError_t launch_carry(int N, const CarryLaunch& p, hipStream_t s);
 
 }  // namespace ss

@@ -17,6 +17,7 @@ struct Plan {
     int64_t chunk;   // steps per chunk (multiple of 8 unless chunk == L)
     int64_t K;       // number of chunks
     int vec;         // L % 8 == 0: 8-step vector loads
+    int quad;        // forward uses the quad-split kernel (N >= 4 and vec)
     // workspace carving (byte offsets, 256-aligned)
     size_t off_bc, off_hend, off_dsum, off_hstart, off_gend, off_gstart, off_red;
     size_t red_bytes;
@@ -32,8 +33,9 @@ inline bool mul_ok(int64_t a, int64_t b, int64_t lim) { return a > 0 && b > 0 &&
 // Target number of 64-lane waves for the sequence-parallel plans: four per SIMD
 // of a 256-CU, 4-SIMD part.
 constexpr int64_t kTargetWaves = 4096;
-// Channel-parallel forward alone when it already yields this many waves.
-constexpr int64_t kSingleWaves = 512;
+// Single pass when one pass already yields two waves per SIMD (a chunked pass costs a
+// second sweep for the chunk aggregates).
+constexpr int64_t kSingleWaves = 2048;
 
 // Number of workgroups the reduction of the backward's per-block partials uses
 // (see ss_bwd.hip); the partial buffers are sized from it.
@@ -56,8 +58,10 @@ inline int make_plan(const ss_dims& d, bool backward, Plan* out) {
     if (d.batch > kMaxGridYZ) return SS_ERR_DIMS;
     p.B = d.batch; p.L = d.seqlen; p.D = d.dim; p.N = N; p.in_dtype = d.in_dtype;
     p.vec = (p.L % 8) == 0;
+    p.quad = p.vec && N >= 4;
 
-    const int64_t waves = (p.B * p.D + 63) / 64;
+    // 64-lane waves of one pass: a lane per channel, or a quad of lanes per channel
+    const int64_t waves = p.quad ? (p.B * p.D + 15) / 16 : (p.B * p.D + 63) / 64;
     int chunked = backward ? 1 : 0;
     if (!backward) {
         if (d.plan == SS_PLAN_CHUNKED) chunked = 1;

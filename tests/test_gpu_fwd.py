@@ -84,6 +84,12 @@ EDGE = [
     (2, 2048, 96, 16, "bf16", True, True, 2, 128),
     (1, 4099, 64, 16, "f32", True, True, 2, 256),   # ragged tail in the last chunk
     (2, 520, 300, 16, "f32", True, True, 1, 0),
+    # quad-split kernel: N = 4 (one state per lane), chunk not a multiple of the 32-step
+    # tile, float32 inputs, D not a multiple of 64, short chunks that are all tail
+    (2, 1024, 40, 4, "f32", True, True, 0, 0),
+    (1, 4000, 70, 16, "bf16", True, True, 2, 40),
+    (3, 96, 200, 16, "f32", False, True, 2, 16),
+    (1, 2056, 33, 32, "bf16", True, True, 2, 264),
 ]
 
 
