@@ -117,4 +117,69 @@ int ss_fwd(const ss_dims* dims, const void* x, const void* dt_raw, const float* 
     return SS_OK;
 }
 
+int ss_bwd(const ss_dims* dims, const void* x, const void* dt_raw, const float* dt_bias,
+           const float* A, const void* Bm, const void* Cm, const float* Dskip, const void* z,
+           const float* h0, const float* dy, const float* dh_final, float* dx, float* ddt_raw,
+           float* ddt_bias, float* dA, float* dB, float* dC, float* dD, float* dz, float* dh0,
+           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!dims) return SS_ERR_NULL;
+    ss::Plan p;
+    const int rc = ss::make_plan(*dims, true, &p);
+    if (rc != SS_OK) return rc;
+    if (!x || !dt_raw || !dt_bias || !A || !Bm || !Cm || !Dskip || !dy) return SS_ERR_NULL;
+    if (!dx || !ddt_raw || !ddt_bias || !dA || !dB || !dC || !dD) return SS_ERR_NULL;
+    if ((z != nullptr) != (dz != nullptr)) return SS_ERR_NULL;
+    if ((h0 != nullptr) != (dh0 != nullptr)) return SS_ERR_NULL;
+    const void* req[] = {x, dt_raw, dt_bias, A, Bm, Cm, Dskip, dy, dx, ddt_raw, ddt_bias, dA, dB, dC, dD};
+    for (const void* q : req)
+        if (!aligned16(q)) return SS_ERR_ALIGN;
+    const void* opt[] = {z, h0, dh_final, dz, dh0};
+    for (const void* q : opt)
+        if (q && !aligned16(q)) return SS_ERR_ALIGN;
+    if (!workspace || workspace_bytes < p.ws_total) return SS_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return SS_ERR_ALIGN;
+
+    char* ws = static_cast<char*>(workspace);
+    float* BC = reinterpret_cast<float*>(ws + p.off_bc);
+    const int bf16 = p.in_dtype == SS_BF16;
+    hipError_t e = ss::launch_bc_stage(bf16, int(p.N), Bm, Cm, BC, p.B, p.L, stream);
+    if (e != hipSuccess) return hip_fail(e);
+
+    ss::BwdLaunch bl{};
+    bl.x = x; bl.dt_raw = dt_raw; bl.z = z; bl.dy = dy; bl.dt_bias = dt_bias; bl.A = A;
+    bl.Dskip = Dskip; bl.BC = BC;
+    bl.h_end = reinterpret_cast<float*>(ws + p.off_hend);
+    bl.rev_end = reinterpret_cast<float*>(ws + p.off_gend);
+    bl.dsum = reinterpret_cast<float*>(ws + p.off_dsum);
+    bl.dbc_part = reinterpret_cast<float*>(ws + p.off_red);
+    bl.ddt_part = reinterpret_cast<float*>(ws + p.off_red + ss::align256(
+        size_t(p.B) * size_t(ss::bwd_reduce_blocks(p)) * size_t(p.L) * size_t(2 * p.N) * 4));
+    bl.dx = dx; bl.ddt_raw = ddt_raw; bl.dz = dz; bl.dA = dA; bl.dB = dB; bl.dC = dC; bl.dD = dD;
+    bl.ddt_bias = ddt_bias;
+    bl.B = p.B; bl.L = p.L; bl.D = p.D; bl.N = p.N; bl.chunk = p.chunk; bl.K = int(p.K);
+    bl.vec = p.vec;
+    // 1. chunk aggregates (forward and reverse pairs)
+    bl.stage = 0;
+    e = ss::launch_bwd(bf16, bl, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    // 2. carries, both in place: chunk start states from h0; adjoints entering each chunk
+    //    from the right, from dh_final, whose final value is dh0
+    ss::CarryLaunch c{};
+    c.dsum = bl.dsum; c.A = A; c.B = p.B; c.D = p.D; c.K = int(p.K);
+    c.h_end = bl.h_end; c.h_start = bl.h_end; c.h_in = h0; c.h_out = nullptr; c.reverse = 0;
+    e = ss::launch_carry(int(p.N), c, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    c.h_end = bl.rev_end; c.h_start = bl.rev_end; c.h_in = dh_final; c.h_out = dh0; c.reverse = 1;
+    e = ss::launch_carry(int(p.N), c, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    // 3. final pass: recomputed states, adjoint sweep, per-element gradients, partials
+    bl.stage = 1;
+    e = ss::launch_bwd(bf16, bl, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    // 4. reductions into dB, dC, dA, dD, ddt_bias
+    e = ss::launch_bwd_reduce(bl, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    return SS_OK;
+}
+
 }  // extern "C"

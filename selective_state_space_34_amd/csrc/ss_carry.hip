@@ -47,11 +47,11 @@ __device__ __forceinline__ void wave_scan_affine(float& P, float& H) {
 }
 
 template <int N>
-__global__ __launch_bounds__(1024) void carry_kernel(const float* __restrict__ h_end,
+__global__ __launch_bounds__(1024) void carry_kernel(const float* h_end,
                                                      const float* __restrict__ dsum,
                                                      const float* __restrict__ A,
                                                      const float* __restrict__ h_in,
-                                                     float* __restrict__ h_start,
+                                                     float* h_start,
                                                      float* __restrict__ h_out, int64_t D, int K,
                                                      int m, int reverse) {
     __shared__ float wP[16][N];
@@ -107,8 +107,10 @@ __global__ __launch_bounds__(1024) void carry_kernel(const float* __restrict__ h
         const float s = dsum[base];
 #pragma unroll
         for (int n = 0; n < N; ++n) {
+            // read before write: h_start may alias h_end (each lane owns its chunks)
+            const float he = h_end[base * N + n];
             h_start[base * N + n] = st[n];
-            st[n] = fmaf(exp2_hw(A2[n] * s), st[n], h_end[base * N + n]);
+            st[n] = fmaf(exp2_hw(A2[n] * s), st[n], he);
         }
     }
     if (h_out && j0 < K && j1 == K) {

@@ -40,11 +40,44 @@ struct CarryLaunch {
     int reverse;
 };
 
+// Backward launches (quad layout).  stage 0: chunk aggregates (h_end, rev_end, dsum);
+// stage 1: final pass (h_end holds chunk start states on entry and dA partials on exit,
+// rev_end holds the adjoints entering each chunk from the right).
+struct BwdLaunch {
+    const void* x;
+    const void* dt_raw;
+    const void* z;
+    const float* dy;
+    const float* dt_bias;
+    const float* A;
+    const float* Dskip;
+    const float* BC;
+    float* h_end;      // [B, K, D, N]
+    float* rev_end;    // [B, K, D, N]
+    float* dsum;       // [B, K, D]
+    float* dbc_part;   // [B, ceil(D/16), L, 2N]
+    float* ddt_part;   // [B, K, D, 2]
+    float* dx;
+    float* ddt_raw;
+    float* dz;
+    float* dA;
+    float* dB;
+    float* dC;
+    float* dD;
+    float* ddt_bias;
+    int64_t B, L, D, N, chunk;
+    int K;
+    int vec;
+    int stage;
+};
+
 hipError_t launch_bc_stage(int bf16, int N, const void* Bm, const void* Cm, float* BC, int64_t B,
                            int64_t L, hipStream_t s);
 hipError_t launch_scan(int bf16, int N, const ScanLaunch& p, hipStream_t s);
 // quad-split layout (N in {4, 8, 16, 32}, L % 8 == 0)
 hipError_t launch_scanq(int bf16, int N, const ScanLaunch& p, hipStream_t s);
 hipError_t launch_carry(int N, const CarryLaunch& p, hipStream_t s);
+hipError_t launch_bwd(int bf16, const BwdLaunch& p, hipStream_t s);
+hipError_t launch_bwd_reduce(const BwdLaunch& p, hipStream_t s);
 
 }  // namespace ss

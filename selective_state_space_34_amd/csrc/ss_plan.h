@@ -69,7 +69,12 @@ inline int make_plan(const ss_dims& d, bool backward, Plan* out) {
         else chunked = (waves < kSingleWaves && p.L > 512) ? 1 : 0;
     }
     int64_t chunk = p.L;
-    if (chunked) {
+    if (backward) {
+        // 16-step tiles, at most four per chunk (tile start states live in LDS)
+        if (d.chunk > 0 && (d.chunk % 16 != 0 || d.chunk > 64)) return SS_ERR_DIMS;
+        chunk = d.chunk > 0 ? d.chunk : 64;
+        if (chunk > p.L) chunk = (p.L + 15) / 16 * 16;
+    } else if (chunked) {
         if (d.chunk > 0) {
             chunk = d.chunk;
         } else {
