@@ -4,6 +4,7 @@
 One step = one ss_fwd call over one batch of synthetic input already resident in
 HBM: B/C staging + the fused scan (softplus step size, exp discretisation,
 recurrence, readout, D skip, SiLU gate), i.e. every forward row of the hot path.
+For the fwd+bwd workload (--workload c4) a step is ss_fwd followed by ss_bwd.
 Default workload: S6 fwd + gate, bf16 x/z/dt_raw/B/C, fp32 A/D/dt_bias/state/y,
 B=8 L=2048 D=5120 N=16.
 
@@ -43,6 +44,17 @@ def min_bytes(w, s_in):
     rd = n_in * BLD * s_in + 2 * w.batch * w.dstate * w.seqlen * s_in
     rd += w.dim * w.dstate * 4 + 2 * w.dim * 4
     wr = BLD * 4 + (w.batch * w.dim * w.dstate * 4 if w.h_final else 0)
+    return rd + wr
+
+
+def bwd_min_bytes(w, s_in):
+    """Algorithmic HBM bytes of one backward: read x, dt_raw, z (s_in), dy (4), B, C and the
+    parameters; write dx, dt_raw-grad, dz (4 each), dB, dC (4·B·N·L each), dA, dD, ddt_bias."""
+    BLD = w.batch * w.seqlen * w.dim
+    BNL = w.batch * w.dstate * w.seqlen
+    n_in = 3 if w.gate else 2
+    rd = n_in * BLD * s_in + BLD * 4 + 2 * BNL * s_in + w.dim * w.dstate * 4 + 2 * w.dim * 4
+    wr = n_in * BLD * 4 + 2 * BNL * 4 + w.dim * w.dstate * 4 + 2 * w.dim * 4
     return rd + wr
 
 
@@ -108,7 +120,7 @@ def main():
     w = workload(args.workload)
     log(f"[bench] workload {w.name}: {w.label}")
     t0 = time.perf_counter()
-    inp = workload_inputs(w, with_dy=False)
+    inp = workload_inputs(w)
     log(f"[bench] inputs generated in {time.perf_counter() - t0:.1f}s")
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     dev = torch.device("cuda:0")
@@ -123,10 +135,22 @@ def main():
                         ss.SS_BF16 if w.dtype == "bf16" else ss.SS_F32, args.plan, 0)
     ws = torch.empty(max(ss.workspace_size(dims), 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
+    if w.backward:
+        dy = t32(inp.dy)
+        wsb = torch.empty(ss.workspace_size(dims, backward=True), dtype=torch.uint8, device=dev)
+        grads = ss.ss_bwd(x, dtr, dtb, A, Bm, Cm, Dk, dy, z=z)
 
-    def step():
+    def fwd_call():
         ss.ss_fwd(x, dtr, dtb, A, Bm, Cm, Dk, z=z, y=y, h_final=hf, workspace=ws,
                   plan=args.plan, stream=stream)
+
+    def bwd_call():
+        ss.ss_bwd(x, dtr, dtb, A, Bm, Cm, Dk, dy, z=z, workspace=wsb, out=grads, stream=stream)
+
+    def step():
+        fwd_call()
+        if w.backward:
+            bwd_call()
 
     for _ in range(args.warmup):
         step()
@@ -150,7 +174,23 @@ def main():
         e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
-    per = np.array([e0.elapsed_time(e1) for e0, e1 in evs]) * 1e-3  # seconds per launch
+    per = np.array([e0.elapsed_time(e1) for e0, e1 in evs]) * 1e-3  # seconds per step
+    split = None
+    if w.backward:
+        # the forward alone, timed the same way, so the backward's share is known
+        fe = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        for e0, e1 in fe:
+            e0.record(stream)
+            fwd_call()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        tf = float(np.mean([e0.elapsed_time(e1) for e0, e1 in fe])) * 1e-3
+        split = {"fwd_us": tf * 1e6, "bwd_us": (float(per.mean()) - tf) * 1e6,
+                 "bwd_min_bytes": bwd_min_bytes(w, 2 if w.dtype == "bf16" else 4)}
+        log(f"[bench] fwd {tf * 1e6:.1f} us, bwd {(float(per.mean()) - tf) * 1e6:.1f} us "
+            f"(bwd min bytes {split['bwd_min_bytes'] / 1e6:.1f} MB -> "
+            f"{split['bwd_min_bytes'] / (float(per.mean()) - tf) / 1e9:.0f} GB/s)")
 
     elems = w.batch * w.seqlen * w.dim
     s_in = 2 if w.dtype == "bf16" else 4
@@ -198,6 +238,8 @@ def main():
                 "frac": hbm_achieved / HBM_PEAK_GBPS},
         "cpu_baseline": cpu,
     }
+    if split:
+        out["fwd_bwd_split"] = split
     print(json.dumps(out), flush=True)
 
 

@@ -27,6 +27,9 @@ namespace {
 
 constexpr int kTile = 32;      // steps per tile
 constexpr int kPer = 8;        // steps prepared per lane (kTile / 4)
+// lane stride (floats) of the partial-readout area: 36 = 4 mod 32 puts the 16-byte
+// writes of 8 consecutive lanes on 8 disjoint groups of 4 banks
+constexpr int kPS = kTile + 4;
 constexpr int kChanPerBlock = 64;
 constexpr int kThreads = 256;  // 4 waves x 16 quads
 
@@ -40,6 +43,24 @@ __device__ __forceinline__ float quad_sum(float v) {
     v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xf, 0xf, false));  // [2,3,0,1]
     return v;
 }
+
+// B or C values of the lane's S states at one step (LDS -> VGPR)
+template <int S>
+struct Row {
+    float v[S];
+    __device__ __forceinline__ void load(const float* p) {
+        if constexpr (S % 4 == 0) {
+#pragma unroll
+            for (int q = 0; q < S; q += 4) {
+                const float4 a = *reinterpret_cast<const float4*>(p + q);
+                v[q] = a.x; v[q + 1] = a.y; v[q + 2] = a.z; v[q + 3] = a.w;
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < S; ++q) v[q] = p[q];
+        }
+    }
+};
 
 // raw (undecoded) storage of 8 input elements
 template <typename Tin> struct Raw8;
@@ -81,8 +102,8 @@ __global__ __launch_bounds__(kThreads) void scanq_kernel(
     constexpr int N = 4 * S;
     constexpr int R = 2 * N;                      // floats per step in the B/C tile
     constexpr int TILE_F = kTile * R;             // floats per B/C tile
-    __shared__ float bc_lds[2][TILE_F];
-    __shared__ float part_lds[kAgg ? 1 : kThreads * kTile];
+    __shared__ __align__(16) float bc_lds[2][TILE_F];
+    __shared__ __align__(16) float part_lds[kAgg ? 1 : kThreads * kPS];
 
     const int tid = threadIdx.x;
     const int j = tid & 3;                        // state group / step block within the quad
@@ -133,7 +154,7 @@ __global__ __launch_bounds__(kThreads) void scanq_kernel(
     };
 
     if (n_tiles > 0) issue_loads(t_begin);
-    float* my_part = part_lds + (kAgg ? 0 : (tid & ~63) * kTile);  // wave-private area
+    float* my_part = part_lds + (kAgg ? 0 : (tid & ~63) * kPS);  // wave-private area
     const int lane = tid & 63;
 
     for (int64_t it = 0; it < n_tiles; ++it) {
@@ -160,19 +181,28 @@ __global__ __launch_bounds__(kThreads) void scanq_kernel(
             if (kAgg) dsum += dl[i];
         }
 
-        // recurrence over the 32 steps
+        // recurrence over the 32 steps; B/C of step t+1 are read from LDS during step t
         float part[kTile];
+        Row<S> bcur, ccur, bnxt, cnxt;
+        bnxt.load(buf + n0);
+        cnxt.load(buf + N + n0);
 #define SS_QSTEP(KK)                                                                        \
         _Pragma("unroll") for (int i = 0; i < kPer; ++i) {                                  \
             const int t = KK * kPer + i;                                                    \
+            bcur = bnxt;                                                                    \
+            ccur = cnxt;                                                                    \
+            if (t + 1 < kTile) {                                                            \
+                bnxt.load(buf + (t + 1) * R + n0);                                          \
+                cnxt.load(buf + (t + 1) * R + N + n0);                                      \
+            }                                                                               \
+            __builtin_amdgcn_sched_barrier(0); /* keep the next step's reads issued here */ \
             const float db = quad_bcast<KK>(dl[i]);                                         \
             const float xb = quad_bcast<KK>(dx[i]);                                         \
-            const float* bt = buf + t * R + n0;                                             \
             float acc = 0.0f;                                                               \
             _Pragma("unroll") for (int s = 0; s < S; ++s) {                                 \
                 const float abar = exp2_hw(db * A2[s]);                                     \
-                h[s] = fmaf(abar, h[s], xb * bt[s]);                                        \
-                if (!kAgg) acc = fmaf(bt[N + s], h[s], acc);                                \
+                h[s] = fmaf(abar, h[s], xb * bcur.v[s]);                                    \
+                if (!kAgg) acc = fmaf(ccur.v[s], h[s], acc);                                \
             }                                                                               \
             part[t] = acc;                                                                  \
         }
@@ -185,19 +215,23 @@ __global__ __launch_bounds__(kThreads) void scanq_kernel(
         if (!kAgg) {
             // partial readouts through the wave's LDS area: lane writes its 32, then
             // gathers the four partials of its own 8 steps
-            float* mine = my_part + lane * kTile;
+            float* mine = my_part + lane * kPS;
 #pragma unroll
             for (int q = 0; q < kTile; q += 4)
                 *reinterpret_cast<float4*>(mine + q) = make_float4(part[q], part[q + 1], part[q + 2], part[q + 3]);
-            __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): own-wave LDS writes done
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             float sum[kPer];
 #pragma unroll
             for (int i = 0; i < kPer; ++i) sum[i] = 0.0f;
             const int qbase = lane & ~3;
+            // lane j starts at source j (rotation): the 8 lanes served together then read
+            // 8 disjoint groups of 4 banks
 #pragma unroll
-            for (int src = 0; src < 4; ++src) {
-                const float* p = my_part + (qbase + src) * kTile + kPer * j;
+            for (int r = 0; r < 4; ++r) {
+                const int src = (j + r) & 3;
+                const float* p = my_part + (qbase + src) * kPS + kPer * j;
                 const float4 a = *reinterpret_cast<const float4*>(p);
                 const float4 c = *reinterpret_cast<const float4*>(p + 4);
                 sum[0] += a.x; sum[1] += a.y; sum[2] += a.z; sum[3] += a.w;
@@ -211,7 +245,9 @@ __global__ __launch_bounds__(kThreads) void scanq_kernel(
                 out[i] = s;
             }
             if (valid) store8(yr + t0 + kPer * j, out);
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         }
     }
 
