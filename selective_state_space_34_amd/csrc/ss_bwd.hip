@@ -173,7 +173,7 @@ __global__ __launch_bounds__(kBThreads) void bwd_agg_kernel(
     }
     dsum = qsum(dsum);
     if (valid) {
-        const int64_t aidx = (int64_t(b) * K + k) * D + d;
+        const int64_t aidx = (int64_t(b) * D + d) * K + k;
 #pragma unroll
         for (int s = 0; s < S; ++s) {
             const int n = j * S + s;
@@ -188,10 +188,10 @@ __global__ __launch_bounds__(kBThreads) void bwd_agg_kernel(
 
 // ---------------------------------------------------------------------------------------
 // 3. final pass.  grid (ceil(D/64), K, B), 256 threads.
-//   h_start [B,K,D,N]: state entering each chunk; overwritten with dA partials.
-//   q       [B,K,D,N]: adjoint entering each chunk from the right.
-//   dbc_part [B, G, L, 2N] (G = ceil(D/16)): per-wave sums over 16 channels of dB | dC.
-//   ddt_part [B, K, D, 2]: per-chunk dD and ddt_bias partials.
+//   h_start [B,D,K,N]: state entering each chunk; overwritten with dA partials.
+//   q       [B,D,K,N]: adjoint entering each chunk from the right.
+//   dbc_part [B, NB, L, 2N] (NB = ceil(D/64)): per-block sums over 64 channels of dB | dC.
+//   ddt_part [B, D, K, 2]: per-chunk dD and ddt_bias partials.
 // ---------------------------------------------------------------------------------------
 template <typename Tin, int S, bool kGate>
 __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(
@@ -203,9 +203,11 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(
     int64_t L, int64_t D, int Nr, int64_t chunk, int K, int vec) {
     constexpr int SQ = 4 * S;
     __shared__ __align__(16) float bc_lds[kBMaxTiles * kBT * 2 * SQ];
-    // per-wave scratch, LS floats per lane (quad reduce-scatter, then dB/dC transpose)
-    constexpr int LS = (8 * S > 32) ? 8 * S : 32;
+    // per-wave scratch, LS floats per lane (quad reduce-scatter, then dB/dC transpose);
+    // LS = 4 mod 32 keeps the 16-byte writes of 8 consecutive lanes on disjoint banks
+    constexpr int LS = ((8 * S > 32) ? 8 * S : 32) + 4;
     __shared__ __align__(16) float scr[kBThreads * LS];
+    __shared__ float comb[4 * 8 * SQ];   // wave totals of one 4-step batch
     // state at each 16-step tile start, [tile][s][thread]
     __shared__ float ck_lds[kBMaxTiles * S * kBThreads];
     const int tid = threadIdx.x;
@@ -223,10 +225,9 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(
     const int R = 2 * Nr;
     stage_bc(bc_lds, BC + (int64_t(b) * L + t0c) * R, nsteps * R, tid);
     float* wscr = scr + wave * 64 * LS;
-    const int64_t G = (D + 15) / 16;
-    const int64_t wg = int64_t(blockIdx.x) * 4 + wave;   // wave group (16 channels)
+    const int64_t NB = (D + kBChan - 1) / kBChan;        // channel blocks
 
-    const int64_t sidx = ((int64_t(b) * K + k) * D + d) * Nr;
+    const int64_t sidx = ((int64_t(b) * D + d) * K + k) * Nr;
     float A2[S], An[S], h[S], g[S], dA[S];
 #pragma unroll
     for (int s = 0; s < S; ++s) {
@@ -370,8 +371,7 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(
 
         // reverse sweep over the tile, in batches of 4 steps (one prepared block each)
         float pdx[kBT], pdd[kBT];
-        const int64_t gidx = int64_t(b) * G + wg;
-#define SS_RV_BATCH(KK)                                                                    \
+    #define SS_RV_BATCH(KK)                                                                    \
         {                                                                                  \
             float cB[kBPer][S], cC[kBPer][S];                                              \
             _Pragma("unroll") for (int i = kBPer - 1; i >= 0; --i) {                       \
@@ -402,36 +402,49 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(
                 pdx[tl] = px;                                                              \
                 pdd[tl] = pd;                                                              \
             }                                                                              \
-            /* dB | dC over the wave's 16 channels: transpose through LDS */               \
+            /* dB | dC over the block's 64 channels: each wave transposes its 16 channels  \
+               through its LDS area (per lane [type][step][state], lane stride LS), the    \
+               wave totals meet in `comb`, and one block partial per (b, t, n) is written  \
+               (fixed order: deterministic).                                              */ \
             float* mine = wscr + lane * LS;                                                \
             _Pragma("unroll") for (int i = 0; i < kBPer; ++i) {                            \
                 _Pragma("unroll") for (int s = 0; s < S; ++s) {                            \
-                    mine[i * 2 * S + s] = cB[i][s];                                        \
-                    mine[i * 2 * S + S + s] = cC[i][s];                                    \
+                    mine[i * S + s] = cB[i][s];                                            \
+                    mine[4 * S + i * S + s] = cC[i][s];                                    \
                 }                                                                          \
             }                                                                              \
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");                         \
             __builtin_amdgcn_wave_barrier();                                               \
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");                         \
-            /* totals: e = (type*4 + step)*SQ + n for e < 8*SQ; lane takes e = lane + 64r */ \
+            /* e = lane + 64r -> (state sp_, lane group jp, type ty, step st): each       \
+               32-lane half reads 32 distinct banks (LS = 4 mod 32)                       */ \
             _Pragma("unroll") for (int r = 0; r < (8 * SQ + 63) / 64; ++r) {               \
                 const int e = lane + 64 * r;                                               \
                 if (e < 8 * SQ) {                                                          \
-                    const int n = e % SQ;                                                  \
-                    const int st = (e / SQ) % 4;                                           \
-                    const int ty = e / (4 * SQ);                                           \
-                    const int jp = n / S, sp_ = n % S;                                     \
-                    const float* col = wscr + jp * LS + st * 2 * S + ty * S + sp_;         \
+                    const int sp_ = e % S;                                                 \
+                    const int jp = (e / S) % 4;                                            \
+                    const int ty = (e / (4 * S)) % 2;                                      \
+                    const int st = e / (8 * S);                                            \
+                    const float* col = wscr + jp * LS + ty * 4 * S + st * S + sp_;         \
                     float tot = 0.0f;                                                      \
                     _Pragma("unroll") for (int c = 0; c < 16; ++c) tot += col[c * 4 * LS]; \
-                    const int64_t t = t0c + t0 + KK * kBPer + st;                          \
-                    if (n < Nr && t < t1c && wg < G)                                       \
-                        dbc_part[(gidx * L + t) * R + ty * Nr + n] = tot;                  \
+                    comb[wave * 8 * SQ + e] = tot;                                         \
                 }                                                                          \
             }                                                                              \
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");                         \
-            __builtin_amdgcn_wave_barrier();                                               \
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");                         \
+            __syncthreads();                                                               \
+            for (int e = tid; e < 8 * SQ; e += kBThreads) {                                \
+                const int sp_ = e % S;                                                     \
+                const int jp = (e / S) % 4;                                                \
+                const int ty = (e / (4 * S)) % 2;                                          \
+                const int st = e / (8 * S);                                                \
+                const int n = jp * S + sp_;                                                \
+                const float tot = (comb[e] + comb[8 * SQ + e]) +                           \
+                                  (comb[16 * SQ + e] + comb[24 * SQ + e]);                 \
+                const int64_t t = t0c + t0 + KK * kBPer + st;                              \
+                if (n < Nr && t < t1c)                                                     \
+                    dbc_part[((int64_t(b) * NB + blockIdx.x) * L + t) * R + ty * Nr + n] = tot; \
+            }                                                                              \
+            __syncthreads();                                                               \
         }
         SS_RV_BATCH(3)
         SS_RV_BATCH(2)
@@ -489,7 +502,7 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(
             if (n < Nr) h_start[sidx + n] = dA[s];   // dA partial of this (b, chunk, d)
         }
         if (j == 0) {
-            const int64_t pidx = ((int64_t(b) * K + k) * D + d) * 2;
+            const int64_t pidx = ((int64_t(b) * D + d) * K + k) * 2;
             ddt_part[pidx] = accD;
             ddt_part[pidx + 1] = accT;
         }
@@ -499,65 +512,59 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(
 // ---------------------------------------------------------------------------------------
 // 4. reductions
 // ---------------------------------------------------------------------------------------
-// dB | dC: part [B, G, L, 2N] summed over G -> dB, dC [B, N, L].  Block: (32 steps, b).
+// dB | dC: part [B, NB, L, 2N] summed over NB -> dB, dC [B, N, L].  One thread per (t, v)
+// of a batch row: reads are coalesced across threads, the sum runs over the channel blocks.
 __global__ __launch_bounds__(256) void bwd_reduce_bc_kernel(const float* __restrict__ part,
                                                             float* __restrict__ dB,
                                                             float* __restrict__ dC, int64_t L,
-                                                            int G, int Nr) {
-    __shared__ float tile[64][33];
+                                                            int NB, int Nr) {
     const int R = 2 * Nr;
     const int b = blockIdx.y;
-    const int64_t t0 = int64_t(blockIdx.x) * 32;
-    const int tid = threadIdx.x;
-    const int nt = (L - t0 < 32) ? int(L - t0) : 32;
-    for (int e = tid; e < 32 * R; e += 256) {
-        const int tl = e / R, v = e % R;
-        float acc = 0.0f;
-        if (tl < nt) {
-            const float* p = part + (int64_t(b) * G * L + t0 + tl) * R + v;
-            for (int gi = 0; gi < G; ++gi) acc += p[int64_t(gi) * L * R];
-        }
-        tile[v][tl] = acc;
-    }
-    __syncthreads();
-    for (int e = tid; e < R * 32; e += 256) {
-        const int v = e / 32, tl = e % 32;
-        if (tl < nt) {
-            float* out = (v < Nr) ? dB + (int64_t(b) * Nr + v) * L : dC + (int64_t(b) * Nr + v - Nr) * L;
-            out[t0 + tl] = tile[v][tl];
-        }
-    }
+    const int64_t f = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    const int64_t LR = L * R;
+    if (f >= LR) return;
+    const float* p = part + int64_t(b) * NB * LR + f;
+    float acc = 0.0f;
+    for (int gi = 0; gi < NB; ++gi) acc += p[int64_t(gi) * LR];
+    const int64_t t = f / R;
+    const int v = int(f % R);
+    float* out = (v < Nr) ? dB + (int64_t(b) * Nr + v) * L : dC + (int64_t(b) * Nr + v - Nr) * L;
+    out[t] = acc;
 }
 
-// dA [D, N] = Σ_{b,k} part[b,k,d,n];  dD, ddt_bias [D] = Σ_{b,k} ddt_part[b,k,d,0|1]
+// dA [D, N] = Σ_{b,k} part[b,d,k,n];  dD, ddt_bias [D] = Σ_{b,k} ddt_part[b,d,k,0|1]
 __global__ __launch_bounds__(256) void bwd_reduce_params_kernel(
     const float* __restrict__ dA_part, const float* __restrict__ ddt_part, float* __restrict__ dA,
-    float* __restrict__ dD, float* __restrict__ ddt_bias, int64_t D, int Nr, int BK) {
+    float* __restrict__ dD, float* __restrict__ ddt_bias, int64_t D, int Nr, int Bn, int K) {
     const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
     const int64_t nA = D * Nr;
     if (i < nA) {
+        const int64_t d = i / Nr, n = i % Nr;
         float acc = 0.0f;
-        for (int r = 0; r < BK; ++r) acc += dA_part[int64_t(r) * nA + i];
+        for (int b = 0; b < Bn; ++b)
+            for (int k = 0; k < K; ++k) acc += dA_part[((int64_t(b) * D + d) * K + k) * Nr + n];
         dA[i] = acc;
     } else if (i < nA + D) {
-        const int64_t dd = i - nA;
+        const int64_t d = i - nA;
         float a0 = 0.0f, a1 = 0.0f;
-        for (int r = 0; r < BK; ++r) {
-            a0 += ddt_part[(int64_t(r) * D + dd) * 2];
-            a1 += ddt_part[(int64_t(r) * D + dd) * 2 + 1];
-        }
-        dD[dd] = a0;
-        ddt_bias[dd] = a1;
+        for (int b = 0; b < Bn; ++b)
+            for (int k = 0; k < K; ++k) {
+                const int64_t q = ((int64_t(b) * D + d) * K + k) * 2;
+                a0 += ddt_part[q];
+                a1 += ddt_part[q + 1];
+            }
+        dD[d] = a0;
+        ddt_bias[d] = a1;
     }
 }
 
 // ---------------------------------------------------------------------------------------
 // plan helpers and launchers
 // ---------------------------------------------------------------------------------------
-int64_t bwd_reduce_blocks(const Plan& p) { return (p.D + 15) / 16; }
+int64_t bwd_reduce_blocks(const Plan& p) { return (p.D + kBChan - 1) / kBChan; }
 
 size_t bwd_partial_bytes(const Plan& p) {
-    // dB|dC per-wave partials + dD/ddt_bias per-chunk partials
+    // dB|dC per-block partials + dD/ddt_bias per-chunk partials
     const size_t bc = size_t(p.B) * size_t(bwd_reduce_blocks(p)) * size_t(p.L) * size_t(2 * p.N) * 4;
     const size_t dt = size_t(p.B) * size_t(p.K) * size_t(p.D) * 2 * 4;
     return align256(bc) + dt;
@@ -614,14 +621,15 @@ hipError_t launch_bwd(int bf16, const BwdLaunch& p, hipStream_t s) {
 }
 
 hipError_t launch_bwd_reduce(const BwdLaunch& p, hipStream_t s) {
-    const int G = int((p.D + 15) / 16);
-    hipLaunchKernelGGL(bwd_reduce_bc_kernel, dim3(unsigned((p.L + 31) / 32), unsigned(p.B)), dim3(256),
-                       0, s, p.dbc_part, p.dB, p.dC, p.L, G, int(p.N));
+    const int NB = int((p.D + kBChan - 1) / kBChan);
+    const int64_t LR = p.L * 2 * p.N;
+    hipLaunchKernelGGL(bwd_reduce_bc_kernel, dim3(unsigned((LR + 255) / 256), unsigned(p.B)), dim3(256),
+                       0, s, p.dbc_part, p.dB, p.dC, p.L, NB, int(p.N));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t n = p.D * p.N + p.D;
     hipLaunchKernelGGL(bwd_reduce_params_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s,
-                       p.h_end, p.ddt_part, p.dA, p.dD, p.ddt_bias, p.D, int(p.N), int(p.B * p.K));
+                       p.h_end, p.ddt_part, p.dA, p.dD, p.ddt_bias, p.D, int(p.N), int(p.B), p.K);
     return hipGetLastError();
 }
 

@@ -72,7 +72,7 @@ __global__ __launch_bounds__(1024) void carry_kernel(const float* h_end,
 #pragma unroll
     for (int n = 0; n < N; ++n) { P[n] = 1.0f; H[n] = 0.0f; }
     for (int j = j0; j < j1; ++j) {
-        const int64_t base = (int64_t(b) * K + chunk_of(j)) * D + d;
+        const int64_t base = (int64_t(b) * D + d) * K + chunk_of(j);
         const float s = dsum[base];
 #pragma unroll
         for (int n = 0; n < N; ++n) {
@@ -103,7 +103,7 @@ __global__ __launch_bounds__(1024) void carry_kernel(const float* h_end,
         st[n] = fmaf(pe, st[n], he);
     }
     for (int j = j0; j < j1; ++j) {
-        const int64_t base = (int64_t(b) * K + chunk_of(j)) * D + d;
+        const int64_t base = (int64_t(b) * D + d) * K + chunk_of(j);
         const float s = dsum[base];
 #pragma unroll
         for (int n = 0; n < N; ++n) {

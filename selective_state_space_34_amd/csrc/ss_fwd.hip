@@ -56,9 +56,9 @@ __global__ __launch_bounds__(256) void bc_stage_kernel(const Tin* __restrict__ B
 // ---------------------------------------------------------------------------------------
 // Channel-parallel scan over one chunk [k*chunk, min(L, (k+1)*chunk)) of each channel.
 // grid = (ceil(D / blockDim), K, B); lane = channel d.
-// h_init: nullable, [B, K, D, N] (K = 1 holds h0).  OUT: y [B, D, L]; h_last (nullable)
-// = h_final [B, D, N], written by chunk K-1.  AGG: h_last = h_end [B, K, D, N],
-// dsum [B, K, D].
+// h_init: nullable, [B, D, K, N] (K = 1 holds h0).  OUT: y [B, D, L]; h_last (nullable)
+// = h_final [B, D, N], written by chunk K-1.  AGG: h_last = h_end [B, D, K, N],
+// dsum [B, D, K].
 // ---------------------------------------------------------------------------------------
 template <typename Tin, int N, bool kGate, bool kAgg>
 __global__ __launch_bounds__(256) void scan_kernel(
@@ -77,7 +77,7 @@ __global__ __launch_bounds__(256) void scan_kernel(
     float A2[N], h[N];
 #pragma unroll
     for (int n = 0; n < N; ++n) A2[n] = A[d * N + n] * kLog2e;
-    const int64_t hidx = ((int64_t(b) * K + k) * D + d) * N;
+    const int64_t hidx = ((int64_t(b) * D + d) * K + k) * N;
 #pragma unroll
     for (int n = 0; n < N; ++n) h[n] = h_init ? h_init[hidx + n] : 0.0f;
 
@@ -128,7 +128,7 @@ __global__ __launch_bounds__(256) void scan_kernel(
     }
 
     if (kAgg) {
-        const int64_t aidx = ((int64_t(b) * K + k) * D + d);
+        const int64_t aidx = (int64_t(b) * D + d) * K + k;
 #pragma unroll
         for (int n = 0; n < N; ++n) h_last[aidx * N + n] = h[n];
         dsum_out[aidx] = dsum;

@@ -121,7 +121,7 @@ __global__ __launch_bounds__(kThreads) void scanq_kernel(
     float A2[S], h[S];
 #pragma unroll
     for (int s = 0; s < S; ++s) A2[s] = A[d * N + n0 + s] * kLog2e;
-    const int64_t hidx = ((int64_t(b) * K + k) * D + d) * N + n0;
+    const int64_t hidx = ((int64_t(b) * D + d) * K + k) * N + n0;
 #pragma unroll
     for (int s = 0; s < S; ++s) h[s] = h_init ? h_init[hidx + s] : 0.0f;
     const float bias = dt_bias[d];
@@ -276,7 +276,7 @@ __global__ __launch_bounds__(kThreads) void scanq_kernel(
 
     if (kAgg) {
         dsum = quad_sum(dsum);
-        const int64_t aidx = (int64_t(b) * K + k) * D + d;
+        const int64_t aidx = (int64_t(b) * D + d) * K + k;
         if (valid) {
 #pragma unroll
             for (int s = 0; s < S; ++s) h_last[aidx * N + n0 + s] = h[s];

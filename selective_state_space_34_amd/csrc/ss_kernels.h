@@ -14,10 +14,10 @@ struct ScanLaunch {
     const float* A;
     const float* Dskip;
     const float* BC;        // [B, L, 2N] float32 staging copy of B and C
-    const float* h_init;    // nullable; [B, K, D, N]
+    const float* h_init;    // nullable; [B, D, K, N]
     float* y;               // OUT mode
-    float* h_last;          // OUT: h_final (nullable); AGG: h_end [B, K, D, N]
-    float* dsum;            // AGG: Σδ per chunk [B, K, D]
+    float* h_last;          // OUT: h_final (nullable); AGG: h_end [B, D, K, N]
+    float* dsum;            // AGG: Σδ per chunk [B, D, K]
     int64_t B, L, D, chunk;
     int K;
     int vec;                // 1: L % 8 == 0, 8-step vector loads
@@ -29,11 +29,11 @@ struct ScanLaunch {
 // (reverse = 1 scans chunks from last to first, for the adjoint), h_out the state
 // after the last one.  h_in, h_out nullable.
 struct CarryLaunch {
-    const float* h_end;     // [B, K, D, N]
-    const float* dsum;      // [B, K, D]
+    const float* h_end;     // [B, D, K, N]
+    const float* dsum;      // [B, D, K]
     const float* A;         // [D, N]
     const float* h_in;      // [B, D, N]
-    float* h_start;         // [B, K, D, N]
+    float* h_start;         // [B, D, K, N]
     float* h_out;           // [B, D, N]
     int64_t B, D;
     int K;
@@ -52,11 +52,11 @@ struct BwdLaunch {
     const float* A;
     const float* Dskip;
     const float* BC;
-    float* h_end;      // [B, K, D, N]
-    float* rev_end;    // [B, K, D, N]
-    float* dsum;       // [B, K, D]
-    float* dbc_part;   // [B, ceil(D/16), L, 2N]
-    float* ddt_part;   // [B, K, D, 2]
+    float* h_end;      // [B, D, K, N]
+    float* rev_end;    // [B, D, K, N]
+    float* dsum;       // [B, D, K]
+    float* dbc_part;   // [B, ceil(D/64), L, 2N]
+    float* ddt_part;   // [B, D, K, 2]
     float* dx;
     float* ddt_raw;
     float* dz;
