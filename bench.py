@@ -102,6 +102,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c2", help="c0..c4 (default c2, D=5120 forward)")
     ap.add_argument("--plan", type=int, default=0)
+    ap.add_argument("--layout", type=int, default=0, help="0 auto, 1 quad, 2 one lane per channel")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also launch one device copy of this many MiB (HBM counter calibration)")
@@ -132,7 +133,7 @@ def main():
     y = torch.empty((w.batch, w.dim, w.seqlen), dtype=torch.float32, device=dev)
     hf = torch.empty((w.batch, w.dim, w.dstate), dtype=torch.float32, device=dev) if w.h_final else None
     dims = ss.make_dims(w.batch, w.seqlen, w.dim, w.dstate,
-                        ss.SS_BF16 if w.dtype == "bf16" else ss.SS_F32, args.plan, 0)
+                        ss.SS_BF16 if w.dtype == "bf16" else ss.SS_F32, args.plan, 0, args.layout)
     ws = torch.empty(max(ss.workspace_size(dims), 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     if w.backward:
@@ -142,7 +143,7 @@ def main():
 
     def fwd_call():
         ss.ss_fwd(x, dtr, dtb, A, Bm, Cm, Dk, z=z, y=y, h_final=hf, workspace=ws,
-                  plan=args.plan, stream=stream)
+                  plan=args.plan, layout=args.layout, stream=stream)
 
     def bwd_call():
         ss.ss_bwd(x, dtr, dtb, A, Bm, Cm, Dk, dy, z=z, workspace=wsb, out=grads, stream=stream)
@@ -228,7 +229,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{w.name}: {w.label}", "batch": w.batch, "seqlen": w.seqlen,
                    "dim": w.dim, "dstate": w.dstate, "in_dtype": w.dtype, "gate": w.gate,
-                   "plan": args.plan},
+                   "plan": args.plan, "layout": args.layout},
         "roofline": {"bound": "alu", "achieved": alu_achieved, "peak": ALU_PEAK_TSLOTS,
                      "unit": "T VALU-slot/s", "frac": alu_achieved / ALU_PEAK_TSLOTS,
                      "traffic": None,

@@ -66,6 +66,14 @@ typedef enum { SS_F32 = 0, SS_BF16 = 1 } ss_dtype;
  * The backward always runs chunked. */
 typedef enum { SS_PLAN_AUTO = 0, SS_PLAN_SINGLE = 1, SS_PLAN_CHUNKED = 2 } ss_plan;
 
+/* Forward lane layout.
+ *   SS_LAYOUT_AUTO — chosen from the dims.
+ *   SS_LAYOUT_QUAD — the N states of a channel on four lanes (N >= 4, L % 8 == 0).
+ *   SS_LAYOUT_LANE — one lane per channel; when A[d,n] = -(n+1) exactly for every
+ *                    channel of a wavefront, exp(δA) is formed as powers of exp(-δ)
+ *                    (checked on the device, otherwise the general path runs). */
+typedef enum { SS_LAYOUT_AUTO = 0, SS_LAYOUT_QUAD = 1, SS_LAYOUT_LANE = 2 } ss_layout;
+
 typedef struct ss_dims {
     int64_t batch;    /* B  >= 1 */
     int64_t seqlen;   /* L  >= 1 */
@@ -73,7 +81,10 @@ typedef struct ss_dims {
     int64_t dstate;   /* N, one of 1, 2, 4, 8, 16, 32 */
     int32_t in_dtype; /* ss_dtype */
     int32_t plan;     /* ss_plan */
-    int64_t chunk;    /* chunk length of the chunked plan (multiple of 8); 0 = automatic */
+    int64_t chunk;    /* chunk length of the chunked plan (multiple of 8; backward: multiple
+                         of 16, at most 64); 0 = automatic */
+    int32_t layout;   /* ss_layout (forward only) */
+    int32_t reserved; /* must be 0 */
 } ss_dims;
 
 /* Return codes: 0 on success, negative on error. */
@@ -81,7 +92,7 @@ enum {
     SS_OK = 0,
     SS_ERR_NULL = -1,        /* a required pointer is NULL */
     SS_ERR_DIMS = -2,        /* a dim <= 0, N unsupported, sizes overflow, or bad chunk */
-    SS_ERR_DTYPE = -3,       /* in_dtype or plan not one of the enums */
+    SS_ERR_DTYPE = -3,       /* in_dtype, plan or layout not one of the enums */
     SS_ERR_ALIGN = -4,       /* a base pointer is not 16-byte aligned */
     SS_ERR_WORKSPACE = -5,   /* workspace NULL while needed, or workspace_bytes too small */
     SS_ERR_HIP = -6,         /* a HIP call failed; see ss_last_hip_error() */

@@ -19,6 +19,7 @@ from ._build import LIB, build, stale  # noqa: F401
 
 SS_F32, SS_BF16 = 0, 1
 SS_PLAN_AUTO, SS_PLAN_SINGLE, SS_PLAN_CHUNKED = 0, 1, 2
+SS_LAYOUT_AUTO, SS_LAYOUT_QUAD, SS_LAYOUT_LANE = 0, 1, 2
 
 ERRORS = {0: "SS_OK", -1: "SS_ERR_NULL", -2: "SS_ERR_DIMS", -3: "SS_ERR_DTYPE", -4: "SS_ERR_ALIGN",
           -5: "SS_ERR_WORKSPACE", -6: "SS_ERR_HIP", -7: "SS_ERR_UNSUPPORTED"}
@@ -30,7 +31,7 @@ EXPORTS = ("ss_fwd", "ss_bwd", "ss_fwd_workspace_size", "ss_bwd_workspace_size",
 class ss_dims(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("dim", ctypes.c_int64),
                 ("dstate", ctypes.c_int64), ("in_dtype", ctypes.c_int32), ("plan", ctypes.c_int32),
-                ("chunk", ctypes.c_int64)]
+                ("chunk", ctypes.c_int64), ("layout", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class SSError(RuntimeError):
@@ -72,8 +73,9 @@ def load(path: str = LIB):
     return lib
 
 
-def make_dims(batch, seqlen, dim, dstate, in_dtype=SS_F32, plan=SS_PLAN_AUTO, chunk=0):
-    return ss_dims(batch, seqlen, dim, dstate, in_dtype, plan, chunk)
+def make_dims(batch, seqlen, dim, dstate, in_dtype=SS_F32, plan=SS_PLAN_AUTO, chunk=0,
+              layout=SS_LAYOUT_AUTO):
+    return ss_dims(batch, seqlen, dim, dstate, in_dtype, plan, chunk, layout, 0)
 
 
 def workspace_size(dims, backward=False) -> int:
@@ -106,7 +108,7 @@ def _check(t, name, shape, dtype, device):
         raise ValueError(f"{name} must be contiguous")
 
 
-def _dims_of(x, A, Bm, plan, chunk):
+def _dims_of(x, A, Bm, plan, chunk, layout=SS_LAYOUT_AUTO):
     import torch
     Bn, D, L = x.shape
     N = A.shape[1]
@@ -116,7 +118,7 @@ def _dims_of(x, A, Bm, plan, chunk):
         dt = SS_BF16
     else:
         raise ValueError(f"x dtype must be float32 or bfloat16, got {x.dtype}")
-    return make_dims(Bn, L, D, N, dt, plan, chunk)
+    return make_dims(Bn, L, D, N, dt, plan, chunk, layout)
 
 
 def _stream(stream):
@@ -144,12 +146,13 @@ def _check_inputs(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, z, h0):
 
 
 def ss_fwd(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, z=None, h0=None, *, return_final=False,
-           y=None, h_final=None, workspace=None, plan=SS_PLAN_AUTO, chunk=0, stream=None):
+           y=None, h_final=None, workspace=None, plan=SS_PLAN_AUTO, chunk=0,
+           layout=SS_LAYOUT_AUTO, stream=None):
     """Forward scan through the C ABI.  Returns y, or (y, h_final) with return_final."""
     import torch
     lib = load()
     _check_inputs(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, z, h0)
-    dims = _dims_of(x, A, Bm, plan, chunk)
+    dims = _dims_of(x, A, Bm, plan, chunk, layout)
     Bn, D, L = x.shape
     N = A.shape[1]
     if y is None:

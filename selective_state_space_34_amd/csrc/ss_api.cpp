@@ -167,9 +167,8 @@ int ss_bwd(const ss_dims* dims, const void* x, const void* dt_raw, const float* 
     ss::CarryLaunch c{};
     c.dsum = bl.dsum; c.A = A; c.B = p.B; c.D = p.D; c.K = int(p.K);
     c.h_end = bl.h_end; c.h_start = bl.h_end; c.h_in = h0; c.h_out = nullptr; c.reverse = 0;
-    e = ss::launch_carry(int(p.N), c, stream);
-    if (e != hipSuccess) return hip_fail(e);
-    c.h_end = bl.rev_end; c.h_start = bl.rev_end; c.h_in = dh_final; c.h_out = dh0; c.reverse = 1;
+    c.dual = 1;
+    c.h_end2 = bl.rev_end; c.h_start2 = bl.rev_end; c.h_in2 = dh_final; c.h_out2 = dh0; c.reverse2 = 1;
     e = ss::launch_carry(int(p.N), c, stream);
     if (e != hipSuccess) return hip_fail(e);
     // 3. final pass: recomputed states, adjoint sweep, per-element gradients, partials

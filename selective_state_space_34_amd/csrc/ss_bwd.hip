@@ -532,29 +532,50 @@ __global__ __launch_bounds__(256) void bwd_reduce_bc_kernel(const float* __restr
     out[t] = acc;
 }
 
-// dA [D, N] = Σ_{b,k} part[b,d,k,n];  dD, ddt_bias [D] = Σ_{b,k} ddt_part[b,d,k,0|1]
+// dA [D, N] = Σ_{b,k} part[b,d,k,n];  dD, ddt_bias [D] = Σ_{b,k} ddt_part[b,d,k,0|1].
+// One block per channel d: for each b the K*N (and K*2) partials of (b, d) are
+// contiguous, so the block reads them coalesced and folds over k through LDS.
 __global__ __launch_bounds__(256) void bwd_reduce_params_kernel(
     const float* __restrict__ dA_part, const float* __restrict__ ddt_part, float* __restrict__ dA,
     float* __restrict__ dD, float* __restrict__ ddt_bias, int64_t D, int Nr, int Bn, int K) {
-    const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
-    const int64_t nA = D * Nr;
-    if (i < nA) {
-        const int64_t d = i / Nr, n = i % Nr;
-        float acc = 0.0f;
-        for (int b = 0; b < Bn; ++b)
-            for (int k = 0; k < K; ++k) acc += dA_part[((int64_t(b) * D + d) * K + k) * Nr + n];
-        dA[i] = acc;
-    } else if (i < nA + D) {
-        const int64_t d = i - nA;
-        float a0 = 0.0f, a1 = 0.0f;
-        for (int b = 0; b < Bn; ++b)
-            for (int k = 0; k < K; ++k) {
-                const int64_t q = ((int64_t(b) * D + d) * K + k) * 2;
-                a0 += ddt_part[q];
-                a1 += ddt_part[q + 1];
-            }
-        dD[d] = a0;
-        ddt_bias[d] = a1;
+    __shared__ float red[256];
+    const int64_t d = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int KN = K * Nr;
+    // thread tid accumulates entries e = tid + 256 i of the K*N block; Nr divides 256,
+    // so every entry a thread touches has state n = tid % Nr
+    float acc = 0.0f;
+    for (int b = 0; b < Bn; ++b) {
+        const float* p = dA_part + (int64_t(b) * D + d) * KN;
+        for (int e = tid; e < KN; e += 256) acc += p[e];
+    }
+    red[tid] = acc;
+    __syncthreads();
+    if (tid < Nr) {
+        float t = 0.0f;
+        for (int i = tid; i < 256; i += Nr) t += red[i];
+        dA[d * Nr + tid] = t;
+    }
+    __syncthreads();
+    float a0 = 0.0f, a1 = 0.0f;
+    for (int b = 0; b < Bn; ++b) {
+        const float* q = ddt_part + (int64_t(b) * D + d) * K * 2;
+        for (int k = tid; k < K; k += 256) { a0 += q[2 * k]; a1 += q[2 * k + 1]; }
+    }
+    red[tid] = a0;
+    __syncthreads();
+    if (tid == 0) {
+        float t = 0.0f;
+        for (int i = 0; i < 256; ++i) t += red[i];
+        dD[d] = t;
+    }
+    __syncthreads();
+    red[tid] = a1;
+    __syncthreads();
+    if (tid == 0) {
+        float t = 0.0f;
+        for (int i = 0; i < 256; ++i) t += red[i];
+        ddt_bias[d] = t;
     }
 }
 
@@ -627,9 +648,8 @@ hipError_t launch_bwd_reduce(const BwdLaunch& p, hipStream_t s) {
                        0, s, p.dbc_part, p.dB, p.dC, p.L, NB, int(p.N));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t n = p.D * p.N + p.D;
-    hipLaunchKernelGGL(bwd_reduce_params_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s,
-                       p.h_end, p.ddt_part, p.dA, p.dD, p.ddt_bias, p.D, int(p.N), int(p.B), p.K);
+    hipLaunchKernelGGL(bwd_reduce_params_kernel, dim3(unsigned(p.D)), dim3(256), 0, s, p.h_end,
+                       p.ddt_part, p.dA, p.dD, p.ddt_bias, p.D, int(p.N), int(p.B), p.K);
     return hipGetLastError();
 }
 

@@ -46,14 +46,27 @@ __device__ __forceinline__ void wave_scan_affine(float& P, float& H) {
 #undef SS_STEP
 }
 
+// One launch may carry two independent sets (blockIdx.z selects): the backward runs
+// its forward-state carry and its reverse-adjoint carry together.
+struct CarrySet {
+    const float* h_end;
+    const float* h_in;
+    float* h_start;
+    float* h_out;
+    int reverse;
+};
+
 template <int N>
-__global__ __launch_bounds__(1024) void carry_kernel(const float* h_end,
+__global__ __launch_bounds__(1024) void carry_kernel(CarrySet s0, CarrySet s1,
                                                      const float* __restrict__ dsum,
-                                                     const float* __restrict__ A,
-                                                     const float* __restrict__ h_in,
-                                                     float* h_start,
-                                                     float* __restrict__ h_out, int64_t D, int K,
-                                                     int m, int reverse) {
+                                                     const float* __restrict__ A, int64_t D, int K,
+                                                     int m) {
+    const CarrySet& cs = blockIdx.z ? s1 : s0;
+    const float* h_end = cs.h_end;
+    const float* h_in = cs.h_in;
+    float* h_start = cs.h_start;
+    float* h_out = cs.h_out;
+    const int reverse = cs.reverse;
     __shared__ float wP[16][N];
     __shared__ float wH[16][N];
     const int64_t d = blockIdx.x;
@@ -124,9 +137,10 @@ static hipError_t launch_carry_t(const CarryLaunch& p, hipStream_t s) {
     const int m = (p.K + 1023) / 1024;
     const int lanes = (p.K + m - 1) / m;
     const int threads = (lanes + 63) / 64 * 64;
-    dim3 grid(unsigned(p.D), unsigned(p.B));
-    hipLaunchKernelGGL(carry_kernel<N>, grid, dim3(threads), 0, s, p.h_end, p.dsum, p.A, p.h_in,
-                       p.h_start, p.h_out, p.D, p.K, m, p.reverse);
+    const CarrySet s0{p.h_end, p.h_in, p.h_start, p.h_out, p.reverse};
+    const CarrySet s1{p.h_end2, p.h_in2, p.h_start2, p.h_out2, p.reverse2};
+    dim3 grid(unsigned(p.D), unsigned(p.B), p.dual ? 2u : 1u);
+    hipLaunchKernelGGL(carry_kernel<N>, grid, dim3(threads), 0, s, s0, s1, p.dsum, p.A, p.D, p.K, m);
     return hipGetLastError();
 }
 

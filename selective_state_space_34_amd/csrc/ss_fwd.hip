@@ -17,6 +17,8 @@
 //   AGG — chunk aggregate for the sequence-parallel plan: the chunk's local scan
 //         from a zero state (h_end) and Σδ over the chunk, whose exp gives the
 //         chunk's product of Ā (Π_t exp(δ_t A) = exp(A Σ_t δ_t)).
+#include <type_traits>
+
 #include "ss_device.h"
 #include "ss_kernels.h"
 
@@ -70,7 +72,7 @@ __global__ __launch_bounds__(256) void scan_kernel(
     const int64_t d = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     const int k = blockIdx.y;
     const int b = blockIdx.z;
-    if (d >= D) return;
+    if (d >= D) return;   // the vote below is over the remaining (active) lanes
     const int64_t t_begin = int64_t(k) * chunk;
     const int64_t t_end = (t_begin + chunk < L) ? t_begin + chunk : L;
 
@@ -91,41 +93,107 @@ __global__ __launch_bounds__(256) void scan_kernel(
     const float* bcb = BC + int64_t(b) * L * (2 * N);
     float dsum = 0.0f;
 
-    auto step = [&](float xv, float dv, float zv, const float* __restrict__ bct) -> float {
-        const float delta = softplus(bias + dv);
+    // One step.  Bq/Cq hold this step's B and C (uniform across the wave: SGPRs).  The
+    // state update reads only Bq and the readout only Cq, so the next step's B row is
+    // loaded right after the update and its C row right after the readout: each scalar
+    // load is covered by about half a step without a second register set.
+    // kS4D: A[d, n] = -(n+1) exactly (S4D-real): Ā_n = exp(-(n+1)δ) = r^(n+1) with
+    // r = exp(-δ) = 1 / (1 + e^u) (δ = softplus(u)), so one reciprocal and a chain of
+    // multiplies replace the N exponentials; r^(n+1) by repeated multiplication carries
+    // about (n+1) ulp of relative error.
+    float Bq[N], Cq[N];
+    auto load_B = [&](int64_t tt) {
+#pragma unroll
+        for (int n = 0; n < N; ++n) Bq[n] = bcb[tt * (2 * N) + n];
+    };
+    auto load_C = [&](int64_t tt) {
+#pragma unroll
+        for (int n = 0; n < N; ++n) Cq[n] = bcb[tt * (2 * N) + N + n];
+    };
+    auto step = [&](auto s4d_tag, float xv, float dv, float zv, int64_t tt) -> float {
+        constexpr bool kS4D = decltype(s4d_tag)::value;
+        float delta, r = 1.0f;
+        if constexpr (kS4D) {
+            const float u = bias + dv;
+            const float w = exp2_hw(-fabsf(u) * kLog2e);            // e^{-|u|}
+            const float v = 1.0f + w;
+            delta = fmaxf(u, 0.0f) + fmaf(log2_hw(v), kLn2, w - (v - 1.0f));
+            r = (u > 0.0f ? w : 1.0f) * rcp_hw(v);                   // e^{-δ}
+        } else {
+            delta = softplus(bias + dv);
+        }
         if (kAgg) dsum += delta;
         const float dx = delta * xv;
-        float acc = 0.0f;
+        float a = r;
 #pragma unroll
         for (int n = 0; n < N; ++n) {
-            const float abar = exp2_hw(delta * A2[n]);
-            h[n] = fmaf(abar, h[n], dx * bct[n]);
-            if (!kAgg) acc = fmaf(bct[N + n], h[n], acc);
+            const float abar = kS4D ? a : exp2_hw(delta * A2[n]);
+            h[n] = fmaf(abar, h[n], dx * Bq[n]);
+            if (kS4D) a *= r;
         }
+        const bool more = tt + 1 < t_end;
+        if (more) load_B(tt + 1);
+        __builtin_amdgcn_sched_barrier(0);
         if (kAgg) return 0.0f;
+        float acc = 0.0f;
+#pragma unroll
+        for (int n = 0; n < N; ++n) acc = fmaf(Cq[n], h[n], acc);
+        if (more) load_C(tt + 1);
+        __builtin_amdgcn_sched_barrier(0);
         float s = fmaf(Dd, xv, acc);
         if (kGate) s *= silu(zv);
         return s;
     };
 
-    int64_t t = t_begin;
-    if (vec) {
-        for (; t + 8 <= t_end; t += 8) {
-            float xv[8], dv[8], zv[8], yv[8];
-            load8(xr + t, xv);
-            load8(dr + t, dv);
-            if (kGate && !kAgg) load8(zr + t, zv);
+    bool s4d = true;
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-                yv[i] = step(xv[i], dv[i], (kGate && !kAgg) ? zv[i] : 0.0f, bcb + (t + i) * (2 * N));
-            if (!kAgg) store8(yr + t, yv);
+    for (int n = 0; n < N; ++n) s4d = s4d && (A[d * N + n] == -float(n + 1));
+    const bool fast = __all(s4d);   // uniform across the (active lanes of the) wave
+
+    using Tag1 = std::integral_constant<bool, true>;
+    using Tag0 = std::integral_constant<bool, false>;
+    auto run = [&](auto s4d_tag) {
+        int64_t t = t_begin;
+        if (t < t_end) {
+            load_B(t);
+            if (!kAgg) load_C(t);
         }
-    }
-    for (; t < t_end; ++t) {
-        const float zv = (kGate && !kAgg) ? to_f32(zr[t]) : 0.0f;
-        const float r = step(to_f32(xr[t]), to_f32(dr[t]), zv, bcb + t * (2 * N));
-        if (!kAgg) yr[t] = r;
-    }
+        if (vec && t + 8 <= t_end) {
+            Tin xr8[8], dr8[8], zr8[8];
+            auto load_group = [&](int64_t tt) {
+                constexpr int V = int(8 * sizeof(Tin) / 16);   // uint4 per 8 elements
+#pragma unroll
+                for (int q = 0; q < V; ++q) {
+                    reinterpret_cast<uint4*>(xr8)[q] = reinterpret_cast<const uint4*>(xr + tt)[q];
+                    reinterpret_cast<uint4*>(dr8)[q] = reinterpret_cast<const uint4*>(dr + tt)[q];
+                    if (kGate && !kAgg)
+                        reinterpret_cast<uint4*>(zr8)[q] = reinterpret_cast<const uint4*>(zr + tt)[q];
+                }
+            };
+            load_group(t);
+            for (; t + 8 <= t_end; t += 8) {
+                float xv[8], dv[8], zv[8], yv[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    xv[i] = to_f32(xr8[i]);
+                    dv[i] = to_f32(dr8[i]);
+                    zv[i] = (kGate && !kAgg) ? to_f32(zr8[i]) : 0.0f;
+                }
+                if (t + 16 <= t_end) load_group(t + 8);
+                // rolled: an unrolled body keeps several B/C rows live and spills SGPRs
+#pragma unroll 1
+                for (int i = 0; i < 8; ++i) yv[i] = step(s4d_tag, xv[i], dv[i], zv[i], t + i);
+                if (!kAgg) store8(yr + t, yv);
+            }
+        }
+        for (; t < t_end; ++t) {
+            const float zv = (kGate && !kAgg) ? to_f32(zr[t]) : 0.0f;
+            const float r = step(s4d_tag, to_f32(xr[t]), to_f32(dr[t]), zv, t);
+            if (!kAgg) yr[t] = r;
+        }
+    };
+    if (fast) run(Tag1{});
+    else run(Tag0{});
 
     if (kAgg) {
         const int64_t aidx = (int64_t(b) * D + d) * K + k;

@@ -38,6 +38,13 @@ struct CarryLaunch {
     int64_t B, D;
     int K;
     int reverse;
+    // optional second set, carried in the same launch when dual = 1
+    int dual;
+    const float* h_end2;
+    const float* h_in2;
+    float* h_start2;
+    float* h_out2;
+    int reverse2;
 };
 
 // Backward launches (quad layout).  stage 0: chunk aggregates (h_end, rev_end, dsum);

@@ -47,6 +47,9 @@ inline int make_plan(const ss_dims& d, bool backward, Plan* out) {
     if (d.in_dtype != SS_F32 && d.in_dtype != SS_BF16) return SS_ERR_DTYPE;
     if (d.plan != SS_PLAN_AUTO && d.plan != SS_PLAN_SINGLE && d.plan != SS_PLAN_CHUNKED)
         return SS_ERR_DTYPE;
+    if (d.layout != SS_LAYOUT_AUTO && d.layout != SS_LAYOUT_QUAD && d.layout != SS_LAYOUT_LANE)
+        return SS_ERR_DTYPE;
+    if (d.reserved != 0) return SS_ERR_DTYPE;
     if (d.batch <= 0 || d.seqlen <= 0 || d.dim <= 0 || d.dstate <= 0) return SS_ERR_DIMS;
     const int64_t N = d.dstate;
     if (N != 1 && N != 2 && N != 4 && N != 8 && N != 16 && N != 32) return SS_ERR_DIMS;
@@ -58,16 +61,22 @@ inline int make_plan(const ss_dims& d, bool backward, Plan* out) {
     if (d.batch > kMaxGridYZ) return SS_ERR_DIMS;
     p.B = d.batch; p.L = d.seqlen; p.D = d.dim; p.N = N; p.in_dtype = d.in_dtype;
     p.vec = (p.L % 8) == 0;
-    p.quad = p.vec && N >= 4;
+    const bool quad_ok = p.vec && N >= 4;
 
-    // 64-lane waves of one pass: a lane per channel, or a quad of lanes per channel
-    const int64_t waves = p.quad ? (p.B * p.D + 15) / 16 : (p.B * p.D + 63) / 64;
+    // 64-lane waves of one pass: a quad of lanes per channel (the quad layout's reason
+    // to exist: 4x the waves of one lane per channel)
+    const int64_t qwaves = quad_ok ? (p.B * p.D + 15) / 16 : (p.B * p.D + 63) / 64;
     int chunked = backward ? 1 : 0;
     if (!backward) {
         if (d.plan == SS_PLAN_CHUNKED) chunked = 1;
         else if (d.plan == SS_PLAN_SINGLE) chunked = 0;
-        else chunked = (waves < kSingleWaves && p.L > 512) ? 1 : 0;
+        else chunked = (qwaves < kSingleWaves && p.L > 512) ? 1 : 0;
     }
+    // layout: the quad layout wherever it applies (measured faster than one lane per
+    // channel on every workload, single-pass or chunked, even with the S4D power path)
+    if (d.layout == SS_LAYOUT_LANE) p.quad = 0;
+    else p.quad = quad_ok;
+    const int64_t waves = p.quad ? qwaves : (p.B * p.D + 63) / 64;
     int64_t chunk = p.L;
     if (backward) {
         // 16-step tiles, at most four per chunk (tile start states live in LDS)

@@ -62,6 +62,10 @@ def test_fwd_validation(lib):
         assert _fwd(lib, bad) == -2
     assert _fwd(lib, ss.make_dims(2, 64, 32, 16, in_dtype=7)) == -3
     assert _fwd(lib, ss.make_dims(2, 64, 32, 16, plan=9)) == -3
+    assert _fwd(lib, ss.make_dims(2, 64, 32, 16, layout=5)) == -3
+    bad_res = ss.make_dims(2, 64, 32, 16)
+    bad_res.reserved = 1
+    assert _fwd(lib, bad_res) == -3
     # required pointers
     for i in (0, 1, 2, 3, 4, 5, 6, 9):
         p = [ctypes.c_void_p(FAKE)] * 11

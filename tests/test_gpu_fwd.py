@@ -116,15 +116,34 @@ def test_step_size_extremes(gpu, bias):
     assert_close(hf, hr, 1e-4, "h_final")
 
 
-def test_plans_agree_and_deterministic(gpu):
-    inp = make_inputs(2, 4096, 192, 16, dtype="bf16", seed=8, gate=True, with_h0=True)
-    note("plan agreement")
-    y1, h1 = gpu_fwd(gpu, inp, plan=1)
-    y2, h2 = gpu_fwd(gpu, inp, plan=2, chunk=512)
-    y3, h3 = gpu_fwd(gpu, inp, plan=2, chunk=512)
-    assert np.array_equal(y2, y3) and np.array_equal(h2, h3), "chunked plan not deterministic"
-    assert_close(y2, y1, 1e-5, "chunked vs single y")
-    assert_close(h2, h1, 1e-5, "chunked vs single h_final")
+@pytest.mark.parametrize("a_perturb", [True, False], ids=["A_general", "A_s4d"])
+def test_plans_agree_and_deterministic(gpu, a_perturb):
+    """single / chunked plans and quad / one-lane layouts agree; each is deterministic."""
+    inp = make_inputs(2, 4096, 192, 16, dtype="bf16", seed=8, gate=True, with_h0=True,
+                      a_perturb=a_perturb)
+    note(f"plan agreement a_perturb={a_perturb}")
+    y1, h1 = gpu_fwd(gpu, inp, plan=1, layout=1)
+    for plan, layout, chunk in ((2, 1, 512), (2, 2, 512), (1, 2, 0), (2, 2, 256)):
+        y2, h2 = gpu_fwd(gpu, inp, plan=plan, layout=layout, chunk=chunk)
+        y3, h3 = gpu_fwd(gpu, inp, plan=plan, layout=layout, chunk=chunk)
+        assert np.array_equal(y2, y3) and np.array_equal(h2, h3), f"not deterministic {plan} {layout}"
+        assert_close(y2, y1, 1e-5, f"plan {plan} layout {layout} y")
+        assert_close(h2, h1, 1e-5, f"plan {plan} layout {layout} h_final")
+    yr, hr = oracle_fwd(inp)
+    assert_close(y1, yr, tol_for(inp), "y")
+
+
+def test_s4d_detection_per_wave(gpu):
+    """A = -(n+1) except for one channel: waves holding it take the general path, the
+    others the power path; every channel matches the oracle either way."""
+    inp = make_inputs(1, 512, 200, 16, seed=12, gate=True, with_h0=True)
+    inp.A[77, 5] *= 1.01
+    note("s4d detection")
+    for layout in (2, 1):
+        y, hf = gpu_fwd(gpu, inp, plan=2, chunk=128, layout=layout)
+        yr, hr = oracle_fwd(inp)
+        assert_close(y, yr, 1e-4, f"y layout {layout}")
+        assert_close(hf, hr, 1e-4, f"h_final layout {layout}")
 
 
 def test_resume_across_calls(gpu):
