@@ -82,13 +82,19 @@ int ss_fwd(const ss_dims* dims, const void* x, const void* dt_raw, const float* 
     if (workspace && !aligned16(workspace)) return SS_ERR_ALIGN;
 
     char* ws = static_cast<char*>(workspace);
-    float* BC = reinterpret_cast<float*>(ws + p.off_bc);
     const int bf16 = p.in_dtype == SS_BF16;
-    hipError_t e = ss::launch_bc_stage(bf16, int(p.N), Bm, Cm, BC, p.B, p.L, stream);
-    if (e != hipSuccess) return hip_fail(e);
+    hipError_t e = hipSuccess;
+    // the quad kernel tiles B/C from the inputs; the one-lane kernel reads a [B, L, 2N] copy
+    float* BC = nullptr;
+    if (!p.quad) {
+        BC = reinterpret_cast<float*>(ws + p.off_bc);
+        e = ss::launch_bc_stage(bf16, int(p.N), Bm, Cm, BC, p.B, p.L, stream);
+        if (e != hipSuccess) return hip_fail(e);
+    }
 
     ss::ScanLaunch s{};
     s.x = x; s.dt_raw = dt_raw; s.z = z; s.dt_bias = dt_bias; s.A = A; s.Dskip = Dskip; s.BC = BC;
+    s.Bm = Bm; s.Cm = Cm;
     s.B = p.B; s.L = p.L; s.D = p.D; s.vec = p.vec;
     if (!p.chunked) {
         s.chunk = p.L; s.K = 1; s.h_init = h0; s.y = y; s.h_last = h_final; s.agg = 0;

@@ -10,9 +10,11 @@
 // Per 32-step tile:
 //   - lane j of a quad loads and prepares steps [8j, 8j+8) of its channel: widening,
 //     δ = softplus(dt_bias + dt_raw), δ·x.  No element is prepared twice.
+//   - the workgroup copies the tile's B and C ([B, N, L] inputs, N rows of 32 steps
+//     each) into LDS transposed to [step][B row | C row] as float32.
 //   - the recurrence walks the 32 steps; step t's δ and δ·x come from lane t/8 of
 //     the quad through a DPP quad_perm broadcast; B_t, C_t for the lane's S states
-//     come from an LDS copy of the tile (one 16-byte broadcast read each).
+//     come from the LDS tile (one 16-byte broadcast read each).
 //   - each lane's partial readouts (its S states) go to a per-wave LDS area; lane j
 //     sums the four partials of its own 8 steps, adds D·x, applies the gate and
 //     stores 8 outputs.
@@ -76,6 +78,24 @@ template <> struct Raw8<bf16_t> {
         }
     }
 };
+// raw storage of 4 consecutive input elements (one B or C row segment)
+template <typename Tin> struct Raw4;
+template <> struct Raw4<bf16_t> {
+    uint2 v;
+    __device__ __forceinline__ void load(const bf16_t* p) { v = *reinterpret_cast<const uint2*>(p); }
+    __device__ __forceinline__ float get(int i) const {
+        const uint32_t w = (i < 2) ? v.x : v.y;
+        return __uint_as_float((i & 1) ? (w & 0xffff0000u) : (w << 16));
+    }
+};
+template <> struct Raw4<float> {
+    float4 v;
+    __device__ __forceinline__ void load(const float* p) { v = *reinterpret_cast<const float4*>(p); }
+    __device__ __forceinline__ float get(int i) const {
+        return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+    }
+};
+
 template <> struct Raw8<float> {
     float4 a, b;
     __device__ __forceinline__ void load(const float* p) {
@@ -96,11 +116,13 @@ template <typename Tin, int S, bool kGate, bool kAgg>
 __global__ __launch_bounds__(kThreads) void scanq_kernel(
     const Tin* __restrict__ x, const Tin* __restrict__ dt_raw, const Tin* __restrict__ z,
     const float* __restrict__ dt_bias, const float* __restrict__ A,
-    const float* __restrict__ Dskip, const float* __restrict__ BC,
+    const float* __restrict__ Dskip, const Tin* __restrict__ Bm, const Tin* __restrict__ Cm,
     const float* __restrict__ h_init, float* __restrict__ y, float* __restrict__ h_last,
     float* __restrict__ dsum_out, int64_t L, int64_t D, int64_t chunk, int K) {
     constexpr int N = 4 * S;
-    constexpr int R = 2 * N;                      // floats per step in the B/C tile
+    // LDS tile row per step: B_t (N floats) then C_t (N floats), padded by 4 floats so
+    // the transposing writes of a wave fall on at most two lanes per bank
+    constexpr int R = 2 * N + 4;
     constexpr int TILE_F = kTile * R;             // floats per B/C tile
     __shared__ __align__(16) float bc_lds[2][TILE_F];
     __shared__ __align__(16) float part_lds[kAgg ? 1 : kThreads * kPS];
@@ -131,21 +153,25 @@ __global__ __launch_bounds__(kThreads) void scanq_kernel(
     const Tin* dr = dt_raw + row;
     const Tin* zr = kGate ? z + row : nullptr;
     float* yr = kAgg ? nullptr : y + row;
-    const float* bcb = BC + int64_t(b) * L * R;
+    const Tin* Bb = Bm + int64_t(b) * N * L;
+    const Tin* Cb = Cm + int64_t(b) * N * L;
     float dsum = 0.0f;
 
-    // B/C tile staging: TILE_F floats, float4 per thread per pass
-    constexpr int BC_VEC = TILE_F / 4;                       // float4 count of a tile
-    constexpr int BC_PASSES = (BC_VEC + kThreads - 1) / kThreads;
-    float4 bc_next[BC_PASSES];
+    // B/C tile copy: 2·N rows of 32 steps; unit e covers steps 4q..4q+3 of state n of
+    // B (m = 0) or C (m = 1), with n fastest across lanes
+    constexpr int BC_UNITS = 2 * N * (kTile / 4);
+    constexpr int BC_PASSES = (BC_UNITS + kThreads - 1) / kThreads;
+    Raw4<Tin> bc_next[BC_PASSES];
     Raw8<Tin> xn, dn, zn;
 
     auto issue_loads = [&](int64_t t0) {
-        const float4* src = reinterpret_cast<const float4*>(bcb + t0 * R);
 #pragma unroll
         for (int p = 0; p < BC_PASSES; ++p) {
             const int e = tid + p * kThreads;
-            if (e < BC_VEC) bc_next[p] = src[e];
+            if (BC_UNITS % kThreads == 0 || e < BC_UNITS) {
+                const int n = e % N, q = (e / N) % (kTile / 4), m = e / (N * (kTile / 4));
+                bc_next[p].load((m ? Cb : Bb) + int64_t(n) * L + t0 + 4 * q);
+            }
         }
         const int64_t te = t0 + kPer * j;
         xn.load(xr + te);
@@ -163,7 +189,12 @@ __global__ __launch_bounds__(kThreads) void scanq_kernel(
 #pragma unroll
         for (int p = 0; p < BC_PASSES; ++p) {
             const int e = tid + p * kThreads;
-            if (e < BC_VEC) reinterpret_cast<float4*>(buf)[e] = bc_next[p];
+            if (BC_UNITS % kThreads == 0 || e < BC_UNITS) {
+                const int n = e % N, q = (e / N) % (kTile / 4), m = e / (N * (kTile / 4));
+                float* dst = buf + 4 * q * R + m * N + n;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dst[i * R] = bc_next[p].get(i);
+            }
         }
         float xv[kPer], dv[kPer], zv[kPer];
         xn.decode(xv);
@@ -252,19 +283,18 @@ __global__ __launch_bounds__(kThreads) void scanq_kernel(
     }
 
     // tail: the last (t_end - t_tiles_end) < 32 steps, one step at a time; every lane
-    // prepares the step itself and reads its B/C straight from the staging buffer
+    // prepares the step itself and reads its B/C straight from the inputs
     for (int64_t t = t_tiles_end; t < t_end; ++t) {
         const float xt = to_f32(xr[t]);
         const float delta = softplus(bias + to_f32(dr[t]));
         const float dxt = delta * xt;
         if (kAgg) dsum += (j == 0) ? delta : 0.0f;
-        const float* bt = bcb + t * R + n0;
         float acc = 0.0f;
 #pragma unroll
         for (int s = 0; s < S; ++s) {
             const float abar = exp2_hw(delta * A2[s]);
-            h[s] = fmaf(abar, h[s], dxt * bt[s]);
-            if (!kAgg) acc = fmaf(bt[N + s], h[s], acc);
+            h[s] = fmaf(abar, h[s], dxt * to_f32(Bb[int64_t(n0 + s) * L + t]));
+            if (!kAgg) acc = fmaf(to_f32(Cb[int64_t(n0 + s) * L + t]), h[s], acc);
         }
         if (!kAgg) {
             acc = quad_sum(acc);
@@ -295,7 +325,9 @@ static hipError_t launch_scanq_t(const ScanLaunch& p, hipStream_t s) {
     const Tin* x = static_cast<const Tin*>(p.x);
     const Tin* dr = static_cast<const Tin*>(p.dt_raw);
     const Tin* z = static_cast<const Tin*>(p.z);
-#define SS_ARGS x, dr, z, p.dt_bias, p.A, p.Dskip, p.BC, p.h_init, p.y, p.h_last, p.dsum, p.L, \
+    const Tin* Bm = static_cast<const Tin*>(p.Bm);
+    const Tin* Cm = static_cast<const Tin*>(p.Cm);
+#define SS_ARGS x, dr, z, p.dt_bias, p.A, p.Dskip, Bm, Cm, p.h_init, p.y, p.h_last, p.dsum, p.L, \
                 p.D, p.chunk, p.K
     if (p.agg)
         hipLaunchKernelGGL((scanq_kernel<Tin, S, false, true>), grid, dim3(kThreads), 0, s, SS_ARGS);

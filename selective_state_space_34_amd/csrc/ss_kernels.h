@@ -13,7 +13,9 @@ struct ScanLaunch {
     const float* dt_bias;
     const float* A;
     const float* Dskip;
-    const float* BC;        // [B, L, 2N] float32 staging copy of B and C
+    const float* BC;        // [B, L, 2N] float32 staging copy of B and C (one-lane kernel)
+    const void* Bm;         // [B, N, L] inputs (quad kernel)
+    const void* Cm;
     const float* h_init;    // nullable; [B, D, K, N]
     float* y;               // OUT mode
     float* h_last;          // OUT: h_final (nullable); AGG: h_end [B, D, K, N]

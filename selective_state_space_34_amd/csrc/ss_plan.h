@@ -102,7 +102,8 @@ inline int make_plan(const ss_dims& d, bool backward, Plan* out) {
 
     size_t off = 0;
     p.off_bc = off;
-    off = align256(off + size_t(p.B) * size_t(p.L) * size_t(2 * N) * sizeof(float));
+    // [B, L, 2N] float32 copy of B and C: the one-lane forward kernel and the backward
+    if (backward || !p.quad) off = align256(off + size_t(p.B) * size_t(p.L) * size_t(2 * N) * sizeof(float));
     p.off_hend = p.off_dsum = p.off_hstart = p.off_gend = p.off_gstart = p.off_red = 0;
     p.red_bytes = 0;
     if (chunked) {

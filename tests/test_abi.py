@@ -53,7 +53,8 @@ def _fwd(lib, dims, ptrs=None, ws=None, wbytes=0):
 
 
 def test_fwd_validation(lib):
-    good = ss.make_dims(2, 64, 32, 16, ss.SS_F32)
+    # chunked, so that a workspace is needed and the workspace checks are reached
+    good = ss.make_dims(2, 64, 32, 16, ss.SS_F32, ss.SS_PLAN_CHUNKED, 32)
     assert _fwd(lib, None) == -1
     for bad in (ss.make_dims(0, 64, 32, 16), ss.make_dims(2, 0, 32, 16), ss.make_dims(2, 64, -1, 16),
                 ss.make_dims(2, 64, 32, 3), ss.make_dims(2, 64, 32, 64), ss.make_dims(2, 64, 32, 0),
@@ -89,15 +90,23 @@ def test_fwd_validation(lib):
 
 
 def test_workspace_sizes(lib):
-    # single pass: staging copy of B and C only
+    # single pass, quad layout: B and C are tiled straight from the inputs, no workspace
     d = ss.make_dims(8, 2048, 5120, 16, ss.SS_BF16, ss.SS_PLAN_SINGLE)
+    assert ss.workspace_size(d) == 0
+    # one lane per channel: float32 [B, L, 2N] copy of B and C
+    d = ss.make_dims(8, 2048, 5120, 16, ss.SS_BF16, ss.SS_PLAN_SINGLE, 0, ss.SS_LAYOUT_LANE)
     assert ss.workspace_size(d) == 8 * 2048 * 32 * 4
-    # chunked: staging + two state buffers + chunk sums, deterministic for the dims
+    d = ss.make_dims(8, 2047, 5120, 16, ss.SS_BF16, ss.SS_PLAN_SINGLE)  # L % 8 != 0: one lane
+    assert ss.workspace_size(d) == 8 * 2047 * 32 * 4
+    # chunked quad: two state buffers + chunk sums, deterministic for the dims
     d = ss.make_dims(1, 1 << 20, 256, 16, ss.SS_BF16, ss.SS_PLAN_CHUNKED, 1024)
     K = 1024
     st = 1 * K * 256 * 16 * 4
-    assert ss.workspace_size(d) == (1 << 20) * 32 * 4 + 2 * st + K * 256 * 4
+    assert ss.workspace_size(d) == 2 * st + K * 256 * 4
     assert ss.workspace_size(d) == ss.workspace_size(d)
+    # the backward always holds the B/C copy
+    d = ss.make_dims(8, 2048, 5120, 16, ss.SS_BF16)
+    assert ss.workspace_size(d, backward=True) > 8 * 2048 * 32 * 4
     n = ctypes.c_size_t()
     assert lib.ss_fwd_workspace_size(None, ctypes.byref(n)) == -1
     assert lib.ss_fwd_workspace_size(ctypes.byref(d), None) == -1
