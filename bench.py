@@ -102,7 +102,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c2", help="c0..c4 (default c2, D=5120 forward)")
     ap.add_argument("--plan", type=int, default=0)
-    ap.add_argument("--layout", type=int, default=0, help="0 auto, 1 quad, 2 one lane per channel")
+    ap.add_argument("--layout", type=int, default=0, help="0 auto, 1 four lanes, 2 one lane, 3 eight lanes per channel")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also launch one device copy of this many MiB (HBM counter calibration)")

@@ -71,8 +71,10 @@ typedef enum { SS_PLAN_AUTO = 0, SS_PLAN_SINGLE = 1, SS_PLAN_CHUNKED = 2 } ss_pl
  *   SS_LAYOUT_QUAD — the N states of a channel on four lanes (N >= 4, L % 8 == 0).
  *   SS_LAYOUT_LANE — one lane per channel; when A[d,n] = -(n+1) exactly for every
  *                    channel of a wavefront, exp(δA) is formed as powers of exp(-δ)
- *                    (checked on the device, otherwise the general path runs). */
-typedef enum { SS_LAYOUT_AUTO = 0, SS_LAYOUT_QUAD = 1, SS_LAYOUT_LANE = 2 } ss_layout;
+ *                    (checked on the device, otherwise the general path runs).
+ *   SS_LAYOUT_OCT  — the N states of a channel on eight lanes (N >= 8, L % 8 == 0).
+ * A layout that does not apply to the dims falls back to the widest narrower one that does. */
+typedef enum { SS_LAYOUT_AUTO = 0, SS_LAYOUT_QUAD = 1, SS_LAYOUT_LANE = 2, SS_LAYOUT_OCT = 3 } ss_layout;
 
 typedef struct ss_dims {
     int64_t batch;    /* B  >= 1 */

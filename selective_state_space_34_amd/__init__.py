@@ -19,7 +19,7 @@ from ._build import LIB, build, stale  # noqa: F401
 
 SS_F32, SS_BF16 = 0, 1
 SS_PLAN_AUTO, SS_PLAN_SINGLE, SS_PLAN_CHUNKED = 0, 1, 2
-SS_LAYOUT_AUTO, SS_LAYOUT_QUAD, SS_LAYOUT_LANE = 0, 1, 2
+SS_LAYOUT_AUTO, SS_LAYOUT_QUAD, SS_LAYOUT_LANE, SS_LAYOUT_OCT = 0, 1, 2, 3
 
 ERRORS = {0: "SS_OK", -1: "SS_ERR_NULL", -2: "SS_ERR_DIMS", -3: "SS_ERR_DTYPE", -4: "SS_ERR_ALIGN",
           -5: "SS_ERR_WORKSPACE", -6: "SS_ERR_HIP", -7: "SS_ERR_UNSUPPORTED"}

@@ -84,9 +84,9 @@ int ss_fwd(const ss_dims* dims, const void* x, const void* dt_raw, const float* 
     char* ws = static_cast<char*>(workspace);
     const int bf16 = p.in_dtype == SS_BF16;
     hipError_t e = hipSuccess;
-    // the quad kernel tiles B/C from the inputs; the one-lane kernel reads a [B, L, 2N] copy
+    // the group kernel tiles B/C from the inputs; the one-lane kernel reads a [B, L, 2N] copy
     float* BC = nullptr;
-    if (!p.quad) {
+    if (!p.group) {
         BC = reinterpret_cast<float*>(ws + p.off_bc);
         e = ss::launch_bc_stage(bf16, int(p.N), Bm, Cm, BC, p.B, p.L, stream);
         if (e != hipSuccess) return hip_fail(e);
@@ -98,7 +98,7 @@ int ss_fwd(const ss_dims* dims, const void* x, const void* dt_raw, const float* 
     s.B = p.B; s.L = p.L; s.D = p.D; s.vec = p.vec;
     if (!p.chunked) {
         s.chunk = p.L; s.K = 1; s.h_init = h0; s.y = y; s.h_last = h_final; s.agg = 0;
-        e = p.quad ? ss::launch_scanq(bf16, int(p.N), s, stream) : ss::launch_scan(bf16, int(p.N), s, stream);
+        e = p.group ? ss::launch_scang(bf16, int(p.N), p.group, s, stream) : ss::launch_scan(bf16, int(p.N), s, stream);
         if (e != hipSuccess) return hip_fail(e);
         return SS_OK;
     }
@@ -108,7 +108,7 @@ int ss_fwd(const ss_dims* dims, const void* x, const void* dt_raw, const float* 
     s.chunk = p.chunk; s.K = int(p.K);
     // 1. per-chunk aggregates
     s.h_init = nullptr; s.y = nullptr; s.h_last = h_end; s.dsum = dsum; s.agg = 1; s.z = nullptr;
-    e = p.quad ? ss::launch_scanq(bf16, int(p.N), s, stream) : ss::launch_scan(bf16, int(p.N), s, stream);
+    e = p.group ? ss::launch_scang(bf16, int(p.N), p.group, s, stream) : ss::launch_scan(bf16, int(p.N), s, stream);
     if (e != hipSuccess) return hip_fail(e);
     // 2. carry across chunks
     ss::CarryLaunch c{};
@@ -118,7 +118,7 @@ int ss_fwd(const ss_dims* dims, const void* x, const void* dt_raw, const float* 
     if (e != hipSuccess) return hip_fail(e);
     // 3. output pass from each chunk's true start state
     s.z = z; s.h_init = h_start; s.y = y; s.h_last = h_final; s.dsum = nullptr; s.agg = 0;
-    e = p.quad ? ss::launch_scanq(bf16, int(p.N), s, stream) : ss::launch_scan(bf16, int(p.N), s, stream);
+    e = p.group ? ss::launch_scang(bf16, int(p.N), p.group, s, stream) : ss::launch_scan(bf16, int(p.N), s, stream);
     if (e != hipSuccess) return hip_fail(e);
     return SS_OK;
 }

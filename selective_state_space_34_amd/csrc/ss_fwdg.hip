@@ -1,0 +1,426 @@
+// Group-split forward selective-scan kernel for gfx950.
+//
+// Same computation as scan_kernel (page "3.2 선택적 스캔(Selective Scan) 알고리즘과
+// 정보의 압축 및 선별": §1.2 softplus step, §2.1 exp discretisation of diagonal A,
+// §2.2 recurrence, §1.1 readout; SiLU gate of the note "상태공간 모델(SSM)과 Mamba
+// 아키텍처", §3), laid out for CDNA4 occupancy: the N states of a channel are split
+// over a group of G adjacent lanes (G = 4 or 8, S = N/G states per lane), so a
+// 64-lane wave covers 64/G channels and B*D channels yield B*D*G/64 waves.  G = 8
+// gives five waves per SIMD at B*D = 40960, where G = 4 leaves the SIMDs unevenly
+// loaded (2.5 waves each), but it moves more operand bytes through LDS per state-step
+// and is LDS-issue bound on gfx950 (measured slower); G = 4 is the default.
+//
+// Per 32-step tile:
+//   - the workgroup copies the tile's B and C ([B, N, L] inputs, N rows of 32 steps
+//     each) into LDS transposed to [step][B row | C row] as float32;
+//   - lane l of a group loads and prepares steps [16h + kH·l, 16h + kH·(l+1)) of both
+//     halves h of the tile (kH = 16/G): widening, δ = softplus(dt_bias + dt_raw), δ·x.
+//     No element is prepared twice.
+// Per 16-step half:
+//   - the lanes write their (δ, δ·x) pairs into a per-wave LDS row of their channel;
+//   - the recurrence walks the 16 steps; each step reads its (δ, δ·x) pair from that
+//     row and B_t, C_t for the lane's S states from the tile, one step ahead, as
+//     broadcast reads (no VALU work moves operands between lanes);
+//   - each lane's partial readouts (its S states, 16 steps) go to the same per-wave
+//     area; lane l sums the G partials of its own kH steps, adds D·x, applies the
+//     gate and stores kH outputs.
+// All global loads of the next tile (x, dt_raw, z, B/C) are issued before the current
+// tile's arithmetic.  The state never leaves VGPRs (§3.2).
+#include "ss_device.h"
+#include "ss_kernels.h"
+
+namespace ss {
+
+namespace {
+
+constexpr int kTile = 32;      // steps per tile (B/C copy, global loads, one block barrier)
+constexpr int kHalf = 16;      // steps per recurrence sweep (LDS exchange granularity)
+constexpr int kThreads = 256;  // 4 waves
+// lane stride (floats) of the partial-readout area: 20 floats = 80 bytes puts the
+// 16-byte writes of 8 consecutive lanes on 8 disjoint groups of 4 banks
+constexpr int kPS = kHalf + 4;
+// channel stride (floats) of the (δ, δ·x) rows: 34 = 2 mod 32, so the 8-byte reads of
+// up to 16 channels fall on distinct bank pairs
+constexpr int kDS = 2 * kHalf + 2;
+
+// S floats (B or C of the lane's states at one step), LDS -> VGPR
+template <int S>
+struct Row {
+    float v[S];
+    __device__ __forceinline__ void load(const float* p) {
+        if constexpr (S % 4 == 0) {
+#pragma unroll
+            for (int q = 0; q < S; q += 4) {
+                const float4 a = *reinterpret_cast<const float4*>(p + q);
+                v[q] = a.x; v[q + 1] = a.y; v[q + 2] = a.z; v[q + 3] = a.w;
+            }
+        } else if constexpr (S % 2 == 0) {
+#pragma unroll
+            for (int q = 0; q < S; q += 2) {
+                const float2 a = *reinterpret_cast<const float2*>(p + q);
+                v[q] = a.x; v[q + 1] = a.y;
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < S; ++q) v[q] = p[q];
+        }
+    }
+};
+
+// K consecutive input elements in their storage type (K = 2, 4, 8)
+template <typename Tin, int K> struct Raw;
+template <int K> struct Raw<bf16_t, K> {
+    uint32_t w[K / 2];
+    __device__ __forceinline__ void load(const bf16_t* p) {
+        if constexpr (K == 2) {
+            w[0] = *reinterpret_cast<const uint32_t*>(p);
+        } else if constexpr (K == 4) {
+            const uint2 a = *reinterpret_cast<const uint2*>(p);
+            w[0] = a.x; w[1] = a.y;
+        } else {
+            const uint4 a = *reinterpret_cast<const uint4*>(p);
+            w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+        }
+    }
+    __device__ __forceinline__ void decode(float (&o)[K]) const {
+#pragma unroll
+        for (int i = 0; i < K / 2; ++i) {
+            o[2 * i] = __uint_as_float(w[i] << 16);
+            o[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    }
+};
+template <int K> struct Raw<float, K> {
+    float v[K];
+    __device__ __forceinline__ void load(const float* p) {
+        if constexpr (K == 2) {
+            const float2 a = *reinterpret_cast<const float2*>(p);
+            v[0] = a.x; v[1] = a.y;
+        } else {
+#pragma unroll
+            for (int q = 0; q < K; q += 4) {
+                const float4 a = *reinterpret_cast<const float4*>(p + q);
+                v[q] = a.x; v[q + 1] = a.y; v[q + 2] = a.z; v[q + 3] = a.w;
+            }
+        }
+    }
+    __device__ __forceinline__ void decode(float (&o)[K]) const {
+#pragma unroll
+        for (int i = 0; i < K; ++i) o[i] = v[i];
+    }
+};
+
+// raw storage of 4 consecutive elements of one B or C row
+template <typename Tin> struct Raw4;
+template <> struct Raw4<bf16_t> {
+    uint2 v;
+    __device__ __forceinline__ void load(const bf16_t* p) { v = *reinterpret_cast<const uint2*>(p); }
+    __device__ __forceinline__ float get(int i) const {
+        const uint32_t w = (i < 2) ? v.x : v.y;
+        return __uint_as_float((i & 1) ? (w & 0xffff0000u) : (w << 16));
+    }
+};
+template <> struct Raw4<float> {
+    float4 v;
+    __device__ __forceinline__ void load(const float* p) { v = *reinterpret_cast<const float4*>(p); }
+    __device__ __forceinline__ float get(int i) const {
+        return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+    }
+};
+
+template <int K>
+__device__ __forceinline__ void store_k(float* p, const float (&v)[K]) {
+    if constexpr (K == 2) {
+        *reinterpret_cast<float2*>(p) = make_float2(v[0], v[1]);
+    } else {
+#pragma unroll
+        for (int q = 0; q < K; q += 4)
+            *reinterpret_cast<float4*>(p + q) = make_float4(v[q], v[q + 1], v[q + 2], v[q + 3]);
+    }
+}
+
+// sum over the G lanes of a group (groups are aligned runs of G lanes)
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+    for (int m = 1; m < G; m <<= 1) v += __shfl_xor(v, m, 64);
+    return v;
+}
+
+// order LDS traffic of one wave: everything before is visible to the wave's lanes after
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+}  // namespace
+
+// grid = (ceil(D / (256/G)), K, B), block = 256.  Requires L % 8 == 0 and chunk % 32 == 0
+// (or K == 1) for the tiled part; the last < 32 steps of a chunk run a per-step tail.
+template <typename Tin, int G, int S, bool kGate, bool kAgg>
+__global__ __launch_bounds__(kThreads) void scang_kernel(
+    const Tin* __restrict__ x, const Tin* __restrict__ dt_raw, const Tin* __restrict__ z,
+    const float* __restrict__ dt_bias, const float* __restrict__ A,
+    const float* __restrict__ Dskip, const Tin* __restrict__ Bm, const Tin* __restrict__ Cm,
+    const float* __restrict__ h_init, float* __restrict__ y, float* __restrict__ h_last,
+    float* __restrict__ dsum_out, int64_t L, int64_t D, int64_t chunk, int K) {
+    constexpr int N = G * S;
+    constexpr int CW = 64 / G;                    // channels per wave
+    constexpr int CB = 4 * CW;                    // channels per block
+    constexpr int kH = kHalf / G;                 // steps per lane per half
+    // LDS tile row per step: B_t (N floats) then C_t (N floats), padded by 4 floats so
+    // the transposing writes of a wave fall on at most two lanes per bank
+    constexpr int R = 2 * N + 4;
+    constexpr int TILE_F = kTile * R;
+    // per-wave exchange area: the (δ, δ·x) rows during a sweep, the partial readouts after
+    constexpr int WAREA = (64 * kPS > CW * kDS) ? 64 * kPS : CW * kDS;
+    __shared__ __align__(16) float bc_lds[2][TILE_F];
+    __shared__ __align__(16) float w_lds[4 * WAREA];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int l = lane & (G - 1);                 // lane within the group: states, steps
+    const int c = lane / G;                       // channel within the wave
+    const int64_t d_raw = int64_t(blockIdx.x) * CB + tid / G;
+    const bool valid = d_raw < D;
+    const int64_t d = valid ? d_raw : D - 1;      // clamped for loads
+    const int k = blockIdx.y;
+    const int b = blockIdx.z;
+    const int64_t t_begin = int64_t(k) * chunk;
+    const int64_t t_end = (t_begin + chunk < L) ? t_begin + chunk : L;
+    const int64_t n_tiles = (t_end - t_begin) / kTile;
+    const int64_t t_tiles_end = t_begin + n_tiles * kTile;
+    const int n0 = l * S;
+
+    float A2[S], h[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) A2[s] = A[d * N + n0 + s] * kLog2e;
+    const int64_t hidx = ((int64_t(b) * D + d) * K + k) * N + n0;
+#pragma unroll
+    for (int s = 0; s < S; ++s) h[s] = h_init ? h_init[hidx + s] : 0.0f;
+    const float bias = dt_bias[d];
+    const float Dd = kAgg ? 0.0f : Dskip[d];
+    const int64_t row = (int64_t(b) * D + d) * L;
+    const Tin* xr = x + row;
+    const Tin* dr = dt_raw + row;
+    const Tin* zr = kGate ? z + row : nullptr;
+    float* yr = kAgg ? nullptr : y + row;
+    const Tin* Bb = Bm + int64_t(b) * N * L;
+    const Tin* Cb = Cm + int64_t(b) * N * L;
+    float dsum = 0.0f;
+
+    // B/C tile copy: 2·N rows of 32 steps; unit e covers steps 4q..4q+3 of state n of
+    // B (m = 0) or C (m = 1), with n fastest across lanes
+    constexpr int BC_UNITS = 2 * N * (kTile / 4);
+    constexpr int BC_PASSES = (BC_UNITS + kThreads - 1) / kThreads;
+    Raw4<Tin> bc_next[BC_PASSES];
+    Raw<Tin, kH> xn[2], dn[2], zn[2];
+
+    auto issue_loads = [&](int64_t t0) {
+#pragma unroll
+        for (int p = 0; p < BC_PASSES; ++p) {
+            const int e = tid + p * kThreads;
+            if (BC_UNITS % kThreads == 0 || e < BC_UNITS) {
+                const int n = e % N, q = (e / N) % (kTile / 4), m = e / (N * (kTile / 4));
+                bc_next[p].load((m ? Cb : Bb) + int64_t(n) * L + t0 + 4 * q);
+            }
+        }
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const int64_t te = t0 + kHalf * hh + kH * l;
+            xn[hh].load(xr + te);
+            dn[hh].load(dr + te);
+            if (kGate && !kAgg) zn[hh].load(zr + te);
+        }
+    };
+
+    if (n_tiles > 0) issue_loads(t_begin);
+    float* wa = w_lds + (tid >> 6) * WAREA;       // this wave's exchange area
+    float* dd_row = wa + c * kDS;                 // (δ, δ·x) of this lane's channel
+    float* mine = wa + lane * kPS;                // this lane's partial readouts
+
+    for (int64_t it = 0; it < n_tiles; ++it) {
+        const int64_t t0 = t_begin + it * kTile;
+        float* buf = bc_lds[it & 1];
+#pragma unroll
+        for (int p = 0; p < BC_PASSES; ++p) {
+            const int e = tid + p * kThreads;
+            if (BC_UNITS % kThreads == 0 || e < BC_UNITS) {
+                const int n = e % N, q = (e / N) % (kTile / 4), m = e / (N * (kTile / 4));
+                float* dst = buf + 4 * q * R + m * N + n;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dst[i * R] = bc_next[p].get(i);
+            }
+        }
+        float xv[2][kH], dv[2][kH], zv[2][kH];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            xn[hh].decode(xv[hh]);
+            dn[hh].decode(dv[hh]);
+            if (kGate && !kAgg) zn[hh].decode(zv[hh]);
+        }
+        if (it + 1 < n_tiles) issue_loads(t0 + kTile);
+        __syncthreads();
+
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            // this lane's kH steps of the half: (δ, δ·x) into the channel's row
+#pragma unroll
+            for (int i = 0; i < kH; ++i) {
+                const float dl = softplus(bias + dv[hh][i]);
+                if (kAgg) dsum += dl;
+                *reinterpret_cast<float2*>(dd_row + 2 * (kH * l + i)) = make_float2(dl, dl * xv[hh][i]);
+            }
+            wave_sync();
+
+            // recurrence over the half; operands of step t+1 are read during step t
+            const float* bh = buf + kHalf * hh * R;
+            float part[kHalf];
+            Row<S> bcur, ccur, bnxt, cnxt;
+            float2 dcur, dnxt;
+            bnxt.load(bh + n0);
+            if (!kAgg) cnxt.load(bh + N + n0);
+            dnxt = *reinterpret_cast<const float2*>(dd_row);
+#pragma unroll
+            for (int t = 0; t < kHalf; ++t) {
+                bcur = bnxt;
+                if (!kAgg) ccur = cnxt;
+                dcur = dnxt;
+                if (t + 1 < kHalf) {
+                    bnxt.load(bh + (t + 1) * R + n0);
+                    if (!kAgg) cnxt.load(bh + (t + 1) * R + N + n0);
+                    dnxt = *reinterpret_cast<const float2*>(dd_row + 2 * (t + 1));
+                }
+                __builtin_amdgcn_sched_barrier(0);  // keep the next step's reads issued here
+                float acc = 0.0f;
+#pragma unroll
+                for (int s = 0; s < S; ++s) {
+                    const float abar = exp2_hw(dcur.x * A2[s]);
+                    h[s] = fmaf(abar, h[s], dcur.y * bcur.v[s]);
+                    if (!kAgg) acc = fmaf(ccur.v[s], h[s], acc);
+                }
+                part[t] = acc;
+            }
+            wave_sync();  // every lane's reads of the rows are done before partials land
+
+            if (!kAgg) {
+                // partial readouts through the wave's area: each lane writes its 16, then
+                // gathers the G partials of its own kH steps
+#pragma unroll
+                for (int q = 0; q < kHalf; q += 4)
+                    *reinterpret_cast<float4*>(mine + q) =
+                        make_float4(part[q], part[q + 1], part[q + 2], part[q + 3]);
+                wave_sync();
+                float sum[kH];
+#pragma unroll
+                for (int i = 0; i < kH; ++i) sum[i] = 0.0f;
+                const int gbase = lane & ~(G - 1);
+                // lane l starts at source l (rotation): lanes served together read
+                // different source rows
+#pragma unroll
+                for (int r = 0; r < G; ++r) {
+                    const int src = (l + r) & (G - 1);
+                    Row<kH> pr;
+                    pr.load(wa + (gbase + src) * kPS + kH * l);
+#pragma unroll
+                    for (int i = 0; i < kH; ++i) sum[i] += pr.v[i];
+                }
+                float out[kH];
+#pragma unroll
+                for (int i = 0; i < kH; ++i) {
+                    float sv = fmaf(Dd, xv[hh][i], sum[i]);
+                    if (kGate) sv *= silu(zv[hh][i]);
+                    out[i] = sv;
+                }
+                if (valid) store_k<kH>(yr + t0 + kHalf * hh + kH * l, out);
+                wave_sync();  // gathers done before the next half's rows overwrite the area
+            }
+        }
+    }
+
+    // tail: the last (t_end - t_tiles_end) < 32 steps, one step at a time; every lane
+    // prepares the step itself and reads its B/C straight from the inputs
+    for (int64_t t = t_tiles_end; t < t_end; ++t) {
+        const float xt = to_f32(xr[t]);
+        const float delta = softplus(bias + to_f32(dr[t]));
+        const float dxt = delta * xt;
+        if (kAgg) dsum += (l == 0) ? delta : 0.0f;
+        float acc = 0.0f;
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            const float abar = exp2_hw(delta * A2[s]);
+            h[s] = fmaf(abar, h[s], dxt * to_f32(Bb[int64_t(n0 + s) * L + t]));
+            if (!kAgg) acc = fmaf(to_f32(Cb[int64_t(n0 + s) * L + t]), h[s], acc);
+        }
+        if (!kAgg) {
+            acc = group_sum<G>(acc);
+            float sv = fmaf(Dd, xt, acc);
+            if (kGate) sv *= silu(to_f32(zr[t]));
+            if (valid && l == 0) yr[t] = sv;
+        }
+    }
+
+    if (kAgg) {
+        dsum = group_sum<G>(dsum);
+        const int64_t aidx = (int64_t(b) * D + d) * K + k;
+        if (valid) {
+#pragma unroll
+            for (int s = 0; s < S; ++s) h_last[aidx * N + n0 + s] = h[s];
+            if (l == 0) dsum_out[aidx] = dsum;
+        }
+    } else if (h_last && k == K - 1 && valid) {
+        const int64_t fidx = (int64_t(b) * D + d) * N + n0;
+#pragma unroll
+        for (int s = 0; s < S; ++s) h_last[fidx + s] = h[s];
+    }
+}
+
+template <typename Tin, int G, int S>
+static hipError_t launch_scang_t(const ScanLaunch& p, hipStream_t s) {
+    constexpr int CB = 4 * 64 / G;
+    dim3 grid(unsigned((p.D + CB - 1) / CB), unsigned(p.K), unsigned(p.B));
+    const Tin* x = static_cast<const Tin*>(p.x);
+    const Tin* dr = static_cast<const Tin*>(p.dt_raw);
+    const Tin* z = static_cast<const Tin*>(p.z);
+    const Tin* Bm = static_cast<const Tin*>(p.Bm);
+    const Tin* Cm = static_cast<const Tin*>(p.Cm);
+#define SS_ARGS x, dr, z, p.dt_bias, p.A, p.Dskip, Bm, Cm, p.h_init, p.y, p.h_last, p.dsum, p.L, \
+                p.D, p.chunk, p.K
+    if (p.agg)
+        hipLaunchKernelGGL((scang_kernel<Tin, G, S, false, true>), grid, dim3(kThreads), 0, s, SS_ARGS);
+    else if (p.z)
+        hipLaunchKernelGGL((scang_kernel<Tin, G, S, true, false>), grid, dim3(kThreads), 0, s, SS_ARGS);
+    else
+        hipLaunchKernelGGL((scang_kernel<Tin, G, S, false, false>), grid, dim3(kThreads), 0, s, SS_ARGS);
+#undef SS_ARGS
+    return hipGetLastError();
+}
+
+template <typename Tin>
+static hipError_t launch_scang_dt(int N, int G, const ScanLaunch& p, hipStream_t s) {
+    if (G == 4) {
+        switch (N) {
+            case 4: return launch_scang_t<Tin, 4, 1>(p, s);
+            case 8: return launch_scang_t<Tin, 4, 2>(p, s);
+            case 16: return launch_scang_t<Tin, 4, 4>(p, s);
+            case 32: return launch_scang_t<Tin, 4, 8>(p, s);
+            default: return hipErrorInvalidValue;
+        }
+    }
+    if (G == 8) {
+        switch (N) {
+            case 8: return launch_scang_t<Tin, 8, 1>(p, s);
+            case 16: return launch_scang_t<Tin, 8, 2>(p, s);
+            case 32: return launch_scang_t<Tin, 8, 4>(p, s);
+            default: return hipErrorInvalidValue;
+        }
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_scang(int bf16, int N, int G, const ScanLaunch& p, hipStream_t s) {
+    return bf16 ? launch_scang_dt<bf16_t>(N, G, p, s) : launch_scang_dt<float>(N, G, p, s);
+}
+
+}  // namespace ss

@@ -14,7 +14,7 @@ struct ScanLaunch {
     const float* A;
     const float* Dskip;
     const float* BC;        // [B, L, 2N] float32 staging copy of B and C (one-lane kernel)
-    const void* Bm;         // [B, N, L] inputs (quad kernel)
+    const void* Bm;         // [B, N, L] inputs (group kernel)
     const void* Cm;
     const float* h_init;    // nullable; [B, D, K, N]
     float* y;               // OUT mode
@@ -83,8 +83,8 @@ struct BwdLaunch {
 hipError_t launch_bc_stage(int bf16, int N, const void* Bm, const void* Cm, float* BC, int64_t B,
                            int64_t L, hipStream_t s);
 hipError_t launch_scan(int bf16, int N, const ScanLaunch& p, hipStream_t s);
-// quad-split layout (N in {4, 8, 16, 32}, L % 8 == 0)
-hipError_t launch_scanq(int bf16, int N, const ScanLaunch& p, hipStream_t s);
+// group-split layout: G = 4 (N in {4, 8, 16, 32}) or G = 8 (N in {8, 16, 32}); L % 8 == 0
+hipError_t launch_scang(int bf16, int N, int G, const ScanLaunch& p, hipStream_t s);
 hipError_t launch_carry(int N, const CarryLaunch& p, hipStream_t s);
 hipError_t launch_bwd(int bf16, const BwdLaunch& p, hipStream_t s);
 hipError_t launch_bwd_reduce(const BwdLaunch& p, hipStream_t s);

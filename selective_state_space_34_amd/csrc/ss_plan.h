@@ -17,7 +17,7 @@ struct Plan {
     int64_t chunk;   // steps per chunk (multiple of 8 unless chunk == L)
     int64_t K;       // number of chunks
     int vec;         // L % 8 == 0: 8-step vector loads
-    int quad;        // forward uses the quad-split kernel (N >= 4 and vec)
+    int group;       // forward: lanes per channel of the group kernel (4 or 8), 0 = one lane
     // workspace carving (byte offsets, 256-aligned)
     size_t off_bc, off_hend, off_dsum, off_hstart, off_gend, off_gstart, off_red;
     size_t red_bytes;
@@ -47,7 +47,8 @@ inline int make_plan(const ss_dims& d, bool backward, Plan* out) {
     if (d.in_dtype != SS_F32 && d.in_dtype != SS_BF16) return SS_ERR_DTYPE;
     if (d.plan != SS_PLAN_AUTO && d.plan != SS_PLAN_SINGLE && d.plan != SS_PLAN_CHUNKED)
         return SS_ERR_DTYPE;
-    if (d.layout != SS_LAYOUT_AUTO && d.layout != SS_LAYOUT_QUAD && d.layout != SS_LAYOUT_LANE)
+    if (d.layout != SS_LAYOUT_AUTO && d.layout != SS_LAYOUT_QUAD && d.layout != SS_LAYOUT_LANE &&
+        d.layout != SS_LAYOUT_OCT)
         return SS_ERR_DTYPE;
     if (d.reserved != 0) return SS_ERR_DTYPE;
     if (d.batch <= 0 || d.seqlen <= 0 || d.dim <= 0 || d.dstate <= 0) return SS_ERR_DIMS;
@@ -61,22 +62,22 @@ inline int make_plan(const ss_dims& d, bool backward, Plan* out) {
     if (d.batch > kMaxGridYZ) return SS_ERR_DIMS;
     p.B = d.batch; p.L = d.seqlen; p.D = d.dim; p.N = N; p.in_dtype = d.in_dtype;
     p.vec = (p.L % 8) == 0;
-    const bool quad_ok = p.vec && N >= 4;
-
-    // 64-lane waves of one pass: a quad of lanes per channel (the quad layout's reason
-    // to exist: 4x the waves of one lane per channel)
-    const int64_t qwaves = quad_ok ? (p.B * p.D + 15) / 16 : (p.B * p.D + 63) / 64;
+    // layout: a group of G lanes per channel (G x the waves of one lane per channel).
+    // Automatic choice: four lanes wherever they apply.  Measured on MI355X, eight lanes
+    // balance the SIMDs better at B*D = 40960 but saturate the LDS (their operand
+    // traffic per state-step is higher) and lose on every workload; one lane per channel
+    // loses on every workload too.
+    const int gmax = !p.vec ? 0 : N >= 8 ? 8 : N >= 4 ? 4 : 0;
+    if (d.layout == SS_LAYOUT_LANE) p.group = 0;
+    else if (d.layout == SS_LAYOUT_OCT) p.group = gmax;
+    else p.group = gmax >= 4 ? 4 : 0;
+    const int64_t waves = p.group ? (p.B * p.D * p.group + 63) / 64 : (p.B * p.D + 63) / 64;
     int chunked = backward ? 1 : 0;
     if (!backward) {
         if (d.plan == SS_PLAN_CHUNKED) chunked = 1;
         else if (d.plan == SS_PLAN_SINGLE) chunked = 0;
-        else chunked = (qwaves < kSingleWaves && p.L > 512) ? 1 : 0;
+        else chunked = (waves < kSingleWaves && p.L > 512) ? 1 : 0;
     }
-    // layout: the quad layout wherever it applies (measured faster than one lane per
-    // channel on every workload, single-pass or chunked, even with the S4D power path)
-    if (d.layout == SS_LAYOUT_LANE) p.quad = 0;
-    else p.quad = quad_ok;
-    const int64_t waves = p.quad ? qwaves : (p.B * p.D + 63) / 64;
     int64_t chunk = p.L;
     if (backward) {
         // 16-step tiles, at most four per chunk (tile start states live in LDS)
@@ -103,7 +104,7 @@ inline int make_plan(const ss_dims& d, bool backward, Plan* out) {
     size_t off = 0;
     p.off_bc = off;
     // [B, L, 2N] float32 copy of B and C: the one-lane forward kernel and the backward
-    if (backward || !p.quad) off = align256(off + size_t(p.B) * size_t(p.L) * size_t(2 * N) * sizeof(float));
+    if (backward || !p.group) off = align256(off + size_t(p.B) * size_t(p.L) * size_t(2 * N) * sizeof(float));
     p.off_hend = p.off_dsum = p.off_hstart = p.off_gend = p.off_gstart = p.off_red = 0;
     p.red_bytes = 0;
     if (chunked) {

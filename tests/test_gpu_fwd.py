@@ -84,8 +84,9 @@ EDGE = [
     (2, 2048, 96, 16, "bf16", True, True, 2, 128),
     (1, 4099, 64, 16, "f32", True, True, 2, 256),   # ragged tail in the last chunk
     (2, 520, 300, 16, "f32", True, True, 1, 0),
-    # quad-split kernel: N = 4 (one state per lane), chunk not a multiple of the 32-step
-    # tile, float32 inputs, D not a multiple of 64, short chunks that are all tail
+    # group kernels: N = 4 (one state per lane at G = 4), chunk not a multiple of the
+    # 32-step tile, float32 inputs, D not a multiple of a block's channels, short chunks
+    # that are all tail
     (2, 1024, 40, 4, "f32", True, True, 0, 0),
     (1, 4000, 70, 16, "bf16", True, True, 2, 40),
     (3, 96, 200, 16, "f32", False, True, 2, 16),
@@ -93,12 +94,13 @@ EDGE = [
 ]
 
 
+@pytest.mark.parametrize("layout", [0, 1, 3], ids=["auto", "quad", "oct"])
 @pytest.mark.parametrize("case", EDGE, ids=lambda c: "B{}L{}D{}N{}-{}-g{}-h{}-p{}-c{}".format(*c))
-def test_edge_shapes(gpu, case):
+def test_edge_shapes(gpu, case, layout):
     Bn, L, D, N, dt, gate, h0, plan, chunk = case
     inp = make_inputs(Bn, L, D, N, dtype=dt, seed=100 + L, gate=gate, with_h0=h0, a_perturb=True)
-    note(f"edge {case}")
-    y, hf = gpu_fwd(gpu, inp, gate=gate, h0=h0, final=True, plan=plan, chunk=chunk)
+    note(f"edge {case} layout={layout}")
+    y, hf = gpu_fwd(gpu, inp, gate=gate, h0=h0, final=True, plan=plan, chunk=chunk, layout=layout)
     yr, hr = oracle_fwd(inp, gate=gate, h0=h0)
     assert_close(y, yr, tol_for(inp), "y")
     assert_close(hf, hr, tol_for(inp), "h_final")
@@ -118,12 +120,14 @@ def test_step_size_extremes(gpu, bias):
 
 @pytest.mark.parametrize("a_perturb", [True, False], ids=["A_general", "A_s4d"])
 def test_plans_agree_and_deterministic(gpu, a_perturb):
-    """single / chunked plans and quad / one-lane layouts agree; each is deterministic."""
+    """single / chunked plans and the eight-, four- and one-lane layouts agree; each is
+    deterministic."""
     inp = make_inputs(2, 4096, 192, 16, dtype="bf16", seed=8, gate=True, with_h0=True,
                       a_perturb=a_perturb)
     note(f"plan agreement a_perturb={a_perturb}")
     y1, h1 = gpu_fwd(gpu, inp, plan=1, layout=1)
-    for plan, layout, chunk in ((2, 1, 512), (2, 2, 512), (1, 2, 0), (2, 2, 256)):
+    for plan, layout, chunk in ((2, 1, 512), (2, 2, 512), (1, 2, 0), (2, 2, 256), (1, 3, 0),
+                                (2, 3, 512), (2, 3, 96)):
         y2, h2 = gpu_fwd(gpu, inp, plan=plan, layout=layout, chunk=chunk)
         y3, h3 = gpu_fwd(gpu, inp, plan=plan, layout=layout, chunk=chunk)
         assert np.array_equal(y2, y3) and np.array_equal(h2, h3), f"not deterministic {plan} {layout}"
@@ -139,7 +143,7 @@ def test_s4d_detection_per_wave(gpu):
     inp = make_inputs(1, 512, 200, 16, seed=12, gate=True, with_h0=True)
     inp.A[77, 5] *= 1.01
     note("s4d detection")
-    for layout in (2, 1):
+    for layout in (2, 1, 3):
         y, hf = gpu_fwd(gpu, inp, plan=2, chunk=128, layout=layout)
         yr, hr = oracle_fwd(inp)
         assert_close(y, yr, 1e-4, f"y layout {layout}")
