@@ -2,7 +2,7 @@
 """Benchmark of the MI355X selective-scan forward (one GPU).
 
 One step = one ss_fwd call over one batch of synthetic input already resident in
-HBM: B/C staging + the fused scan (softplus step size, exp discretisation,
+HBM: the fused scan (B/C tiles through LDS, softplus step size, exp discretisation,
 recurrence, readout, D skip, SiLU gate), i.e. every forward row of the hot path.
 For the fwd+bwd workload (--workload c4) a step is ss_fwd followed by ss_bwd.
 Default workload: S6 fwd + gate, bf16 x/z/dt_raw/B/C, fp32 A/D/dt_bias/state/y,
@@ -10,12 +10,15 @@ B=8 L=2048 D=5120 N=16.
 
 Prints ONE JSON line on stdout (everything else goes to stderr):
   value        B·L·D elements/s over the timed steps
-  roofline     the scan kernel against its binding roof (ALU), with the
-               HBM view (minimum bytes / time vs 8 TB/s) beside it
+  roofline     the scan kernel against its binding roof (the VALU issue rate: 256 CUs x
+               4 SIMDs x 16 lanes x 2.4 GHz, packed fp32 unused), with its measured HBM
+               traffic while the sources match the profiled ones, and the HBM view
+               (minimum bytes / time vs 8 TB/s) beside it
   cpu_baseline the fp64 C oracle on a bounded sample of the same workload, host cores
 """
 import argparse
 import ctypes
+import hashlib
 import json
 import os
 import sys
@@ -30,6 +33,34 @@ HBM_PEAK_GBPS = 8000.0
 # ALU roof: 256 CUs x 4 SIMDs x 16 fp32 lanes x 2.4 GHz = 39.32e12 VALU lane-slots/s
 # (packed fp32 is not used; transcendentals issue at half rate = 2 slots each).
 ALU_PEAK_TSLOTS = 256 * 4 * 16 * 2.4e9 / 1e12
+
+
+# HBM traffic of the forward kernel per launch, from two rocprofv3 counter passes
+# (FETCH_SIZE, WRITE_SIZE) that each also ran a 1 GiB device copy: the copy reads
+# FETCH_SIZE = 512 MiB and WRITE_SIZE = 1 GiB, so reads = 2.0 x FETCH_SIZE and writes =
+# 1.0 x WRITE_SIZE.  A figure is reported only while the forward's sources hash to the
+# value it was measured with; after any change it is null until measured again.
+FWD_SOURCES = ["ss_fwdg.hip", "ss_device.h", "ss_plan.h", "ss_api.cpp", "ss_kernels.h"]
+FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
+MEASURED_TRAFFIC = {
+    "c2": {"sources_sha256": "e0b51490fa527f1349b6074c056f7e04694af5be09d0bb2f69cba0453ecc872d",
+           "fetch_kib": 339216, "write_kib": 413083},
+}
+
+
+def fwd_sources_sha256():
+    h = hashlib.sha256()
+    for f in FWD_SOURCES:
+        with open(os.path.join(ROOT, "selective_state_space_34_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(w):
+    m = MEASURED_TRAFFIC.get(w.name)
+    if m is None or w.backward or m["sources_sha256"] != fwd_sources_sha256():
+        return None
+    return FETCH_SCALE * m["fetch_kib"] * 1024 + WRITE_SCALE * m["write_kib"] * 1024
 
 
 def log(*a):
@@ -72,6 +103,20 @@ def alu_slots_per_elem(w):
     return per_state + elem
 
 
+def bwd_alu_slots_per_elem(w):
+    """Algorithmic VALU lane-slots per element of the backward (transcendental = 2 slots).
+    Per state: recompute h (δ·A, exp 2, δx·B, FMA: 5); adjoint g += ds·C (1), dC term ds·h (1),
+    dB term g·δx (1), Σ g·B (1), g·Ā·h_prev (2), dA FMA (1), Σ A·g·Ā·h_prev (1), g *= Ā (1);
+    the channel sums of dB and dC (2) -> 17 x N.  Per element: softplus 9, sigmoid(u) 4,
+    dx 2, dΔ 2, dD 1, with a gate sigmoid(z) 4 + ds 2 + dz 5; bf16 widening per bf16 input."""
+    elem = 9 + 4 + 2 + 2 + 1
+    if w.gate:
+        elem += 4 + 2 + 5
+    if w.dtype == "bf16":
+        elem += 3 if w.gate else 2
+    return 17 * w.dstate + elem
+
+
 def cpu_baseline(w, inp, budget_s=4.0):
     """Time the fp64 C oracle (as it stands) on a growing sample of channels until
     one run takes about budget_s seconds of wall time on all host threads."""
@@ -95,6 +140,11 @@ def cpu_baseline(w, inp, budget_s=4.0):
                       f"{dt:.2f} s wall on {threads} OpenMP threads"}
 
 
+def dims_plan_single(ss, dims):
+    """True when the forward runs as one kernel launch (no chunk workspace)."""
+    return ss.workspace_size(dims) == 0
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -110,7 +160,7 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the scan shards by batch/channel with no exchange in the forward; see DESIGN.md)",
+              "(the forward would shard by batch or channel with no exchange)",
               file=sys.stderr)
         sys.exit(2)
 
@@ -198,14 +248,15 @@ def main():
     mb = min_bytes(w, s_in)
     t_avg = float(per.mean())
     value = elems * args.steps / wall
-    slots = elems * alu_slots_per_elem(w)
+    slots_pe = alu_slots_per_elem(w) + (bwd_alu_slots_per_elem(w) if w.backward else 0)
+    slots = elems * slots_pe
     alu_achieved = slots / t_avg / 1e12
     hbm_achieved = mb / t_avg / 1e9
     log(f"[bench] per-step event time avg {t_avg * 1e6:.1f} us (min {per.min() * 1e6:.1f}, "
         f"max {per.max() * 1e6:.1f}); wall {wall / args.steps * 1e6:.1f} us/step")
     log(f"[bench] HBM view: {mb / 1e6:.1f} MB min bytes -> {hbm_achieved:.0f} GB/s "
         f"({hbm_achieved / HBM_PEAK_GBPS:.3f} of 8 TB/s)")
-    log(f"[bench] ALU view: {alu_slots_per_elem(w)} slots/elem -> {alu_achieved:.2f} T slots/s "
+    log(f"[bench] ALU view: {slots_pe} slots/elem -> {alu_achieved:.2f} T slots/s "
         f"({alu_achieved / ALU_PEAK_TSLOTS:.3f} of {ALU_PEAK_TSLOTS:.2f})")
 
     cpu = None
@@ -232,9 +283,12 @@ def main():
                    "plan": args.plan, "layout": args.layout},
         "roofline": {"bound": "alu", "achieved": alu_achieved, "peak": ALU_PEAK_TSLOTS,
                      "unit": "T VALU-slot/s", "frac": alu_achieved / ALU_PEAK_TSLOTS,
-                     "traffic": None,
-                     "kernel": "ss_fwd (bc_stage + scan)", "launch_us": t_avg * 1e6,
-                     "slots_per_elem": alu_slots_per_elem(w)},
+                     "traffic": measured_traffic(w),
+                     "kernel": ("ss_fwd + ss_bwd step (every kernel of both calls)" if w.backward
+                                else "ss_fwd (scang_kernel, one launch per call)"
+                                if dims_plan_single(ss, dims) else "ss_fwd (all passes)"),
+                     "launch_us": t_avg * 1e6, "slots_per_elem": slots_pe,
+                     "traffic_algorithmic_bytes": mb if not w.backward else None},
         "hbm": {"min_bytes": mb, "achieved_gbps": hbm_achieved, "peak_gbps": HBM_PEAK_GBPS,
                 "frac": hbm_achieved / HBM_PEAK_GBPS},
         "cpu_baseline": cpu,

@@ -13,8 +13,15 @@ Sources (cited by page title and section):
   [REV]  Review of "Mamba: Linear-Time Sequence Modeling with Selective State
          Spaces" (honbul.tistory.com): §2 definition of S6.
 
-What it computes, per batch row b and channel d (readings of the pages that the
-text leaves open are marked R#, listed in the design doc):
+Where the pages leave a point open, the plainest reading the rest supports is taken
+(marked R#):
+  R1  B̄ = δ·B, the first-order form; the exact zero-order-hold (δA)⁻¹(e^{δA} − 1)·δB that
+      [SEL §2.1] prints reduces to it as δA -> 0, and [SEL §4.1] reasons with it.
+  R5  the readout adds D·x to Σ_n C h (D = 0 gives the pages' form).
+  R6  the SiLU branch multiplies the readout: y = (C·h + D·x)·silu(z).
+  R7  the state before the first step is h0 (or 0); h_final is the state after the last.
+
+What it computes, per batch row b and channel d:
   u_t     = dt_bias[d] + dt_raw[b,d,t]                    [SEL §1.2], [REV §2]
   δ_t     = softplus(u_t) = log(1 + e^{u_t})              [SEL §1.2]
   Ā_{t,n} = exp(δ_t A[d,n])                               [SEL §2.1]; A diagonal, so elementwise
