@@ -154,6 +154,8 @@ def main():
     ap.add_argument("--plan", type=int, default=0)
     ap.add_argument("--layout", type=int, default=0, help="0 auto, 1 four lanes, 2 one lane, 3 eight lanes per channel")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ckpt", action="store_true",
+                    help="fwd+bwd: recompute chunk start states instead of using checkpoints")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also launch one device copy of this many MiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -186,17 +188,23 @@ def main():
                         ss.SS_BF16 if w.dtype == "bf16" else ss.SS_F32, args.plan, 0, args.layout)
     ws = torch.empty(max(ss.workspace_size(dims), 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
+    hck = None
     if w.backward:
         dy = t32(inp.dy)
         wsb = torch.empty(ss.workspace_size(dims, backward=True), dtype=torch.uint8, device=dev)
         grads = ss.ss_bwd(x, dtr, dtb, A, Bm, Cm, Dk, dy, z=z)
+        # training use: the forward keeps its 16-step state checkpoints for the backward
+        if not args.no_ckpt:
+            nck = (w.seqlen + ss.CKPT_STEPS - 1) // ss.CKPT_STEPS
+            hck = torch.empty((w.batch, w.dim, nck, w.dstate), dtype=torch.float32, device=dev)
 
     def fwd_call():
-        ss.ss_fwd(x, dtr, dtb, A, Bm, Cm, Dk, z=z, y=y, h_final=hf, workspace=ws,
+        ss.ss_fwd(x, dtr, dtb, A, Bm, Cm, Dk, z=z, y=y, h_final=hf, h_ckpt=hck, workspace=ws,
                   plan=args.plan, layout=args.layout, stream=stream)
 
     def bwd_call():
-        ss.ss_bwd(x, dtr, dtb, A, Bm, Cm, Dk, dy, z=z, workspace=wsb, out=grads, stream=stream)
+        ss.ss_bwd(x, dtr, dtb, A, Bm, Cm, Dk, dy, z=z, h_ckpt=hck, workspace=wsb, out=grads,
+                  stream=stream)
 
     def step():
         fwd_call()
@@ -280,7 +288,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{w.name}: {w.label}", "batch": w.batch, "seqlen": w.seqlen,
                    "dim": w.dim, "dstate": w.dstate, "in_dtype": w.dtype, "gate": w.gate,
-                   "plan": args.plan, "layout": args.layout},
+                   "plan": args.plan, "layout": args.layout,
+                   "checkpoints": bool(w.backward and not args.no_ckpt)},
         "roofline": {"bound": "alu", "achieved": alu_achieved, "peak": ALU_PEAK_TSLOTS,
                      "unit": "T VALU-slot/s", "frac": alu_achieved / ALU_PEAK_TSLOTS,
                      "traffic": measured_traffic(w),

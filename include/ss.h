@@ -23,6 +23,7 @@
  *   A, dA                                 : [D, N]
  *   dt_bias, Dskip, ddt_bias, dD          : [D]
  *   h0, h_final, dh_final, dh0            : [B, D, N]
+ *   h_ckpt                                : [B, D, ceil(L / 16), N]
  * x, dt_raw, z, Bm, Cm have the dtype ss_dims.in_dtype (float32 or bfloat16);
  * every other array, including all outputs and all gradients, is float32.
  *
@@ -52,7 +53,7 @@ extern "C" {
 #endif
 
 #define SS_VERSION_MAJOR 0
-#define SS_VERSION_MINOR 1
+#define SS_VERSION_MINOR 2
 
 /* dtype of x, dt_raw, z, Bm, Cm */
 typedef enum { SS_F32 = 0, SS_BF16 = 1 } ss_dtype;
@@ -111,23 +112,30 @@ int ss_bwd_workspace_size(const ss_dims* dims, size_t* bytes);
  *   z       : NULL = no gate.
  *   h0      : NULL = zero initial state.
  *   h_final : NULL = final state not written.
+ *   h_ckpt  : NULL = not written; else the state entering steps 0, 16, 32, ... (entry i is
+ *             the state before step 16·i; entry 0 is h0 or 0): the checkpoints ss_bwd can
+ *             take instead of recomputing chunk start states.  With a user-chosen chunk
+ *             that is not a multiple of 16 on the four-lane layout: SS_ERR_UNSUPPORTED.
  *   workspace / workspace_bytes : at least ss_fwd_workspace_size bytes of device memory. */
 int ss_fwd(const ss_dims* dims,
            const void* x, const void* dt_raw, const float* dt_bias, const float* A,
            const void* Bm, const void* Cm, const float* Dskip, const void* z, const float* h0,
-           float* y, float* h_final,
+           float* y, float* h_final, float* h_ckpt,
            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Backward: gradients of sum(dy·y) + sum(dh_final·h_final) with respect to every
  * input, recomputing the states from the inputs (§3.3) instead of storing them.
  *   Inputs as ss_fwd; dy required; dh_final NULL = zero.
+ *   h_ckpt : NULL = the chunk start states are recomputed here; else the checkpoints an
+ *            ss_fwd call on these same inputs (and h0) wrote, from which every 16-step
+ *            tile's states are recomputed (one forward sweep and one carry fewer).
  *   dx, ddt_raw, ddt_bias, dA, dB, dC, dD : required outputs.
  *   dz  : required iff z is given (else must be NULL).
  *   dh0 : required iff h0 is given (else must be NULL). */
 int ss_bwd(const ss_dims* dims,
            const void* x, const void* dt_raw, const float* dt_bias, const float* A,
            const void* Bm, const void* Cm, const float* Dskip, const void* z, const float* h0,
-           const float* dy, const float* dh_final,
+           const float* dy, const float* dh_final, const float* h_ckpt,
            float* dx, float* ddt_raw, float* ddt_bias, float* dA, float* dB, float* dC,
            float* dD, float* dz, float* dh0,
            void* workspace, size_t workspace_bytes, hipStream_t stream);

@@ -6,10 +6,12 @@ PyTorch fallback: if the compiled library is missing, ``load()`` raises.
 
     y = ss_fwd(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, z=None, h0=None)
     y, h_final = ss_fwd(..., return_final=True)
-    grads = ss_bwd(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, dy, z=None, h0=None, dh_final=None)
+    y, h_final, h_ckpt = ss_fwd(..., return_final=True, return_ckpt=True)
+    grads = ss_bwd(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, dy, z=None, h0=None, dh_final=None,
+                   h_ckpt=None)
 
 Layouts: x, dt_raw, z, y [B, D, L]; Bm, Cm [B, N, L]; A [D, N]; dt_bias, Dskip [D];
-h0, h_final [B, D, N].  x, dt_raw, z, Bm, Cm are float32 or bfloat16 (all the same);
+h0, h_final [B, D, N]; h_ckpt [B, D, ceil(L/16), N] (state entering every 16th step).  x, dt_raw, z, Bm, Cm are float32 or bfloat16 (all the same);
 everything else is float32.
 """
 import ctypes
@@ -58,9 +60,9 @@ def load(path: str = LIB):
     lib = ctypes.CDLL(path)
     P = ctypes.c_void_p
     D = ctypes.POINTER(ss_dims)
-    lib.ss_fwd.argtypes = [D] + [P] * 11 + [P, ctypes.c_size_t, P]
+    lib.ss_fwd.argtypes = [D] + [P] * 12 + [P, ctypes.c_size_t, P]
     lib.ss_fwd.restype = ctypes.c_int
-    lib.ss_bwd.argtypes = [D] + [P] * 9 + [P, P] + [P] * 9 + [P, ctypes.c_size_t, P]
+    lib.ss_bwd.argtypes = [D] + [P] * 9 + [P, P, P] + [P] * 9 + [P, ctypes.c_size_t, P]
     lib.ss_bwd.restype = ctypes.c_int
     for f in ("ss_fwd_workspace_size", "ss_bwd_workspace_size"):
         getattr(lib, f).argtypes = [D, ctypes.POINTER(ctypes.c_size_t)]
@@ -145,10 +147,14 @@ def _check_inputs(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, z, h0):
         raise ValueError("x must be contiguous")
 
 
+CKPT_STEPS = 16
+
+
 def ss_fwd(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, z=None, h0=None, *, return_final=False,
-           y=None, h_final=None, workspace=None, plan=SS_PLAN_AUTO, chunk=0,
-           layout=SS_LAYOUT_AUTO, stream=None):
-    """Forward scan through the C ABI.  Returns y, or (y, h_final) with return_final."""
+           return_ckpt=False, y=None, h_final=None, h_ckpt=None, workspace=None,
+           plan=SS_PLAN_AUTO, chunk=0, layout=SS_LAYOUT_AUTO, stream=None):
+    """Forward scan through the C ABI.  Returns y, (y, h_final) with return_final, and
+    the checkpoints last with return_ckpt (or when h_ckpt is passed)."""
     import torch
     lib = load()
     _check_inputs(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, z, h0)
@@ -161,22 +167,32 @@ def ss_fwd(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, z=None, h0=None, *, return_fina
     if return_final and h_final is None:
         h_final = torch.empty((Bn, D, N), dtype=torch.float32, device=x.device)
     _check(h_final, "h_final", (Bn, D, N), torch.float32, x.device)
+    nck = (L + CKPT_STEPS - 1) // CKPT_STEPS
+    if return_ckpt and h_ckpt is None:
+        h_ckpt = torch.empty((Bn, D, nck, N), dtype=torch.float32, device=x.device)
+    _check(h_ckpt, "h_ckpt", (Bn, D, nck, N), torch.float32, x.device)
     need = workspace_size(dims)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rc = lib.ss_fwd(ctypes.byref(dims), _ptr(x), _ptr(dt_raw), _ptr(dt_bias), _ptr(A), _ptr(Bm),
-                    _ptr(Cm), _ptr(Dskip), _ptr(z), _ptr(h0), _ptr(y), _ptr(h_final),
+                    _ptr(Cm), _ptr(Dskip), _ptr(z), _ptr(h0), _ptr(y), _ptr(h_final), _ptr(h_ckpt),
                     _ptr(workspace), wbytes, _stream(stream))
     if rc != 0:
         raise SSError(rc, lib)
-    return (y, h_final) if (return_final or h_final is not None) else y
+    out = (y,)
+    if return_final or h_final is not None:
+        out += (h_final,)
+    if h_ckpt is not None:
+        out += (h_ckpt,)
+    return out if len(out) > 1 else y
 
 
 def ss_bwd(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, dy, z=None, h0=None, dh_final=None, *,
-           workspace=None, chunk=0, out=None, stream=None):
+           h_ckpt=None, workspace=None, chunk=0, out=None, stream=None):
     """Backward through the C ABI.  Returns a dict dx, ddt_raw, ddt_bias, dA, dB, dC, dD,
-    dz (None without gate), dh0 (None without h0); all float32."""
+    dz (None without gate), dh0 (None without h0); all float32.  h_ckpt: the checkpoints
+    of an ss_fwd call on the same inputs (optional)."""
     import torch
     lib = load()
     _check_inputs(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, z, h0)
@@ -187,6 +203,7 @@ def ss_bwd(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, dy, z=None, h0=None, dh_final=N
     f32 = torch.float32
     _check(dy, "dy", (Bn, D, L), f32, dev)
     _check(dh_final, "dh_final", (Bn, D, N), f32, dev)
+    _check(h_ckpt, "h_ckpt", (Bn, D, (L + CKPT_STEPS - 1) // CKPT_STEPS, N), f32, dev)
     shapes = dict(dx=(Bn, D, L), ddt_raw=(Bn, D, L), ddt_bias=(D,), dA=(D, N), dB=(Bn, N, L),
                   dC=(Bn, N, L), dD=(D,), dz=(Bn, D, L), dh0=(Bn, D, N))
     g = {} if out is None else dict(out)
@@ -202,7 +219,7 @@ def ss_bwd(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, dy, z=None, h0=None, dh_final=N
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rc = lib.ss_bwd(ctypes.byref(dims), _ptr(x), _ptr(dt_raw), _ptr(dt_bias), _ptr(A), _ptr(Bm),
-                    _ptr(Cm), _ptr(Dskip), _ptr(z), _ptr(h0), _ptr(dy), _ptr(dh_final),
+                    _ptr(Cm), _ptr(Dskip), _ptr(z), _ptr(h0), _ptr(dy), _ptr(dh_final), _ptr(h_ckpt),
                     _ptr(g["dx"]), _ptr(g["ddt_raw"]), _ptr(g["ddt_bias"]), _ptr(g["dA"]),
                     _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]), _ptr(g["dh0"]),
                     _ptr(workspace), wbytes, _stream(stream))

@@ -66,8 +66,8 @@ int ss_bwd_workspace_size(const ss_dims* dims, size_t* bytes) {
 
 int ss_fwd(const ss_dims* dims, const void* x, const void* dt_raw, const float* dt_bias,
            const float* A, const void* Bm, const void* Cm, const float* Dskip, const void* z,
-           const float* h0, float* y, float* h_final, void* workspace, size_t workspace_bytes,
-           hipStream_t stream) {
+           const float* h0, float* y, float* h_final, float* h_ckpt, void* workspace,
+           size_t workspace_bytes, hipStream_t stream) {
     if (!dims) return SS_ERR_NULL;
     ss::Plan p;
     int rc = ss::make_plan(*dims, false, &p);
@@ -76,8 +76,11 @@ int ss_fwd(const ss_dims* dims, const void* x, const void* dt_raw, const float* 
     const void* ptrs[] = {x, dt_raw, dt_bias, A, Bm, Cm, Dskip, y};
     for (const void* q : ptrs)
         if (!aligned16(q)) return SS_ERR_ALIGN;
-    if ((z && !aligned16(z)) || (h0 && !aligned16(h0)) || (h_final && !aligned16(h_final)))
+    if ((z && !aligned16(z)) || (h0 && !aligned16(h0)) || (h_final && !aligned16(h_final)) ||
+        (h_ckpt && !aligned16(h_ckpt)))
         return SS_ERR_ALIGN;
+    // the group kernel checkpoints at its 16-step sweep starts, which need chunk % 16 == 0
+    if (h_ckpt && p.group && p.chunked && p.chunk % ss::kCkptSteps != 0) return SS_ERR_UNSUPPORTED;
     if (p.ws_total > 0 && (!workspace || workspace_bytes < p.ws_total)) return SS_ERR_WORKSPACE;
     if (workspace && !aligned16(workspace)) return SS_ERR_ALIGN;
 
@@ -97,7 +100,7 @@ int ss_fwd(const ss_dims* dims, const void* x, const void* dt_raw, const float* 
     s.Bm = Bm; s.Cm = Cm;
     s.B = p.B; s.L = p.L; s.D = p.D; s.vec = p.vec;
     if (!p.chunked) {
-        s.chunk = p.L; s.K = 1; s.h_init = h0; s.y = y; s.h_last = h_final; s.agg = 0;
+        s.chunk = p.L; s.K = 1; s.h_init = h0; s.y = y; s.h_last = h_final; s.h_ckpt = h_ckpt; s.agg = 0;
         e = p.group ? ss::launch_scang(bf16, int(p.N), p.group, s, stream) : ss::launch_scan(bf16, int(p.N), s, stream);
         if (e != hipSuccess) return hip_fail(e);
         return SS_OK;
@@ -117,7 +120,8 @@ int ss_fwd(const ss_dims* dims, const void* x, const void* dt_raw, const float* 
     e = ss::launch_carry(int(p.N), c, stream);
     if (e != hipSuccess) return hip_fail(e);
     // 3. output pass from each chunk's true start state
-    s.z = z; s.h_init = h_start; s.y = y; s.h_last = h_final; s.dsum = nullptr; s.agg = 0;
+    s.z = z; s.h_init = h_start; s.y = y; s.h_last = h_final; s.h_ckpt = h_ckpt; s.dsum = nullptr;
+    s.agg = 0;
     e = p.group ? ss::launch_scang(bf16, int(p.N), p.group, s, stream) : ss::launch_scan(bf16, int(p.N), s, stream);
     if (e != hipSuccess) return hip_fail(e);
     return SS_OK;
@@ -125,7 +129,8 @@ int ss_fwd(const ss_dims* dims, const void* x, const void* dt_raw, const float* 
 
 int ss_bwd(const ss_dims* dims, const void* x, const void* dt_raw, const float* dt_bias,
            const float* A, const void* Bm, const void* Cm, const float* Dskip, const void* z,
-           const float* h0, const float* dy, const float* dh_final, float* dx, float* ddt_raw,
+           const float* h0, const float* dy, const float* dh_final, const float* h_ckpt, float* dx,
+           float* ddt_raw,
            float* ddt_bias, float* dA, float* dB, float* dC, float* dD, float* dz, float* dh0,
            void* workspace, size_t workspace_bytes, hipStream_t stream) {
     if (!dims) return SS_ERR_NULL;
@@ -139,21 +144,19 @@ int ss_bwd(const ss_dims* dims, const void* x, const void* dt_raw, const float* 
     const void* req[] = {x, dt_raw, dt_bias, A, Bm, Cm, Dskip, dy, dx, ddt_raw, ddt_bias, dA, dB, dC, dD};
     for (const void* q : req)
         if (!aligned16(q)) return SS_ERR_ALIGN;
-    const void* opt[] = {z, h0, dh_final, dz, dh0};
+    const void* opt[] = {z, h0, dh_final, dz, dh0, h_ckpt};
     for (const void* q : opt)
         if (q && !aligned16(q)) return SS_ERR_ALIGN;
     if (!workspace || workspace_bytes < p.ws_total) return SS_ERR_WORKSPACE;
     if (!aligned16(workspace)) return SS_ERR_ALIGN;
 
     char* ws = static_cast<char*>(workspace);
-    float* BC = reinterpret_cast<float*>(ws + p.off_bc);
     const int bf16 = p.in_dtype == SS_BF16;
-    hipError_t e = ss::launch_bc_stage(bf16, int(p.N), Bm, Cm, BC, p.B, p.L, stream);
-    if (e != hipSuccess) return hip_fail(e);
+    hipError_t e = hipSuccess;
 
     ss::BwdLaunch bl{};
     bl.x = x; bl.dt_raw = dt_raw; bl.z = z; bl.dy = dy; bl.dt_bias = dt_bias; bl.A = A;
-    bl.Dskip = Dskip; bl.BC = BC;
+    bl.Dskip = Dskip; bl.Bm = Bm; bl.Cm = Cm; bl.h_ckpt = h_ckpt;
     bl.h_end = reinterpret_cast<float*>(ws + p.off_hend);
     bl.rev_end = reinterpret_cast<float*>(ws + p.off_gend);
     bl.dsum = reinterpret_cast<float*>(ws + p.off_dsum);
@@ -168,13 +171,15 @@ int ss_bwd(const ss_dims* dims, const void* x, const void* dt_raw, const float* 
     bl.stage = 0;
     e = ss::launch_bwd(bf16, bl, stream);
     if (e != hipSuccess) return hip_fail(e);
-    // 2. carries, both in place: chunk start states from h0; adjoints entering each chunk
-    //    from the right, from dh_final, whose final value is dh0
+    // 2. carries, in place: adjoints entering each chunk from the right, from dh_final,
+    //    whose final value is dh0; without checkpoints also the chunk start states from h0
     ss::CarryLaunch c{};
     c.dsum = bl.dsum; c.A = A; c.B = p.B; c.D = p.D; c.K = int(p.K);
-    c.h_end = bl.h_end; c.h_start = bl.h_end; c.h_in = h0; c.h_out = nullptr; c.reverse = 0;
-    c.dual = 1;
-    c.h_end2 = bl.rev_end; c.h_start2 = bl.rev_end; c.h_in2 = dh_final; c.h_out2 = dh0; c.reverse2 = 1;
+    c.h_end = bl.rev_end; c.h_start = bl.rev_end; c.h_in = dh_final; c.h_out = dh0; c.reverse = 1;
+    if (!h_ckpt) {
+        c.dual = 1;
+        c.h_end2 = bl.h_end; c.h_start2 = bl.h_end; c.h_in2 = h0; c.h_out2 = nullptr; c.reverse2 = 0;
+    }
     e = ss::launch_carry(int(p.N), c, stream);
     if (e != hipSuccess) return hip_fail(e);
     // 3. final pass: recomputed states, adjoint sweep, per-element gradients, partials

@@ -7,23 +7,27 @@
 // skip term and the SiLU gate; with g = ∂/∂h_t swept from t = L-1 to 0:
 //   ds = dy·z·σ(z) (dy without gate); dz = dy·s·σ(z)(1 + z(1 - σ(z)))
 //   g += ds·C_t;  dC_t += ds·h_t;  dB_t += g·δ·x;  dx = ds·D + δ Σ_n g B_t
-//   dδ = Σ_n g (A Ā h_{t-1}) + x Σ_n g B_t;  dA += g δ Ā h_{t-1};  ddt_raw = dδ σ(u)
-//   g ← Ā_t g  (after t = 0 this is dh0)
+//   g ← Ā_t g;  w = g·h_{t-1};  dA += δ w;  dδ = Σ_n A w + x Σ_n g B_t (g before ← Ā_t g)
+//   ddt_raw = dδ σ(u)   (after t = 0, g is dh0)
 //
-// Plan (sequence split into chunks of 16..64 steps, quad layout as the forward: the
-// N states of a channel on four lanes, 16 channels per wave):
-//   1. bwd_agg_kernel: per chunk, the forward pair (Π Ā, local state from zero) and the
-//      reverse pair (Π Ā, Σ_t (Π_{s<=t} Ā_s) ds_t C_t), both from one forward sweep (the
-//      cumulative product only shrinks, so no division ever appears);
-//   2. the carry kernel scans the forward pairs (chunk start states, from h0) and the
-//      reverse pairs from the last chunk down (the adjoint entering each chunk from the
-//      right, from dh_final; its final value is dh0);
-//   3. bwd_chunk_kernel: per chunk, one forward sweep keeps the state at each 16-step
-//      tile start in LDS, then tile by tile from the last: recompute the tile's 16
-//      states, sweep the adjoint backwards through them, reduce the Σ_n terms over the
-//      quad through LDS, and reduce the dB/dC terms over the wave's 16 channels by an
-//      LDS transpose into per-wave partials;
+// Plan (sequence split into chunks of 16..64 steps; the N states of a channel on four
+// lanes, 16 channels per wave, 64 per workgroup):
+//   1. bwd_agg_kernel: per chunk, the reverse pair (Π Ā, Σ_t (Π_{s<=t} Ā_s) ds_t C_t) and,
+//      without checkpoints, the forward pair (Π Ā, local state from zero), from one
+//      forward sweep (the cumulative product only shrinks: no division ever appears);
+//   2. the carry kernel scans the reverse pairs from the last chunk down (the adjoint
+//      entering each chunk from the right, from dh_final; its final value is dh0) and,
+//      without checkpoints, the forward pairs (chunk start states, from h0);
+//   3. bwd_chunk_kernel: per chunk, the state at each 16-step tile start comes from the
+//      forward's checkpoints or, without them, from one forward sweep over the chunk;
+//      then tile by tile from the last: recompute the tile's 16 states, sweep the adjoint backwards through them, sum the Σ_n terms over the four
+//      lanes of a channel through LDS, and sum the dB/dC terms over the wave's 16
+//      channels by an LDS transpose and over the workgroup's 4 waves once per tile;
 //   4. reduce kernels sum the partials into dB, dC, dA, dD, ddt_bias.
+// Both sweeping kernels copy the chunk's B and C from the [B, N, L] inputs into LDS
+// (float32, zero past the chunk's end and past N), and broadcast each step's (δ, δ·x, ds)
+// to the four lanes of a channel through a per-wave LDS row.  Steps past the end of the
+// sequence run as identities (δ = 0, ds = 0), so the sweeps carry no per-step branches.
 #include "ss_device.h"
 #include "ss_kernels.h"
 #include "ss_plan.h"
@@ -32,21 +36,52 @@ namespace ss {
 
 namespace {
 
-constexpr int kBT = 16;          // steps per tile
-constexpr int kBPer = 4;         // steps prepared per lane per tile
-constexpr int kBMaxTiles = 4;    // chunk <= 64 steps
-constexpr int kBThreads = 256;   // 4 waves x 16 quads = 64 channels
+constexpr int kBMaxSteps = 64;                // chunk <= 64 steps
+constexpr int kBThreads = 256;                // 4 waves x 16 channels x 4 lanes
 constexpr int kBChan = 64;
+// 16-step tiles (the forward's checkpoint interval), 4 steps prepared per lane
+constexpr int kBT = kCkptSteps;
+constexpr int kBPer = 4;
+constexpr int kBMaxTiles = kBMaxSteps / kBT;
+// floats per channel in a wave's step rows: steps x (δ, δ·x, ds, 0), +4 so that the
+// rows of different channels start on different banks
+constexpr int kRW = 4 * kBT + 4;
 
-template <int K>
-__device__ __forceinline__ float qbc(float v) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), K * 0x55, 0xf, 0xf, false));
-}
 __device__ __forceinline__ float qsum(float v) {
     v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xf, 0xf, false));
     v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xf, 0xf, false));
     return v;
 }
+
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// S floats from LDS (16-byte aligned when S % 4 == 0)
+template <int S>
+struct Vec {
+    float v[S];
+    __device__ __forceinline__ void load(const float* p) {
+        if constexpr (S % 4 == 0) {
+#pragma unroll
+            for (int q = 0; q < S; q += 4) {
+                const float4 a = *reinterpret_cast<const float4*>(p + q);
+                v[q] = a.x; v[q + 1] = a.y; v[q + 2] = a.z; v[q + 3] = a.w;
+            }
+        } else if constexpr (S % 2 == 0) {
+#pragma unroll
+            for (int q = 0; q < S; q += 2) {
+                const float2 a = *reinterpret_cast<const float2*>(p + q);
+                v[q] = a.x; v[q + 1] = a.y;
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < S; ++q) v[q] = p[q];
+        }
+    }
+};
 
 // 4 consecutive elements [t, t+4) of a row, zero past t_end; vector load when full and aligned
 __device__ __forceinline__ void load4(const float* __restrict__ p, int64_t t, int64_t t_end, int vec,
@@ -81,14 +116,60 @@ __device__ __forceinline__ void store4(float* __restrict__ p, int64_t t, int64_t
     }
 }
 
-// Stage the B/C rows of steps [t0, t0 + n) from the [B, L, 2N] staging copy into LDS.
-__device__ __forceinline__ void stage_bc(float* __restrict__ lds, const float* __restrict__ src,
-                                         int nfloats, int tid) {
-    // float4 copies only when the source rows are 16-byte aligned (not so for N = 1, odd L)
-    const int nv = (reinterpret_cast<uintptr_t>(src) & 15u) ? 0 : nfloats / 4;
-    for (int e = tid; e < nv; e += kBThreads)
-        reinterpret_cast<float4*>(lds)[e] = reinterpret_cast<const float4*>(src)[e];
-    for (int e = nv * 4 + tid; e < nfloats; e += kBThreads) lds[e] = src[e];
+// 4 consecutive input elements [t, t+4) of a row in their storage type, zero past t_end
+// (vector load when full and aligned); decoded to float32 when used
+template <typename T> struct In4;
+template <> struct In4<bf16_t> {
+    uint2 v;
+    __device__ __forceinline__ void load(const bf16_t* __restrict__ p, int64_t t, int64_t t_end, int vec) {
+        if (vec && t + 4 <= t_end) {
+            v = *reinterpret_cast<const uint2*>(p + t);
+        } else {
+            uint32_t e[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) e[i] = (t + i < t_end) ? p[t + i].bits : 0u;
+            v = make_uint2(e[0] | (e[1] << 16), e[2] | (e[3] << 16));
+        }
+    }
+    __device__ __forceinline__ void decode(float (&o)[4]) const {
+        o[0] = __uint_as_float(v.x << 16); o[1] = __uint_as_float(v.x & 0xffff0000u);
+        o[2] = __uint_as_float(v.y << 16); o[3] = __uint_as_float(v.y & 0xffff0000u);
+    }
+};
+template <> struct In4<float> {
+    float4 v;
+    __device__ __forceinline__ void load(const float* __restrict__ p, int64_t t, int64_t t_end, int vec) {
+        if (vec && t + 4 <= t_end) {
+            v = *reinterpret_cast<const float4*>(p + t);
+        } else {
+            v.x = (t < t_end) ? p[t] : 0.0f;
+            v.y = (t + 1 < t_end) ? p[t + 1] : 0.0f;
+            v.z = (t + 2 < t_end) ? p[t + 2] : 0.0f;
+            v.w = (t + 3 < t_end) ? p[t + 3] : 0.0f;
+        }
+    }
+    __device__ __forceinline__ void decode(float (&o)[4]) const {
+        o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+    }
+};
+
+// B and C of steps [t0, t0 + nsteps) of batch row b, from the [B, Nr, L] inputs into LDS as
+// [step][B_0 .. B_{NP-1} | C_0 .. C_{NP-1}] float32 with row stride R; zero for steps past
+// nsteps (up to kBMaxSteps) and states past Nr.  Lanes run along L: coalesced reads.
+template <typename Tin, int NP>
+__device__ __forceinline__ void load_chunk_bc(float* __restrict__ lds, const Tin* __restrict__ Bm,
+                                              const Tin* __restrict__ Cm, int b, int Nr, int64_t L,
+                                              int64_t t0, int nsteps, int tid) {
+    constexpr int R = 2 * NP + 4;
+    constexpr int total = 2 * NP * kBMaxSteps;
+    for (int e = tid; e < total; e += kBThreads) {
+        const int t = e % kBMaxSteps;
+        const int n = (e / kBMaxSteps) % NP;
+        const int m = e / (kBMaxSteps * NP);
+        float v = 0.0f;
+        if (n < Nr && t < nsteps) v = to_f32((m ? Cm : Bm)[(int64_t(b) * Nr + n) * L + t0 + t]);
+        lds[t * R + m * NP + n] = v;
+    }
 }
 
 }  // namespace
@@ -96,16 +177,21 @@ __device__ __forceinline__ void stage_bc(float* __restrict__ lds, const float* _
 // ---------------------------------------------------------------------------------------
 // 1. chunk aggregates.  grid (ceil(D/64), K, B), 256 threads.
 // ---------------------------------------------------------------------------------------
-template <typename Tin, int S, bool kGate>
+template <typename Tin, int S, bool kGate, bool kFwd>
 __global__ __launch_bounds__(kBThreads) void bwd_agg_kernel(
     const Tin* __restrict__ x, const Tin* __restrict__ dt_raw, const Tin* __restrict__ z,
     const float* __restrict__ dy, const float* __restrict__ dt_bias, const float* __restrict__ A,
-    const float* __restrict__ BC, float* __restrict__ h_end, float* __restrict__ rev_end,
-    float* __restrict__ dsum_out, int64_t L, int64_t D, int Nr, int64_t chunk, int K, int vec) {
-    constexpr int SQ = 4 * S;
-    __shared__ __align__(16) float bc_lds[kBMaxTiles * kBT * 2 * SQ];
+    const Tin* __restrict__ Bm, const Tin* __restrict__ Cm, float* __restrict__ h_end,
+    float* __restrict__ rev_end, float* __restrict__ dsum_out, int64_t L, int64_t D, int Nr,
+    int64_t chunk, int K, int vec) {
+    constexpr int NP = 4 * S;
+    constexpr int R = 2 * NP + 4;
+    __shared__ __align__(16) float bc_lds[kBMaxSteps * R];
+    __shared__ __align__(16) float rows[4 * 16 * kRW];
     const int tid = threadIdx.x;
+    const int lane = tid & 63;
     const int j = tid & 3;
+    const int n0 = j * S;
     const int64_t d_raw = int64_t(blockIdx.x) * kBChan + (tid >> 2);
     const bool valid = d_raw < D;
     const int64_t d = valid ? d_raw : D - 1;
@@ -113,72 +199,72 @@ __global__ __launch_bounds__(kBThreads) void bwd_agg_kernel(
     const int64_t t0c = int64_t(k) * chunk;
     const int64_t t1c = (t0c + chunk < L) ? t0c + chunk : L;
     const int nsteps = int(t1c - t0c);
-    const int R = 2 * Nr;
-    stage_bc(bc_lds, BC + (int64_t(b) * L + t0c) * R, nsteps * R, tid);
+    const int ntiles = (nsteps + kBT - 1) / kBT;
+    load_chunk_bc<Tin, NP>(bc_lds, Bm, Cm, b, Nr, L, t0c, nsteps, tid);
 
     float A2[S], h[S], P[S], Rv[S];
 #pragma unroll
     for (int s = 0; s < S; ++s) {
-        const int n = j * S + s;
+        const int n = n0 + s;
         A2[s] = (n < Nr) ? A[d * Nr + n] * kLog2e : 0.0f;
         h[s] = 0.0f; P[s] = 1.0f; Rv[s] = 0.0f;
     }
     const float bias = dt_bias[d];
     const int64_t row = (int64_t(b) * D + d) * L;
+    float* myrow = rows + (tid >> 6) * 16 * kRW + (lane >> 2) * kRW;
     float dsum = 0.0f;
     __syncthreads();
 
-    for (int t0 = 0; t0 < nsteps; t0 += kBT) {
-        const int64_t te = t0c + t0 + kBPer * j;
-        float xv[4], dv[4], zv[4], gv[4];
+    for (int tile = 0; tile < ntiles; ++tile) {
+        const int tb = tile * kBT;
+        const int64_t te = t0c + tb + kBPer * j;
+        float xv[4], dv[4], gv[4], zv[4];
         load4(x + row, te, t1c, vec, xv);
         load4(dt_raw + row, te, t1c, vec, dv);
         load4(dy + row, te, t1c, vec, gv);
         if (kGate) load4(z + row, te, t1c, vec, zv);
-        else zv[0] = zv[1] = zv[2] = zv[3] = 0.0f;
-        float dl[4], dx[4], ds[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < kBPer; ++i) {
             const bool ok = te + i < t1c;
-            dl[i] = ok ? softplus(bias + dv[i]) : 0.0f;
-            dx[i] = dl[i] * xv[i];
-            ds[i] = kGate ? gv[i] * silu(zv[i]) : gv[i];
-            dsum += dl[i];
+            const float dl = ok ? softplus(bias + dv[i]) : 0.0f;
+            const float ds = ok ? (kGate ? gv[i] * silu(zv[i]) : gv[i]) : 0.0f;
+            dsum += dl;
+            *reinterpret_cast<float4*>(myrow + 4 * (kBPer * j + i)) = make_float4(dl, dl * xv[i], ds, 0.0f);
         }
-        const int nt = (nsteps - t0 < kBT) ? nsteps - t0 : kBT;
-#define SS_AGG_STEP(KK)                                                              \
-        _Pragma("unroll") for (int i = 0; i < kBPer; ++i) {                          \
-            const int tl = KK * kBPer + i;                                           \
-            const float db = qbc<KK>(dl[i]);                                         \
-            const float xb = qbc<KK>(dx[i]);                                         \
-            const float sb = qbc<KK>(ds[i]);                                         \
-            if (tl < nt) {                                                           \
-                const float* bt = bc_lds + (t0 + tl) * R;                            \
-                _Pragma("unroll") for (int s = 0; s < S; ++s) {                      \
-                    const int n = j * S + s;                                         \
-                    const float Bn = (S > 1 || n < Nr) ? bt[n] : 0.0f;               \
-                    const float Cn = (S > 1 || n < Nr) ? bt[Nr + n] : 0.0f;          \
-                    const float a = exp2_hw(db * A2[s]);                             \
-                    h[s] = fmaf(a, h[s], xb * Bn);                                   \
-                    P[s] *= a;                                                       \
-                    Rv[s] = fmaf(P[s], sb * Cn, Rv[s]);                              \
-                }                                                                    \
-            }                                                                        \
+        wave_sync();
+        const float* bt = bc_lds + tb * R;
+        float4 rc, rn = *reinterpret_cast<const float4*>(myrow);
+        Vec<S> bc, cc, bn, cn;
+        if (kFwd) bn.load(bt + n0);
+        cn.load(bt + NP + n0);
+#pragma unroll
+        for (int t = 0; t < kBT; ++t) {
+            rc = rn; cc = cn;
+            if (kFwd) bc = bn;
+            if (t + 1 < kBT) {
+                rn = *reinterpret_cast<const float4*>(myrow + 4 * (t + 1));
+                if (kFwd) bn.load(bt + (t + 1) * R + n0);
+                cn.load(bt + (t + 1) * R + NP + n0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int s = 0; s < S; ++s) {
+                const float a = exp2_hw(rc.x * A2[s]);
+                if (kFwd) h[s] = fmaf(a, h[s], rc.y * bc.v[s]);
+                P[s] *= a;
+                Rv[s] = fmaf(P[s], rc.z * cc.v[s], Rv[s]);
+            }
         }
-        SS_AGG_STEP(0)
-        SS_AGG_STEP(1)
-        SS_AGG_STEP(2)
-        SS_AGG_STEP(3)
-#undef SS_AGG_STEP
+        wave_sync();
     }
     dsum = qsum(dsum);
     if (valid) {
         const int64_t aidx = (int64_t(b) * D + d) * K + k;
 #pragma unroll
         for (int s = 0; s < S; ++s) {
-            const int n = j * S + s;
+            const int n = n0 + s;
             if (n < Nr) {
-                h_end[aidx * Nr + n] = h[s];
+                if (kFwd) h_end[aidx * Nr + n] = h[s];
                 rev_end[aidx * Nr + n] = Rv[s];
             }
         }
@@ -188,32 +274,46 @@ __global__ __launch_bounds__(kBThreads) void bwd_agg_kernel(
 
 // ---------------------------------------------------------------------------------------
 // 3. final pass.  grid (ceil(D/64), K, B), 256 threads.
-//   h_start [B,D,K,N]: state entering each chunk; overwritten with dA partials.
+//   h_start [B,D,K,N]: state entering each chunk (kCk = false); overwritten with dA partials.
+//   h_ckpt  [B,D,ceil(L/16),N]: the forward's state entering every 16th step (kCk = true).
 //   q       [B,D,K,N]: adjoint entering each chunk from the right.
 //   dbc_part [B, NB, L, 2N] (NB = ceil(D/64)): per-block sums over 64 channels of dB | dC.
 //   ddt_part [B, D, K, 2]: per-chunk dD and ddt_bias partials.
 // ---------------------------------------------------------------------------------------
-template <typename Tin, int S, bool kGate>
-__global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(
+// Two waves per SIMD: the tile's 16 recomputed states per lane and the per-step Σ_n
+// partials take most of the 256 registers a wave then has.
+template <typename Tin, int S, bool kGate, bool kCk>
+__global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_chunk_kernel(
     const Tin* __restrict__ x, const Tin* __restrict__ dt_raw, const Tin* __restrict__ z,
     const float* __restrict__ dy, const float* __restrict__ dt_bias, const float* __restrict__ A,
-    const float* __restrict__ Dskip, const float* __restrict__ BC, float* h_start,
-    const float* __restrict__ q, float* __restrict__ dxo, float* __restrict__ ddto,
-    float* __restrict__ dzo, float* __restrict__ dbc_part, float* __restrict__ ddt_part,
-    int64_t L, int64_t D, int Nr, int64_t chunk, int K, int vec) {
-    constexpr int SQ = 4 * S;
-    __shared__ __align__(16) float bc_lds[kBMaxTiles * kBT * 2 * SQ];
-    // per-wave scratch, LS floats per lane (quad reduce-scatter, then dB/dC transpose);
-    // LS = 4 mod 32 keeps the 16-byte writes of 8 consecutive lanes on disjoint banks
-    constexpr int LS = ((8 * S > 32) ? 8 * S : 32) + 4;
-    __shared__ __align__(16) float scr[kBThreads * LS];
-    __shared__ float comb[4 * 8 * SQ];   // wave totals of one 4-step batch
-    // state at each 16-step tile start, [tile][s][thread]
-    __shared__ float ck_lds[kBMaxTiles * S * kBThreads];
+    const float* __restrict__ Dskip, const Tin* __restrict__ Bm, const Tin* __restrict__ Cm,
+    const float* __restrict__ h_ckpt, float* h_start, const float* __restrict__ q,
+    float* __restrict__ dxo, float* __restrict__ ddto, float* __restrict__ dzo,
+    float* __restrict__ dbc_part, float* __restrict__ ddt_part, int64_t L, int64_t D, int Nr,
+    int64_t chunk, int K, int vec) {
+    constexpr int NP = 4 * S;
+    constexpr int R = 2 * NP + 4;
+    // steps per reverse batch = steps a lane prepares: batch bi is lane bi's steps, so the
+    // lane that owns a batch's elements finishes their gradients right after the batch
+    constexpr int kBB = kBPer;
+    constexpr int kNBat = kBT / kBB;
+    // per-wave exchange area, per lane: the batch's dB|dC terms (kBB x S x 2), its Σ_n
+    // partials (kBB x 2), and the readout partials of a tile (kBT) share it in turn; the
+    // lane stride is an odd multiple of 4 floats, so 16-byte writes of 8 consecutive lanes
+    // hit disjoint banks, and it keeps the 32 reads of a transpose half on distinct banks
+    constexpr int XW = (2 * kBB * S + 2 * kBB > kBT) ? 2 * kBB * S + 2 * kBB : kBT;
+    constexpr int LS = ((XW + 4) / 8) * 8 + 4;
+    constexpr int PXO = 2 * kBB * S;            // offset of the Σ_n partials in a lane's area
+    constexpr int OUTW = kBT * 2 * NP;          // dB|dC sums of one tile for one wave
+    __shared__ __align__(16) float bc_lds[kBMaxSteps * R];
+    __shared__ __align__(16) float rows[4 * 16 * kRW];
+    __shared__ __align__(16) float xch[4 * 64 * LS];
+    __shared__ float comb[4 * OUTW];            // the wave sums of a tile
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int j = tid & 3;
+    const int n0 = j * S;
     const int64_t d_raw = int64_t(blockIdx.x) * kBChan + (tid >> 2);
     const bool valid = d_raw < D;
     const int64_t d = valid ? d_raw : D - 1;
@@ -222,275 +322,289 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(
     const int64_t t1c = (t0c + chunk < L) ? t0c + chunk : L;
     const int nsteps = int(t1c - t0c);
     const int ntiles = (nsteps + kBT - 1) / kBT;
-    const int R = 2 * Nr;
-    stage_bc(bc_lds, BC + (int64_t(b) * L + t0c) * R, nsteps * R, tid);
-    float* wscr = scr + wave * 64 * LS;
-    const int64_t NB = (D + kBChan - 1) / kBChan;        // channel blocks
+    const int64_t NB = (D + kBChan - 1) / kBChan;
+    float* wx = xch + wave * 64 * LS;           // this wave's exchange area
+    float* mine = wx + lane * LS;
+    float* myrow = rows + wave * 16 * kRW + (lane >> 2) * kRW;
 
     const int64_t sidx = ((int64_t(b) * D + d) * K + k) * Nr;
-    float A2[S], An[S], h[S], g[S], dA[S];
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-        const int n = j * S + s;
-        const bool ok = n < Nr;
-        An[s] = ok ? A[d * Nr + n] : 0.0f;
-        A2[s] = An[s] * kLog2e;
-        h[s] = ok ? h_start[sidx + n] : 0.0f;
-        g[s] = ok ? q[sidx + n] : 0.0f;
-        dA[s] = 0.0f;
-    }
     const float bias = dt_bias[d];
     const float Dd = Dskip[d];
     const int64_t row = (int64_t(b) * D + d) * L;
+    const Tin* xr = x + row;
+    const Tin* drr = dt_raw + row;
+    const Tin* zr = kGate ? z + row : nullptr;
+    const float* gr = dy + row;
+    // checkpoints of this channel: tile tt of the chunk starts at checkpoint (t0c / 16) + tt
+    const int64_t nck = (L + kBT - 1) / kBT;
+    const float* ckr = kCk ? h_ckpt + (int64_t(b) * D + d) * nck * Nr + (t0c / kBT) * Nr : nullptr;
+    // with checkpoints, the reverse sweep's global loads run one tile ahead (its first
+    // tile is issued here); without, registers are short and each tile loads on entry
+    In4<Tin> bx, bd, bz;
+    In4<float> bg;
+    float ckn[S];                               // next tile's start state (kCk)
+    auto load_tile = [&](int tt) {
+        const int64_t tl = t0c + tt * kBT + kBPer * j;
+        bx.load(xr, tl, t1c, vec);
+        bd.load(drr, tl, t1c, vec);
+        bg.load(gr, tl, t1c, vec);
+        if (kGate) bz.load(zr, tl, t1c, vec);
+        if (kCk) {
+#pragma unroll
+            for (int s = 0; s < S; ++s) ckn[s] = (n0 + s < Nr) ? ckr[tt * Nr + n0 + s] : 0.0f;
+        }
+    };
+    if (kCk) load_tile(ntiles - 1);
+    load_chunk_bc<Tin, NP>(bc_lds, Bm, Cm, b, Nr, L, t0c, nsteps, tid);
+    float A2[S], An[S], g[S], dA[S];
+    float ck[kCk ? 1 : kBMaxTiles][S];          // state entering each tile (uniform index)
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        const int n = n0 + s;
+        const bool ok = n < Nr;
+        An[s] = ok ? A[d * Nr + n] : 0.0f;
+        A2[s] = An[s] * kLog2e;
+        g[s] = ok ? q[sidx + n] : 0.0f;
+        dA[s] = 0.0f;
+        if (!kCk) ck[0][s] = ok ? h_start[sidx + n] : 0.0f;
+    }
     float accD = 0.0f, accT = 0.0f;
     __syncthreads();
 
-    auto BCn = [&](const float* bt, int s, float& Bn, float& Cn) {
-        const int n = j * S + s;
-        const bool ok = (S > 1) || n < Nr;
-        Bn = ok ? bt[n] : 0.0f;
-        Cn = ok ? bt[Nr + n] : 0.0f;
-    };
-
-    // ---- forward sweep: state at every tile start ----
-    auto CK = [&](int tile, int s) -> float& { return ck_lds[(tile * S + s) * kBThreads + tid]; };
-    for (int tile = 0; tile < ntiles; ++tile) {
+    if constexpr (!kCk) {
+        // ---- forward sweep: the state entering every tile but the first ----
+        In4<Tin> ax, ad;
+        ax.load(xr, t0c + kBPer * j, t1c, vec);
+        ad.load(drr, t0c + kBPer * j, t1c, vec);
+        float h[S];
 #pragma unroll
-        for (int s = 0; s < S; ++s) CK(tile, s) = h[s];
-        if (tile == ntiles - 1) break;     // the last tile's end state is not needed
-        const int t0 = tile * kBT;
-        const int64_t te = t0c + t0 + kBPer * j;
-        float xv[4], dv[4];
-        load4(x + row, te, t1c, vec, xv);
-        load4(dt_raw + row, te, t1c, vec, dv);
-        float dl[4], dx[4];
+        for (int s = 0; s < S; ++s) h[s] = ck[0][s];
+#pragma unroll 1
+        for (int tile = 0; tile + 1 < ntiles; ++tile) {
+            const int tb = tile * kBT;
+            float xv[4], dv[4];
+            ax.decode(xv);
+            ad.decode(dv);
+            if (tile + 2 < ntiles) {
+                const int64_t ta = t0c + tb + kBT + kBPer * j;
+                ax.load(xr, ta, t1c, vec);
+                ad.load(drr, ta, t1c, vec);
+            }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            dl[i] = softplus(bias + dv[i]);
-            dx[i] = dl[i] * xv[i];
+            for (int i = 0; i < kBPer; ++i) {
+                const float dl = softplus(bias + dv[i]);  // every step of a non-last tile is real
+                *reinterpret_cast<float2*>(myrow + 4 * (kBPer * j + i)) = make_float2(dl, dl * xv[i]);
+            }
+            wave_sync();
+            const float* bt = bc_lds + tb * R;
+            float2 rc, rn = *reinterpret_cast<const float2*>(myrow);
+            Vec<S> bc, bn;
+            bn.load(bt + n0);
+#pragma unroll
+            for (int t = 0; t < kBT; ++t) {
+                rc = rn; bc = bn;
+                if (t + 1 < kBT) {
+                    rn = *reinterpret_cast<const float2*>(myrow + 4 * (t + 1));
+                    bn.load(bt + (t + 1) * R + n0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int s = 0; s < S; ++s) h[s] = fmaf(exp2_hw(rc.x * A2[s]), h[s], rc.y * bc.v[s]);
+            }
+#pragma unroll
+            for (int s = 0; s < S; ++s) ck[tile + 1][s] = h[s];
+            wave_sync();
         }
-#define SS_FW_STEP(KK)                                                                \
-        _Pragma("unroll") for (int i = 0; i < kBPer; ++i) {                           \
-            const float db = qbc<KK>(dl[i]);                                          \
-            const float xb = qbc<KK>(dx[i]);                                          \
-            const float* bt = bc_lds + (t0 + KK * kBPer + i) * R;                     \
-            _Pragma("unroll") for (int s = 0; s < S; ++s) {                           \
-                float Bn, Cn;                                                         \
-                BCn(bt, s, Bn, Cn);                                                   \
-                h[s] = fmaf(exp2_hw(db * A2[s]), h[s], xb * Bn);                      \
-            }                                                                         \
-        }
-        SS_FW_STEP(0)
-        SS_FW_STEP(1)
-        SS_FW_STEP(2)
-        SS_FW_STEP(3)
-#undef SS_FW_STEP
     }
 
     // ---- tiles from the last to the first ----
-    for (int tile = ntiles - 1; tile >= 0; --tile) {
-        const int t0 = tile * kBT;
-        const int nt = (nsteps - t0 < kBT) ? nsteps - t0 : kBT;
-        const int64_t te = t0c + t0 + kBPer * j;
+#pragma unroll 1
+    for (int tt = ntiles - 1; tt >= 0; --tt) {
+        const int tb = tt * kBT;
+        const int64_t te = t0c + tb + kBPer * j;
+        if (!kCk) load_tile(tt);
         float xv[4], dv[4], zv[4], gv[4];
-        load4(x + row, te, t1c, vec, xv);
-        load4(dt_raw + row, te, t1c, vec, dv);
-        load4(dy + row, te, t1c, vec, gv);
-        if (kGate) load4(z + row, te, t1c, vec, zv);
-        float dl[4], dx[4], ds[4], su[4], sz[4];
+        bx.decode(xv);
+        bd.decode(dv);
+        bg.decode(gv);
+        if (kGate) bz.decode(zv);
+        float hc[S];                            // state entering this tile
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int s = 0; s < S; ++s) hc[s] = kCk ? ckn[s] : ck[kCk ? 0 : tt][s];
+        if (kCk && tt > 0) load_tile(tt - 1);
+        float dl[4], ds[4], su[4], sz[4];
+#pragma unroll
+        for (int i = 0; i < kBPer; ++i) {
             const bool ok = te + i < t1c;
             const float u = bias + dv[i];
             dl[i] = ok ? softplus(u) : 0.0f;
             su[i] = sigmoid(u);
-            dx[i] = dl[i] * xv[i];
             if (kGate) {
                 sz[i] = sigmoid(zv[i]);
                 ds[i] = ok ? gv[i] * zv[i] * sz[i] : 0.0f;
             } else {
                 ds[i] = ok ? gv[i] : 0.0f;
             }
-            if (!valid) { ds[i] = 0.0f; dx[i] = 0.0f; }
+            // channels past D compute on a clamped copy: they must add nothing to dB, dC
+            const float dsv = valid ? ds[i] : 0.0f;
+            const float dxv = valid ? dl[i] * xv[i] : 0.0f;
+            *reinterpret_cast<float4*>(myrow + 4 * (kBPer * j + i)) = make_float4(dl[i], dxv, dsv, 0.0f);
         }
+        wave_sync();
+        const float* bt = bc_lds + tb * R;
 
-        // recompute the tile's states (and the readout for dz)
+        // recompute the tile's states (and, with the gate, the readout for dz)
         float hs[kBT][S];
-        float sp[kBT];
-        float hc[S];
+        {
+            float sp[kBT];
+            float h[S];
+            float4 rc, rn = *reinterpret_cast<const float4*>(myrow);
+            Vec<S> bc, cc, bn, cn;
+            bn.load(bt + n0);
+            if (kGate) cn.load(bt + NP + n0);
 #pragma unroll
-        for (int s = 0; s < S; ++s) { hc[s] = CK(tile, s); h[s] = hc[s]; }
-#define SS_RC_STEP(KK)                                                                \
-        _Pragma("unroll") for (int i = 0; i < kBPer; ++i) {                           \
-            const int tl = KK * kBPer + i;                                            \
-            const float db = qbc<KK>(dl[i]);                                          \
-            const float xb = qbc<KK>(dx[i]);                                          \
-            const float* bt = bc_lds + (t0 + tl) * R;                                 \
-            float acc = 0.0f;                                                         \
-            _Pragma("unroll") for (int s = 0; s < S; ++s) {                           \
-                float Bn, Cn;                                                         \
-                BCn(bt, s, Bn, Cn);                                                   \
-                h[s] = fmaf(exp2_hw(db * A2[s]), h[s], xb * Bn);                      \
-                hs[tl][s] = h[s];                                                     \
-                if (kGate) acc = fmaf(Cn, h[s], acc);                                 \
-            }                                                                         \
-            sp[tl] = acc;                                                             \
+            for (int s = 0; s < S; ++s) h[s] = hc[s];
+#pragma unroll
+            for (int t = 0; t < kBT; ++t) {
+                rc = rn; bc = bn;
+                if (kGate) cc = cn;
+                if (t + 1 < kBT) {
+                    rn = *reinterpret_cast<const float4*>(myrow + 4 * (t + 1));
+                    bn.load(bt + (t + 1) * R + n0);
+                    if (kGate) cn.load(bt + (t + 1) * R + NP + n0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                float acc = 0.0f;
+#pragma unroll
+                for (int s = 0; s < S; ++s) {
+                    h[s] = fmaf(exp2_hw(rc.x * A2[s]), h[s], rc.y * bc.v[s]);
+                    hs[t][s] = h[s];
+                    if (kGate) acc = fmaf(cc.v[s], h[s], acc);
+                }
+                sp[t] = acc;
+            }
+            if (kGate) {
+#pragma unroll
+                for (int i = 0; i < kBT; i += 4)
+                    *reinterpret_cast<float4*>(mine + i) = make_float4(sp[i], sp[i + 1], sp[i + 2], sp[i + 3]);
+            }
         }
-        SS_RC_STEP(0)
-        SS_RC_STEP(1)
-        SS_RC_STEP(2)
-        SS_RC_STEP(3)
-#undef SS_RC_STEP
-
-        float dzv[4];
+        const int qb = lane & ~3;
         if (kGate) {
-            // readout partials -> owner lanes (steps 4j..4j+3 of lane j)
-            float* mine = wscr + lane * LS;
-#pragma unroll
-            for (int q4 = 0; q4 < kBT; q4 += 4)
-                *reinterpret_cast<float4*>(mine + q4) = make_float4(sp[q4], sp[q4 + 1], sp[q4 + 2], sp[q4 + 3]);
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            // readout partials -> owner lanes (steps 4j..4j+3 of lane j); dz right away
+            wave_sync();
             float stot[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-            const int qb = lane & ~3;
 #pragma unroll
-            for (int src = 0; src < 4; ++src) {
-                const float4 v = *reinterpret_cast<const float4*>(wscr + (qb + src) * LS + kBPer * j);
+            for (int r = 0; r < 4; ++r) {
+                const int src = (j + r) & 3;
+                const float4 v = *reinterpret_cast<const float4*>(wx + (qb + src) * LS + kBPer * j);
                 stot[0] += v.x; stot[1] += v.y; stot[2] += v.z; stot[3] += v.w;
             }
+            float dzv[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float sv = fmaf(Dd, xv[i], stot[i]);
                 dzv[i] = gv[i] * sv * sz[i] * fmaf(zv[i], 1.0f - sz[i], 1.0f);
             }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            if (valid) store4(dzo + row, te, t1c, vec, dzv);
+            wave_sync();
         }
 
-        // reverse sweep over the tile, in batches of 4 steps (one prepared block each)
-        float pdx[kBT], pdd[kBT];
-    #define SS_RV_BATCH(KK)                                                                    \
-        {                                                                                  \
-            float cB[kBPer][S], cC[kBPer][S];                                              \
-            _Pragma("unroll") for (int i = kBPer - 1; i >= 0; --i) {                       \
-                const int tl = KK * kBPer + i;                                             \
-                const float db = qbc<KK>(ds[i]);                                           \
-                const float lb = qbc<KK>(dl[i]);                                           \
-                const float xb = qbc<KK>(dx[i]);                                           \
-                float px = 0.0f, pd = 0.0f;                                                \
-                if (tl < nt) {                                                             \
-                    const float* bt = bc_lds + (t0 + tl) * R;                              \
-                    _Pragma("unroll") for (int s = 0; s < S; ++s) {                        \
-                        float Bn, Cn;                                                      \
-                        BCn(bt, s, Bn, Cn);                                                \
-                        const float hp = (tl > 0) ? hs[tl > 0 ? tl - 1 : 0][s] : hc[s];  \
-                        g[s] = fmaf(db, Cn, g[s]);                                         \
-                        cC[i][s] = db * hs[tl][s];                                         \
-                        cB[i][s] = g[s] * xb;                                              \
-                        px = fmaf(g[s], Bn, px);                                           \
-                        const float a = exp2_hw(lb * A2[s]);                               \
-                        const float wa = g[s] * (a * hp);                                  \
-                        dA[s] = fmaf(wa, lb, dA[s]);                                       \
-                        pd = fmaf(wa, An[s], pd);                                          \
-                        g[s] *= a;                                                         \
-                    }                                                                      \
-                } else {                                                                   \
-                    _Pragma("unroll") for (int s = 0; s < S; ++s) { cB[i][s] = 0.0f; cC[i][s] = 0.0f; } \
-                }                                                                          \
-                pdx[tl] = px;                                                              \
-                pdd[tl] = pd;                                                              \
-            }                                                                              \
-            /* dB | dC over the block's 64 channels: each wave transposes its 16 channels  \
-               through its LDS area (per lane [type][step][state], lane stride LS), the    \
-               wave totals meet in `comb`, and one block partial per (b, t, n) is written  \
-               (fixed order: deterministic).                                              */ \
-            float* mine = wscr + lane * LS;                                                \
-            _Pragma("unroll") for (int i = 0; i < kBPer; ++i) {                            \
-                _Pragma("unroll") for (int s = 0; s < S; ++s) {                            \
-                    mine[i * S + s] = cB[i][s];                                            \
-                    mine[4 * S + i * S + s] = cC[i][s];                                    \
-                }                                                                          \
-            }                                                                              \
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");                         \
-            __builtin_amdgcn_wave_barrier();                                               \
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");                         \
-            /* e = lane + 64r -> (state sp_, lane group jp, type ty, step st): each       \
-               32-lane half reads 32 distinct banks (LS = 4 mod 32)                       */ \
-            _Pragma("unroll") for (int r = 0; r < (8 * SQ + 63) / 64; ++r) {               \
-                const int e = lane + 64 * r;                                               \
-                if (e < 8 * SQ) {                                                          \
-                    const int sp_ = e % S;                                                 \
-                    const int jp = (e / S) % 4;                                            \
-                    const int ty = (e / (4 * S)) % 2;                                      \
-                    const int st = e / (8 * S);                                            \
-                    const float* col = wscr + jp * LS + ty * 4 * S + st * S + sp_;         \
-                    float tot = 0.0f;                                                      \
-                    _Pragma("unroll") for (int c = 0; c < 16; ++c) tot += col[c * 4 * LS]; \
-                    comb[wave * 8 * SQ + e] = tot;                                         \
-                }                                                                          \
-            }                                                                              \
-            __syncthreads();                                                               \
-            for (int e = tid; e < 8 * SQ; e += kBThreads) {                                \
-                const int sp_ = e % S;                                                     \
-                const int jp = (e / S) % 4;                                                \
-                const int ty = (e / (4 * S)) % 2;                                          \
-                const int st = e / (8 * S);                                                \
-                const int n = jp * S + sp_;                                                \
-                const float tot = (comb[e] + comb[8 * SQ + e]) +                           \
-                                  (comb[16 * SQ + e] + comb[24 * SQ + e]);                 \
-                const int64_t t = t0c + t0 + KK * kBPer + st;                              \
-                if (n < Nr && t < t1c)                                                     \
-                    dbc_part[((int64_t(b) * NB + blockIdx.x) * L + t) * R + ty * Nr + n] = tot; \
-            }                                                                              \
-            __syncthreads();                                                               \
+        // reverse sweep over the tile, in batches of kBB steps
+        float* cbuf = comb + wave * OUTW;
+#pragma unroll
+        for (int bi = kNBat - 1; bi >= 0; --bi) {
+            float pxb[kBB], pdb[kBB];
+#pragma unroll
+            for (int i = kBB - 1; i >= 0; --i) {
+                const int t = bi * kBB + i;
+                const float4 rc = *reinterpret_cast<const float4*>(myrow + 4 * t);
+                Vec<S> bc, cc;
+                bc.load(bt + t * R + n0);
+                cc.load(bt + t * R + NP + n0);
+                float pxa = 0.0f, pda = 0.0f;
+                float cB[S], cC[S];
+#pragma unroll
+                for (int s = 0; s < S; ++s) {
+                    const float hp = (t > 0) ? hs[t > 0 ? t - 1 : 0][s] : hc[s];
+                    g[s] = fmaf(rc.z, cc.v[s], g[s]);
+                    cC[s] = rc.z * hs[t][s];
+                    cB[s] = g[s] * rc.y;
+                    pxa = fmaf(g[s], bc.v[s], pxa);
+                    g[s] *= exp2_hw(rc.x * A2[s]);
+                    const float w = g[s] * hp;
+                    dA[s] = fmaf(w, rc.x, dA[s]);
+                    pda = fmaf(w, An[s], pda);
+                }
+                pxb[i] = pxa;
+                pdb[i] = pda;
+                // this step's dB|dC terms into the lane's area as [type][step][state]
+#pragma unroll
+                for (int s = 0; s < S; ++s) {
+                    mine[i * S + s] = cB[s];
+                    mine[kBB * S + i * S + s] = cC[s];
+                }
+            }
+            *reinterpret_cast<float4*>(mine + PXO) = make_float4(pxb[0], pxb[1], pxb[2], pxb[3]);
+            *reinterpret_cast<float4*>(mine + PXO + 4) = make_float4(pdb[0], pdb[1], pdb[2], pdb[3]);
+            wave_sync();
+            // sum over the wave's 16 channels: output e -> (state sp_, lane group jp, type
+            // ty, step st)
+#pragma unroll
+            for (int r = 0; r < (2 * kBB * NP + 63) / 64; ++r) {
+                const int e = lane + 64 * r;
+                if (e < 2 * kBB * NP) {
+                    const int sp_ = e % S;
+                    const int jp = (e / S) % 4;
+                    const int ty = (e / (4 * S)) % 2;
+                    const int st = e / (8 * S);
+                    const float* col = wx + jp * LS + ty * kBB * S + st * S + sp_;
+                    float tot = 0.0f;
+#pragma unroll
+                    for (int c = 0; c < 16; ++c) tot += col[c * 4 * LS];
+                    cbuf[(bi * kBB + st) * 2 * NP + ty * NP + jp * S + sp_] = tot;
+                }
+            }
+            if (j == bi) {
+                // the batch is this lane's 4 steps: Σ_n over the quad, then dx and dΔ
+                float PX[4] = {0.0f, 0.0f, 0.0f, 0.0f}, PD[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float* src = wx + (qb + r) * LS + PXO;
+                    const float4 a = *reinterpret_cast<const float4*>(src);
+                    const float4 c = *reinterpret_cast<const float4*>(src + 4);
+                    PX[0] += a.x; PX[1] += a.y; PX[2] += a.z; PX[3] += a.w;
+                    PD[0] += c.x; PD[1] += c.y; PD[2] += c.z; PD[3] += c.w;
+                }
+                float ox[4], od[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    ox[i] = fmaf(ds[i], Dd, dl[i] * PX[i]);
+                    od[i] = fmaf(xv[i], PX[i], PD[i]) * su[i];
+                    const bool ok = te + i < t1c;
+                    accD += ok ? ds[i] * xv[i] : 0.0f;
+                    accT += ok ? od[i] : 0.0f;
+                }
+                if (valid) {
+                    store4(dxo + row, te, t1c, vec, ox);
+                    store4(ddto + row, te, t1c, vec, od);
+                }
+            }
+            wave_sync();
         }
-        SS_RV_BATCH(3)
-        SS_RV_BATCH(2)
-        SS_RV_BATCH(1)
-        SS_RV_BATCH(0)
-#undef SS_RV_BATCH
 
-        // Σ_n partials -> owner lanes; per-element gradients
-        {
-            float* mine = wscr + lane * LS;
-#pragma unroll
-            for (int q4 = 0; q4 < kBT; q4 += 4) {
-                *reinterpret_cast<float4*>(mine + q4) = make_float4(pdx[q4], pdx[q4 + 1], pdx[q4 + 2], pdx[q4 + 3]);
-                *reinterpret_cast<float4*>(mine + 16 + q4) = make_float4(pdd[q4], pdd[q4 + 1], pdd[q4 + 2], pdd[q4 + 3]);
-            }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            float PX[4] = {0.0f, 0.0f, 0.0f, 0.0f}, PD[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-            const int qb = lane & ~3;
-#pragma unroll
-            for (int src = 0; src < 4; ++src) {
-                const float4 a = *reinterpret_cast<const float4*>(wscr + (qb + src) * LS + kBPer * j);
-                const float4 c = *reinterpret_cast<const float4*>(wscr + (qb + src) * LS + 16 + kBPer * j);
-                PX[0] += a.x; PX[1] += a.y; PX[2] += a.z; PX[3] += a.w;
-                PD[0] += c.x; PD[1] += c.y; PD[2] += c.z; PD[3] += c.w;
-            }
-            float ox[4], od[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                ox[i] = fmaf(ds[i], Dd, dl[i] * PX[i]);
-                const float ddel = fmaf(xv[i], PX[i], PD[i]);
-                od[i] = ddel * su[i];
-                const bool ok = te + i < t1c;
-                accD += ok ? ds[i] * xv[i] : 0.0f;
-                accT += ok ? od[i] : 0.0f;
-            }
-            if (valid) {
-                store4(dxo + row, te, t1c, vec, ox);
-                store4(ddto + row, te, t1c, vec, od);
-                if (kGate) store4(dzo + row, te, t1c, vec, dzv);
-            }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // dB|dC of the tile: the four waves' sums meet once per tile
+        __syncthreads();
+        for (int e = tid; e < OUTW; e += kBThreads) {
+            const int st = e / (2 * NP);
+            const int v = e % (2 * NP);
+            const int ty = v / NP, n = v % NP;
+            const float tot = (comb[e] + comb[OUTW + e]) + (comb[2 * OUTW + e] + comb[3 * OUTW + e]);
+            const int64_t t = t0c + tb + st;
+            if (n < Nr && t < t1c)
+                dbc_part[((int64_t(b) * NB + blockIdx.x) * L + t) * (2 * Nr) + ty * Nr + n] = tot;
         }
+        __syncthreads();
     }
 
     accD = qsum(accD);
@@ -498,7 +612,7 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(
     if (valid) {
 #pragma unroll
         for (int s = 0; s < S; ++s) {
-            const int n = j * S + s;
+            const int n = n0 + s;
             if (n < Nr) h_start[sidx + n] = dA[s];   // dA partial of this (b, chunk, d)
         }
         if (j == 0) {
@@ -591,33 +705,41 @@ size_t bwd_partial_bytes(const Plan& p) {
     return align256(bc) + dt;
 }
 
-template <typename Tin, int S>
-static hipError_t launch_bwd_t(const BwdLaunch& p, hipStream_t s) {
-    dim3 grid(unsigned((p.D + kBChan - 1) / kBChan), unsigned(p.K), unsigned(p.B));
+template <typename Tin, int S, bool kGate>
+static void launch_bwd_g(const BwdLaunch& p, dim3 grid, hipStream_t s) {
     const Tin* x = static_cast<const Tin*>(p.x);
     const Tin* dr = static_cast<const Tin*>(p.dt_raw);
     const Tin* z = static_cast<const Tin*>(p.z);
+    const Tin* Bm = static_cast<const Tin*>(p.Bm);
+    const Tin* Cm = static_cast<const Tin*>(p.Cm);
     if (p.stage == 0) {
-        if (z)
-            hipLaunchKernelGGL((bwd_agg_kernel<Tin, S, true>), grid, dim3(kBThreads), 0, s, x, dr, z,
-                               p.dy, p.dt_bias, p.A, p.BC, p.h_end, p.rev_end, p.dsum, p.L, p.D,
+        if (p.h_ckpt)
+            hipLaunchKernelGGL((bwd_agg_kernel<Tin, S, kGate, false>), grid, dim3(kBThreads), 0, s, x, dr,
+                               z, p.dy, p.dt_bias, p.A, Bm, Cm, p.h_end, p.rev_end, p.dsum, p.L, p.D,
                                int(p.N), p.chunk, p.K, p.vec);
         else
-            hipLaunchKernelGGL((bwd_agg_kernel<Tin, S, false>), grid, dim3(kBThreads), 0, s, x, dr, z,
-                               p.dy, p.dt_bias, p.A, p.BC, p.h_end, p.rev_end, p.dsum, p.L, p.D,
+            hipLaunchKernelGGL((bwd_agg_kernel<Tin, S, kGate, true>), grid, dim3(kBThreads), 0, s, x, dr,
+                               z, p.dy, p.dt_bias, p.A, Bm, Cm, p.h_end, p.rev_end, p.dsum, p.L, p.D,
                                int(p.N), p.chunk, p.K, p.vec);
     } else {
-        if (z)
-            hipLaunchKernelGGL((bwd_chunk_kernel<Tin, S, true>), grid, dim3(kBThreads), 0, s, x, dr, z,
-                               p.dy, p.dt_bias, p.A, p.Dskip, p.BC, p.h_end, p.rev_end, p.dx,
-                               p.ddt_raw, p.dz, p.dbc_part, p.ddt_part, p.L, p.D, int(p.N), p.chunk,
-                               p.K, p.vec);
+        if (p.h_ckpt)
+            hipLaunchKernelGGL((bwd_chunk_kernel<Tin, S, kGate, true>), grid, dim3(kBThreads), 0, s, x, dr,
+                               z, p.dy, p.dt_bias, p.A, p.Dskip, Bm, Cm, p.h_ckpt, p.h_end, p.rev_end,
+                               p.dx, p.ddt_raw, p.dz, p.dbc_part, p.ddt_part, p.L, p.D, int(p.N),
+                               p.chunk, p.K, p.vec);
         else
-            hipLaunchKernelGGL((bwd_chunk_kernel<Tin, S, false>), grid, dim3(kBThreads), 0, s, x, dr, z,
-                               p.dy, p.dt_bias, p.A, p.Dskip, p.BC, p.h_end, p.rev_end, p.dx,
-                               p.ddt_raw, p.dz, p.dbc_part, p.ddt_part, p.L, p.D, int(p.N), p.chunk,
-                               p.K, p.vec);
+            hipLaunchKernelGGL((bwd_chunk_kernel<Tin, S, kGate, false>), grid, dim3(kBThreads), 0, s, x, dr,
+                               z, p.dy, p.dt_bias, p.A, p.Dskip, Bm, Cm, p.h_ckpt, p.h_end, p.rev_end,
+                               p.dx, p.ddt_raw, p.dz, p.dbc_part, p.ddt_part, p.L, p.D, int(p.N),
+                               p.chunk, p.K, p.vec);
     }
+}
+
+template <typename Tin, int S>
+static hipError_t launch_bwd_t(const BwdLaunch& p, hipStream_t s) {
+    dim3 grid(unsigned((p.D + kBChan - 1) / kBChan), unsigned(p.K), unsigned(p.B));
+    if (p.z) launch_bwd_g<Tin, S, true>(p, grid, s);
+    else launch_bwd_g<Tin, S, false>(p, grid, s);
     return hipGetLastError();
 }
 

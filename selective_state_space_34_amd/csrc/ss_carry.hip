@@ -15,6 +15,8 @@
 //      the waves before it onto the initial state,
 //   4. wave_shr:1 turns the inclusive prefix into each lane's entering state, and
 //      the lane walks its run again writing every chunk's start state.
+// With few chunks and many channels a plain sequential walk per (channel, state) is
+// faster (carry_seq_kernel): the scan's depth is then small and its lanes mostly idle.
 #include "ss_device.h"
 #include "ss_kernels.h"
 
@@ -132,6 +134,49 @@ __global__ __launch_bounds__(1024) void carry_kernel(CarrySet s0, CarrySet s1,
     }
 }
 
+// Few chunks (K <= kSeqMaxK) and many channels: one thread per (batch row, channel, state)
+// walks its K chunks in order.  The chunk pairs are loaded kSeqBatch at a time ahead of
+// the dependent chain of FMAs.  Threads run along n, then d: each chunk's N states of a
+// channel are contiguous, so a group of N threads reads one contiguous run.
+constexpr int kSeqMaxK = 128;
+constexpr int kSeqBatch = 16;
+
+__global__ __launch_bounds__(256) void carry_seq_kernel(CarrySet s0, CarrySet s1,
+                                                        const float* __restrict__ dsum,
+                                                        const float* __restrict__ A, int64_t BDN,
+                                                        int64_t D, int N, int K) {
+    const CarrySet& cs = blockIdx.y ? s1 : s0;
+    const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= BDN) return;
+    const int n = int(i % N);
+    const int64_t bd = i / N;                  // b * D + d
+    const int64_t d = bd % D;
+    const float a2 = A[d * N + n] * kLog2e;
+    float st = cs.h_in ? cs.h_in[bd * N + n] : 0.0f;
+    for (int j0 = 0; j0 < K; j0 += kSeqBatch) {
+        float he[kSeqBatch], sm[kSeqBatch];
+#pragma unroll
+        for (int u = 0; u < kSeqBatch; ++u) {
+            const int j = j0 + u;
+            const int c = cs.reverse ? K - 1 - j : j;
+            const int64_t base = bd * K + c;
+            he[u] = (j < K) ? cs.h_end[base * N + n] : 0.0f;
+            sm[u] = (j < K) ? dsum[base] : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < kSeqBatch; ++u) {
+            const int j = j0 + u;
+            if (j < K) {
+                const int c = cs.reverse ? K - 1 - j : j;
+                // read before write: h_start may alias h_end (the loads above came first)
+                cs.h_start[(bd * K + c) * N + n] = st;
+                st = fmaf(exp2_hw(a2 * sm[u]), st, he[u]);
+            }
+        }
+    }
+    if (cs.h_out) cs.h_out[bd * N + n] = st;
+}
+
 template <int N>
 static hipError_t launch_carry_t(const CarryLaunch& p, hipStream_t s) {
     const int m = (p.K + 1023) / 1024;
@@ -145,6 +190,15 @@ static hipError_t launch_carry_t(const CarryLaunch& p, hipStream_t s) {
 }
 
 hipError_t launch_carry(int N, const CarryLaunch& p, hipStream_t s) {
+    const int64_t BDN = p.B * p.D * N;
+    if (p.K <= kSeqMaxK && BDN >= 16384) {
+        const CarrySet s0{p.h_end, p.h_in, p.h_start, p.h_out, p.reverse};
+        const CarrySet s1{p.h_end2, p.h_in2, p.h_start2, p.h_out2, p.reverse2};
+        dim3 grid(unsigned((BDN + 255) / 256), p.dual ? 2u : 1u);
+        hipLaunchKernelGGL(carry_seq_kernel, grid, dim3(256), 0, s, s0, s1, p.dsum, p.A, BDN, p.D, N,
+                           p.K);
+        return hipGetLastError();
+    }
     switch (N) {
         case 1: return launch_carry_t<1>(p, s);
         case 2: return launch_carry_t<2>(p, s);

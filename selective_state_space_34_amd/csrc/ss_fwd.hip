@@ -68,7 +68,8 @@ __global__ __launch_bounds__(256) void scan_kernel(
     const float* __restrict__ dt_bias, const float* __restrict__ A,
     const float* __restrict__ Dskip, const float* __restrict__ BC,
     const float* __restrict__ h_init, float* __restrict__ y, float* __restrict__ h_last,
-    float* __restrict__ dsum_out, int64_t L, int64_t D, int64_t chunk, int K, int vec) {
+    float* __restrict__ h_ckpt, float* __restrict__ dsum_out, int64_t L, int64_t D,
+    int64_t chunk, int K, int vec) {
     const int64_t d = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     const int k = blockIdx.y;
     const int b = blockIdx.z;
@@ -92,6 +93,9 @@ __global__ __launch_bounds__(256) void scan_kernel(
     float* yr = kAgg ? nullptr : y + row;
     const float* bcb = BC + int64_t(b) * L * (2 * N);
     float dsum = 0.0f;
+    // checkpoints: the state entering step t for every t % kCkptSteps == 0
+    const int64_t nck = (L + kCkptSteps - 1) / kCkptSteps;
+    float* ckr = (!kAgg && h_ckpt) ? h_ckpt + (int64_t(b) * D + d) * nck * N : nullptr;
 
     // One step.  Bq/Cq hold this step's B and C (uniform across the wave: SGPRs).  The
     // state update reads only Bq and the readout only Cq, so the next step's B row is
@@ -112,6 +116,10 @@ __global__ __launch_bounds__(256) void scan_kernel(
     };
     auto step = [&](auto s4d_tag, float xv, float dv, float zv, int64_t tt) -> float {
         constexpr bool kS4D = decltype(s4d_tag)::value;
+        if (ckr && tt % kCkptSteps == 0) {      // uniform: every lane is at step tt
+#pragma unroll
+            for (int n = 0; n < N; ++n) ckr[(tt / kCkptSteps) * N + n] = h[n];
+        }
         float delta, r = 1.0f;
         if constexpr (kS4D) {
             const float u = bias + dv;
@@ -226,8 +234,8 @@ static hipError_t launch_scan_t(const ScanLaunch& p, hipStream_t s) {
     const Tin* x = static_cast<const Tin*>(p.x);
     const Tin* dr = static_cast<const Tin*>(p.dt_raw);
     const Tin* z = static_cast<const Tin*>(p.z);
-#define SS_SCAN_ARGS x, dr, z, p.dt_bias, p.A, p.Dskip, p.BC, p.h_init, p.y, p.h_last, p.dsum, \
-                     p.L, p.D, p.chunk, p.K, p.vec
+#define SS_SCAN_ARGS x, dr, z, p.dt_bias, p.A, p.Dskip, p.BC, p.h_init, p.y, p.h_last, p.h_ckpt, \
+                     p.dsum, p.L, p.D, p.chunk, p.K, p.vec
     if (p.agg)
         hipLaunchKernelGGL((scan_kernel<Tin, N, false, true>), grid, dim3(wg), 0, s, SS_SCAN_ARGS);
     else if (p.z)

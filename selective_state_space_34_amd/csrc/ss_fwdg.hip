@@ -164,7 +164,8 @@ __global__ __launch_bounds__(kThreads) void scang_kernel(
     const float* __restrict__ dt_bias, const float* __restrict__ A,
     const float* __restrict__ Dskip, const Tin* __restrict__ Bm, const Tin* __restrict__ Cm,
     const float* __restrict__ h_init, float* __restrict__ y, float* __restrict__ h_last,
-    float* __restrict__ dsum_out, int64_t L, int64_t D, int64_t chunk, int K) {
+    float* __restrict__ h_ckpt, float* __restrict__ dsum_out, int64_t L, int64_t D,
+    int64_t chunk, int K) {
     constexpr int N = G * S;
     constexpr int CW = 64 / G;                    // channels per wave
     constexpr int CB = 4 * CW;                    // channels per block
@@ -209,6 +210,13 @@ __global__ __launch_bounds__(kThreads) void scang_kernel(
     const Tin* Bb = Bm + int64_t(b) * N * L;
     const Tin* Cb = Cm + int64_t(b) * N * L;
     float dsum = 0.0f;
+    // checkpoints: the state entering step t for every t % kCkptSteps == 0
+    const int64_t nck = (L + kCkptSteps - 1) / kCkptSteps;
+    float* ckr = (!kAgg && h_ckpt && valid) ? h_ckpt + (int64_t(b) * D + d) * nck * N + n0 : nullptr;
+    auto checkpoint = [&](int64_t t) {
+#pragma unroll
+        for (int s = 0; s < S; ++s) ckr[(t / kCkptSteps) * N + s] = h[s];
+    };
 
     // B/C tile copy: 2·N rows of 32 steps; unit e covers steps 4q..4q+3 of state n of
     // B (m = 0) or C (m = 1), with n fastest across lanes
@@ -265,6 +273,7 @@ __global__ __launch_bounds__(kThreads) void scang_kernel(
 
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
+            if (ckr) checkpoint(t0 + kHalf * hh);      // sweeps start on multiples of 16
             // this lane's kH steps of the half: (δ, δ·x) into the channel's row
 #pragma unroll
             for (int i = 0; i < kH; ++i) {
@@ -342,6 +351,7 @@ __global__ __launch_bounds__(kThreads) void scang_kernel(
     // tail: the last (t_end - t_tiles_end) < 32 steps, one step at a time; every lane
     // prepares the step itself and reads its B/C straight from the inputs
     for (int64_t t = t_tiles_end; t < t_end; ++t) {
+        if (ckr && t % kCkptSteps == 0) checkpoint(t);
         const float xt = to_f32(xr[t]);
         const float delta = softplus(bias + to_f32(dr[t]));
         const float dxt = delta * xt;
@@ -385,8 +395,8 @@ static hipError_t launch_scang_t(const ScanLaunch& p, hipStream_t s) {
     const Tin* z = static_cast<const Tin*>(p.z);
     const Tin* Bm = static_cast<const Tin*>(p.Bm);
     const Tin* Cm = static_cast<const Tin*>(p.Cm);
-#define SS_ARGS x, dr, z, p.dt_bias, p.A, p.Dskip, Bm, Cm, p.h_init, p.y, p.h_last, p.dsum, p.L, \
-                p.D, p.chunk, p.K
+#define SS_ARGS x, dr, z, p.dt_bias, p.A, p.Dskip, Bm, Cm, p.h_init, p.y, p.h_last, p.h_ckpt, \
+                p.dsum, p.L, p.D, p.chunk, p.K
     if (p.agg)
         hipLaunchKernelGGL((scang_kernel<Tin, G, S, false, true>), grid, dim3(kThreads), 0, s, SS_ARGS);
     else if (p.z)

@@ -6,6 +6,9 @@
 
 namespace ss {
 
+// Steps between the forward's state checkpoints (the backward's tile length).
+constexpr int kCkptSteps = 16;
+
 struct ScanLaunch {
     const void* x;
     const void* dt_raw;
@@ -19,6 +22,8 @@ struct ScanLaunch {
     const float* h_init;    // nullable; [B, D, K, N]
     float* y;               // OUT mode
     float* h_last;          // OUT: h_final (nullable); AGG: h_end [B, D, K, N]
+    float* h_ckpt;          // OUT: nullable; [B, D, ceil(L / kCkptSteps), N]: state entering
+                            // every kCkptSteps-th step
     float* dsum;            // AGG: Σδ per chunk [B, D, K]
     int64_t B, L, D, chunk;
     int K;
@@ -49,7 +54,7 @@ struct CarryLaunch {
     int reverse2;
 };
 
-// Backward launches (quad layout).  stage 0: chunk aggregates (h_end, rev_end, dsum);
+// Backward launches (four lanes per channel).  stage 0: chunk aggregates (h_end, rev_end, dsum);
 // stage 1: final pass (h_end holds chunk start states on entry and dA partials on exit,
 // rev_end holds the adjoints entering each chunk from the right).
 struct BwdLaunch {
@@ -60,7 +65,9 @@ struct BwdLaunch {
     const float* dt_bias;
     const float* A;
     const float* Dskip;
-    const float* BC;
+    const void* Bm;    // [B, N, L] inputs
+    const void* Cm;
+    const float* h_ckpt;  // nullable: the forward's checkpoints; then h_end holds only dA
     float* h_end;      // [B, D, K, N]
     float* rev_end;    // [B, D, K, N]
     float* dsum;       // [B, D, K]

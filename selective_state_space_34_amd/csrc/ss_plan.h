@@ -92,7 +92,9 @@ inline int make_plan(const ss_dims& d, bool backward, Plan* out) {
             int64_t c = (p.L + K - 1) / K;
             const int64_t cmin = backward ? 64 : 128;
             if (c < cmin) c = cmin;
-            chunk = (c + 7) / 8 * 8;
+            // whole 32-step tiles for the group kernel (no per-step tail; checkpoints at its
+            // 16-step sweep starts)
+            chunk = p.group ? (c + 31) / 32 * 32 : (c + 7) / 8 * 8;
         }
         if (chunk > p.L) chunk = (p.L + 7) / 8 * 8;
     }
@@ -103,8 +105,8 @@ inline int make_plan(const ss_dims& d, bool backward, Plan* out) {
 
     size_t off = 0;
     p.off_bc = off;
-    // [B, L, 2N] float32 copy of B and C: the one-lane forward kernel and the backward
-    if (backward || !p.group) off = align256(off + size_t(p.B) * size_t(p.L) * size_t(2 * N) * sizeof(float));
+    // [B, L, 2N] float32 copy of B and C: the one-lane forward kernel only
+    if (!backward && !p.group) off = align256(off + size_t(p.B) * size_t(p.L) * size_t(2 * N) * sizeof(float));
     p.off_hend = p.off_dsum = p.off_hstart = p.off_gend = p.off_gstart = p.off_red = 0;
     p.red_bytes = 0;
     if (chunked) {

@@ -37,7 +37,7 @@ def test_exports_match_header(lib):
 
 
 def test_version_and_strerror(lib):
-    assert lib.ss_version() == (0 << 16) | 1
+    assert lib.ss_version() == (0 << 16) | 2
     for code in ss.ERRORS:
         assert len(lib.ss_strerror(code)) > 0
     assert b"unknown" in lib.ss_strerror(12345)
@@ -47,7 +47,7 @@ FAKE = 0x10000  # 16-byte aligned, never dereferenced: every call below fails va
 
 
 def _fwd(lib, dims, ptrs=None, ws=None, wbytes=0):
-    p = [ctypes.c_void_p(FAKE)] * 11 if ptrs is None else ptrs
+    p = [ctypes.c_void_p(FAKE)] * 12 if ptrs is None else ptrs
     return lib.ss_fwd(None if dims is None else ctypes.byref(dims), *p,
                       ws, ctypes.c_size_t(wbytes), None)
 
@@ -69,16 +69,21 @@ def test_fwd_validation(lib):
     assert _fwd(lib, bad_res) == -3
     # required pointers
     for i in (0, 1, 2, 3, 4, 5, 6, 9):
-        p = [ctypes.c_void_p(FAKE)] * 11
+        p = [ctypes.c_void_p(FAKE)] * 12
         p[i] = None
         assert _fwd(lib, good, p) == -1, i
-    # optional pointers (z, h0, h_final) may be NULL: the call then reaches the workspace check
-    p = [ctypes.c_void_p(FAKE)] * 11
-    p[7] = p[8] = p[10] = None
+    # optional pointers (z, h0, h_final, h_ckpt) may be NULL: the call then reaches the
+    # workspace check
+    p = [ctypes.c_void_p(FAKE)] * 12
+    p[7] = p[8] = p[10] = p[11] = None
     assert _fwd(lib, good, p) == -5
+    # checkpoints need chunks that are multiples of 16 on the four-lane layout
+    assert _fwd(lib, ss.make_dims(2, 80, 32, 16, ss.SS_F32, ss.SS_PLAN_CHUNKED, 40)) == -7
+    lane40 = ss.make_dims(2, 80, 32, 16, ss.SS_F32, ss.SS_PLAN_CHUNKED, 40, ss.SS_LAYOUT_LANE)
+    assert _fwd(lib, lane40) == -5
     # alignment
-    for i in range(11):
-        p = [ctypes.c_void_p(FAKE)] * 11
+    for i in range(12):
+        p = [ctypes.c_void_p(FAKE)] * 12
         p[i] = ctypes.c_void_p(FAKE + 4)
         assert _fwd(lib, good, p) == -4, i
     # workspace
@@ -104,9 +109,14 @@ def test_workspace_sizes(lib):
     st = 1 * K * 256 * 16 * 4
     assert ss.workspace_size(d) == 2 * st + K * 256 * 4
     assert ss.workspace_size(d) == ss.workspace_size(d)
-    # the backward always holds the B/C copy
+    # the backward: chunk state buffers (forward and reverse pairs), chunk sums, dB|dC
+    # partials per 64-channel block and dD / ddt_bias partials per chunk
     d = ss.make_dims(8, 2048, 5120, 16, ss.SS_BF16)
-    assert ss.workspace_size(d, backward=True) > 8 * 2048 * 32 * 4
+    K, NB = 2048 // 64, 5120 // 64
+    st = 8 * K * 5120 * 16 * 4
+    a256 = lambda v: (v + 255) // 256 * 256
+    assert ss.workspace_size(d, backward=True) == (4 * st + a256(8 * K * 5120 * 4)
+                                                   + a256(8 * NB * 2048 * 32 * 4) + 8 * K * 5120 * 2 * 4)
     n = ctypes.c_size_t()
     assert lib.ss_fwd_workspace_size(None, ctypes.byref(n)) == -1
     assert lib.ss_fwd_workspace_size(ctypes.byref(d), None) == -1
@@ -116,8 +126,9 @@ def test_workspace_sizes(lib):
 def test_bwd_validation(lib):
     good = ss.make_dims(2, 64, 32, 16, ss.SS_F32)
     F = ctypes.c_void_p(FAKE)
-    # x dt_raw dt_bias A Bm Cm Dskip | z h0 | dy dh_final | dx ddt_raw ddt_bias dA dB dC dD | dz dh0
-    args = [F] * 7 + [None, None] + [F, None] + [F] * 7 + [None, None]
+    # x dt_raw dt_bias A Bm Cm Dskip | z h0 | dy dh_final h_ckpt | dx ddt_raw ddt_bias dA dB dC dD
+    # | dz dh0
+    args = [F] * 7 + [None, None] + [F, None, None] + [F] * 7 + [None, None]
 
     def call(dims, a, ws=None, wbytes=0):
         return lib.ss_bwd(None if dims is None else ctypes.byref(dims), *a, ws,
@@ -137,6 +148,10 @@ def test_bwd_validation(lib):
     # dz given without z
     a = list(args)
     a[7] = None
-    a[18] = F
+    a[19] = F
     assert call(good, a) == -1
+    # misaligned checkpoints
+    a = list(args)
+    a[11] = ctypes.c_void_p(FAKE + 4)
+    assert call(good, a) == -4
     assert call(good, args) == -5

@@ -16,12 +16,18 @@ pytestmark = pytest.mark.gpu
 GRADS = ("dx", "ddt_raw", "dz", "ddt_bias", "dA", "dB", "dC", "dD", "dh0")
 
 
-def gpu_bwd(ss, inp, gate, h0, dhf, chunk=0):
+def gpu_bwd(ss, inp, gate, h0, dhf, chunk=0, ckpt=False, layout=0):
+    """ss_bwd; with ckpt, on the checkpoints of an ss_fwd call (in the given layout)."""
     import torch
     t = dev(inp)
+    hck = None
+    if ckpt:
+        _, hck = ss.ss_fwd(t["x"], t["dt_raw"], t["dt_bias"], t["A"], t["Bm"], t["Cm"], t["Dskip"],
+                           z=t["z"] if gate else None, h0=t["h0"] if h0 else None,
+                           return_ckpt=True, layout=layout)
     g = ss.ss_bwd(t["x"], t["dt_raw"], t["dt_bias"], t["A"], t["Bm"], t["Cm"], t["Dskip"], t["dy"],
                   z=t["z"] if gate else None, h0=t["h0"] if h0 else None,
-                  dh_final=t["dh_final"] if dhf else None, chunk=chunk)
+                  dh_final=t["dh_final"] if dhf else None, h_ckpt=hck, chunk=chunk)
     torch.cuda.synchronize()
     return {k: (None if v is None else v.cpu().numpy()) for k, v in g.items()}
 
@@ -53,16 +59,18 @@ CASES = [
     (1, 96, 24, 2, "f32", True, True, True, 16),        # N = 2: two padded states per quad
     (3, 130, 9, 1, "bf16", False, True, True, 48),      # N = 1, odd L
     (2, 1024, 130, 16, "bf16", True, False, False, 0),
+    (1, 300, 1024, 16, "bf16", True, True, True, 0),    # B*D*N >= 16384: sequential carries
 ]
 
 
+@pytest.mark.parametrize("ckpt", [False, True], ids=["recompute", "ckpt"])
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "B{}L{}D{}N{}-{}-g{}-h{}-f{}-c{}".format(*c))
-def test_bwd_small(gpu, case):
+def test_bwd_small(gpu, case, ckpt):
     Bn, L, D, N, dt, gate, h0, dhf, chunk = case
     inp = make_inputs(Bn, L, D, N, dtype=dt, seed=300 + L + N, gate=gate, with_h0=h0, with_dy=True,
                       with_dh_final=dhf, a_perturb=True)
-    note(f"bwd {case}")
-    got = gpu_bwd(gpu, inp, gate, h0, dhf, chunk)
+    note(f"bwd {case} ckpt={ckpt}")
+    got = gpu_bwd(gpu, inp, gate, h0, dhf, chunk, ckpt=ckpt)
     ref = oracle_bwd(inp, gate, h0, dhf)
     compare(got, ref)
 
@@ -88,12 +96,25 @@ def test_bwd_chunk_sizes_agree(gpu):
             assert_close(got[k], ref[k], 2e-5, f"{k} chunk={c}")
 
 
-def test_c4_full_backward(gpu):
+@pytest.mark.parametrize("layout", [1, 2, 3], ids=["quad", "lane", "oct"])
+def test_bwd_checkpoints_from_every_layout(gpu, layout):
+    """Checkpoints written by each forward layout drive the backward to the same result."""
+    inp = make_inputs(2, 520, 72, 16, dtype="bf16", seed=7, gate=True, with_h0=True, with_dy=True,
+                      with_dh_final=True, a_perturb=True)
+    note(f"bwd checkpoints from layout {layout}")
+    ref = gpu_bwd(gpu, inp, True, True, True)
+    got = gpu_bwd(gpu, inp, True, True, True, ckpt=True, layout=layout)
+    for k in GRADS:
+        assert_close(got[k], ref[k], 2e-5, f"{k} layout={layout}")
+
+
+@pytest.mark.parametrize("ckpt", [False, True], ids=["recompute", "ckpt"])
+def test_c4_full_backward(gpu, ckpt):
     """The full B=4 L=4096 D=2048 N=16 bf16 fwd+bwd workload, every gradient element."""
     w = workload("c4")
     inp = workload_inputs(w)
-    note("c4 backward full")
-    got = gpu_bwd(gpu, inp, True, False, False)
+    note(f"c4 backward full ckpt={ckpt}")
+    got = gpu_bwd(gpu, inp, True, False, False, ckpt=ckpt)
     ref = oracle_bwd(inp, True, False, False)
     errs = compare(got, ref)
     print("c4 gradient errors:", {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)

@@ -91,6 +91,8 @@ EDGE = [
     (1, 4000, 70, 16, "bf16", True, True, 2, 40),
     (3, 96, 200, 16, "f32", False, True, 2, 16),
     (1, 2056, 33, 32, "bf16", True, True, 2, 264),
+    # B*D*N >= 16384 with few chunks: the sequential per-(channel, state) carry
+    (1, 520, 1024, 16, "bf16", True, True, 2, 64),
 ]
 
 
@@ -194,3 +196,45 @@ def test_guard_bands_untouched(gpu):
     yr, hr = oracle_fwd(inp)
     assert_close(y.cpu().numpy(), yr, 1e-4, "y")
     assert_close(hf.cpu().numpy(), hr, 1e-4, "h_final")
+
+
+CKPT_CASES = [
+    # B, L, D, N, dtype, gate, h0, plan, chunk, layout
+    (2, 200, 40, 16, "f32", True, True, 0, 0, 0),       # single pass, ragged last block
+    (1, 1000, 70, 16, "bf16", True, True, 2, 96, 1),    # chunked, four lanes, chunk 96
+    (2, 256, 24, 8, "f32", False, True, 2, 64, 3),      # eight lanes per channel
+    (1, 333, 20, 16, "bf16", True, True, 2, 40, 2),     # one lane per channel, chunk 40
+    (3, 64, 9, 2, "f32", True, False, 0, 0, 0),         # N = 2: one-lane kernel
+]
+
+
+@pytest.mark.parametrize("case", CKPT_CASES,
+                         ids=lambda c: "B{}L{}D{}N{}-{}-g{}-h{}-p{}-c{}-l{}".format(*c))
+def test_checkpoints(gpu, case):
+    """Entry i of h_ckpt is the state before step 16 i: the oracle's final state of the
+    first 16 i steps (h0 or 0 for i = 0); y and h_final are unchanged by asking for it."""
+    import torch
+    Bn, L, D, N, dt, gate, h0, plan, chunk, layout = case
+    inp = make_inputs(Bn, L, D, N, dtype=dt, seed=400 + L, gate=gate, with_h0=h0, a_perturb=True)
+    note(f"checkpoints {case}")
+    from tests.gpu_util import dev
+    t = dev(inp)
+    y, hf, ck = gpu.ss_fwd(t["x"], t["dt_raw"], t["dt_bias"], t["A"], t["Bm"], t["Cm"], t["Dskip"],
+                           z=t["z"] if gate else None, h0=t["h0"] if h0 else None,
+                           return_final=True, return_ckpt=True, plan=plan, chunk=chunk,
+                           layout=layout)
+    y2, hf2 = gpu_fwd(gpu, inp, gate=gate, h0=h0, final=True, plan=plan, chunk=chunk, layout=layout)
+    torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().numpy(), y2) and np.array_equal(hf.cpu().numpy(), hf2)
+    ck = ck.cpu().numpy()
+    nck = (L + 15) // 16
+    assert ck.shape == (Bn, D, nck, N)
+    exp = np.empty_like(ck, dtype=np.float64)
+    exp[:, :, 0] = inp.h0 if h0 else 0.0
+    for i in range(1, nck):
+        tl = 16 * i
+        cut = lambda a: None if a is None else a[..., :tl]
+        _, hp = cref.fwd(cut(inp.x), cut(inp.dt_raw), inp.dt_bias, inp.A, cut(inp.Bm), cut(inp.Cm),
+                         inp.Dskip, z=cut(inp.z) if gate else None, h0=inp.h0 if h0 else None)
+        exp[:, :, i] = hp
+    assert_close(ck, exp, tol_for(inp), "h_ckpt")
