@@ -101,7 +101,10 @@ int ss_fwd(const ss_dims* dims, const void* x, const void* dt_raw, const float* 
     s.B = p.B; s.L = p.L; s.D = p.D; s.vec = p.vec;
     if (!p.chunked) {
         s.chunk = p.L; s.K = 1; s.h_init = h0; s.y = y; s.h_last = h_final; s.h_ckpt = h_ckpt; s.agg = 0;
-        e = p.group ? ss::launch_scang(bf16, int(p.N), p.group, s, stream) : ss::launch_scan(bf16, int(p.N), s, stream);
+        s.d4 = p.d4; s.nb4 = p.nb4;
+        e = p.mixed ? ss::launch_scang_mixed(bf16, int(p.N), s, stream)
+            : p.group ? ss::launch_scang(bf16, int(p.N), p.group, s, stream)
+                      : ss::launch_scan(bf16, int(p.N), s, stream);
         if (e != hipSuccess) return hip_fail(e);
         return SS_OK;
     }

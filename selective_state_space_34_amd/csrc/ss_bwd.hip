@@ -432,23 +432,23 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
 #pragma unroll
         for (int s = 0; s < S; ++s) hc[s] = kCk ? ckn[s] : ck[kCk ? 0 : tt][s];
         if (kCk && tt > 0) load_tile(tt - 1);
-        float dl[4], ds[4], su[4], sz[4];
+        float sz[4];
 #pragma unroll
         for (int i = 0; i < kBPer; ++i) {
             const bool ok = te + i < t1c;
             const float u = bias + dv[i];
-            dl[i] = ok ? softplus(u) : 0.0f;
-            su[i] = sigmoid(u);
+            const float dl = ok ? softplus(u) : 0.0f;
+            float ds;
             if (kGate) {
                 sz[i] = sigmoid(zv[i]);
-                ds[i] = ok ? gv[i] * zv[i] * sz[i] : 0.0f;
+                ds = ok ? gv[i] * zv[i] * sz[i] : 0.0f;
             } else {
-                ds[i] = ok ? gv[i] : 0.0f;
+                ds = ok ? gv[i] : 0.0f;
             }
-            // channels past D compute on a clamped copy: they must add nothing to dB, dC
-            const float dsv = valid ? ds[i] : 0.0f;
-            const float dxv = valid ? dl[i] * xv[i] : 0.0f;
-            *reinterpret_cast<float4*>(myrow + 4 * (kBPer * j + i)) = make_float4(dl[i], dxv, dsv, 0.0f);
+            // step row (δ, x, ds, σ(u)); channels past D compute on a clamped copy and must
+            // add nothing to dB, dC: their x and ds are zero
+            *reinterpret_cast<float4*>(myrow + 4 * (kBPer * j + i)) =
+                make_float4(dl, valid ? xv[i] : 0.0f, valid ? ds : 0.0f, sigmoid(u));
         }
         wave_sync();
         const float* bt = bc_lds + tb * R;
@@ -474,10 +474,11 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
                     if (kGate) cn.load(bt + (t + 1) * R + NP + n0);
                 }
                 __builtin_amdgcn_sched_barrier(0);
+                const float dxr = rc.x * rc.y;
                 float acc = 0.0f;
 #pragma unroll
                 for (int s = 0; s < S; ++s) {
-                    h[s] = fmaf(exp2_hw(rc.x * A2[s]), h[s], rc.y * bc.v[s]);
+                    h[s] = fmaf(exp2_hw(rc.x * A2[s]), h[s], dxr * bc.v[s]);
                     hs[t][s] = h[s];
                     if (kGate) acc = fmaf(cc.v[s], h[s], acc);
                 }
@@ -522,6 +523,7 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
                 Vec<S> bc, cc;
                 bc.load(bt + t * R + n0);
                 cc.load(bt + t * R + NP + n0);
+                const float dxr = rc.x * rc.y;
                 float pxa = 0.0f, pda = 0.0f;
                 float cB[S], cC[S];
 #pragma unroll
@@ -529,7 +531,7 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
                     const float hp = (t > 0) ? hs[t > 0 ? t - 1 : 0][s] : hc[s];
                     g[s] = fmaf(rc.z, cc.v[s], g[s]);
                     cC[s] = rc.z * hs[t][s];
-                    cB[s] = g[s] * rc.y;
+                    cB[s] = g[s] * dxr;
                     pxa = fmaf(g[s], bc.v[s], pxa);
                     g[s] *= exp2_hw(rc.x * A2[s]);
                     const float w = g[s] * hp;
@@ -565,29 +567,27 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
                     cbuf[(bi * kBB + st) * 2 * NP + ty * NP + jp * S + sp_] = tot;
                 }
             }
-            if (j == bi) {
-                // the batch is this lane's 4 steps: Σ_n over the quad, then dx and dΔ
-                float PX[4] = {0.0f, 0.0f, 0.0f, 0.0f}, PD[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            {
+                // lane j finishes step 4 bi + j of its channel: Σ_n over the quad's partials
+                // of that step, then dx and dΔ from the step's row
+                const int tj = bi * kBB + j;
+                float PX = 0.0f, PD = 0.0f;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float* src = wx + (qb + r) * LS + PXO;
-                    const float4 a = *reinterpret_cast<const float4*>(src);
-                    const float4 c = *reinterpret_cast<const float4*>(src + 4);
-                    PX[0] += a.x; PX[1] += a.y; PX[2] += a.z; PX[3] += a.w;
-                    PD[0] += c.x; PD[1] += c.y; PD[2] += c.z; PD[3] += c.w;
+                    const float* src = wx + (qb + r) * LS + PXO + j;
+                    PX += src[0];
+                    PD += src[4];
                 }
-                float ox[4], od[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    ox[i] = fmaf(ds[i], Dd, dl[i] * PX[i]);
-                    od[i] = fmaf(xv[i], PX[i], PD[i]) * su[i];
-                    const bool ok = te + i < t1c;
-                    accD += ok ? ds[i] * xv[i] : 0.0f;
-                    accT += ok ? od[i] : 0.0f;
-                }
-                if (valid) {
-                    store4(dxo + row, te, t1c, vec, ox);
-                    store4(ddto + row, te, t1c, vec, od);
+                const float4 rw = *reinterpret_cast<const float4*>(myrow + 4 * tj);  // (δ, x, ds, σ)
+                const int64_t tg = t0c + tb + tj;
+                const bool ok = tg < t1c;
+                const float ox = fmaf(rw.z, Dd, rw.x * PX);
+                const float od = fmaf(rw.y, PX, PD) * rw.w;
+                accD += ok ? rw.z * rw.y : 0.0f;
+                accT += ok ? od : 0.0f;
+                if (valid && ok) {
+                    dxo[row + tg] = ox;
+                    ddto[row + tg] = od;
                 }
             }
             wave_sync();

@@ -156,38 +156,51 @@ __device__ __forceinline__ void wave_sync() {
 
 }  // namespace
 
-// grid = (ceil(D / (256/G)), K, B), block = 256.  Requires L % 8 == 0 and chunk % 32 == 0
-// (or K == 1) for the tiled part; the last < 32 steps of a chunk run a per-step tail.
+// LDS floats the body of a G-lane workgroup needs: a double-buffered B/C tile, then the
+// four waves' exchange areas
+template <int G, int S>
+struct GroupLds {
+    static constexpr int N = G * S;
+    static constexpr int CW = 64 / G;
+    static constexpr int R = 2 * N + 4;           // B_t | C_t row, padded by 4 floats
+    static constexpr int TILE_F = kTile * R;
+    static constexpr int WAREA = (64 * kPS > CW * kDS) ? 64 * kPS : CW * kDS;
+    static constexpr int FLOATS = 2 * TILE_F + 4 * WAREA;
+};
+
+// One workgroup's scan: channels d_lo + blk * (256 / G) + [0, 256 / G) of batch row b (those
+// below d_hi), chunk k.  lds: GroupLds<G, S>::FLOATS floats, 16-byte aligned.  Requires
+// L % 8 == 0 and chunk % 32 == 0 (or K == 1) for the tiled part; the last < 32 steps of a
+// chunk run a per-step tail.
 template <typename Tin, int G, int S, bool kGate, bool kAgg>
-__global__ __launch_bounds__(kThreads) void scang_kernel(
+__device__ __forceinline__ void scang_body(
+    float* __restrict__ lds, int64_t blk, int k, int b, int64_t d_lo, int64_t d_hi,
     const Tin* __restrict__ x, const Tin* __restrict__ dt_raw, const Tin* __restrict__ z,
     const float* __restrict__ dt_bias, const float* __restrict__ A,
     const float* __restrict__ Dskip, const Tin* __restrict__ Bm, const Tin* __restrict__ Cm,
     const float* __restrict__ h_init, float* __restrict__ y, float* __restrict__ h_last,
     float* __restrict__ h_ckpt, float* __restrict__ dsum_out, int64_t L, int64_t D,
     int64_t chunk, int K) {
+    using Lay = GroupLds<G, S>;
     constexpr int N = G * S;
     constexpr int CW = 64 / G;                    // channels per wave
     constexpr int CB = 4 * CW;                    // channels per block
     constexpr int kH = kHalf / G;                 // steps per lane per half
     // LDS tile row per step: B_t (N floats) then C_t (N floats), padded by 4 floats so
     // the transposing writes of a wave fall on at most two lanes per bank
-    constexpr int R = 2 * N + 4;
-    constexpr int TILE_F = kTile * R;
+    constexpr int R = Lay::R;
+    constexpr int TILE_F = Lay::TILE_F;
     // per-wave exchange area: the (δ, δ·x) rows during a sweep, the partial readouts after
-    constexpr int WAREA = (64 * kPS > CW * kDS) ? 64 * kPS : CW * kDS;
-    __shared__ __align__(16) float bc_lds[2][TILE_F];
-    __shared__ __align__(16) float w_lds[4 * WAREA];
+    constexpr int WAREA = Lay::WAREA;
+    float* const w_lds = lds + 2 * TILE_F;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int l = lane & (G - 1);                 // lane within the group: states, steps
     const int c = lane / G;                       // channel within the wave
-    const int64_t d_raw = int64_t(blockIdx.x) * CB + tid / G;
-    const bool valid = d_raw < D;
-    const int64_t d = valid ? d_raw : D - 1;      // clamped for loads
-    const int k = blockIdx.y;
-    const int b = blockIdx.z;
+    const int64_t d_raw = d_lo + blk * CB + tid / G;
+    const bool valid = d_raw < d_hi;
+    const int64_t d = valid ? d_raw : d_hi - 1;   // clamped for loads
     const int64_t t_begin = int64_t(k) * chunk;
     const int64_t t_end = (t_begin + chunk < L) ? t_begin + chunk : L;
     const int64_t n_tiles = (t_end - t_begin) / kTile;
@@ -250,7 +263,7 @@ __global__ __launch_bounds__(kThreads) void scang_kernel(
 
     for (int64_t it = 0; it < n_tiles; ++it) {
         const int64_t t0 = t_begin + it * kTile;
-        float* buf = bc_lds[it & 1];
+        float* buf = lds + (it & 1) * TILE_F;
 #pragma unroll
         for (int p = 0; p < BC_PASSES; ++p) {
             const int e = tid + p * kThreads;
@@ -386,6 +399,69 @@ __global__ __launch_bounds__(kThreads) void scang_kernel(
     }
 }
 
+// grid = (ceil(D / (256/G)), K, B), block = 256.
+template <typename Tin, int G, int S, bool kGate, bool kAgg>
+__global__ __launch_bounds__(kThreads) void scang_kernel(
+    const Tin* __restrict__ x, const Tin* __restrict__ dt_raw, const Tin* __restrict__ z,
+    const float* __restrict__ dt_bias, const float* __restrict__ A,
+    const float* __restrict__ Dskip, const Tin* __restrict__ Bm, const Tin* __restrict__ Cm,
+    const float* __restrict__ h_init, float* __restrict__ y, float* __restrict__ h_last,
+    float* __restrict__ h_ckpt, float* __restrict__ dsum_out, int64_t L, int64_t D,
+    int64_t chunk, int K) {
+    __shared__ __align__(16) float lds[GroupLds<G, S>::FLOATS];
+    scang_body<Tin, G, S, kGate, kAgg>(lds, blockIdx.x, blockIdx.y, blockIdx.z, 0, D, x, dt_raw, z,
+                                       dt_bias, A, Dskip, Bm, Cm, h_init, y, h_last, h_ckpt,
+                                       dsum_out, L, D, chunk, K);
+}
+
+// Single pass over every channel with two layouts in one launch: per batch row, channels
+// [0, d4) on four lanes (64 per workgroup) and [d4, D) on eight lanes (32 per workgroup).
+// The workgroups are numbered four-lane first, so a round-robin dispatch hands each CU its
+// four-lane workgroups and then its eight-lane one: whole rounds of four-lane waves per
+// SIMD, the remainder as eight-lane waves that take about half a four-lane wave's time.
+// grid = B * (nb4 + nb8), block = 256.
+template <typename Tin, int N, bool kGate>
+__global__ __launch_bounds__(kThreads) void scang_mixed_kernel(
+    const Tin* __restrict__ x, const Tin* __restrict__ dt_raw, const Tin* __restrict__ z,
+    const float* __restrict__ dt_bias, const float* __restrict__ A,
+    const float* __restrict__ Dskip, const Tin* __restrict__ Bm, const Tin* __restrict__ Cm,
+    const float* __restrict__ h_init, float* __restrict__ y, float* __restrict__ h_last,
+    float* __restrict__ h_ckpt, int64_t L, int64_t D, int64_t d4, int nb4, int nb8, int B) {
+    constexpr int F4 = GroupLds<4, N / 4>::FLOATS, F8 = GroupLds<8, N / 8>::FLOATS;
+    __shared__ __align__(16) float lds[F4 > F8 ? F4 : F8];
+    const int64_t f = blockIdx.x;
+    const int64_t n4 = int64_t(B) * nb4;
+    if (f < n4) {
+        scang_body<Tin, 4, N / 4, kGate, false>(lds, f % nb4, 0, int(f / nb4), 0, d4, x, dt_raw, z,
+                                                dt_bias, A, Dskip, Bm, Cm, h_init, y, h_last, h_ckpt,
+                                                nullptr, L, D, L, 1);
+    } else {
+        const int64_t g = f - n4;
+        scang_body<Tin, 8, N / 8, kGate, false>(lds, g % nb8, 0, int(g / nb8), d4, D, x, dt_raw, z,
+                                                dt_bias, A, Dskip, Bm, Cm, h_init, y, h_last, h_ckpt,
+                                                nullptr, L, D, L, 1);
+    }
+}
+
+template <typename Tin, int N>
+static hipError_t launch_scang_mixed_t(const ScanLaunch& p, hipStream_t s) {
+    const int nb8 = int((p.D - p.d4 + 31) / 32);
+    dim3 grid(unsigned(p.B * (p.nb4 + nb8)));
+    const Tin* x = static_cast<const Tin*>(p.x);
+    const Tin* dr = static_cast<const Tin*>(p.dt_raw);
+    const Tin* z = static_cast<const Tin*>(p.z);
+    const Tin* Bm = static_cast<const Tin*>(p.Bm);
+    const Tin* Cm = static_cast<const Tin*>(p.Cm);
+#define SS_ARGS x, dr, z, p.dt_bias, p.A, p.Dskip, Bm, Cm, p.h_init, p.y, p.h_last, p.h_ckpt, p.L, \
+                p.D, p.d4, p.nb4, nb8, int(p.B)
+    if (p.z)
+        hipLaunchKernelGGL((scang_mixed_kernel<Tin, N, true>), grid, dim3(kThreads), 0, s, SS_ARGS);
+    else
+        hipLaunchKernelGGL((scang_mixed_kernel<Tin, N, false>), grid, dim3(kThreads), 0, s, SS_ARGS);
+#undef SS_ARGS
+    return hipGetLastError();
+}
+
 template <typename Tin, int G, int S>
 static hipError_t launch_scang_t(const ScanLaunch& p, hipStream_t s) {
     constexpr int CB = 4 * 64 / G;
@@ -431,6 +507,20 @@ static hipError_t launch_scang_dt(int N, int G, const ScanLaunch& p, hipStream_t
 
 hipError_t launch_scang(int bf16, int N, int G, const ScanLaunch& p, hipStream_t s) {
     return bf16 ? launch_scang_dt<bf16_t>(N, G, p, s) : launch_scang_dt<float>(N, G, p, s);
+}
+
+template <typename Tin>
+static hipError_t launch_scang_mixed_dt(int N, const ScanLaunch& p, hipStream_t s) {
+    switch (N) {
+        case 8: return launch_scang_mixed_t<Tin, 8>(p, s);
+        case 16: return launch_scang_mixed_t<Tin, 16>(p, s);
+        case 32: return launch_scang_mixed_t<Tin, 32>(p, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_scang_mixed(int bf16, int N, const ScanLaunch& p, hipStream_t s) {
+    return bf16 ? launch_scang_mixed_dt<bf16_t>(N, p, s) : launch_scang_mixed_dt<float>(N, p, s);
 }
 
 }  // namespace ss

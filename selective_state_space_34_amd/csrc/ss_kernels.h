@@ -29,6 +29,8 @@ struct ScanLaunch {
     int K;
     int vec;                // 1: L % 8 == 0, 8-step vector loads
     int agg;                // 1: AGG mode
+    int64_t d4;             // mixed layout: channels [0, d4) on four lanes, [d4, D) on eight
+    int nb4;                //               four-lane workgroups per batch row (d4 / 64)
 };
 
 // Affine-pair carry across chunks (one workgroup per channel).  Chunk c's pair is
@@ -92,6 +94,8 @@ hipError_t launch_bc_stage(int bf16, int N, const void* Bm, const void* Cm, floa
 hipError_t launch_scan(int bf16, int N, const ScanLaunch& p, hipStream_t s);
 // group-split layout: G = 4 (N in {4, 8, 16, 32}) or G = 8 (N in {8, 16, 32}); L % 8 == 0
 hipError_t launch_scang(int bf16, int N, int G, const ScanLaunch& p, hipStream_t s);
+// single pass, N in {8, 16, 32}: four lanes for channels [0, d4), eight for [d4, D)
+hipError_t launch_scang_mixed(int bf16, int N, const ScanLaunch& p, hipStream_t s);
 hipError_t launch_carry(int N, const CarryLaunch& p, hipStream_t s);
 hipError_t launch_bwd(int bf16, const BwdLaunch& p, hipStream_t s);
 hipError_t launch_bwd_reduce(const BwdLaunch& p, hipStream_t s);

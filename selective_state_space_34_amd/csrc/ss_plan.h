@@ -18,6 +18,9 @@ struct Plan {
     int64_t K;       // number of chunks
     int vec;         // L % 8 == 0: 8-step vector loads
     int group;       // forward: lanes per channel of the group kernel (4 or 8), 0 = one lane
+    int mixed;       // forward, single pass: four lanes for channels [0, d4), eight for the rest
+    int64_t d4;
+    int nb4;         // four-lane workgroups per batch row (d4 / 64)
     // workspace carving (byte offsets, 256-aligned)
     size_t off_bc, off_hend, off_dsum, off_hstart, off_gend, off_gstart, off_red;
     size_t red_bytes;
@@ -36,6 +39,8 @@ constexpr int64_t kTargetWaves = 4096;
 // Single pass when one pass already yields two waves per SIMD (a chunked pass costs a
 // second sweep for the chunk aggregates).
 constexpr int64_t kSingleWaves = 2048;
+// SIMDs of the part (256 CUs x 4): one round of waves
+constexpr int64_t kSimds = 1024;
 
 // Number of workgroups the reduction of the backward's per-block partials uses
 // (see ss_bwd.hip); the partial buffers are sized from it.
@@ -100,6 +105,19 @@ inline int make_plan(const ss_dims& d, bool backward, Plan* out) {
     }
     p.chunked = chunked;
     p.chunk = chunk;
+    // Mixed layout for a single pass whose four-lane waves leave a last round at most half
+    // full: the whole rounds stay on four lanes, the remainder goes to eight lanes (twice the
+    // waves, each about half as long), so every SIMD ends up with about the same work.  Used
+    // when the whole rounds split evenly over batch rows into 64-channel workgroups.
+    p.mixed = 0; p.d4 = 0; p.nb4 = 0;
+    if (!backward && !chunked && d.layout == SS_LAYOUT_AUTO && p.group == 4 && N >= 8) {
+        const int64_t U = p.B * ((p.D + 15) / 16);       // four-lane waves
+        const int64_t full = U / kSimds, rem = U % kSimds;
+        if (full >= 1 && rem > 0 && 2 * rem <= kSimds && (full * kSimds) % (4 * p.B) == 0) {
+            const int64_t nb4 = full * kSimds / (4 * p.B);
+            if (nb4 * 64 < p.D) { p.mixed = 1; p.nb4 = int(nb4); p.d4 = nb4 * 64; }
+        }
+    }
     p.K = (p.L + chunk - 1) / chunk;
     if (p.K > kMaxGridYZ) return SS_ERR_DIMS;
 

@@ -93,6 +93,10 @@ EDGE = [
     (1, 2056, 33, 32, "bf16", True, True, 2, 264),
     # B*D*N >= 16384 with few chunks: the sequential per-(channel, state) carry
     (1, 520, 1024, 16, "bf16", True, True, 2, 64),
+    # single pass with a half-full last round of four-lane waves: the mixed four/eight-lane
+    # launch (channels past 16384, resp. 8192 per row, on eight lanes)
+    (1, 64, 24576, 16, "bf16", True, True, 0, 0),
+    (2, 96, 10240, 8, "f32", False, True, 1, 0),
 ]
 
 
@@ -205,6 +209,7 @@ CKPT_CASES = [
     (2, 256, 24, 8, "f32", False, True, 2, 64, 3),      # eight lanes per channel
     (1, 333, 20, 16, "bf16", True, True, 2, 40, 2),     # one lane per channel, chunk 40
     (3, 64, 9, 2, "f32", True, False, 0, 0, 0),         # N = 2: one-lane kernel
+    (1, 64, 24576, 16, "bf16", True, True, 0, 0, 0),    # mixed four/eight-lane launch
 ]
 
 
