@@ -585,12 +585,24 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
                 const float od = fmaf(rw.y, PX, PD) * rw.w;
                 accD += ok ? rw.z * rw.y : 0.0f;
                 accT += ok ? od : 0.0f;
-                if (valid && ok) {
-                    dxo[row + tg] = ox;
-                    ddto[row + tg] = od;
-                }
+                // park (dx, dΔraw) in the step's row, which no later batch reads: the tile's
+                // outputs leave in 16-byte runs per lane once the sweep is done
+                *reinterpret_cast<float2*>(myrow + 4 * tj) = make_float2(ox, od);
             }
             wave_sync();
+        }
+
+        // dx, dΔraw of the lane's own 4 steps, from the rows
+        if (valid) {
+            float ox[4], od[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float2 v = *reinterpret_cast<const float2*>(myrow + 4 * (kBPer * j + i));
+                ox[i] = v.x;
+                od[i] = v.y;
+            }
+            store4(dxo + row, te, t1c, vec, ox);
+            store4(ddto + row, te, t1c, vec, od);
         }
 
         // dB|dC of the tile: the four waves' sums meet once per tile
