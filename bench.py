@@ -129,7 +129,9 @@ def cpu_baseline(w, inp, budget_s=4.0):
     while True:
         chans = np.sort(rng.choice(C, n, replace=False))
         t0 = time.perf_counter()
-        cref.fwd(*args, z=inp.z if w.gate else None, chans=chans, want_h_final=False)
+        # the decode step starts from the carried state and produces the next one
+        cref.fwd(*args, z=inp.z if w.gate else None, h0=inp.h0 if w.decode else None,
+                 chans=chans, want_h_final=w.decode)
         dt = time.perf_counter() - t0
         if dt >= budget_s / 4 or n == C:
             break
@@ -138,6 +140,83 @@ def cpu_baseline(w, inp, budget_s=4.0):
     return {"value": elems / dt, "unit": "elem/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{n} of {C} channels x full L={w.seqlen} (B*L*D elements {elems}), "
                       f"{dt:.2f} s wall on {threads} OpenMP threads"}
+
+
+def step_min_bytes(w, s_in):
+    """Algorithmic HBM bytes of one decode step: read x, dt_raw (, z) [B, D], B, C [B, N] and the
+    parameters, read and write the state [B, D, N], write y [B, D]."""
+    BD = w.batch * w.dim
+    n_in = 3 if w.gate else 2
+    return (n_in * BD * s_in + 2 * w.batch * w.dstate * s_in + w.dim * (w.dstate + 2) * 4
+            + 2 * BD * w.dstate * 4 + BD * 4)
+
+
+def run_decode(args, w, inp):
+    """Decode workload: K timed ss_step calls, each carrying every (batch row, channel) one
+    token further with the state updated in place.  Roofline: HBM (state in and out)."""
+    import torch
+    import selective_state_space_34_amd as ss
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    dev = torch.device("cuda:0")
+    col = lambda a: torch.from_numpy(np.ascontiguousarray(a[..., 0])).to(dt).to(dev)
+    t32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
+    x, dtr, Bm, Cm = col(inp.x), col(inp.dt_raw), col(inp.Bm), col(inp.Cm)
+    z = col(inp.z) if w.gate else None
+    dtb, A, Dk = t32(inp.dt_bias), t32(inp.A), t32(inp.Dskip)
+    h = t32(inp.h0)
+    y = torch.empty((w.batch, w.dim), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        ss.ss_step(x, dtr, dtb, A, Bm, Cm, Dk, h, z=z, y=y, stream=stream)
+
+    # the state (B*D*N*4 bytes) fits in the 256 MB Infinity Cache: an untimed 1 GiB write
+    # between steps evicts it, so each timed step reads and writes HBM
+    flush = torch.empty(args.flush_mib << 20, dtype=torch.uint8, device=dev) if args.flush_mib else None
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for e0, e1 in evs:
+        if flush is not None:
+            flush.fill_(1)
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    per = np.array([e0.elapsed_time(e1) for e0, e1 in evs]) * 1e-3
+    t_avg = float(per.mean())
+    s_in = 2 if w.dtype == "bf16" else 4
+    mb = step_min_bytes(w, s_in)
+    gbps = mb / t_avg / 1e9
+    elems = w.batch * w.dim
+    log(f"[bench] decode step event avg {t_avg * 1e6:.2f} us (min {per.min() * 1e6:.2f}); "
+        f"{mb / 1e6:.1f} MB min bytes -> {gbps:.0f} GB/s ({gbps / HBM_PEAK_GBPS:.3f} of 8 TB/s)")
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, inp)
+        log(f"[bench] cpu baseline {cpu['value']:.3e} elem/s ({cpu['sample']})")
+    out = {
+        "metric": "selective-scan decode step B·D channel-steps/s; achieved HBM GB/s vs MI355X peak",
+        # with flushes between steps the wall clock includes them: value and ms_per_step
+        # come from the HIP events around each step
+        "value": elems / t_avg, "unit": "elem/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": t_avg * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{w.name}: {w.label}", "batch": w.batch, "seqlen": 1,
+                   "dim": w.dim, "dstate": w.dstate, "in_dtype": w.dtype, "gate": w.gate,
+                   "cache_flush_mib": args.flush_mib},
+        "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": gbps / HBM_PEAK_GBPS, "traffic": None,
+                     "kernel": "ss_step (step_kernel, one launch per call)",
+                     "launch_us": t_avg * 1e6, "traffic_algorithmic_bytes": mb},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
 
 
 def dims_plan_single(ss, dims):
@@ -150,12 +229,15 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="c2", help="c0..c4 (default c2, D=5120 forward)")
+    ap.add_argument("--workload", default="c2",
+                    help="c0..c4 (default c2, D=5120 forward); d1 = decode step")
     ap.add_argument("--plan", type=int, default=0)
     ap.add_argument("--layout", type=int, default=0, help="0 auto, 1 four lanes, 2 one lane, 3 eight lanes per channel")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ckpt", action="store_true",
                     help="fwd+bwd: recompute chunk start states instead of using checkpoints")
+    ap.add_argument("--flush-mib", type=int, default=1024,
+                    help="decode: untimed write of this many MiB before each timed step (0 = none)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also launch one device copy of this many MiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -175,6 +257,9 @@ def main():
     t0 = time.perf_counter()
     inp = workload_inputs(w)
     log(f"[bench] inputs generated in {time.perf_counter() - t0:.1f}s")
+    if w.decode:
+        run_decode(args, w, inp)
+        return
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     dev = torch.device("cuda:0")
     t_in = lambda a: torch.from_numpy(a).to(dt).to(dev)

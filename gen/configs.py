@@ -1,8 +1,9 @@
-"""The five synthetic workloads of the selective scan (S6), by shape and input recipe.
+"""The synthetic workloads of the selective scan (S6), by shape and input recipe.
 
-Each workload is named by what it is.  The shapes and distributions restate the
-benchmark configurations this library is measured on; nothing here computes any
-part of the scan.
+Each workload is named by what it is.  c0..c4 restate the benchmark configurations this
+library is measured on; d1 is a decode step (one token per sequence, the state carried in
+and out) at the D=5120 width with a serving-size batch.  Nothing here computes any part of
+the scan.
 """
 from dataclasses import dataclass
 
@@ -20,6 +21,7 @@ class Workload:
     a_perturb: bool    # A[d,n] = -(n+1)*exp(eps), eps ~ N(0, 0.1^2)
     backward: bool     # workload also exercises the backward pass
     h_final: bool      # final state is an output of the workload
+    decode: bool = False  # one token per (batch row, channel) through ss_step, state in place
 
     @property
     def elems(self) -> int:
@@ -42,6 +44,8 @@ WORKLOADS = (
              1, 1048576, 256, 16, "bf16", False, False, False, True),
     Workload("c4", "S6 fwd+bwd+gate bf16-in B=4 L=4096 D=2048 N=16",
              4, 4096, 2048, 16, "bf16", True, False, True, False),
+    Workload("d1", "S6 decode step (one token, state in place) bf16-in B=256 D=5120 N=16 gate",
+             256, 1, 5120, 16, "bf16", True, True, False, True, decode=True),
 )
 
 BY_NAME = {w.name: w for w in WORKLOADS}

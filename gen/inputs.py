@@ -132,6 +132,6 @@ def make_inputs(batch: int, seqlen: int, dim: int, dstate: int, *, dtype: str = 
 def workload_inputs(w: Workload, **overrides) -> S6Inputs:
     """Inputs of a named workload, seeded with its index."""
     kw = dict(dtype=w.dtype, seed=seed_of(w), gate=w.gate, a_perturb=w.a_perturb,
-              with_dy=w.backward)
+              with_dy=w.backward, with_h0=w.decode)
     kw.update(overrides)
     return make_inputs(w.batch, w.seqlen, w.dim, w.dstate, **kw)

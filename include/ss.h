@@ -53,7 +53,7 @@ extern "C" {
 #endif
 
 #define SS_VERSION_MAJOR 0
-#define SS_VERSION_MINOR 2
+#define SS_VERSION_MINOR 3
 
 /* dtype of x, dt_raw, z, Bm, Cm */
 typedef enum { SS_F32 = 0, SS_BF16 = 1 } ss_dtype;
@@ -139,6 +139,23 @@ int ss_bwd(const ss_dims* dims,
            float* dx, float* ddt_raw, float* ddt_bias, float* dA, float* dB, float* dC,
            float* dD, float* dz, float* dh0,
            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Single-token (decode) step: the recurrence carried one token further for every (batch
+ * row, channel), as in recurrent inference (note "상태공간 모델(SSM)과 Mamba 아키텍처", §2):
+ *   δ = softplus(dt_bias + dt_raw);  h ← exp(δ·A)⊙h + δ·B·x;  y = (C·h + Dskip·x)·silu(z)
+ *   dims   : batch, dim, dstate, in_dtype as for ss_fwd; seqlen must be 1; plan, chunk and
+ *            layout must be 0.
+ *   x, dt_raw, z : [B, D] (in_dtype; z NULL = no gate); Bm, Cm : [B, N] (in_dtype);
+ *   A [D, N], dt_bias [D], Dskip [D] : float32.
+ *   h_in   : [B, D, N] float32, the state before the token (required).
+ *   h_out  : [B, D, N] float32, the state after it; may equal h_in (the state is updated in
+ *            place), otherwise it must not overlap h_in.
+ *   y      : [B, D] float32.
+ * Needs no workspace.  Same conventions and return codes as ss_fwd. */
+int ss_step(const ss_dims* dims,
+            const void* x, const void* dt_raw, const float* dt_bias, const float* A,
+            const void* Bm, const void* Cm, const float* Dskip, const void* z,
+            const float* h_in, float* h_out, float* y, hipStream_t stream);
 
 /* Static description of a return code. */
 const char* ss_strerror(int code);

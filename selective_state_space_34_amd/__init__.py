@@ -9,6 +9,7 @@ PyTorch fallback: if the compiled library is missing, ``load()`` raises.
     y, h_final, h_ckpt = ss_fwd(..., return_final=True, return_ckpt=True)
     grads = ss_bwd(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, dy, z=None, h0=None, dh_final=None,
                    h_ckpt=None)
+    y_t = ss_step(x_t, dt_raw_t, dt_bias, A, B_t, C_t, Dskip, h, z_t=None)   # h updated in place
 
 Layouts: x, dt_raw, z, y [B, D, L]; Bm, Cm [B, N, L]; A [D, N]; dt_bias, Dskip [D];
 h0, h_final [B, D, N]; h_ckpt [B, D, ceil(L/16), N] (state entering every 16th step).  x, dt_raw, z, Bm, Cm are float32 or bfloat16 (all the same);
@@ -26,8 +27,8 @@ SS_LAYOUT_AUTO, SS_LAYOUT_QUAD, SS_LAYOUT_LANE, SS_LAYOUT_OCT = 0, 1, 2, 3
 ERRORS = {0: "SS_OK", -1: "SS_ERR_NULL", -2: "SS_ERR_DIMS", -3: "SS_ERR_DTYPE", -4: "SS_ERR_ALIGN",
           -5: "SS_ERR_WORKSPACE", -6: "SS_ERR_HIP", -7: "SS_ERR_UNSUPPORTED"}
 
-EXPORTS = ("ss_fwd", "ss_bwd", "ss_fwd_workspace_size", "ss_bwd_workspace_size", "ss_strerror",
-           "ss_last_hip_error", "ss_version")
+EXPORTS = ("ss_fwd", "ss_bwd", "ss_step", "ss_fwd_workspace_size", "ss_bwd_workspace_size",
+           "ss_strerror", "ss_last_hip_error", "ss_version")
 
 
 class ss_dims(ctypes.Structure):
@@ -64,6 +65,8 @@ def load(path: str = LIB):
     lib.ss_fwd.restype = ctypes.c_int
     lib.ss_bwd.argtypes = [D] + [P] * 9 + [P, P, P] + [P] * 9 + [P, ctypes.c_size_t, P]
     lib.ss_bwd.restype = ctypes.c_int
+    lib.ss_step.argtypes = [D] + [P] * 12
+    lib.ss_step.restype = ctypes.c_int
     for f in ("ss_fwd_workspace_size", "ss_bwd_workspace_size"):
         getattr(lib, f).argtypes = [D, ctypes.POINTER(ctypes.c_size_t)]
         getattr(lib, f).restype = ctypes.c_int
@@ -226,3 +229,44 @@ def ss_bwd(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, dy, z=None, h0=None, dh_final=N
     if rc != 0:
         raise SSError(rc, lib)
     return g
+
+
+def ss_step(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, h, z=None, *, h_out=None, y=None, stream=None):
+    """One decode step through the C ABI: x, dt_raw, z [B, D]; Bm, Cm [B, N]; h [B, D, N]
+    float32, the state before the token.  The state after it goes to h_out (default: h
+    itself, updated in place).  Returns y [B, D] float32."""
+    import torch
+    lib = load()
+    if x.dim() != 2:
+        raise ValueError(f"x must be [B, D], got shape {tuple(x.shape)}")
+    Bn, D = x.shape
+    N = A.shape[1]
+    dev = x.device
+    f32 = torch.float32
+    if x.dtype == torch.float32:
+        dt = SS_F32
+    elif x.dtype == torch.bfloat16:
+        dt = SS_BF16
+    else:
+        raise ValueError(f"x dtype must be float32 or bfloat16, got {x.dtype}")
+    _check(x, "x", (Bn, D), x.dtype, dev)
+    _check(dt_raw, "dt_raw", (Bn, D), x.dtype, dev)
+    _check(z, "z", (Bn, D), x.dtype, dev)
+    _check(Bm, "Bm", (Bn, N), x.dtype, dev)
+    _check(Cm, "Cm", (Bn, N), x.dtype, dev)
+    _check(A, "A", (D, N), f32, dev)
+    _check(dt_bias, "dt_bias", (D,), f32, dev)
+    _check(Dskip, "Dskip", (D,), f32, dev)
+    _check(h, "h", (Bn, D, N), f32, dev)
+    if h_out is None:
+        h_out = h
+    _check(h_out, "h_out", (Bn, D, N), f32, dev)
+    if y is None:
+        y = torch.empty((Bn, D), dtype=f32, device=dev)
+    _check(y, "y", (Bn, D), f32, dev)
+    dims = make_dims(Bn, 1, D, N, dt)
+    rc = lib.ss_step(ctypes.byref(dims), _ptr(x), _ptr(dt_raw), _ptr(dt_bias), _ptr(A), _ptr(Bm),
+                     _ptr(Cm), _ptr(Dskip), _ptr(z), _ptr(h), _ptr(h_out), _ptr(y), _stream(stream))
+    if rc != 0:
+        raise SSError(rc, lib)
+    return y

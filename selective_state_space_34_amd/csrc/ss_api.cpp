@@ -130,6 +130,29 @@ int ss_fwd(const ss_dims* dims, const void* x, const void* dt_raw, const float* 
     return SS_OK;
 }
 
+int ss_step(const ss_dims* dims, const void* x, const void* dt_raw, const float* dt_bias,
+            const float* A, const void* Bm, const void* Cm, const float* Dskip, const void* z,
+            const float* h_in, float* h_out, float* y, hipStream_t stream) {
+    if (!dims) return SS_ERR_NULL;
+    if (dims->plan != SS_PLAN_AUTO || dims->layout != SS_LAYOUT_AUTO) return SS_ERR_DTYPE;
+    if (dims->seqlen != 1 || dims->chunk != 0) return SS_ERR_DIMS;
+    ss::Plan p;
+    const int rc = ss::make_plan(*dims, false, &p);
+    if (rc != SS_OK) return rc;
+    if (!x || !dt_raw || !dt_bias || !A || !Bm || !Cm || !Dskip || !h_in || !h_out || !y)
+        return SS_ERR_NULL;
+    const void* ptrs[] = {x, dt_raw, dt_bias, A, Bm, Cm, Dskip, h_in, h_out, y};
+    for (const void* q : ptrs)
+        if (!aligned16(q)) return SS_ERR_ALIGN;
+    if (z && !aligned16(z)) return SS_ERR_ALIGN;
+    ss::StepLaunch s{};
+    s.x = x; s.dt_raw = dt_raw; s.z = z; s.dt_bias = dt_bias; s.A = A; s.Bm = Bm; s.Cm = Cm;
+    s.Dskip = Dskip; s.h_in = h_in; s.h_out = h_out; s.y = y; s.B = p.B; s.D = p.D; s.N = int(p.N);
+    const hipError_t e = ss::launch_step(p.in_dtype == SS_BF16, s, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    return SS_OK;
+}
+
 int ss_bwd(const ss_dims* dims, const void* x, const void* dt_raw, const float* dt_bias,
            const float* A, const void* Bm, const void* Cm, const float* Dskip, const void* z,
            const float* h0, const float* dy, const float* dh_final, const float* h_ckpt, float* dx,

@@ -89,6 +89,23 @@ struct BwdLaunch {
     int stage;
 };
 
+// Single-token step: x, dt_raw, z [B, D]; Bm, Cm [B, N]; h_in, h_out [B, D, N] (may be equal).
+struct StepLaunch {
+    const void* x;
+    const void* dt_raw;
+    const void* z;          // nullable
+    const float* dt_bias;
+    const float* A;
+    const void* Bm;
+    const void* Cm;
+    const float* Dskip;
+    const float* h_in;
+    float* h_out;
+    float* y;
+    int64_t B, D;
+    int N;
+};
+
 hipError_t launch_bc_stage(int bf16, int N, const void* Bm, const void* Cm, float* BC, int64_t B,
                            int64_t L, hipStream_t s);
 hipError_t launch_scan(int bf16, int N, const ScanLaunch& p, hipStream_t s);
@@ -97,6 +114,7 @@ hipError_t launch_scang(int bf16, int N, int G, const ScanLaunch& p, hipStream_t
 // single pass, N in {8, 16, 32}: four lanes for channels [0, d4), eight for [d4, D)
 hipError_t launch_scang_mixed(int bf16, int N, const ScanLaunch& p, hipStream_t s);
 hipError_t launch_carry(int N, const CarryLaunch& p, hipStream_t s);
+hipError_t launch_step(int bf16, const StepLaunch& p, hipStream_t s);
 hipError_t launch_bwd(int bf16, const BwdLaunch& p, hipStream_t s);
 hipError_t launch_bwd_reduce(const BwdLaunch& p, hipStream_t s);
 

@@ -37,7 +37,7 @@ def test_exports_match_header(lib):
 
 
 def test_version_and_strerror(lib):
-    assert lib.ss_version() == (0 << 16) | 2
+    assert lib.ss_version() == (0 << 16) | 3
     for code in ss.ERRORS:
         assert len(lib.ss_strerror(code)) > 0
     assert b"unknown" in lib.ss_strerror(12345)
@@ -155,3 +155,27 @@ def test_bwd_validation(lib):
     a[11] = ctypes.c_void_p(FAKE + 4)
     assert call(good, a) == -4
     assert call(good, args) == -5
+
+
+def test_step_validation(lib):
+    F = ctypes.c_void_p(FAKE)
+    # x dt_raw dt_bias A Bm Cm Dskip | z | h_in h_out y
+    args = [F] * 7 + [None] + [F] * 3
+
+    def call(dims, a):
+        return lib.ss_step(None if dims is None else ctypes.byref(dims), *a, None)
+    assert call(None, args) == -1
+    assert call(ss.make_dims(4, 2, 32, 16), args) == -2          # seqlen must be 1
+    assert call(ss.make_dims(4, 1, 32, 7), args) == -2           # unsupported dstate
+    assert call(ss.make_dims(4, 1, 32, 16, plan=1), args) == -3  # plan must be automatic
+    assert call(ss.make_dims(4, 1, 32, 16, layout=1), args) == -3
+    assert call(ss.make_dims(4, 1, 32, 16, in_dtype=9), args) == -3
+    good = ss.make_dims(4, 1, 32, 16)
+    for i in (0, 1, 2, 3, 4, 5, 6, 8, 9, 10):
+        a = list(args)
+        a[i] = None
+        assert call(good, a) == -1, i
+    for i in range(11):
+        a = list(args)
+        a[i] = ctypes.c_void_p(FAKE + 4)
+        assert call(good, a) == -4, i

@@ -46,7 +46,9 @@ def test_recipe():
 
 def test_workloads_table():
     names = [w.name for w in WORKLOADS]
-    assert names == ["c0", "c1", "c2", "c3", "c4"]
+    assert names == ["c0", "c1", "c2", "c3", "c4", "d1"]
     c2 = WORKLOADS[2]
     assert (c2.batch, c2.seqlen, c2.dim, c2.dstate, c2.dtype, c2.gate) == (8, 2048, 5120, 16, "bf16", True)
     assert WORKLOADS[3].seqlen == 1048576 and WORKLOADS[4].backward
+    d1 = WORKLOADS[5]
+    assert d1.decode and d1.seqlen == 1 and (d1.batch, d1.dim, d1.dstate) == (256, 5120, 16)
