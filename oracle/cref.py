@@ -36,7 +36,7 @@ def load():
         I = ctypes.c_int64
         lib.s6o_threads.argtypes = [ctypes.c_int]
         lib.s6o_threads.restype = ctypes.c_int
-        lib.s6o_fwd.argtypes = [I, I, I, I] + [P] * 9 + [P, I, P, P]
+        lib.s6o_fwd.argtypes = [I, I, I, I] + [P] * 9 + [P, I, P, P, ctypes.c_int]
         lib.s6o_fwd.restype = ctypes.c_int
         lib.s6o_bwd.argtypes = [I, I, I, I] + [P] * 11 + [P] * 9
         lib.s6o_bwd.restype = ctypes.c_int
@@ -57,10 +57,12 @@ def threads(n: int = 0) -> int:
     return load().s6o_threads(int(n))
 
 
-def fwd(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, z=None, h0=None, chans=None, want_h_final=True):
+def fwd(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, z=None, h0=None, chans=None, want_h_final=True,
+        zoh=False):
     """Forward for all channels (chans None) or for channels chans[i] = b*D + d.
 
     Returns (y, h_final): y [B,D,L] (all) or [len(chans), L]; h_final likewise with N.
+    zoh: exact zero-order-hold B̄ instead of the first-order δ·B.
     """
     lib = load()
     x, dt_raw, dt_bias, A, Bm, Cm, Dskip, z, h0 = map(
@@ -78,7 +80,7 @@ def fwd(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, z=None, h0=None, chans=None, want_
         y = np.empty((nchan, L))
         hf = np.empty((nchan, N)) if want_h_final else None
     rc = lib.s6o_fwd(Bn, L, D, N, _p(x), _p(dt_raw), _p(dt_bias), _p(A), _p(Bm), _p(Cm),
-                     _p(Dskip), _p(z), _p(h0), _p(c_arr), nchan, _p(y), _p(hf))
+                     _p(Dskip), _p(z), _p(h0), _p(c_arr), nchan, _p(y), _p(hf), int(bool(zoh)))
     if rc != 0:
         raise RuntimeError(f"s6o_fwd failed: {rc}")
     return y, hf

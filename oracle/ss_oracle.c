@@ -8,6 +8,7 @@
  *   u_t = dt_bias[d] + dt_raw[b,d,t];  δ_t = softplus(u_t)      ("3.2 선택적 스캔 알고리즘…" page, §1.2)
  *   Ā_{t,n} = exp(δ_t A[d,n])                                  (same page, §2.1; A diagonal)
  *   h_t = Ā_t ⊙ h_{t-1} + δ_t B_t x_t                          (same page, §2.2; first-order B̄ as in §4.1)
+ *     or, with zoh, + (exp(δ_t A) - 1)/A · B_t x_t               (the exact zero-order hold of §2.1)
  *   y_t = (Σ_n C_{t,n} h_{t,n} + D[d] x_t) · silu(z_t)         (readout §1.1; gate: "상태공간 모델(SSM)과
  *                                                               Mamba 아키텍처" note, §3 flowchart)
  * One channel (b,d) at a time, t in order, every operation in double.  OpenMP
@@ -46,12 +47,13 @@ int s6o_threads(int nthreads) {
 /*
  * Forward over a list of channels.  chans[i] = b*D + d (NULL: all B*D channels
  * in order, nchan must then be B*D).  y is [nchan, L]; h_final (nullable) is
- * [nchan, N].  z and h0 are nullable.  Returns 0, or -1 on bad sizes.
+ * [nchan, N].  z and h0 are nullable.  zoh = 1: exact zero-order-hold B̄ (expm1(δA)/A;
+ * δ where A = 0).  Returns 0, or -1 on bad sizes.
  */
 int s6o_fwd(int64_t B, int64_t L, int64_t D, int64_t N,
             const float* x, const float* dt_raw, const float* dt_bias, const float* A,
             const float* Bm, const float* Cm, const float* Dskip, const float* z, const float* h0,
-            const int64_t* chans, int64_t nchan, double* y, double* h_final) {
+            const int64_t* chans, int64_t nchan, double* y, double* h_final, int zoh) {
     if (B <= 0 || L <= 0 || D <= 0 || N <= 0 || nchan <= 0) return -1;
     if (!chans && nchan != B * D) return -1;
     int64_t i;
@@ -72,8 +74,10 @@ int s6o_fwd(int64_t B, int64_t L, int64_t D, int64_t N,
             double delta = softplus_d(bias + (double)dr[t]);
             double s = 0.0;
             for (int64_t n = 0; n < N; ++n) {
-                double abar = exp(delta * (double)A[d * N + n]);
-                h[n] = abar * h[n] + delta * (double)Br[n * L + t] * xt;
+                double an = (double)A[d * N + n];
+                double abar = exp(delta * an);
+                double fb = (zoh && an != 0.0) ? expm1(delta * an) / an : delta;
+                h[n] = abar * h[n] + fb * (double)Br[n * L + t] * xt;
                 s += (double)Cr[n * L + t] * h[n];
             }
             s += Dd * xt;

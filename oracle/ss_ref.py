@@ -20,6 +20,9 @@ Where the pages leave a point open, the plainest reading the rest supports is ta
   R5  the readout adds D·x to Σ_n C h (D = 0 gives the pages' form).
   R6  the SiLU branch multiplies the readout: y = (C·h + D·x)·silu(z).
   R7  the state before the first step is h0 (or 0); h_final is the state after the last.
+  With zoh=True the exact zero-order-hold form that [SEL §2.1] prints replaces R1:
+      B̄x = (exp(δA) - 1) / A · B x    (δ B x where A = 0, its limit)
+  the exact solution over one step of dh/dt = A h + B x with x held constant.
 
 What it computes, per batch row b and channel d:
   u_t     = dt_bias[d] + dt_raw[b,d,t]                    [SEL §1.2], [REV §2]
@@ -59,10 +62,21 @@ def _f64(a):
     return None if a is None else np.asarray(a, dtype=np.float64)
 
 
-def ss_fwd(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, z=None, h0=None):
+def bbar_factor(dl, A, zoh):
+    """The factor of B x in B̄x: δ (first order, R1) or (exp(δA) - 1)/A (exact zero-order
+    hold, [SEL §2.1]), evaluated with expm1 so small δA loses nothing."""
+    if not zoh:
+        return dl * np.ones_like(A)
+    num = np.expm1(dl * A)
+    safe = np.where(A == 0.0, 1.0, A)
+    return np.where(A == 0.0, dl * np.ones_like(A), num / safe)
+
+
+def ss_fwd(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, z=None, h0=None, zoh=False):
     """Forward scan.  Returns (y [B,D,L], h_final [B,D,N]) in float64.
 
     Shapes: x, dt_raw, z [B,D,L]; Bm, Cm [B,N,L]; A [D,N]; dt_bias, Dskip [D]; h0 [B,D,N].
+    zoh: exact zero-order-hold B̄ instead of the first-order δ·B.
     """
     x, dt_raw, dt_bias, A, Bm, Cm, Dskip, z, h0 = map(
         _f64, (x, dt_raw, dt_bias, A, Bm, Cm, Dskip, z, h0))
@@ -74,7 +88,7 @@ def ss_fwd(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, z=None, h0=None):
     for t in range(L):
         dl = delta[:, :, t, None]                                  # [B,D,1]
         abar = np.exp(dl * A[None, :, :])                          # [B,D,N]
-        bx = dl * Bm[:, None, :, t] * x[:, :, t, None]             # [B,D,N]
+        bx = bbar_factor(dl, A[None, :, :], zoh) * Bm[:, None, :, t] * x[:, :, t, None]
         h = abar * h + bx
         s = (Cm[:, None, :, t] * h).sum(axis=-1) + Dskip[None, :] * x[:, :, t]
         if z is not None:
