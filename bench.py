@@ -35,30 +35,36 @@ HBM_PEAK_GBPS = 8000.0
 ALU_PEAK_TSLOTS = 256 * 4 * 16 * 2.4e9 / 1e12
 
 
-# HBM traffic of the forward kernel per launch, from two rocprofv3 counter passes
+# HBM traffic of the dominant kernel per launch, from two rocprofv3 counter passes
 # (FETCH_SIZE, WRITE_SIZE) that each also ran a 1 GiB device copy: the copy reads
 # FETCH_SIZE = 512 MiB and WRITE_SIZE = 1 GiB, so reads = 2.0 x FETCH_SIZE and writes =
-# 1.0 x WRITE_SIZE.  A figure is reported only while the forward's sources hash to the
+# 1.0 x WRITE_SIZE.  A figure is reported only while the kernel's sources hash to the
 # value it was measured with; after any change it is null until measured again.
 FWD_SOURCES = ["ss_fwdg.hip", "ss_device.h", "ss_plan.h", "ss_api.cpp", "ss_kernels.h"]
+STEP_SOURCES = ["ss_step.hip", "ss_device.h", "ss_plan.h", "ss_api.cpp", "ss_kernels.h"]
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 MEASURED_TRAFFIC = {
-    "c2": {"sources_sha256": "6f01fe535189a403cf8652214f2c5c0a4c330fd4e08bad26da8aa82f94ac6c05",
-           "fetch_kib": 328825, "write_kib": 394601},
+    # (workload, disc): first-order (0) or exact zero-order hold (1)
+    ("c2", 0): {"sources": FWD_SOURCES, "fetch_kib": 323075, "write_kib": 399107,
+                "sources_sha256": "3057dccd95a97f3bcdb62bf8373fab26d1937509dc6b0e01cafdeebdc4e111df"},
+    ("c2", 1): {"sources": FWD_SOURCES, "fetch_kib": 329492, "write_kib": 396194,
+                "sources_sha256": "3057dccd95a97f3bcdb62bf8373fab26d1937509dc6b0e01cafdeebdc4e111df"},
+    ("d1", 0): {"sources": STEP_SOURCES, "fetch_kib": 45071, "write_kib": 87040,
+                "sources_sha256": "df0ce1f23149492f9a50e44a13847060c50e27f296b1f498e20474f70e01c9a5"},
 }
 
 
-def fwd_sources_sha256():
+def sources_sha256(files):
     h = hashlib.sha256()
-    for f in FWD_SOURCES:
+    for f in files:
         with open(os.path.join(ROOT, "selective_state_space_34_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
-def measured_traffic(w):
-    m = MEASURED_TRAFFIC.get(w.name)
-    if m is None or w.backward or m["sources_sha256"] != fwd_sources_sha256():
+def measured_traffic(w, disc=0):
+    m = MEASURED_TRAFFIC.get((w.name, disc))
+    if m is None or w.backward or m["sources_sha256"] != sources_sha256(m["sources"]):
         return None
     return FETCH_SCALE * m["fetch_kib"] * 1024 + WRITE_SCALE * m["write_kib"] * 1024
 
@@ -89,12 +95,14 @@ def bwd_min_bytes(w, s_in):
     return rd + wr
 
 
-def alu_slots_per_elem(w):
+def alu_slots_per_elem(w, disc=0):
     """Algorithmic VALU lane-slots per (b,t,d) element (transcendental = 2 slots).
     Per state: exp (2) + δ·A, δx·B, state fma, readout fma (4)  -> 6 x N.
+    The exact zero-order hold adds, at its cheapest, Ā - 1, x/A_n and one product per state
+    (3; 1/A_n is a per-channel constant) -> 9 x N.
     Per element: softplus 5 VALU + 2 trans; δ·x 1; D·x fma 1; gate 4 VALU + 2 trans (if any);
     bf16 widening 1 per bf16 input tensor."""
-    per_state = 6 * w.dstate
+    per_state = (9 if disc else 6) * w.dstate
     elem = 5 + 2 * 2 + 1 + 1
     if w.gate:
         elem += 4 + 2 * 2
@@ -117,7 +125,7 @@ def bwd_alu_slots_per_elem(w):
     return 17 * w.dstate + elem
 
 
-def cpu_baseline(w, inp, budget_s=4.0):
+def cpu_baseline(w, inp, budget_s=4.0, disc=0):
     """Time the fp64 C oracle (as it stands) on a growing sample of channels until
     one run takes about budget_s seconds of wall time on all host threads."""
     from oracle import cref
@@ -131,7 +139,7 @@ def cpu_baseline(w, inp, budget_s=4.0):
         t0 = time.perf_counter()
         # the decode step starts from the carried state and produces the next one
         cref.fwd(*args, z=inp.z if w.gate else None, h0=inp.h0 if w.decode else None,
-                 chans=chans, want_h_final=w.decode)
+                 chans=chans, want_h_final=w.decode, zoh=bool(disc))
         dt = time.perf_counter() - t0
         if dt >= budget_s / 4 or n == C:
             break
@@ -168,7 +176,7 @@ def run_decode(args, w, inp):
     stream = torch.cuda.current_stream()
 
     def step():
-        ss.ss_step(x, dtr, dtb, A, Bm, Cm, Dk, h, z=z, y=y, stream=stream)
+        ss.ss_step(x, dtr, dtb, A, Bm, Cm, Dk, h, z=z, y=y, disc=args.disc, stream=stream)
 
     # the state (B*D*N*4 bytes) fits in the 256 MB Infinity Cache: an untimed 1 GiB write
     # between steps evicts it, so each timed step reads and writes HBM
@@ -176,6 +184,7 @@ def run_decode(args, w, inp):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    calib_copy(args, dev)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -198,7 +207,7 @@ def run_decode(args, w, inp):
         f"{mb / 1e6:.1f} MB min bytes -> {gbps:.0f} GB/s ({gbps / HBM_PEAK_GBPS:.3f} of 8 TB/s)")
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, inp)
+        cpu = cpu_baseline(w, inp, disc=args.disc)
         log(f"[bench] cpu baseline {cpu['value']:.3e} elem/s ({cpu['sample']})")
     out = {
         "metric": "selective-scan decode step B·D channel-steps/s; achieved HBM GB/s vs MI355X peak",
@@ -209,14 +218,28 @@ def run_decode(args, w, inp):
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": f"{w.name}: {w.label}", "batch": w.batch, "seqlen": 1,
                    "dim": w.dim, "dstate": w.dstate, "in_dtype": w.dtype, "gate": w.gate,
-                   "cache_flush_mib": args.flush_mib},
+                   "cache_flush_mib": args.flush_mib,
+                   "disc": "zoh" if args.disc else "first-order"},
         "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": gbps / HBM_PEAK_GBPS, "traffic": None,
+                     "frac": gbps / HBM_PEAK_GBPS, "traffic": measured_traffic(w, args.disc),
                      "kernel": "ss_step (step_kernel, one launch per call)",
                      "launch_us": t_avg * 1e6, "traffic_algorithmic_bytes": mb},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def calib_copy(args, dev):
+    """One device copy of a known size, for scaling the HBM byte counters."""
+    import torch
+    if not args.calib_copy_mib:
+        return
+    nb = args.calib_copy_mib << 20
+    a = torch.empty(nb, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"[bench] calibration copy of {nb} bytes done")
 
 
 def dims_plan_single(ss, dims):
@@ -234,6 +257,8 @@ def main():
     ap.add_argument("--plan", type=int, default=0)
     ap.add_argument("--layout", type=int, default=0, help="0 auto, 1 four lanes, 2 one lane, 3 eight lanes per channel")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--disc", type=int, default=0,
+                    help="0 first-order input term (δ·B·x), 1 exact zero-order hold (forward only)")
     ap.add_argument("--no-ckpt", action="store_true",
                     help="fwd+bwd: recompute chunk start states instead of using checkpoints")
     ap.add_argument("--flush-mib", type=int, default=1024,
@@ -254,6 +279,10 @@ def main():
 
     w = workload(args.workload)
     log(f"[bench] workload {w.name}: {w.label}")
+    if args.disc and w.backward:
+        print("bench.py: the exact zero-order hold has no backward (ss_bwd rejects it)",
+              file=sys.stderr)
+        sys.exit(2)
     t0 = time.perf_counter()
     inp = workload_inputs(w)
     log(f"[bench] inputs generated in {time.perf_counter() - t0:.1f}s")
@@ -270,7 +299,8 @@ def main():
     y = torch.empty((w.batch, w.dim, w.seqlen), dtype=torch.float32, device=dev)
     hf = torch.empty((w.batch, w.dim, w.dstate), dtype=torch.float32, device=dev) if w.h_final else None
     dims = ss.make_dims(w.batch, w.seqlen, w.dim, w.dstate,
-                        ss.SS_BF16 if w.dtype == "bf16" else ss.SS_F32, args.plan, 0, args.layout)
+                        ss.SS_BF16 if w.dtype == "bf16" else ss.SS_F32, args.plan, 0, args.layout,
+                        args.disc)
     ws = torch.empty(max(ss.workspace_size(dims), 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     hck = None
@@ -285,7 +315,7 @@ def main():
 
     def fwd_call():
         ss.ss_fwd(x, dtr, dtb, A, Bm, Cm, Dk, z=z, y=y, h_final=hf, h_ckpt=hck, workspace=ws,
-                  plan=args.plan, layout=args.layout, stream=stream)
+                  plan=args.plan, layout=args.layout, disc=args.disc, stream=stream)
 
     def bwd_call():
         ss.ss_bwd(x, dtr, dtb, A, Bm, Cm, Dk, dy, z=z, h_ckpt=hck, workspace=wsb, out=grads,
@@ -299,13 +329,7 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    if args.calib_copy_mib:
-        nb = args.calib_copy_mib << 20
-        a = torch.empty(nb, dtype=torch.uint8, device=dev)
-        b = torch.empty_like(a)
-        b.copy_(a)
-        torch.cuda.synchronize()
-        log(f"[bench] calibration copy of {nb} bytes done")
+    calib_copy(args, dev)
 
     # timed region: K steps, HIP events around every step on the stream the kernels run on
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -341,7 +365,7 @@ def main():
     mb = min_bytes(w, s_in)
     t_avg = float(per.mean())
     value = elems * args.steps / wall
-    slots_pe = alu_slots_per_elem(w) + (bwd_alu_slots_per_elem(w) if w.backward else 0)
+    slots_pe = alu_slots_per_elem(w, args.disc) + (bwd_alu_slots_per_elem(w) if w.backward else 0)
     slots = elems * slots_pe
     alu_achieved = slots / t_avg / 1e12
     hbm_achieved = mb / t_avg / 1e9
@@ -355,7 +379,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle baseline ...")
-        cpu = cpu_baseline(w, inp)
+        cpu = cpu_baseline(w, inp, disc=args.disc)
         log(f"[bench] cpu baseline {cpu['value']:.3e} elem/s ({cpu['sample']})")
 
     out = {
@@ -374,10 +398,11 @@ def main():
         "config": {"workload": f"{w.name}: {w.label}", "batch": w.batch, "seqlen": w.seqlen,
                    "dim": w.dim, "dstate": w.dstate, "in_dtype": w.dtype, "gate": w.gate,
                    "plan": args.plan, "layout": args.layout,
+                   "disc": "zoh" if args.disc else "first-order",
                    "checkpoints": bool(w.backward and not args.no_ckpt)},
         "roofline": {"bound": "alu", "achieved": alu_achieved, "peak": ALU_PEAK_TSLOTS,
                      "unit": "T VALU-slot/s", "frac": alu_achieved / ALU_PEAK_TSLOTS,
-                     "traffic": measured_traffic(w),
+                     "traffic": measured_traffic(w, args.disc),
                      "kernel": ("ss_fwd + ss_bwd step (every kernel of both calls)" if w.backward
                                 else "ss_fwd (scang_kernel, one launch per call)"
                                 if dims_plan_single(ss, dims) else "ss_fwd (all passes)"),

@@ -53,7 +53,7 @@ extern "C" {
 #endif
 
 #define SS_VERSION_MAJOR 0
-#define SS_VERSION_MINOR 3
+#define SS_VERSION_MINOR 4
 
 /* dtype of x, dt_raw, z, Bm, Cm */
 typedef enum { SS_F32 = 0, SS_BF16 = 1 } ss_dtype;
@@ -77,6 +77,13 @@ typedef enum { SS_PLAN_AUTO = 0, SS_PLAN_SINGLE = 1, SS_PLAN_CHUNKED = 2 } ss_pl
  * A layout that does not apply to the dims falls back to the widest narrower one that does. */
 typedef enum { SS_LAYOUT_AUTO = 0, SS_LAYOUT_QUAD = 1, SS_LAYOUT_LANE = 2, SS_LAYOUT_OCT = 3 } ss_layout;
 
+/* Discretisation of the input term (page "3.2 선택적 스캔(Selective Scan) 알고리즘과 정보의
+ * 압축 및 선별", §2.1; Ā = exp(δA) in both).
+ *   SS_DISC_EULER — B̄x = δ·B·x, the first-order form of the hold (the default).
+ *   SS_DISC_ZOH   — B̄x = (exp(δA) - 1)/A · B·x, the exact zero-order hold (forward and
+ *                   ss_step; ss_bwd returns SS_ERR_UNSUPPORTED). */
+typedef enum { SS_DISC_EULER = 0, SS_DISC_ZOH = 1 } ss_disc;
+
 typedef struct ss_dims {
     int64_t batch;    /* B  >= 1 */
     int64_t seqlen;   /* L  >= 1 */
@@ -87,7 +94,7 @@ typedef struct ss_dims {
     int64_t chunk;    /* chunk length of the chunked plan (multiple of 8; backward: multiple
                          of 16, at most 64); 0 = automatic */
     int32_t layout;   /* ss_layout (forward only) */
-    int32_t reserved; /* must be 0 */
+    int32_t disc;     /* ss_disc */
 } ss_dims;
 
 /* Return codes: 0 on success, negative on error. */
@@ -95,7 +102,7 @@ enum {
     SS_OK = 0,
     SS_ERR_NULL = -1,        /* a required pointer is NULL */
     SS_ERR_DIMS = -2,        /* a dim <= 0, N unsupported, sizes overflow, or bad chunk */
-    SS_ERR_DTYPE = -3,       /* in_dtype, plan or layout not one of the enums */
+    SS_ERR_DTYPE = -3,       /* in_dtype, plan, layout or disc not one of the enums */
     SS_ERR_ALIGN = -4,       /* a base pointer is not 16-byte aligned */
     SS_ERR_WORKSPACE = -5,   /* workspace NULL while needed, or workspace_bytes too small */
     SS_ERR_HIP = -6,         /* a HIP call failed; see ss_last_hip_error() */
@@ -143,8 +150,9 @@ int ss_bwd(const ss_dims* dims,
 /* Single-token (decode) step: the recurrence carried one token further for every (batch
  * row, channel), as in recurrent inference (note "상태공간 모델(SSM)과 Mamba 아키텍처", §2):
  *   δ = softplus(dt_bias + dt_raw);  h ← exp(δ·A)⊙h + δ·B·x;  y = (C·h + Dskip·x)·silu(z)
- *   dims   : batch, dim, dstate, in_dtype as for ss_fwd; seqlen must be 1; plan, chunk and
- *            layout must be 0.
+ *   (with dims->disc = SS_DISC_ZOH the input term is (exp(δA) - 1)/A · B·x)
+ *   dims   : batch, dim, dstate, in_dtype, disc as for ss_fwd; seqlen must be 1; plan, chunk
+ *            and layout must be 0.
  *   x, dt_raw, z : [B, D] (in_dtype; z NULL = no gate); Bm, Cm : [B, N] (in_dtype);
  *   A [D, N], dt_bias [D], Dskip [D] : float32.
  *   h_in   : [B, D, N] float32, the state before the token (required).

@@ -23,6 +23,7 @@ from ._build import LIB, build, stale  # noqa: F401
 SS_F32, SS_BF16 = 0, 1
 SS_PLAN_AUTO, SS_PLAN_SINGLE, SS_PLAN_CHUNKED = 0, 1, 2
 SS_LAYOUT_AUTO, SS_LAYOUT_QUAD, SS_LAYOUT_LANE, SS_LAYOUT_OCT = 0, 1, 2, 3
+SS_DISC_EULER, SS_DISC_ZOH = 0, 1
 
 ERRORS = {0: "SS_OK", -1: "SS_ERR_NULL", -2: "SS_ERR_DIMS", -3: "SS_ERR_DTYPE", -4: "SS_ERR_ALIGN",
           -5: "SS_ERR_WORKSPACE", -6: "SS_ERR_HIP", -7: "SS_ERR_UNSUPPORTED"}
@@ -34,7 +35,7 @@ EXPORTS = ("ss_fwd", "ss_bwd", "ss_step", "ss_fwd_workspace_size", "ss_bwd_works
 class ss_dims(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("dim", ctypes.c_int64),
                 ("dstate", ctypes.c_int64), ("in_dtype", ctypes.c_int32), ("plan", ctypes.c_int32),
-                ("chunk", ctypes.c_int64), ("layout", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("chunk", ctypes.c_int64), ("layout", ctypes.c_int32), ("disc", ctypes.c_int32)]
 
 
 class SSError(RuntimeError):
@@ -79,8 +80,8 @@ def load(path: str = LIB):
 
 
 def make_dims(batch, seqlen, dim, dstate, in_dtype=SS_F32, plan=SS_PLAN_AUTO, chunk=0,
-              layout=SS_LAYOUT_AUTO):
-    return ss_dims(batch, seqlen, dim, dstate, in_dtype, plan, chunk, layout, 0)
+              layout=SS_LAYOUT_AUTO, disc=SS_DISC_EULER):
+    return ss_dims(batch, seqlen, dim, dstate, in_dtype, plan, chunk, layout, disc)
 
 
 def workspace_size(dims, backward=False) -> int:
@@ -113,7 +114,7 @@ def _check(t, name, shape, dtype, device):
         raise ValueError(f"{name} must be contiguous")
 
 
-def _dims_of(x, A, Bm, plan, chunk, layout=SS_LAYOUT_AUTO):
+def _dims_of(x, A, Bm, plan, chunk, layout=SS_LAYOUT_AUTO, disc=SS_DISC_EULER):
     import torch
     Bn, D, L = x.shape
     N = A.shape[1]
@@ -123,7 +124,7 @@ def _dims_of(x, A, Bm, plan, chunk, layout=SS_LAYOUT_AUTO):
         dt = SS_BF16
     else:
         raise ValueError(f"x dtype must be float32 or bfloat16, got {x.dtype}")
-    return make_dims(Bn, L, D, N, dt, plan, chunk, layout)
+    return make_dims(Bn, L, D, N, dt, plan, chunk, layout, disc)
 
 
 def _stream(stream):
@@ -155,13 +156,14 @@ CKPT_STEPS = 16
 
 def ss_fwd(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, z=None, h0=None, *, return_final=False,
            return_ckpt=False, y=None, h_final=None, h_ckpt=None, workspace=None,
-           plan=SS_PLAN_AUTO, chunk=0, layout=SS_LAYOUT_AUTO, stream=None):
+           plan=SS_PLAN_AUTO, chunk=0, layout=SS_LAYOUT_AUTO, disc=SS_DISC_EULER, stream=None):
     """Forward scan through the C ABI.  Returns y, (y, h_final) with return_final, and
-    the checkpoints last with return_ckpt (or when h_ckpt is passed)."""
+    the checkpoints last with return_ckpt (or when h_ckpt is passed).  disc: SS_DISC_EULER
+    (input term δ·B·x) or SS_DISC_ZOH (exact zero-order hold)."""
     import torch
     lib = load()
     _check_inputs(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, z, h0)
-    dims = _dims_of(x, A, Bm, plan, chunk, layout)
+    dims = _dims_of(x, A, Bm, plan, chunk, layout, disc)
     Bn, D, L = x.shape
     N = A.shape[1]
     if y is None:
@@ -231,7 +233,8 @@ def ss_bwd(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, dy, z=None, h0=None, dh_final=N
     return g
 
 
-def ss_step(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, h, z=None, *, h_out=None, y=None, stream=None):
+def ss_step(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, h, z=None, *, h_out=None, y=None,
+            disc=SS_DISC_EULER, stream=None):
     """One decode step through the C ABI: x, dt_raw, z [B, D]; Bm, Cm [B, N]; h [B, D, N]
     float32, the state before the token.  The state after it goes to h_out (default: h
     itself, updated in place).  Returns y [B, D] float32."""
@@ -264,7 +267,7 @@ def ss_step(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, h, z=None, *, h_out=None, y=No
     if y is None:
         y = torch.empty((Bn, D), dtype=f32, device=dev)
     _check(y, "y", (Bn, D), f32, dev)
-    dims = make_dims(Bn, 1, D, N, dt)
+    dims = make_dims(Bn, 1, D, N, dt, disc=disc)
     rc = lib.ss_step(ctypes.byref(dims), _ptr(x), _ptr(dt_raw), _ptr(dt_bias), _ptr(A), _ptr(Bm),
                      _ptr(Cm), _ptr(Dskip), _ptr(z), _ptr(h), _ptr(h_out), _ptr(y), _stream(stream))
     if rc != 0:

@@ -98,7 +98,7 @@ int ss_fwd(const ss_dims* dims, const void* x, const void* dt_raw, const float* 
     ss::ScanLaunch s{};
     s.x = x; s.dt_raw = dt_raw; s.z = z; s.dt_bias = dt_bias; s.A = A; s.Dskip = Dskip; s.BC = BC;
     s.Bm = Bm; s.Cm = Cm;
-    s.B = p.B; s.L = p.L; s.D = p.D; s.vec = p.vec;
+    s.B = p.B; s.L = p.L; s.D = p.D; s.vec = p.vec; s.zoh = p.zoh;
     if (!p.chunked) {
         s.chunk = p.L; s.K = 1; s.h_init = h0; s.y = y; s.h_last = h_final; s.h_ckpt = h_ckpt; s.agg = 0;
         s.d4 = p.d4; s.nb4 = p.nb4;
@@ -148,6 +148,7 @@ int ss_step(const ss_dims* dims, const void* x, const void* dt_raw, const float*
     ss::StepLaunch s{};
     s.x = x; s.dt_raw = dt_raw; s.z = z; s.dt_bias = dt_bias; s.A = A; s.Bm = Bm; s.Cm = Cm;
     s.Dskip = Dskip; s.h_in = h_in; s.h_out = h_out; s.y = y; s.B = p.B; s.D = p.D; s.N = int(p.N);
+    s.zoh = p.zoh;
     const hipError_t e = ss::launch_step(p.in_dtype == SS_BF16, s, stream);
     if (e != hipSuccess) return hip_fail(e);
     return SS_OK;
@@ -173,6 +174,8 @@ int ss_bwd(const ss_dims* dims, const void* x, const void* dt_raw, const float* 
     const void* opt[] = {z, h0, dh_final, dz, dh0, h_ckpt};
     for (const void* q : opt)
         if (q && !aligned16(q)) return SS_ERR_ALIGN;
+    // the adjoint kernels implement the first-order input term only
+    if (p.zoh) return SS_ERR_UNSUPPORTED;
     if (!workspace || workspace_bytes < p.ws_total) return SS_ERR_WORKSPACE;
     if (!aligned16(workspace)) return SS_ERR_ALIGN;
 

@@ -31,6 +31,27 @@ __device__ __forceinline__ float softplus(float u) {
     return fmaxf(u, 0.0f) + fmaf(log2_hw(v), kLn2, w - (v - 1.0f));
 }
 
+// Exact zero-order hold (page "3.2 선택적 스캔(Selective Scan) 알고리즘과 정보의 압축 및
+// 선별", §2.1): B̄x = g·B x with the gain g = (e^{δA} - 1)/A = δ·φ(u), u = δA,
+// φ(u) = (e^u - 1)/u.  For |u| < 1/8, δ times the degree-4 series of φ (truncation below
+// u^5/6! < 4.3e-8), written in t2 = u·log2(e) so the caller's exponent argument serves;
+// elsewhere (Ā - 1)·(1/A) in one fused rounding, whose relative error is at most
+// |Ā/(Ā - 1)| < 7.6 times that of Ā.  t2 and abar = 2^t2 as the caller computed them,
+// inv_a = 1/A (a per-channel constant; A = 0 gives t2 = 0, the series side).
+constexpr float kZohC1 = 0.34657359027997264f;    // ln2^k / (k+1)!
+constexpr float kZohC2 = 0.08007550231970023f;
+constexpr float kZohC3 = 0.013876027166205394f;
+constexpr float kZohC4 = 0.0019236258215256953f;
+constexpr float kZohSwitch2 = 0.18033688011112042f;  // |u| = 1/8 in units of t2
+__device__ __forceinline__ float zoh_gain(float t2, float abar, float delta, float inv_a) {
+    float p = fmaf(t2, kZohC4, kZohC3);
+    p = fmaf(t2, p, kZohC2);
+    p = fmaf(t2, p, kZohC1);
+    p = fmaf(t2, p, 1.0f);
+    const float q = fmaf(abar, inv_a, -inv_a);
+    return fabsf(t2) < kZohSwitch2 ? delta * p : q;
+}
+
 // sigmoid(z) = 1 / (1 + e^{-z}); e^{-z} = inf for z << 0 gives exactly 0.
 __device__ __forceinline__ float sigmoid(float z) { return rcp_hw(1.0f + exp2_hw(-z * kLog2e)); }
 

@@ -62,7 +62,7 @@ __global__ __launch_bounds__(256) void bc_stage_kernel(const Tin* __restrict__ B
 // = h_final [B, D, N], written by chunk K-1.  AGG: h_last = h_end [B, D, K, N],
 // dsum [B, D, K].
 // ---------------------------------------------------------------------------------------
-template <typename Tin, int N, bool kGate, bool kAgg>
+template <typename Tin, int N, bool kGate, bool kAgg, bool kZoh>
 __global__ __launch_bounds__(256) void scan_kernel(
     const Tin* __restrict__ x, const Tin* __restrict__ dt_raw, const Tin* __restrict__ z,
     const float* __restrict__ dt_bias, const float* __restrict__ A,
@@ -77,9 +77,13 @@ __global__ __launch_bounds__(256) void scan_kernel(
     const int64_t t_begin = int64_t(k) * chunk;
     const int64_t t_end = (t_begin + chunk < L) ? t_begin + chunk : L;
 
-    float A2[N], h[N];
+    float A2[N], iA[N], h[N];
 #pragma unroll
-    for (int n = 0; n < N; ++n) A2[n] = A[d * N + n] * kLog2e;
+    for (int n = 0; n < N; ++n) {
+        const float a = A[d * N + n];
+        A2[n] = a * kLog2e;
+        if (kZoh) iA[n] = 1.0f / a;
+    }
     const int64_t hidx = ((int64_t(b) * D + d) * K + k) * N;
 #pragma unroll
     for (int n = 0; n < N; ++n) h[n] = h_init ? h_init[hidx + n] : 0.0f;
@@ -135,8 +139,11 @@ __global__ __launch_bounds__(256) void scan_kernel(
         float a = r;
 #pragma unroll
         for (int n = 0; n < N; ++n) {
-            const float abar = kS4D ? a : exp2_hw(delta * A2[n]);
-            h[n] = fmaf(abar, h[n], dx * Bq[n]);
+            const float t2 = delta * A2[n];
+            const float abar = kS4D ? a : exp2_hw(t2);
+            float bx = (kZoh ? xv : dx) * Bq[n];
+            if (kZoh) bx *= zoh_gain(t2, abar, delta, iA[n]);
+            h[n] = fmaf(abar, h[n], bx);
             if (kS4D) a *= r;
         }
         const bool more = tt + 1 < t_end;
@@ -236,12 +243,21 @@ static hipError_t launch_scan_t(const ScanLaunch& p, hipStream_t s) {
     const Tin* z = static_cast<const Tin*>(p.z);
 #define SS_SCAN_ARGS x, dr, z, p.dt_bias, p.A, p.Dskip, p.BC, p.h_init, p.y, p.h_last, p.h_ckpt, \
                      p.dsum, p.L, p.D, p.chunk, p.K, p.vec
-    if (p.agg)
-        hipLaunchKernelGGL((scan_kernel<Tin, N, false, true>), grid, dim3(wg), 0, s, SS_SCAN_ARGS);
-    else if (p.z)
-        hipLaunchKernelGGL((scan_kernel<Tin, N, true, false>), grid, dim3(wg), 0, s, SS_SCAN_ARGS);
-    else
-        hipLaunchKernelGGL((scan_kernel<Tin, N, false, false>), grid, dim3(wg), 0, s, SS_SCAN_ARGS);
+    if (p.zoh) {
+        if (p.agg)
+            hipLaunchKernelGGL((scan_kernel<Tin, N, false, true, true>), grid, dim3(wg), 0, s, SS_SCAN_ARGS);
+        else if (p.z)
+            hipLaunchKernelGGL((scan_kernel<Tin, N, true, false, true>), grid, dim3(wg), 0, s, SS_SCAN_ARGS);
+        else
+            hipLaunchKernelGGL((scan_kernel<Tin, N, false, false, true>), grid, dim3(wg), 0, s, SS_SCAN_ARGS);
+    } else {
+        if (p.agg)
+            hipLaunchKernelGGL((scan_kernel<Tin, N, false, true, false>), grid, dim3(wg), 0, s, SS_SCAN_ARGS);
+        else if (p.z)
+            hipLaunchKernelGGL((scan_kernel<Tin, N, true, false, false>), grid, dim3(wg), 0, s, SS_SCAN_ARGS);
+        else
+            hipLaunchKernelGGL((scan_kernel<Tin, N, false, false, false>), grid, dim3(wg), 0, s, SS_SCAN_ARGS);
+    }
 #undef SS_SCAN_ARGS
     return hipGetLastError();
 }

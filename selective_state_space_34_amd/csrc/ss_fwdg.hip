@@ -20,7 +20,8 @@
 //   - the lanes write their (δ, δ·x) pairs into a per-wave LDS row of their channel;
 //   - the recurrence walks the 16 steps; each step reads its (δ, δ·x) pair from that
 //     row and B_t, C_t for the lane's S states from the tile, one step ahead, as
-//     broadcast reads (no VALU work moves operands between lanes);
+//     broadcast reads (no VALU work moves operands between lanes); under the exact
+//     zero-order hold the pair is (δ, x) and each state forms its own gain;
 //   - each lane's partial readouts (its S states, 16 steps) go to the same per-wave
 //     area; lane l sums the G partials of its own kH steps, adds D·x, applies the
 //     gate and stores kH outputs.
@@ -172,7 +173,7 @@ struct GroupLds {
 // below d_hi), chunk k.  lds: GroupLds<G, S>::FLOATS floats, 16-byte aligned.  Requires
 // L % 8 == 0 and chunk % 32 == 0 (or K == 1) for the tiled part; the last < 32 steps of a
 // chunk run a per-step tail.
-template <typename Tin, int G, int S, bool kGate, bool kAgg>
+template <typename Tin, int G, int S, bool kGate, bool kAgg, bool kZoh>
 __device__ __forceinline__ void scang_body(
     float* __restrict__ lds, int64_t blk, int k, int b, int64_t d_lo, int64_t d_hi,
     const Tin* __restrict__ x, const Tin* __restrict__ dt_raw, const Tin* __restrict__ z,
@@ -207,9 +208,13 @@ __device__ __forceinline__ void scang_body(
     const int64_t t_tiles_end = t_begin + n_tiles * kTile;
     const int n0 = l * S;
 
-    float A2[S], h[S];
+    float A2[S], iA[S], h[S];
 #pragma unroll
-    for (int s = 0; s < S; ++s) A2[s] = A[d * N + n0 + s] * kLog2e;
+    for (int s = 0; s < S; ++s) {
+        const float a = A[d * N + n0 + s];
+        A2[s] = a * kLog2e;
+        if (kZoh) iA[s] = 1.0f / a;
+    }
     const int64_t hidx = ((int64_t(b) * D + d) * K + k) * N + n0;
 #pragma unroll
     for (int s = 0; s < S; ++s) h[s] = h_init ? h_init[hidx + s] : 0.0f;
@@ -292,7 +297,8 @@ __device__ __forceinline__ void scang_body(
             for (int i = 0; i < kH; ++i) {
                 const float dl = softplus(bias + dv[hh][i]);
                 if (kAgg) dsum += dl;
-                *reinterpret_cast<float2*>(dd_row + 2 * (kH * l + i)) = make_float2(dl, dl * xv[hh][i]);
+                *reinterpret_cast<float2*>(dd_row + 2 * (kH * l + i)) =
+                    make_float2(dl, kZoh ? xv[hh][i] : dl * xv[hh][i]);
             }
             wave_sync();
 
@@ -318,8 +324,12 @@ __device__ __forceinline__ void scang_body(
                 float acc = 0.0f;
 #pragma unroll
                 for (int s = 0; s < S; ++s) {
-                    const float abar = exp2_hw(dcur.x * A2[s]);
-                    h[s] = fmaf(abar, h[s], dcur.y * bcur.v[s]);
+                    const float t2 = dcur.x * A2[s];
+                    const float abar = exp2_hw(t2);
+                    // first order: dcur.y = δ·x; exact hold: dcur.y = x, times the gain
+                    float bx = dcur.y * bcur.v[s];
+                    if (kZoh) bx *= zoh_gain(t2, abar, dcur.x, iA[s]);
+                    h[s] = fmaf(abar, h[s], bx);
                     if (!kAgg) acc = fmaf(ccur.v[s], h[s], acc);
                 }
                 part[t] = acc;
@@ -372,8 +382,11 @@ __device__ __forceinline__ void scang_body(
         float acc = 0.0f;
 #pragma unroll
         for (int s = 0; s < S; ++s) {
-            const float abar = exp2_hw(delta * A2[s]);
-            h[s] = fmaf(abar, h[s], dxt * to_f32(Bb[int64_t(n0 + s) * L + t]));
+            const float t2 = delta * A2[s];
+            const float abar = exp2_hw(t2);
+            float bx = (kZoh ? xt : dxt) * to_f32(Bb[int64_t(n0 + s) * L + t]);
+            if (kZoh) bx *= zoh_gain(t2, abar, delta, iA[s]);
+            h[s] = fmaf(abar, h[s], bx);
             if (!kAgg) acc = fmaf(to_f32(Cb[int64_t(n0 + s) * L + t]), h[s], acc);
         }
         if (!kAgg) {
@@ -400,7 +413,7 @@ __device__ __forceinline__ void scang_body(
 }
 
 // grid = (ceil(D / (256/G)), K, B), block = 256.
-template <typename Tin, int G, int S, bool kGate, bool kAgg>
+template <typename Tin, int G, int S, bool kGate, bool kAgg, bool kZoh>
 __global__ __launch_bounds__(kThreads) void scang_kernel(
     const Tin* __restrict__ x, const Tin* __restrict__ dt_raw, const Tin* __restrict__ z,
     const float* __restrict__ dt_bias, const float* __restrict__ A,
@@ -409,7 +422,7 @@ __global__ __launch_bounds__(kThreads) void scang_kernel(
     float* __restrict__ h_ckpt, float* __restrict__ dsum_out, int64_t L, int64_t D,
     int64_t chunk, int K) {
     __shared__ __align__(16) float lds[GroupLds<G, S>::FLOATS];
-    scang_body<Tin, G, S, kGate, kAgg>(lds, blockIdx.x, blockIdx.y, blockIdx.z, 0, D, x, dt_raw, z,
+    scang_body<Tin, G, S, kGate, kAgg, kZoh>(lds, blockIdx.x, blockIdx.y, blockIdx.z, 0, D, x, dt_raw, z,
                                        dt_bias, A, Dskip, Bm, Cm, h_init, y, h_last, h_ckpt,
                                        dsum_out, L, D, chunk, K);
 }
@@ -420,7 +433,7 @@ __global__ __launch_bounds__(kThreads) void scang_kernel(
 // four-lane workgroups and then its eight-lane one: whole rounds of four-lane waves per
 // SIMD, the remainder as eight-lane waves that take about half a four-lane wave's time.
 // grid = B * (nb4 + nb8), block = 256.
-template <typename Tin, int N, bool kGate>
+template <typename Tin, int N, bool kGate, bool kZoh>
 __global__ __launch_bounds__(kThreads) void scang_mixed_kernel(
     const Tin* __restrict__ x, const Tin* __restrict__ dt_raw, const Tin* __restrict__ z,
     const float* __restrict__ dt_bias, const float* __restrict__ A,
@@ -432,12 +445,12 @@ __global__ __launch_bounds__(kThreads) void scang_mixed_kernel(
     const int64_t f = blockIdx.x;
     const int64_t n4 = int64_t(B) * nb4;
     if (f < n4) {
-        scang_body<Tin, 4, N / 4, kGate, false>(lds, f % nb4, 0, int(f / nb4), 0, d4, x, dt_raw, z,
+        scang_body<Tin, 4, N / 4, kGate, false, kZoh>(lds, f % nb4, 0, int(f / nb4), 0, d4, x, dt_raw, z,
                                                 dt_bias, A, Dskip, Bm, Cm, h_init, y, h_last, h_ckpt,
                                                 nullptr, L, D, L, 1);
     } else {
         const int64_t g = f - n4;
-        scang_body<Tin, 8, N / 8, kGate, false>(lds, g % nb8, 0, int(g / nb8), d4, D, x, dt_raw, z,
+        scang_body<Tin, 8, N / 8, kGate, false, kZoh>(lds, g % nb8, 0, int(g / nb8), d4, D, x, dt_raw, z,
                                                 dt_bias, A, Dskip, Bm, Cm, h_init, y, h_last, h_ckpt,
                                                 nullptr, L, D, L, 1);
     }
@@ -454,10 +467,17 @@ static hipError_t launch_scang_mixed_t(const ScanLaunch& p, hipStream_t s) {
     const Tin* Cm = static_cast<const Tin*>(p.Cm);
 #define SS_ARGS x, dr, z, p.dt_bias, p.A, p.Dskip, Bm, Cm, p.h_init, p.y, p.h_last, p.h_ckpt, p.L, \
                 p.D, p.d4, p.nb4, nb8, int(p.B)
-    if (p.z)
-        hipLaunchKernelGGL((scang_mixed_kernel<Tin, N, true>), grid, dim3(kThreads), 0, s, SS_ARGS);
-    else
-        hipLaunchKernelGGL((scang_mixed_kernel<Tin, N, false>), grid, dim3(kThreads), 0, s, SS_ARGS);
+    if (p.zoh) {
+        if (p.z)
+            hipLaunchKernelGGL((scang_mixed_kernel<Tin, N, true, true>), grid, dim3(kThreads), 0, s, SS_ARGS);
+        else
+            hipLaunchKernelGGL((scang_mixed_kernel<Tin, N, false, true>), grid, dim3(kThreads), 0, s, SS_ARGS);
+    } else {
+        if (p.z)
+            hipLaunchKernelGGL((scang_mixed_kernel<Tin, N, true, false>), grid, dim3(kThreads), 0, s, SS_ARGS);
+        else
+            hipLaunchKernelGGL((scang_mixed_kernel<Tin, N, false, false>), grid, dim3(kThreads), 0, s, SS_ARGS);
+    }
 #undef SS_ARGS
     return hipGetLastError();
 }
@@ -473,12 +493,21 @@ static hipError_t launch_scang_t(const ScanLaunch& p, hipStream_t s) {
     const Tin* Cm = static_cast<const Tin*>(p.Cm);
 #define SS_ARGS x, dr, z, p.dt_bias, p.A, p.Dskip, Bm, Cm, p.h_init, p.y, p.h_last, p.h_ckpt, \
                 p.dsum, p.L, p.D, p.chunk, p.K
-    if (p.agg)
-        hipLaunchKernelGGL((scang_kernel<Tin, G, S, false, true>), grid, dim3(kThreads), 0, s, SS_ARGS);
-    else if (p.z)
-        hipLaunchKernelGGL((scang_kernel<Tin, G, S, true, false>), grid, dim3(kThreads), 0, s, SS_ARGS);
-    else
-        hipLaunchKernelGGL((scang_kernel<Tin, G, S, false, false>), grid, dim3(kThreads), 0, s, SS_ARGS);
+    if (p.zoh) {
+        if (p.agg)
+            hipLaunchKernelGGL((scang_kernel<Tin, G, S, false, true, true>), grid, dim3(kThreads), 0, s, SS_ARGS);
+        else if (p.z)
+            hipLaunchKernelGGL((scang_kernel<Tin, G, S, true, false, true>), grid, dim3(kThreads), 0, s, SS_ARGS);
+        else
+            hipLaunchKernelGGL((scang_kernel<Tin, G, S, false, false, true>), grid, dim3(kThreads), 0, s, SS_ARGS);
+    } else {
+        if (p.agg)
+            hipLaunchKernelGGL((scang_kernel<Tin, G, S, false, true, false>), grid, dim3(kThreads), 0, s, SS_ARGS);
+        else if (p.z)
+            hipLaunchKernelGGL((scang_kernel<Tin, G, S, true, false, false>), grid, dim3(kThreads), 0, s, SS_ARGS);
+        else
+            hipLaunchKernelGGL((scang_kernel<Tin, G, S, false, false, false>), grid, dim3(kThreads), 0, s, SS_ARGS);
+    }
 #undef SS_ARGS
     return hipGetLastError();
 }

@@ -31,6 +31,7 @@ struct ScanLaunch {
     int agg;                // 1: AGG mode
     int64_t d4;             // mixed layout: channels [0, d4) on four lanes, [d4, D) on eight
     int nb4;                //               four-lane workgroups per batch row (d4 / 64)
+    int zoh;                // 1: exact zero-order-hold B̄
 };
 
 // Affine-pair carry across chunks (one workgroup per channel).  Chunk c's pair is
@@ -104,6 +105,7 @@ struct StepLaunch {
     float* y;
     int64_t B, D;
     int N;
+    int zoh;                // 1: exact zero-order-hold B̄
 };
 
 hipError_t launch_bc_stage(int bf16, int N, const void* Bm, const void* Cm, float* BC, int64_t B,

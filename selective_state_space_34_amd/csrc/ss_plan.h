@@ -21,6 +21,7 @@ struct Plan {
     int mixed;       // forward, single pass: four lanes for channels [0, d4), eight for the rest
     int64_t d4;
     int nb4;         // four-lane workgroups per batch row (d4 / 64)
+    int zoh;         // exact zero-order-hold input term
     // workspace carving (byte offsets, 256-aligned)
     size_t off_bc, off_hend, off_dsum, off_hstart, off_gend, off_gstart, off_red;
     size_t red_bytes;
@@ -55,7 +56,7 @@ inline int make_plan(const ss_dims& d, bool backward, Plan* out) {
     if (d.layout != SS_LAYOUT_AUTO && d.layout != SS_LAYOUT_QUAD && d.layout != SS_LAYOUT_LANE &&
         d.layout != SS_LAYOUT_OCT)
         return SS_ERR_DTYPE;
-    if (d.reserved != 0) return SS_ERR_DTYPE;
+    if (d.disc != SS_DISC_EULER && d.disc != SS_DISC_ZOH) return SS_ERR_DTYPE;
     if (d.batch <= 0 || d.seqlen <= 0 || d.dim <= 0 || d.dstate <= 0) return SS_ERR_DIMS;
     const int64_t N = d.dstate;
     if (N != 1 && N != 2 && N != 4 && N != 8 && N != 16 && N != 32) return SS_ERR_DIMS;
@@ -66,6 +67,7 @@ inline int make_plan(const ss_dims& d, bool backward, Plan* out) {
         return SS_ERR_DIMS;
     if (d.batch > kMaxGridYZ) return SS_ERR_DIMS;
     p.B = d.batch; p.L = d.seqlen; p.D = d.dim; p.N = N; p.in_dtype = d.in_dtype;
+    p.zoh = d.disc == SS_DISC_ZOH;
     p.vec = (p.L % 8) == 0;
     // layout: a group of G lanes per channel (G x the waves of one lane per channel).
     // Automatic choice: four lanes wherever they apply.  Measured on MI355X, eight lanes

@@ -28,7 +28,7 @@ __device__ __forceinline__ float group_sum(float v) {
 }  // namespace
 
 // one thread per (batch row, channel, lane of the channel's group); grid = ceil(B·D·G / 256)
-template <typename Tin, int S, int G, bool kGate>
+template <typename Tin, int S, int G, bool kGate, bool kZoh>
 __global__ __launch_bounds__(256) void step_kernel(
     const Tin* __restrict__ x, const Tin* __restrict__ dt_raw, const Tin* __restrict__ z,
     const float* __restrict__ dt_bias, const float* __restrict__ A, const Tin* __restrict__ Bm,
@@ -58,8 +58,12 @@ __global__ __launch_bounds__(256) void step_kernel(
 #pragma unroll
     for (int s = 0; s < S; ++s) {
         const int n = n0 + s;
-        const float abar = exp2_hw(delta * (A[d * N + n] * kLog2e));
-        h[s] = fmaf(abar, h[s], dx * to_f32(Bm[b * N + n]));
+        const float a = A[d * N + n];
+        const float t2 = delta * (a * kLog2e);
+        const float abar = exp2_hw(t2);
+        float bx = (kZoh ? xv : dx) * to_f32(Bm[b * N + n]);
+        if (kZoh) bx *= zoh_gain(t2, abar, delta, 1.0f / a);
+        h[s] = fmaf(abar, h[s], bx);
         acc = fmaf(to_f32(Cm[b * N + n]), h[s], acc);
     }
     float* ho = h_out + ch * N + n0;             // may be h_in: this lane read its states above
@@ -86,12 +90,15 @@ static hipError_t launch_step_t(const StepLaunch& p, hipStream_t s) {
     const Tin* z = static_cast<const Tin*>(p.z);
     const Tin* Bm = static_cast<const Tin*>(p.Bm);
     const Tin* Cm = static_cast<const Tin*>(p.Cm);
-    if (z)
-        hipLaunchKernelGGL((step_kernel<Tin, S, G, true>), grid, dim3(256), 0, s, x, dr, z, p.dt_bias,
-                           p.A, Bm, Cm, p.Dskip, p.h_in, p.h_out, p.y, p.B * p.D, p.D);
-    else
-        hipLaunchKernelGGL((step_kernel<Tin, S, G, false>), grid, dim3(256), 0, s, x, dr, z, p.dt_bias,
-                           p.A, Bm, Cm, p.Dskip, p.h_in, p.h_out, p.y, p.B * p.D, p.D);
+#define SS_STEP_ARGS x, dr, z, p.dt_bias, p.A, Bm, Cm, p.Dskip, p.h_in, p.h_out, p.y, p.B * p.D, p.D
+    if (p.zoh) {
+        if (z) hipLaunchKernelGGL((step_kernel<Tin, S, G, true, true>), grid, dim3(256), 0, s, SS_STEP_ARGS);
+        else hipLaunchKernelGGL((step_kernel<Tin, S, G, false, true>), grid, dim3(256), 0, s, SS_STEP_ARGS);
+    } else {
+        if (z) hipLaunchKernelGGL((step_kernel<Tin, S, G, true, false>), grid, dim3(256), 0, s, SS_STEP_ARGS);
+        else hipLaunchKernelGGL((step_kernel<Tin, S, G, false, false>), grid, dim3(256), 0, s, SS_STEP_ARGS);
+    }
+#undef SS_STEP_ARGS
     return hipGetLastError();
 }
 

@@ -35,12 +35,12 @@ def dev(inp):
                 h0=t32(inp.h0), dy=t32(inp.dy), dh_final=t32(inp.dh_final))
 
 
-def gpu_fwd(ss, inp, *, gate=True, h0=True, final=True, plan=0, chunk=0, layout=0):
+def gpu_fwd(ss, inp, *, gate=True, h0=True, final=True, plan=0, chunk=0, layout=0, disc=0):
     import torch
     t = dev(inp)
     out = ss.ss_fwd(t["x"], t["dt_raw"], t["dt_bias"], t["A"], t["Bm"], t["Cm"], t["Dskip"],
                     z=t["z"] if gate else None, h0=t["h0"] if h0 else None,
-                    return_final=final, plan=plan, chunk=chunk, layout=layout)
+                    return_final=final, plan=plan, chunk=chunk, layout=layout, disc=disc)
     torch.cuda.synchronize()
     if final:
         return out[0].cpu().numpy(), out[1].cpu().numpy()

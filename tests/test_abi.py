@@ -37,7 +37,7 @@ def test_exports_match_header(lib):
 
 
 def test_version_and_strerror(lib):
-    assert lib.ss_version() == (0 << 16) | 3
+    assert lib.ss_version() == (0 << 16) | 4
     for code in ss.ERRORS:
         assert len(lib.ss_strerror(code)) > 0
     assert b"unknown" in lib.ss_strerror(12345)
@@ -64,9 +64,8 @@ def test_fwd_validation(lib):
     assert _fwd(lib, ss.make_dims(2, 64, 32, 16, in_dtype=7)) == -3
     assert _fwd(lib, ss.make_dims(2, 64, 32, 16, plan=9)) == -3
     assert _fwd(lib, ss.make_dims(2, 64, 32, 16, layout=5)) == -3
-    bad_res = ss.make_dims(2, 64, 32, 16)
-    bad_res.reserved = 1
-    assert _fwd(lib, bad_res) == -3
+    assert _fwd(lib, ss.make_dims(2, 64, 32, 16, disc=2)) == -3
+    assert _fwd(lib, ss.make_dims(2, 64, 32, 16, disc=-1)) == -3
     # required pointers
     for i in (0, 1, 2, 3, 4, 5, 6, 9):
         p = [ctypes.c_void_p(FAKE)] * 12
@@ -155,6 +154,9 @@ def test_bwd_validation(lib):
     a[11] = ctypes.c_void_p(FAKE + 4)
     assert call(good, a) == -4
     assert call(good, args) == -5
+    # the exact zero-order hold has no backward; an unknown disc is rejected as an enum
+    assert call(ss.make_dims(2, 64, 32, 16, ss.SS_F32, disc=ss.SS_DISC_ZOH), args) == -7
+    assert call(ss.make_dims(2, 64, 32, 16, ss.SS_F32, disc=3), args) == -3
 
 
 def test_step_validation(lib):
@@ -170,6 +172,7 @@ def test_step_validation(lib):
     assert call(ss.make_dims(4, 1, 32, 16, plan=1), args) == -3  # plan must be automatic
     assert call(ss.make_dims(4, 1, 32, 16, layout=1), args) == -3
     assert call(ss.make_dims(4, 1, 32, 16, in_dtype=9), args) == -3
+    assert call(ss.make_dims(4, 1, 32, 16, disc=2), args) == -3
     good = ss.make_dims(4, 1, 32, 16)
     for i in (0, 1, 2, 3, 4, 5, 6, 8, 9, 10):
         a = list(args)
