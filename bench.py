@@ -73,25 +73,33 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def min_bytes(w, s_in):
+def min_bytes(w, s_in, dt_shared=False):
     """Algorithmic HBM bytes of one forward: read x, dt_raw (, z), B, C and parameters,
-    write y (the (B,L,D,N) state and Ā/B̄ are never materialised)."""
+    write y (the (B,L,D,N) state and Ā/B̄ are never materialised).  A shared Δraw is
+    B·L values instead of B·L·D."""
     BLD = w.batch * w.seqlen * w.dim
-    n_in = 3 if w.gate else 2
+    n_in = (3 if w.gate else 2) - (1 if dt_shared else 0)
     rd = n_in * BLD * s_in + 2 * w.batch * w.dstate * w.seqlen * s_in
+    rd += w.batch * w.seqlen * s_in if dt_shared else 0
     rd += w.dim * w.dstate * 4 + 2 * w.dim * 4
     wr = BLD * 4 + (w.batch * w.dim * w.dstate * 4 if w.h_final else 0)
     return rd + wr
 
 
-def bwd_min_bytes(w, s_in):
+def bwd_min_bytes(w, s_in, dt_shared=False):
     """Algorithmic HBM bytes of one backward: read x, dt_raw, z (s_in), dy (4), B, C and the
-    parameters; write dx, dt_raw-grad, dz (4 each), dB, dC (4·B·N·L each), dA, dD, ddt_bias."""
+    parameters; write dx, dt_raw-grad, dz (4 each), dB, dC (4·B·N·L each), dA, dD, ddt_bias.
+    A shared Δraw and its gradient are B·L values each."""
     BLD = w.batch * w.seqlen * w.dim
+    BL = w.batch * w.seqlen
     BNL = w.batch * w.dstate * w.seqlen
     n_in = 3 if w.gate else 2
-    rd = n_in * BLD * s_in + BLD * 4 + 2 * BNL * s_in + w.dim * w.dstate * 4 + 2 * w.dim * 4
-    wr = n_in * BLD * 4 + 2 * BNL * 4 + w.dim * w.dstate * 4 + 2 * w.dim * 4
+    n_seq = n_in - (1 if dt_shared else 0)
+    rd = n_seq * BLD * s_in + BLD * 4 + 2 * BNL * s_in + w.dim * w.dstate * 4 + 2 * w.dim * 4
+    wr = n_seq * BLD * 4 + 2 * BNL * 4 + w.dim * w.dstate * 4 + 2 * w.dim * 4
+    if dt_shared:
+        rd += BL * s_in
+        wr += BL * 4
     return rd + wr
 
 
@@ -150,12 +158,13 @@ def cpu_baseline(w, inp, budget_s=4.0, disc=0):
                       f"{dt:.2f} s wall on {threads} OpenMP threads"}
 
 
-def step_min_bytes(w, s_in):
-    """Algorithmic HBM bytes of one decode step: read x, dt_raw (, z) [B, D], B, C [B, N] and the
-    parameters, read and write the state [B, D, N], write y [B, D]."""
+def step_min_bytes(w, s_in, dt_shared=False):
+    """Algorithmic HBM bytes of one decode step: read x, dt_raw (, z) [B, D] (a shared dt_raw:
+    [B]), B, C [B, N] and the parameters, read and write the state [B, D, N], write y [B, D]."""
     BD = w.batch * w.dim
-    n_in = 3 if w.gate else 2
-    return (n_in * BD * s_in + 2 * w.batch * w.dstate * s_in + w.dim * (w.dstate + 2) * 4
+    n_in = (3 if w.gate else 2) - (1 if dt_shared else 0)
+    return (n_in * BD * s_in + (w.batch * s_in if dt_shared else 0)
+            + 2 * w.batch * w.dstate * s_in + w.dim * (w.dstate + 2) * 4
             + 2 * BD * w.dstate * 4 + BD * 4)
 
 
@@ -168,7 +177,8 @@ def run_decode(args, w, inp):
     dev = torch.device("cuda:0")
     col = lambda a: torch.from_numpy(np.ascontiguousarray(a[..., 0])).to(dt).to(dev)
     t32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
-    x, dtr, Bm, Cm = col(inp.x), col(inp.dt_raw), col(inp.Bm), col(inp.Cm)
+    x, Bm, Cm = col(inp.x), col(inp.Bm), col(inp.Cm)
+    dtr = col(inp.dt_tok) if args.dt_shared else col(inp.dt_raw)
     z = col(inp.z) if w.gate else None
     dtb, A, Dk = t32(inp.dt_bias), t32(inp.A), t32(inp.Dskip)
     h = t32(inp.h0)
@@ -200,7 +210,7 @@ def run_decode(args, w, inp):
     per = np.array([e0.elapsed_time(e1) for e0, e1 in evs]) * 1e-3
     t_avg = float(per.mean())
     s_in = 2 if w.dtype == "bf16" else 4
-    mb = step_min_bytes(w, s_in)
+    mb = step_min_bytes(w, s_in, args.dt_shared)
     gbps = mb / t_avg / 1e9
     elems = w.batch * w.dim
     log(f"[bench] decode step event avg {t_avg * 1e6:.2f} us (min {per.min() * 1e6:.2f}); "
@@ -221,7 +231,8 @@ def run_decode(args, w, inp):
                    "cache_flush_mib": args.flush_mib,
                    "disc": "zoh" if args.disc else "first-order"},
         "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": gbps / HBM_PEAK_GBPS, "traffic": measured_traffic(w, args.disc),
+                     "frac": gbps / HBM_PEAK_GBPS,
+                     "traffic": None if args.dt_shared else measured_traffic(w, args.disc),
                      "kernel": "ss_step (step_kernel, one launch per call)",
                      "launch_us": t_avg * 1e6, "traffic_algorithmic_bytes": mb},
         "cpu_baseline": cpu,
@@ -257,6 +268,10 @@ def main():
     ap.add_argument("--plan", type=int, default=0)
     ap.add_argument("--layout", type=int, default=0, help="0 auto, 1 four lanes, 2 one lane, 3 eight lanes per channel")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--order", type=int, default=0,
+                    help="0 channel-major [B,D,L] sequences, 1 token-major [B,L,D] (B, C [B,L,N])")
+    ap.add_argument("--dt-shared", action="store_true",
+                    help="one dt_raw value per token [B, L], shared by the channels")
     ap.add_argument("--disc", type=int, default=0,
                     help="0 first-order input term (δ·B·x), 1 exact zero-order hold (forward only)")
     ap.add_argument("--no-ckpt", action="store_true",
@@ -284,30 +299,35 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     t0 = time.perf_counter()
-    inp = workload_inputs(w)
+    inp = workload_inputs(w, dt_shared=args.dt_shared)
     log(f"[bench] inputs generated in {time.perf_counter() - t0:.1f}s")
     if w.decode:
         run_decode(args, w, inp)
         return
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     dev = torch.device("cuda:0")
-    t_in = lambda a: torch.from_numpy(a).to(dt).to(dev)
+    # the same values in the requested memory order
+    lay = (lambda a: np.ascontiguousarray(np.swapaxes(a, 1, 2))) if args.order else (lambda a: a)
+    t_in = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dt).to(dev)
     t32 = lambda a: torch.from_numpy(a).to(dev)
-    x, dtr, Bm, Cm = t_in(inp.x), t_in(inp.dt_raw), t_in(inp.Bm), t_in(inp.Cm)
-    z = t_in(inp.z) if w.gate else None
+    x, Bm, Cm = t_in(lay(inp.x)), t_in(lay(inp.Bm)), t_in(lay(inp.Cm))
+    dtr = t_in(inp.dt_tok) if args.dt_shared else t_in(lay(inp.dt_raw))
+    z = t_in(lay(inp.z)) if w.gate else None
     dtb, A, Dk = t32(inp.dt_bias), t32(inp.A), t32(inp.Dskip)
-    y = torch.empty((w.batch, w.dim, w.seqlen), dtype=torch.float32, device=dev)
+    yshape = (w.batch, w.seqlen, w.dim) if args.order else (w.batch, w.dim, w.seqlen)
+    y = torch.empty(yshape, dtype=torch.float32, device=dev)
     hf = torch.empty((w.batch, w.dim, w.dstate), dtype=torch.float32, device=dev) if w.h_final else None
     dims = ss.make_dims(w.batch, w.seqlen, w.dim, w.dstate,
                         ss.SS_BF16 if w.dtype == "bf16" else ss.SS_F32, args.plan, 0, args.layout,
-                        args.disc)
+                        args.disc, args.order,
+                        ss.SS_DT_SHARED if args.dt_shared else ss.SS_DT_FULL)
     ws = torch.empty(max(ss.workspace_size(dims), 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     hck = None
     if w.backward:
-        dy = t32(inp.dy)
+        dy = t32(np.ascontiguousarray(lay(inp.dy)))
         wsb = torch.empty(ss.workspace_size(dims, backward=True), dtype=torch.uint8, device=dev)
-        grads = ss.ss_bwd(x, dtr, dtb, A, Bm, Cm, Dk, dy, z=z)
+        grads = ss.ss_bwd(x, dtr, dtb, A, Bm, Cm, Dk, dy, z=z, order=args.order)
         # training use: the forward keeps its 16-step state checkpoints for the backward
         if not args.no_ckpt:
             nck = (w.seqlen + ss.CKPT_STEPS - 1) // ss.CKPT_STEPS
@@ -315,11 +335,12 @@ def main():
 
     def fwd_call():
         ss.ss_fwd(x, dtr, dtb, A, Bm, Cm, Dk, z=z, y=y, h_final=hf, h_ckpt=hck, workspace=ws,
-                  plan=args.plan, layout=args.layout, disc=args.disc, stream=stream)
+                  plan=args.plan, layout=args.layout, disc=args.disc, order=args.order,
+                  stream=stream)
 
     def bwd_call():
         ss.ss_bwd(x, dtr, dtb, A, Bm, Cm, Dk, dy, z=z, h_ckpt=hck, workspace=wsb, out=grads,
-                  stream=stream)
+                  order=args.order, stream=stream)
 
     def step():
         fwd_call()
@@ -355,14 +376,14 @@ def main():
         torch.cuda.synchronize()
         tf = float(np.mean([e0.elapsed_time(e1) for e0, e1 in fe])) * 1e-3
         split = {"fwd_us": tf * 1e6, "bwd_us": (float(per.mean()) - tf) * 1e6,
-                 "bwd_min_bytes": bwd_min_bytes(w, 2 if w.dtype == "bf16" else 4)}
+                 "bwd_min_bytes": bwd_min_bytes(w, 2 if w.dtype == "bf16" else 4, args.dt_shared)}
         log(f"[bench] fwd {tf * 1e6:.1f} us, bwd {(float(per.mean()) - tf) * 1e6:.1f} us "
             f"(bwd min bytes {split['bwd_min_bytes'] / 1e6:.1f} MB -> "
             f"{split['bwd_min_bytes'] / (float(per.mean()) - tf) / 1e9:.0f} GB/s)")
 
     elems = w.batch * w.seqlen * w.dim
     s_in = 2 if w.dtype == "bf16" else 4
-    mb = min_bytes(w, s_in)
+    mb = min_bytes(w, s_in, args.dt_shared)
     t_avg = float(per.mean())
     value = elems * args.steps / wall
     slots_pe = alu_slots_per_elem(w, args.disc) + (bwd_alu_slots_per_elem(w) if w.backward else 0)
@@ -399,10 +420,13 @@ def main():
                    "dim": w.dim, "dstate": w.dstate, "in_dtype": w.dtype, "gate": w.gate,
                    "plan": args.plan, "layout": args.layout,
                    "disc": "zoh" if args.disc else "first-order",
+                   "order": "BLD" if args.order else "BDL",
+                   "dt_raw": "shared [B,L]" if args.dt_shared else "per channel",
                    "checkpoints": bool(w.backward and not args.no_ckpt)},
         "roofline": {"bound": "alu", "achieved": alu_achieved, "peak": ALU_PEAK_TSLOTS,
                      "unit": "T VALU-slot/s", "frac": alu_achieved / ALU_PEAK_TSLOTS,
-                     "traffic": measured_traffic(w, args.disc),
+                     "traffic": (None if args.order or args.dt_shared
+                                 else measured_traffic(w, args.disc)),
                      "kernel": ("ss_fwd + ss_bwd step (every kernel of both calls)" if w.backward
                                 else "ss_fwd (scang_kernel, one launch per call)"
                                 if dims_plan_single(ss, dims) else "ss_fwd (all passes)"),

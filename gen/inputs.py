@@ -12,7 +12,8 @@ whose values are exactly representable in bf16 (the low 16 bits are zero): the
 GPU receives those bits, the oracle widens the same values exactly.
 
 Layouts (dense, row-major): x, dt_raw, z, dy: [B, D, L]; Bm, Cm: [B, N, L];
-A: [D, N]; dt_bias, Dskip: [D]; h0, dh_final: [B, D, N].
+A: [D, N]; dt_bias, Dskip: [D]; h0, dh_final: [B, D, N].  With dt_shared, dt_tok [B, L] holds
+one dt_raw value per token and dt_raw is its read-only broadcast over the channels.
 """
 from dataclasses import dataclass, field
 from typing import Optional
@@ -78,6 +79,7 @@ class S6Inputs:
     h0: Optional[np.ndarray] = None
     dy: Optional[np.ndarray] = None
     dh_final: Optional[np.ndarray] = None
+    dt_tok: Optional[np.ndarray] = None  # [B, L] when dt_raw is shared by the channels
     meta: dict = field(default_factory=dict)
 
     def oracle_args(self):
@@ -88,12 +90,13 @@ class S6Inputs:
 def make_inputs(batch: int, seqlen: int, dim: int, dstate: int, *, dtype: str = "f32",
                 seed: int = 0, gate: bool = False, a_perturb: bool = False,
                 with_h0: bool = False, with_dy: bool = False, with_dh_final: bool = False,
-                dt_min: float = 1e-3, dt_max: float = 1e-1) -> S6Inputs:
+                dt_min: float = 1e-3, dt_max: float = 1e-1, dt_shared: bool = False) -> S6Inputs:
     """Draw one seeded case with the benchmark recipe.
 
     x, z ~ N(0,1); dt_raw ~ 0.5*N(0,1); dt ~ logU[dt_min, dt_max] per channel and
     dt_bias = log(expm1(dt)); A[d,n] = -(n+1), times exp(eps) with eps ~ N(0, 0.1^2)
-    per (d,n) when a_perturb; B, C, D ~ N(0,1); h0, dy, dh_final ~ N(0,1).
+    per (d,n) when a_perturb; B, C, D ~ N(0,1); h0, dy, dh_final ~ N(0,1).  dt_shared: dt_raw
+    drawn per token [B, L] (same distribution) and broadcast over the channels.
     """
     if dtype not in ("f32", "bf16"):
         raise ValueError(f"dtype must be 'f32' or 'bf16', got {dtype!r}")
@@ -103,7 +106,12 @@ def make_inputs(batch: int, seqlen: int, dim: int, dstate: int, *, dtype: str = 
     narrow = round_bf16 if dtype == "bf16" else (lambda a: a)
 
     x = narrow(_normal(rng["x"], (Bn, D, L)))
-    dt_raw = narrow(_normal(rng["dt_raw"], (Bn, D, L), 0.5))
+    dt_tok = None
+    if dt_shared:
+        dt_tok = narrow(_normal(rng["dt_raw"], (Bn, L), 0.5))
+        dt_raw = np.broadcast_to(dt_tok[:, None, :], (Bn, D, L))
+    else:
+        dt_raw = narrow(_normal(rng["dt_raw"], (Bn, D, L), 0.5))
     z = narrow(_normal(rng["z"], (Bn, D, L))) if gate else None
 
     log_dt = rng["dt"].uniform(np.log(dt_min), np.log(dt_max), size=D)
@@ -125,8 +133,8 @@ def make_inputs(batch: int, seqlen: int, dim: int, dstate: int, *, dtype: str = 
     dh_final = _normal(rng["dh_final"], (Bn, D, N)) if with_dh_final else None
 
     return S6Inputs(Bn, L, D, N, dtype, x, dt_raw, dt_bias, A, Bm, Cm, Dskip,
-                    z=z, h0=h0, dy=dy, dh_final=dh_final,
-                    meta=dict(seed=seed, gate=gate, a_perturb=a_perturb))
+                    z=z, h0=h0, dy=dy, dh_final=dh_final, dt_tok=dt_tok,
+                    meta=dict(seed=seed, gate=gate, a_perturb=a_perturb, dt_shared=dt_shared))
 
 
 def workload_inputs(w: Workload, **overrides) -> S6Inputs:

@@ -17,7 +17,8 @@
  *   y[b,d,t] = (Σ_n C[b,n,t]·h[n] + Dskip[d]·x[b,d,t]) · silu(z[b,d,t])   (gate optional)
  * with h = h0[b,d,:] (or 0) before t = 0 and h_final[b,d,:] = h after t = L-1.
  *
- * Layouts (dense, row-major, element strides implied by the dims):
+ * Layouts (dense, row-major, element strides implied by the dims; shown for the default
+ * SS_ORDER_BDL and SS_DT_FULL, see ss_order and ss_dt_layout for the others):
  *   x, dt_raw, z, y, dy, dx, ddt_raw, dz : [B, D, L]
  *   Bm, Cm, dB, dC                        : [B, N, L]
  *   A, dA                                 : [D, N]
@@ -53,7 +54,7 @@ extern "C" {
 #endif
 
 #define SS_VERSION_MAJOR 0
-#define SS_VERSION_MINOR 4
+#define SS_VERSION_MINOR 5
 
 /* dtype of x, dt_raw, z, Bm, Cm */
 typedef enum { SS_F32 = 0, SS_BF16 = 1 } ss_dtype;
@@ -69,11 +70,13 @@ typedef enum { SS_PLAN_AUTO = 0, SS_PLAN_SINGLE = 1, SS_PLAN_CHUNKED = 2 } ss_pl
 
 /* Forward lane layout.
  *   SS_LAYOUT_AUTO — chosen from the dims.
- *   SS_LAYOUT_QUAD — the N states of a channel on four lanes (N >= 4, L % 8 == 0).
+ *   SS_LAYOUT_QUAD — the N states of a channel on four lanes (N >= 4; L % 8 == 0 in the
+ *                    channel-major order).
  *   SS_LAYOUT_LANE — one lane per channel; when A[d,n] = -(n+1) exactly for every
  *                    channel of a wavefront, exp(δA) is formed as powers of exp(-δ)
  *                    (checked on the device, otherwise the general path runs).
- *   SS_LAYOUT_OCT  — the N states of a channel on eight lanes (N >= 8, L % 8 == 0).
+ *   SS_LAYOUT_OCT  — the N states of a channel on eight lanes (N >= 8; L % 8 == 0 in the
+ *                    channel-major order).
  * A layout that does not apply to the dims falls back to the widest narrower one that does. */
 typedef enum { SS_LAYOUT_AUTO = 0, SS_LAYOUT_QUAD = 1, SS_LAYOUT_LANE = 2, SS_LAYOUT_OCT = 3 } ss_layout;
 
@@ -83,6 +86,21 @@ typedef enum { SS_LAYOUT_AUTO = 0, SS_LAYOUT_QUAD = 1, SS_LAYOUT_LANE = 2, SS_LA
  *   SS_DISC_ZOH   — B̄x = (exp(δA) - 1)/A · B·x, the exact zero-order hold (forward and
  *                   ss_step; ss_bwd returns SS_ERR_UNSUPPORTED). */
 typedef enum { SS_DISC_EULER = 0, SS_DISC_ZOH = 1 } ss_disc;
+
+/* Memory order of the sequence tensors (the pages write x as (B, L, D)).
+ *   SS_ORDER_BDL — x, dt_raw, z, y, dy, dx, ddt_raw, dz [B, D, L]; B, C, dB, dC [B, N, L].
+ *   SS_ORDER_BLD — token-major: x, dt_raw, z, y, dy, dx, ddt_raw, dz [B, L, D];
+ *                  B, C, dB, dC [B, L, N].
+ * States (h0, h_final, h_ckpt, dh0, dh_final) are [B, D, N] (h_ckpt [B, D, ceil(L/16), N])
+ * in both orders. */
+typedef enum { SS_ORDER_BDL = 0, SS_ORDER_BLD = 1 } ss_order;
+
+/* Shape of dt_raw (page "3.2 선택적 스캔(Selective Scan) 알고리즘과 정보의 압축 및 선별",
+ * §1.2: Δ from a one-output projection of the token, broadcast over the channels).
+ *   SS_DT_FULL   — one value per (batch row, channel, step), in the order above.
+ *   SS_DT_SHARED — one value per (batch row, step): dt_raw and ddt_raw are [B, L] (ss_step:
+ *                  [B]); each channel adds its own dt_bias. */
+typedef enum { SS_DT_FULL = 0, SS_DT_SHARED = 1 } ss_dt_layout;
 
 typedef struct ss_dims {
     int64_t batch;    /* B  >= 1 */
@@ -95,6 +113,8 @@ typedef struct ss_dims {
                          of 16, at most 64); 0 = automatic */
     int32_t layout;   /* ss_layout (forward only) */
     int32_t disc;     /* ss_disc */
+    int32_t order;    /* ss_order */
+    int32_t dt_layout; /* ss_dt_layout */
 } ss_dims;
 
 /* Return codes: 0 on success, negative on error. */
@@ -102,7 +122,7 @@ enum {
     SS_OK = 0,
     SS_ERR_NULL = -1,        /* a required pointer is NULL */
     SS_ERR_DIMS = -2,        /* a dim <= 0, N unsupported, sizes overflow, or bad chunk */
-    SS_ERR_DTYPE = -3,       /* in_dtype, plan, layout or disc not one of the enums */
+    SS_ERR_DTYPE = -3,       /* in_dtype, plan, layout, disc, order or dt_layout not one of the enums */
     SS_ERR_ALIGN = -4,       /* a base pointer is not 16-byte aligned */
     SS_ERR_WORKSPACE = -5,   /* workspace NULL while needed, or workspace_bytes too small */
     SS_ERR_HIP = -6,         /* a HIP call failed; see ss_last_hip_error() */
@@ -151,9 +171,10 @@ int ss_bwd(const ss_dims* dims,
  * row, channel), as in recurrent inference (note "상태공간 모델(SSM)과 Mamba 아키텍처", §2):
  *   δ = softplus(dt_bias + dt_raw);  h ← exp(δ·A)⊙h + δ·B·x;  y = (C·h + Dskip·x)·silu(z)
  *   (with dims->disc = SS_DISC_ZOH the input term is (exp(δA) - 1)/A · B·x)
- *   dims   : batch, dim, dstate, in_dtype, disc as for ss_fwd; seqlen must be 1; plan, chunk
- *            and layout must be 0.
- *   x, dt_raw, z : [B, D] (in_dtype; z NULL = no gate); Bm, Cm : [B, N] (in_dtype);
+ *   dims   : batch, dim, dstate, in_dtype, disc, dt_layout as for ss_fwd; seqlen must be 1;
+ *            plan, chunk and layout must be 0; order is either (one token: the same memory).
+ *   x, z : [B, D] (in_dtype; z NULL = no gate); dt_raw : [B, D], or [B] with SS_DT_SHARED;
+ *   Bm, Cm : [B, N] (in_dtype);
  *   A [D, N], dt_bias [D], Dskip [D] : float32.
  *   h_in   : [B, D, N] float32, the state before the token (required).
  *   h_out  : [B, D, N] float32, the state after it; may equal h_in (the state is updated in

@@ -24,6 +24,8 @@ SS_F32, SS_BF16 = 0, 1
 SS_PLAN_AUTO, SS_PLAN_SINGLE, SS_PLAN_CHUNKED = 0, 1, 2
 SS_LAYOUT_AUTO, SS_LAYOUT_QUAD, SS_LAYOUT_LANE, SS_LAYOUT_OCT = 0, 1, 2, 3
 SS_DISC_EULER, SS_DISC_ZOH = 0, 1
+SS_ORDER_BDL, SS_ORDER_BLD = 0, 1
+SS_DT_FULL, SS_DT_SHARED = 0, 1
 
 ERRORS = {0: "SS_OK", -1: "SS_ERR_NULL", -2: "SS_ERR_DIMS", -3: "SS_ERR_DTYPE", -4: "SS_ERR_ALIGN",
           -5: "SS_ERR_WORKSPACE", -6: "SS_ERR_HIP", -7: "SS_ERR_UNSUPPORTED"}
@@ -35,7 +37,8 @@ EXPORTS = ("ss_fwd", "ss_bwd", "ss_step", "ss_fwd_workspace_size", "ss_bwd_works
 class ss_dims(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("dim", ctypes.c_int64),
                 ("dstate", ctypes.c_int64), ("in_dtype", ctypes.c_int32), ("plan", ctypes.c_int32),
-                ("chunk", ctypes.c_int64), ("layout", ctypes.c_int32), ("disc", ctypes.c_int32)]
+                ("chunk", ctypes.c_int64), ("layout", ctypes.c_int32), ("disc", ctypes.c_int32),
+                ("order", ctypes.c_int32), ("dt_layout", ctypes.c_int32)]
 
 
 class SSError(RuntimeError):
@@ -80,8 +83,9 @@ def load(path: str = LIB):
 
 
 def make_dims(batch, seqlen, dim, dstate, in_dtype=SS_F32, plan=SS_PLAN_AUTO, chunk=0,
-              layout=SS_LAYOUT_AUTO, disc=SS_DISC_EULER):
-    return ss_dims(batch, seqlen, dim, dstate, in_dtype, plan, chunk, layout, disc)
+              layout=SS_LAYOUT_AUTO, disc=SS_DISC_EULER, order=SS_ORDER_BDL, dt_layout=SS_DT_FULL):
+    return ss_dims(batch, seqlen, dim, dstate, in_dtype, plan, chunk, layout, disc, order,
+                   dt_layout)
 
 
 def workspace_size(dims, backward=False) -> int:
@@ -114,9 +118,22 @@ def _check(t, name, shape, dtype, device):
         raise ValueError(f"{name} must be contiguous")
 
 
-def _dims_of(x, A, Bm, plan, chunk, layout=SS_LAYOUT_AUTO, disc=SS_DISC_EULER):
+def _seq_shape(x, order):
+    """(B, D, L) of a sequence tensor in the given order."""
+    if x.dim() != 3:
+        raise ValueError(f"x must be 3-D, got shape {tuple(x.shape)}")
+    if order == SS_ORDER_BDL:
+        return tuple(x.shape)
+    if order == SS_ORDER_BLD:
+        Bn, L, D = x.shape
+        return Bn, D, L
+    raise ValueError(f"order must be SS_ORDER_BDL or SS_ORDER_BLD, got {order}")
+
+
+def _dims_of(x, A, dt_raw, plan, chunk, layout=SS_LAYOUT_AUTO, disc=SS_DISC_EULER,
+             order=SS_ORDER_BDL):
     import torch
-    Bn, D, L = x.shape
+    Bn, D, L = _seq_shape(x, order)
     N = A.shape[1]
     if x.dtype == torch.float32:
         dt = SS_F32
@@ -124,7 +141,8 @@ def _dims_of(x, A, Bm, plan, chunk, layout=SS_LAYOUT_AUTO, disc=SS_DISC_EULER):
         dt = SS_BF16
     else:
         raise ValueError(f"x dtype must be float32 or bfloat16, got {x.dtype}")
-    return make_dims(Bn, L, D, N, dt, plan, chunk, layout, disc)
+    dtl = SS_DT_SHARED if dt_raw.dim() == 2 else SS_DT_FULL
+    return make_dims(Bn, L, D, N, dt, plan, chunk, layout, disc, order, dtl)
 
 
 def _stream(stream):
@@ -133,16 +151,22 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _check_inputs(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, z, h0):
+def _seq(Bn, D, L, order):
+    return (Bn, D, L) if order == SS_ORDER_BDL else (Bn, L, D)
+
+
+def _check_inputs(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, z, h0, order=SS_ORDER_BDL):
+    """Shapes: x, z [B, D, L] ([B, L, D] token-major); dt_raw as x, or [B, L] (one value
+    per token); Bm, Cm [B, N, L] ([B, L, N]); A [D, N]; dt_bias, Dskip [D]; h0 [B, D, N]."""
     import torch
-    Bn, D, L = x.shape
+    Bn, D, L = _seq_shape(x, order)
     N = A.shape[1]
     dev = x.device
     f32 = torch.float32
-    _check(dt_raw, "dt_raw", (Bn, D, L), x.dtype, dev)
-    _check(z, "z", (Bn, D, L), x.dtype, dev)
-    _check(Bm, "Bm", (Bn, N, L), x.dtype, dev)
-    _check(Cm, "Cm", (Bn, N, L), x.dtype, dev)
+    _check(dt_raw, "dt_raw", (Bn, L) if dt_raw.dim() == 2 else _seq(Bn, D, L, order), x.dtype, dev)
+    _check(z, "z", _seq(Bn, D, L, order), x.dtype, dev)
+    _check(Bm, "Bm", _seq(Bn, N, L, order), x.dtype, dev)
+    _check(Cm, "Cm", _seq(Bn, N, L, order), x.dtype, dev)
     _check(A, "A", (D, N), f32, dev)
     _check(dt_bias, "dt_bias", (D,), f32, dev)
     _check(Dskip, "Dskip", (D,), f32, dev)
@@ -156,19 +180,21 @@ CKPT_STEPS = 16
 
 def ss_fwd(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, z=None, h0=None, *, return_final=False,
            return_ckpt=False, y=None, h_final=None, h_ckpt=None, workspace=None,
-           plan=SS_PLAN_AUTO, chunk=0, layout=SS_LAYOUT_AUTO, disc=SS_DISC_EULER, stream=None):
+           plan=SS_PLAN_AUTO, chunk=0, layout=SS_LAYOUT_AUTO, disc=SS_DISC_EULER,
+           order=SS_ORDER_BDL, stream=None):
     """Forward scan through the C ABI.  Returns y, (y, h_final) with return_final, and
     the checkpoints last with return_ckpt (or when h_ckpt is passed).  disc: SS_DISC_EULER
-    (input term δ·B·x) or SS_DISC_ZOH (exact zero-order hold)."""
+    (input term δ·B·x) or SS_DISC_ZOH (exact zero-order hold).  order: SS_ORDER_BDL or
+    SS_ORDER_BLD (token-major x, z, y, Bm, Cm); a 2-D dt_raw [B, L] is one value per token."""
     import torch
     lib = load()
-    _check_inputs(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, z, h0)
-    dims = _dims_of(x, A, Bm, plan, chunk, layout, disc)
-    Bn, D, L = x.shape
+    _check_inputs(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, z, h0, order)
+    dims = _dims_of(x, A, dt_raw, plan, chunk, layout, disc, order)
+    Bn, D, L = _seq_shape(x, order)
     N = A.shape[1]
     if y is None:
-        y = torch.empty((Bn, D, L), dtype=torch.float32, device=x.device)
-    _check(y, "y", (Bn, D, L), torch.float32, x.device)
+        y = torch.empty(_seq(Bn, D, L, order), dtype=torch.float32, device=x.device)
+    _check(y, "y", _seq(Bn, D, L, order), torch.float32, x.device)
     if return_final and h_final is None:
         h_final = torch.empty((Bn, D, N), dtype=torch.float32, device=x.device)
     _check(h_final, "h_final", (Bn, D, N), torch.float32, x.device)
@@ -194,23 +220,26 @@ def ss_fwd(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, z=None, h0=None, *, return_fina
 
 
 def ss_bwd(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, dy, z=None, h0=None, dh_final=None, *,
-           h_ckpt=None, workspace=None, chunk=0, out=None, stream=None):
+           h_ckpt=None, workspace=None, chunk=0, order=SS_ORDER_BDL, out=None, stream=None):
     """Backward through the C ABI.  Returns a dict dx, ddt_raw, ddt_bias, dA, dB, dC, dD,
-    dz (None without gate), dh0 (None without h0); all float32.  h_ckpt: the checkpoints
-    of an ss_fwd call on the same inputs (optional)."""
+    dz (None without gate), dh0 (None without h0); all float32, each shaped like its input
+    (order as in ss_fwd).  h_ckpt: the checkpoints of an ss_fwd call on the same inputs
+    (optional)."""
     import torch
     lib = load()
-    _check_inputs(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, z, h0)
-    dims = _dims_of(x, A, Bm, SS_PLAN_CHUNKED, chunk)
-    Bn, D, L = x.shape
+    _check_inputs(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, z, h0, order)
+    dims = _dims_of(x, A, dt_raw, SS_PLAN_CHUNKED, chunk, order=order)
+    Bn, D, L = _seq_shape(x, order)
     N = A.shape[1]
     dev = x.device
     f32 = torch.float32
-    _check(dy, "dy", (Bn, D, L), f32, dev)
+    sq = _seq(Bn, D, L, order)
+    _check(dy, "dy", sq, f32, dev)
     _check(dh_final, "dh_final", (Bn, D, N), f32, dev)
     _check(h_ckpt, "h_ckpt", (Bn, D, (L + CKPT_STEPS - 1) // CKPT_STEPS, N), f32, dev)
-    shapes = dict(dx=(Bn, D, L), ddt_raw=(Bn, D, L), ddt_bias=(D,), dA=(D, N), dB=(Bn, N, L),
-                  dC=(Bn, N, L), dD=(D,), dz=(Bn, D, L), dh0=(Bn, D, N))
+    shapes = dict(dx=sq, ddt_raw=tuple(dt_raw.shape), ddt_bias=(D,), dA=(D, N),
+                  dB=_seq(Bn, N, L, order), dC=_seq(Bn, N, L, order), dD=(D,), dz=sq,
+                  dh0=(Bn, D, N))
     g = {} if out is None else dict(out)
     for k, shp in shapes.items():
         if (k == "dz" and z is None) or (k == "dh0" and h0 is None):
@@ -235,7 +264,8 @@ def ss_bwd(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, dy, z=None, h0=None, dh_final=N
 
 def ss_step(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, h, z=None, *, h_out=None, y=None,
             disc=SS_DISC_EULER, stream=None):
-    """One decode step through the C ABI: x, dt_raw, z [B, D]; Bm, Cm [B, N]; h [B, D, N]
+    """One decode step through the C ABI: x, z [B, D]; dt_raw [B, D] or [B] (one value per
+    token); Bm, Cm [B, N]; h [B, D, N]
     float32, the state before the token.  The state after it goes to h_out (default: h
     itself, updated in place).  Returns y [B, D] float32."""
     import torch
@@ -253,7 +283,7 @@ def ss_step(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, h, z=None, *, h_out=None, y=No
     else:
         raise ValueError(f"x dtype must be float32 or bfloat16, got {x.dtype}")
     _check(x, "x", (Bn, D), x.dtype, dev)
-    _check(dt_raw, "dt_raw", (Bn, D), x.dtype, dev)
+    _check(dt_raw, "dt_raw", (Bn,) if dt_raw.dim() == 1 else (Bn, D), x.dtype, dev)
     _check(z, "z", (Bn, D), x.dtype, dev)
     _check(Bm, "Bm", (Bn, N), x.dtype, dev)
     _check(Cm, "Cm", (Bn, N), x.dtype, dev)
@@ -267,7 +297,8 @@ def ss_step(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, h, z=None, *, h_out=None, y=No
     if y is None:
         y = torch.empty((Bn, D), dtype=f32, device=dev)
     _check(y, "y", (Bn, D), f32, dev)
-    dims = make_dims(Bn, 1, D, N, dt, disc=disc)
+    dims = make_dims(Bn, 1, D, N, dt, disc=disc,
+                     dt_layout=SS_DT_SHARED if dt_raw.dim() == 1 else SS_DT_FULL)
     rc = lib.ss_step(ctypes.byref(dims), _ptr(x), _ptr(dt_raw), _ptr(dt_bias), _ptr(A), _ptr(Bm),
                      _ptr(Cm), _ptr(Dskip), _ptr(z), _ptr(h), _ptr(h_out), _ptr(y), _stream(stream))
     if rc != 0:

@@ -24,6 +24,17 @@ int hip_fail(hipError_t e) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Rows of a [B, D, L] (channel-major) or [B, L, D] (token-major) tensor: element (b, d, t) at
+// b·sb + d·sd + t·ts.
+ss::DtRows seq_rows(const ss::Plan& p) {
+    return p.tok ? ss::DtRows{p.L * p.D, 1, p.D} : ss::DtRows{p.D * p.L, p.L, 1};
+}
+
+// Rows of dt_raw: as the sequence tensors, or one value per token [B, L] shared by channels.
+ss::DtRows dt_rows(const ss::Plan& p) {
+    return p.dt_shared ? ss::DtRows{p.L, 0, 1} : seq_rows(p);
+}
+
 }  // namespace
 
 extern "C" {
@@ -91,14 +102,15 @@ int ss_fwd(const ss_dims* dims, const void* x, const void* dt_raw, const float* 
     float* BC = nullptr;
     if (!p.group) {
         BC = reinterpret_cast<float*>(ws + p.off_bc);
-        e = ss::launch_bc_stage(bf16, int(p.N), Bm, Cm, BC, p.B, p.L, stream);
+        e = ss::launch_bc_stage(bf16, int(p.N), Bm, Cm, BC, p.B, p.L, p.tok, stream);
         if (e != hipSuccess) return hip_fail(e);
     }
 
     ss::ScanLaunch s{};
     s.x = x; s.dt_raw = dt_raw; s.z = z; s.dt_bias = dt_bias; s.A = A; s.Dskip = Dskip; s.BC = BC;
     s.Bm = Bm; s.Cm = Cm;
-    s.B = p.B; s.L = p.L; s.D = p.D; s.vec = p.vec; s.zoh = p.zoh;
+    s.B = p.B; s.L = p.L; s.D = p.D; s.vec = p.vec; s.zoh = p.zoh; s.tok = p.tok;
+    s.dtr = dt_rows(p);
     if (!p.chunked) {
         s.chunk = p.L; s.K = 1; s.h_init = h0; s.y = y; s.h_last = h_final; s.h_ckpt = h_ckpt; s.agg = 0;
         s.d4 = p.d4; s.nb4 = p.nb4;
@@ -149,6 +161,7 @@ int ss_step(const ss_dims* dims, const void* x, const void* dt_raw, const float*
     s.x = x; s.dt_raw = dt_raw; s.z = z; s.dt_bias = dt_bias; s.A = A; s.Bm = Bm; s.Cm = Cm;
     s.Dskip = Dskip; s.h_in = h_in; s.h_out = h_out; s.y = y; s.B = p.B; s.D = p.D; s.N = int(p.N);
     s.zoh = p.zoh;
+    s.dt_shared = p.dt_shared;
     const hipError_t e = ss::launch_step(p.in_dtype == SS_BF16, s, stream);
     if (e != hipSuccess) return hip_fail(e);
     return SS_OK;
@@ -196,6 +209,17 @@ int ss_bwd(const ss_dims* dims, const void* x, const void* dt_raw, const float* 
     bl.ddt_bias = ddt_bias;
     bl.B = p.B; bl.L = p.L; bl.D = p.D; bl.N = p.N; bl.chunk = p.chunk; bl.K = int(p.K);
     bl.vec = p.vec;
+    bl.tok = p.tok;
+    bl.dtr = dt_rows(p);
+    bl.gdr = seq_rows(p);
+    bl.ddt_shared = nullptr;
+    bl.ddt_blk = nullptr;
+    if (p.dt_shared) {
+        // the final pass sums each 64-channel block; the reduction sums the blocks
+        bl.ddt_raw = nullptr;
+        bl.ddt_shared = ddt_raw;
+        bl.ddt_blk = reinterpret_cast<float*>(ws + p.off_ddt);
+    }
     // 1. chunk aggregates (forward and reverse pairs)
     bl.stage = 0;
     e = ss::launch_bwd(bf16, bl, stream);

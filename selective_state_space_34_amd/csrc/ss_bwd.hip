@@ -83,36 +83,38 @@ struct Vec {
     }
 };
 
-// 4 consecutive elements [t, t+4) of a row, zero past t_end; vector load when full and aligned
+// Elements [t, t+4) of a channel's row, element t at p[t·ts] (ts = 1: channel-major,
+// ts = D: token-major), zero past t_end; one vector access when the four are contiguous,
+// in range and aligned (vec: rows start on 8-element boundaries)
 __device__ __forceinline__ void load4(const float* __restrict__ p, int64_t t, int64_t t_end, int vec,
-                                      float (&o)[4]) {
-    if (vec && t + 4 <= t_end) {
+                                      int64_t ts, float (&o)[4]) {
+    if (vec && ts == 1 && t + 4 <= t_end) {
         const float4 v = *reinterpret_cast<const float4*>(p + t);
         o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
     } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) o[i] = (t + i < t_end) ? p[t + i] : 0.0f;
+        for (int i = 0; i < 4; ++i) o[i] = (t + i < t_end) ? p[(t + i) * ts] : 0.0f;
     }
 }
 __device__ __forceinline__ void load4(const bf16_t* __restrict__ p, int64_t t, int64_t t_end, int vec,
-                                      float (&o)[4]) {
-    if (vec && t + 4 <= t_end) {
+                                      int64_t ts, float (&o)[4]) {
+    if (vec && ts == 1 && t + 4 <= t_end) {
         const uint2 v = *reinterpret_cast<const uint2*>(p + t);
         o[0] = __uint_as_float(v.x << 16); o[1] = __uint_as_float(v.x & 0xffff0000u);
         o[2] = __uint_as_float(v.y << 16); o[3] = __uint_as_float(v.y & 0xffff0000u);
     } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) o[i] = (t + i < t_end) ? to_f32(p[t + i]) : 0.0f;
+        for (int i = 0; i < 4; ++i) o[i] = (t + i < t_end) ? to_f32(p[(t + i) * ts]) : 0.0f;
     }
 }
 __device__ __forceinline__ void store4(float* __restrict__ p, int64_t t, int64_t t_end, int vec,
-                                       const float (&v)[4]) {
-    if (vec && t + 4 <= t_end) {
+                                       int64_t ts, const float (&v)[4]) {
+    if (vec && ts == 1 && t + 4 <= t_end) {
         *reinterpret_cast<float4*>(p + t) = make_float4(v[0], v[1], v[2], v[3]);
     } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            if (t + i < t_end) p[t + i] = v[i];
+            if (t + i < t_end) p[(t + i) * ts] = v[i];
     }
 }
 
@@ -121,13 +123,14 @@ __device__ __forceinline__ void store4(float* __restrict__ p, int64_t t, int64_t
 template <typename T> struct In4;
 template <> struct In4<bf16_t> {
     uint2 v;
-    __device__ __forceinline__ void load(const bf16_t* __restrict__ p, int64_t t, int64_t t_end, int vec) {
-        if (vec && t + 4 <= t_end) {
+    __device__ __forceinline__ void load(const bf16_t* __restrict__ p, int64_t t, int64_t t_end, int vec,
+                                         int64_t ts) {
+        if (vec && ts == 1 && t + 4 <= t_end) {
             v = *reinterpret_cast<const uint2*>(p + t);
         } else {
             uint32_t e[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) e[i] = (t + i < t_end) ? p[t + i].bits : 0u;
+            for (int i = 0; i < 4; ++i) e[i] = (t + i < t_end) ? p[(t + i) * ts].bits : 0u;
             v = make_uint2(e[0] | (e[1] << 16), e[2] | (e[3] << 16));
         }
     }
@@ -138,14 +141,15 @@ template <> struct In4<bf16_t> {
 };
 template <> struct In4<float> {
     float4 v;
-    __device__ __forceinline__ void load(const float* __restrict__ p, int64_t t, int64_t t_end, int vec) {
-        if (vec && t + 4 <= t_end) {
+    __device__ __forceinline__ void load(const float* __restrict__ p, int64_t t, int64_t t_end, int vec,
+                                         int64_t ts) {
+        if (vec && ts == 1 && t + 4 <= t_end) {
             v = *reinterpret_cast<const float4*>(p + t);
         } else {
-            v.x = (t < t_end) ? p[t] : 0.0f;
-            v.y = (t + 1 < t_end) ? p[t + 1] : 0.0f;
-            v.z = (t + 2 < t_end) ? p[t + 2] : 0.0f;
-            v.w = (t + 3 < t_end) ? p[t + 3] : 0.0f;
+            v.x = (t < t_end) ? p[t * ts] : 0.0f;
+            v.y = (t + 1 < t_end) ? p[(t + 1) * ts] : 0.0f;
+            v.z = (t + 2 < t_end) ? p[(t + 2) * ts] : 0.0f;
+            v.w = (t + 3 < t_end) ? p[(t + 3) * ts] : 0.0f;
         }
     }
     __device__ __forceinline__ void decode(float (&o)[4]) const {
@@ -153,21 +157,25 @@ template <> struct In4<float> {
     }
 };
 
-// B and C of steps [t0, t0 + nsteps) of batch row b, from the [B, Nr, L] inputs into LDS as
-// [step][B_0 .. B_{NP-1} | C_0 .. C_{NP-1}] float32 with row stride R; zero for steps past
-// nsteps (up to kBMaxSteps) and states past Nr.  Lanes run along L: coalesced reads.
+// B and C of steps [t0, t0 + nsteps) of batch row b, from the [B, Nr, L] (token-major:
+// [B, L, Nr]) inputs into LDS as [step][B_0 .. B_{NP-1} | C_0 .. C_{NP-1}] float32 with row
+// stride R; zero for steps past nsteps (up to kBMaxSteps) and states past Nr.  Lanes run
+// along the contiguous dimension: coalesced reads.
 template <typename Tin, int NP>
 __device__ __forceinline__ void load_chunk_bc(float* __restrict__ lds, const Tin* __restrict__ Bm,
                                               const Tin* __restrict__ Cm, int b, int Nr, int64_t L,
-                                              int64_t t0, int nsteps, int tid) {
+                                              int64_t t0, int nsteps, int tid, int tok) {
     constexpr int R = 2 * NP + 4;
     constexpr int total = 2 * NP * kBMaxSteps;
     for (int e = tid; e < total; e += kBThreads) {
-        const int t = e % kBMaxSteps;
-        const int n = (e / kBMaxSteps) % NP;
+        const int t = tok ? (e / NP) % kBMaxSteps : e % kBMaxSteps;
+        const int n = tok ? e % NP : (e / kBMaxSteps) % NP;
         const int m = e / (kBMaxSteps * NP);
         float v = 0.0f;
-        if (n < Nr && t < nsteps) v = to_f32((m ? Cm : Bm)[(int64_t(b) * Nr + n) * L + t0 + t]);
+        if (n < Nr && t < nsteps) {
+            const int64_t i = tok ? (int64_t(b) * L + t0 + t) * Nr + n : (int64_t(b) * Nr + n) * L + t0 + t;
+            v = to_f32((m ? Cm : Bm)[i]);
+        }
         lds[t * R + m * NP + n] = v;
     }
 }
@@ -183,7 +191,7 @@ __global__ __launch_bounds__(kBThreads) void bwd_agg_kernel(
     const float* __restrict__ dy, const float* __restrict__ dt_bias, const float* __restrict__ A,
     const Tin* __restrict__ Bm, const Tin* __restrict__ Cm, float* __restrict__ h_end,
     float* __restrict__ rev_end, float* __restrict__ dsum_out, int64_t L, int64_t D, int Nr,
-    int64_t chunk, int K, int vec) {
+    int64_t chunk, int K, int vec, int tok, DtRows dtr) {
     constexpr int NP = 4 * S;
     constexpr int R = 2 * NP + 4;
     __shared__ __align__(16) float bc_lds[kBMaxSteps * R];
@@ -200,7 +208,7 @@ __global__ __launch_bounds__(kBThreads) void bwd_agg_kernel(
     const int64_t t1c = (t0c + chunk < L) ? t0c + chunk : L;
     const int nsteps = int(t1c - t0c);
     const int ntiles = (nsteps + kBT - 1) / kBT;
-    load_chunk_bc<Tin, NP>(bc_lds, Bm, Cm, b, Nr, L, t0c, nsteps, tid);
+    load_chunk_bc<Tin, NP>(bc_lds, Bm, Cm, b, Nr, L, t0c, nsteps, tid, tok);
 
     float A2[S], h[S], P[S], Rv[S];
 #pragma unroll
@@ -210,7 +218,10 @@ __global__ __launch_bounds__(kBThreads) void bwd_agg_kernel(
         h[s] = 0.0f; P[s] = 1.0f; Rv[s] = 0.0f;
     }
     const float bias = dt_bias[d];
-    const int64_t row = (int64_t(b) * D + d) * L;
+    // element t of channel (b, d) at row[t·ts]; Δraw at its own rows
+    const int64_t row = tok ? int64_t(b) * L * D + d : (int64_t(b) * D + d) * L;
+    const int64_t ts = tok ? D : 1;
+    const Tin* drr = dt_raw + int64_t(b) * dtr.sb + d * dtr.sd;
     float* myrow = rows + (tid >> 6) * 16 * kRW + (lane >> 2) * kRW;
     float dsum = 0.0f;
     __syncthreads();
@@ -219,10 +230,10 @@ __global__ __launch_bounds__(kBThreads) void bwd_agg_kernel(
         const int tb = tile * kBT;
         const int64_t te = t0c + tb + kBPer * j;
         float xv[4], dv[4], gv[4], zv[4];
-        load4(x + row, te, t1c, vec, xv);
-        load4(dt_raw + row, te, t1c, vec, dv);
-        load4(dy + row, te, t1c, vec, gv);
-        if (kGate) load4(z + row, te, t1c, vec, zv);
+        load4(x + row, te, t1c, vec, ts, xv);
+        load4(drr, te, t1c, vec, dtr.ts, dv);
+        load4(dy + row, te, t1c, vec, ts, gv);
+        if (kGate) load4(z + row, te, t1c, vec, ts, zv);
 #pragma unroll
         for (int i = 0; i < kBPer; ++i) {
             const bool ok = te + i < t1c;
@@ -289,8 +300,8 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     const float* __restrict__ Dskip, const Tin* __restrict__ Bm, const Tin* __restrict__ Cm,
     const float* __restrict__ h_ckpt, float* h_start, const float* __restrict__ q,
     float* __restrict__ dxo, float* __restrict__ ddto, float* __restrict__ dzo,
-    float* __restrict__ dbc_part, float* __restrict__ ddt_part, int64_t L, int64_t D, int Nr,
-    int64_t chunk, int K, int vec) {
+    float* __restrict__ dbc_part, float* __restrict__ ddt_part, float* __restrict__ ddt_blk,
+    int64_t L, int64_t D, int Nr, int64_t chunk, int K, int vec, int tok, DtRows dtr, DtRows gdr) {
     constexpr int NP = 4 * S;
     constexpr int R = 2 * NP + 4;
     // steps per reverse batch = steps a lane prepares: batch bi is lane bi's steps, so the
@@ -330,9 +341,14 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     const int64_t sidx = ((int64_t(b) * D + d) * K + k) * Nr;
     const float bias = dt_bias[d];
     const float Dd = Dskip[d];
-    const int64_t row = (int64_t(b) * D + d) * L;
+    // element t of channel (b, d) at row[t·ts] for x, z, dy, dx, dz; Δraw and its gradient
+    // at their own rows (dtr, gdr)
+    const int64_t row = tok ? int64_t(b) * L * D + d : (int64_t(b) * D + d) * L;
+    const int64_t ts = tok ? D : 1;
     const Tin* xr = x + row;
-    const Tin* drr = dt_raw + row;
+    const Tin* drr = dt_raw + int64_t(b) * dtr.sb + d * dtr.sd;
+    const int64_t dts = dtr.ts;
+    float* ddr = ddto + int64_t(b) * gdr.sb + d * gdr.sd;
     const Tin* zr = kGate ? z + row : nullptr;
     const float* gr = dy + row;
     // checkpoints of this channel: tile tt of the chunk starts at checkpoint (t0c / 16) + tt
@@ -345,17 +361,17 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     float ckn[S];                               // next tile's start state (kCk)
     auto load_tile = [&](int tt) {
         const int64_t tl = t0c + tt * kBT + kBPer * j;
-        bx.load(xr, tl, t1c, vec);
-        bd.load(drr, tl, t1c, vec);
-        bg.load(gr, tl, t1c, vec);
-        if (kGate) bz.load(zr, tl, t1c, vec);
+        bx.load(xr, tl, t1c, vec, ts);
+        bd.load(drr, tl, t1c, vec, dts);
+        bg.load(gr, tl, t1c, vec, ts);
+        if (kGate) bz.load(zr, tl, t1c, vec, ts);
         if (kCk) {
 #pragma unroll
             for (int s = 0; s < S; ++s) ckn[s] = (n0 + s < Nr) ? ckr[tt * Nr + n0 + s] : 0.0f;
         }
     };
     if (kCk) load_tile(ntiles - 1);
-    load_chunk_bc<Tin, NP>(bc_lds, Bm, Cm, b, Nr, L, t0c, nsteps, tid);
+    load_chunk_bc<Tin, NP>(bc_lds, Bm, Cm, b, Nr, L, t0c, nsteps, tid, tok);
     float A2[S], An[S], g[S], dA[S];
     float ck[kCk ? 1 : kBMaxTiles][S];          // state entering each tile (uniform index)
 #pragma unroll
@@ -374,8 +390,8 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     if constexpr (!kCk) {
         // ---- forward sweep: the state entering every tile but the first ----
         In4<Tin> ax, ad;
-        ax.load(xr, t0c + kBPer * j, t1c, vec);
-        ad.load(drr, t0c + kBPer * j, t1c, vec);
+        ax.load(xr, t0c + kBPer * j, t1c, vec, ts);
+        ad.load(drr, t0c + kBPer * j, t1c, vec, dts);
         float h[S];
 #pragma unroll
         for (int s = 0; s < S; ++s) h[s] = ck[0][s];
@@ -387,8 +403,8 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
             ad.decode(dv);
             if (tile + 2 < ntiles) {
                 const int64_t ta = t0c + tb + kBT + kBPer * j;
-                ax.load(xr, ta, t1c, vec);
-                ad.load(drr, ta, t1c, vec);
+                ax.load(xr, ta, t1c, vec, ts);
+                ad.load(drr, ta, t1c, vec, dts);
             }
 #pragma unroll
             for (int i = 0; i < kBPer; ++i) {
@@ -507,7 +523,7 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
                 const float sv = fmaf(Dd, xv[i], stot[i]);
                 dzv[i] = gv[i] * sv * sz[i] * fmaf(zv[i], 1.0f - sz[i], 1.0f);
             }
-            if (valid) store4(dzo + row, te, t1c, vec, dzv);
+            if (valid) store4(dzo + row, te, t1c, vec, ts, dzv);
             wave_sync();
         }
 
@@ -592,8 +608,10 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
             wave_sync();
         }
 
-        // dx, dΔraw of the lane's own 4 steps, from the rows
-        if (valid) {
+        // dx, dΔraw of the lane's own 4 steps, from the rows.  A Δraw shared by the channels
+        // (ddt_blk) takes the sum over the block's channels instead: each wave parks its 16
+        // channels' values in its own exchange area (its sweep is over), summed below.
+        {
             float ox[4], od[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -601,12 +619,25 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
                 ox[i] = v.x;
                 od[i] = v.y;
             }
-            store4(dxo + row, te, t1c, vec, ox);
-            store4(ddto + row, te, t1c, vec, od);
+            if (valid) store4(dxo + row, te, t1c, vec, ts, ox);
+            if (ddt_blk) {
+                *reinterpret_cast<float4*>(wx + (lane >> 2) * kBT + kBPer * j) =
+                    valid ? make_float4(od[0], od[1], od[2], od[3]) : make_float4(0.f, 0.f, 0.f, 0.f);
+            } else if (valid) {
+                store4(ddr, te, t1c, vec, gdr.ts, od);
+            }
         }
 
         // dB|dC of the tile: the four waves' sums meet once per tile
         __syncthreads();
+        if (ddt_blk && tid < kBT) {
+            // Σ over the block's 64 channels of dΔraw at step tb + tid
+            float sdt = 0.0f;
+            for (int w = 0; w < 4; ++w)
+                for (int cl = 0; cl < 16; ++cl) sdt += xch[w * 64 * LS + cl * kBT + tid];
+            const int64_t t = t0c + tb + tid;
+            if (t < t1c) ddt_blk[(int64_t(b) * NB + blockIdx.x) * L + t] = sdt;
+        }
         for (int e = tid; e < OUTW; e += kBThreads) {
             const int st = e / (2 * NP);
             const int v = e % (2 * NP);
@@ -638,12 +669,13 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
 // ---------------------------------------------------------------------------------------
 // 4. reductions
 // ---------------------------------------------------------------------------------------
-// dB | dC: part [B, NB, L, 2N] summed over NB -> dB, dC [B, N, L].  One thread per (t, v)
-// of a batch row: reads are coalesced across threads, the sum runs over the channel blocks.
+// dB | dC: part [B, NB, L, 2N] summed over NB -> dB, dC [B, N, L] (token-major: [B, L, N]).
+// One thread per (t, v) of a batch row: reads are coalesced across threads, the sum runs over
+// the channel blocks.
 __global__ __launch_bounds__(256) void bwd_reduce_bc_kernel(const float* __restrict__ part,
                                                             float* __restrict__ dB,
                                                             float* __restrict__ dC, int64_t L,
-                                                            int NB, int Nr) {
+                                                            int NB, int Nr, int tok) {
     const int R = 2 * Nr;
     const int b = blockIdx.y;
     const int64_t f = int64_t(blockIdx.x) * 256 + threadIdx.x;
@@ -654,8 +686,25 @@ __global__ __launch_bounds__(256) void bwd_reduce_bc_kernel(const float* __restr
     for (int gi = 0; gi < NB; ++gi) acc += p[int64_t(gi) * LR];
     const int64_t t = f / R;
     const int v = int(f % R);
-    float* out = (v < Nr) ? dB + (int64_t(b) * Nr + v) * L : dC + (int64_t(b) * Nr + v - Nr) * L;
-    out[t] = acc;
+    const int n = v < Nr ? v : v - Nr;
+    float* out = v < Nr ? dB : dC;
+    out[tok ? (int64_t(b) * L + t) * Nr + n : (int64_t(b) * Nr + n) * L + t] = acc;
+}
+
+// Δraw shared by the channels (one value per token): its gradient [B, L] is the sum over
+// channels of the per-channel gradients, which the final pass has already summed over each
+// block of 64 channels: part [B, NB, L] summed over NB.  One thread per (b, t), coalesced
+// across t.
+__global__ __launch_bounds__(256) void bwd_reduce_dt_kernel(const float* __restrict__ part,
+                                                            float* __restrict__ out, int NB,
+                                                            int64_t L) {
+    const int b = blockIdx.y;
+    const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    if (t >= L) return;
+    const float* p = part + int64_t(b) * NB * L + t;
+    float acc = 0.0f;
+    for (int gi = 0; gi < NB; ++gi) acc += p[int64_t(gi) * L];
+    out[int64_t(b) * L + t] = acc;
 }
 
 // dA [D, N] = Σ_{b,k} part[b,d,k,n];  dD, ddt_bias [D] = Σ_{b,k} ddt_part[b,d,k,0|1].
@@ -724,27 +773,19 @@ static void launch_bwd_g(const BwdLaunch& p, dim3 grid, hipStream_t s) {
     const Tin* z = static_cast<const Tin*>(p.z);
     const Tin* Bm = static_cast<const Tin*>(p.Bm);
     const Tin* Cm = static_cast<const Tin*>(p.Cm);
-    if (p.stage == 0) {
-        if (p.h_ckpt)
-            hipLaunchKernelGGL((bwd_agg_kernel<Tin, S, kGate, false>), grid, dim3(kBThreads), 0, s, x, dr,
-                               z, p.dy, p.dt_bias, p.A, Bm, Cm, p.h_end, p.rev_end, p.dsum, p.L, p.D,
-                               int(p.N), p.chunk, p.K, p.vec);
+    with_bool(p.h_ckpt != nullptr, [&](auto ck) {
+        if (p.stage == 0)
+            hipLaunchKernelGGL((bwd_agg_kernel<Tin, S, kGate, !ck.value>), grid, dim3(kBThreads), 0,
+                               s, x, dr, z, p.dy, p.dt_bias, p.A, Bm, Cm, p.h_end, p.rev_end, p.dsum,
+                               p.L, p.D, int(p.N), p.chunk, p.K, p.vec, p.tok, p.dtr);
         else
-            hipLaunchKernelGGL((bwd_agg_kernel<Tin, S, kGate, true>), grid, dim3(kBThreads), 0, s, x, dr,
-                               z, p.dy, p.dt_bias, p.A, Bm, Cm, p.h_end, p.rev_end, p.dsum, p.L, p.D,
-                               int(p.N), p.chunk, p.K, p.vec);
-    } else {
-        if (p.h_ckpt)
-            hipLaunchKernelGGL((bwd_chunk_kernel<Tin, S, kGate, true>), grid, dim3(kBThreads), 0, s, x, dr,
-                               z, p.dy, p.dt_bias, p.A, p.Dskip, Bm, Cm, p.h_ckpt, p.h_end, p.rev_end,
-                               p.dx, p.ddt_raw, p.dz, p.dbc_part, p.ddt_part, p.L, p.D, int(p.N),
-                               p.chunk, p.K, p.vec);
-        else
-            hipLaunchKernelGGL((bwd_chunk_kernel<Tin, S, kGate, false>), grid, dim3(kBThreads), 0, s, x, dr,
-                               z, p.dy, p.dt_bias, p.A, p.Dskip, Bm, Cm, p.h_ckpt, p.h_end, p.rev_end,
-                               p.dx, p.ddt_raw, p.dz, p.dbc_part, p.ddt_part, p.L, p.D, int(p.N),
-                               p.chunk, p.K, p.vec);
-    }
+            hipLaunchKernelGGL((bwd_chunk_kernel<Tin, S, kGate, ck.value>), grid, dim3(kBThreads), 0,
+                               s, x, dr, z, p.dy, p.dt_bias, p.A, p.Dskip, Bm, Cm, p.h_ckpt, p.h_end,
+                               p.rev_end, p.dx, p.ddt_raw, p.dz, p.dbc_part, p.ddt_part,
+                               p.ddt_shared ? p.ddt_blk : nullptr, p.L, p.D, int(p.N), p.chunk,
+                               p.K, p.vec, p.tok, p.dtr, p.gdr);
+        return hipSuccess;
+    });
 }
 
 template <typename Tin, int S>
@@ -779,9 +820,15 @@ hipError_t launch_bwd_reduce(const BwdLaunch& p, hipStream_t s) {
     const int NB = int((p.D + kBChan - 1) / kBChan);
     const int64_t LR = p.L * 2 * p.N;
     hipLaunchKernelGGL(bwd_reduce_bc_kernel, dim3(unsigned((LR + 255) / 256), unsigned(p.B)), dim3(256),
-                       0, s, p.dbc_part, p.dB, p.dC, p.L, NB, int(p.N));
+                       0, s, p.dbc_part, p.dB, p.dC, p.L, NB, int(p.N), p.tok);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (p.ddt_shared) {
+        hipLaunchKernelGGL(bwd_reduce_dt_kernel, dim3(unsigned((p.L + 255) / 256), unsigned(p.B)),
+                           dim3(256), 0, s, p.ddt_blk, p.ddt_shared, NB, p.L);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     hipLaunchKernelGGL(bwd_reduce_params_kernel, dim3(unsigned(p.D)), dim3(256), 0, s, p.h_end,
                        p.ddt_part, p.dA, p.dD, p.ddt_bias, p.D, int(p.N), int(p.B), p.K);
     return hipGetLastError();

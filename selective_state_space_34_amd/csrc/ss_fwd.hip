@@ -25,13 +25,14 @@
 namespace ss {
 
 // ---------------------------------------------------------------------------------------
-// B, C [B, N, L] (in dtype) -> BC [B, L, 2N] float32: row t holds B[:, t] then C[:, t].
-// A 256-thread block stages a 64-step tile through LDS so both sides are coalesced.
+// B, C [B, N, L] (or token-major [B, L, N]; in dtype) -> BC [B, L, 2N] float32: row t
+// holds B[:, t] then C[:, t].  A 256-thread block stages a 64-step tile through LDS so both
+// sides are coalesced.
 // ---------------------------------------------------------------------------------------
 template <typename Tin, int N>
 __global__ __launch_bounds__(256) void bc_stage_kernel(const Tin* __restrict__ Bm,
                                                        const Tin* __restrict__ Cm,
-                                                       float* __restrict__ BC, int64_t L) {
+                                                       float* __restrict__ BC, int64_t L, int tok) {
     constexpr int TT = 64;
     constexpr int R = 2 * N;  // rows of the tile
     __shared__ float tile[R][TT + 1];
@@ -39,13 +40,14 @@ __global__ __launch_bounds__(256) void bc_stage_kernel(const Tin* __restrict__ B
     const int64_t t0 = int64_t(blockIdx.x) * TT;
     const int tid = threadIdx.x;
     for (int e = tid; e < R * TT; e += 256) {
-        const int r = e / TT, c = e % TT;
+        // channel-major: steps fastest across threads; token-major: states fastest
+        const int r = tok ? e % R : e / TT, c = tok ? e / R : e % TT;
         const int64_t t = t0 + c;
         float v = 0.0f;
         if (t < L) {
             const Tin* src = (r < N) ? Bm : Cm;
             const int n = (r < N) ? r : r - N;
-            v = to_f32(src[(int64_t(b) * N + n) * L + t]);
+            v = to_f32(src[tok ? (int64_t(b) * L + t) * N + n : (int64_t(b) * N + n) * L + t]);
         }
         tile[r][c] = v;
     }
@@ -69,7 +71,7 @@ __global__ __launch_bounds__(256) void scan_kernel(
     const float* __restrict__ Dskip, const float* __restrict__ BC,
     const float* __restrict__ h_init, float* __restrict__ y, float* __restrict__ h_last,
     float* __restrict__ h_ckpt, float* __restrict__ dsum_out, int64_t L, int64_t D,
-    int64_t chunk, int K, int vec) {
+    int64_t chunk, int K, int vec, int tok, DtRows dtr) {
     const int64_t d = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     const int k = blockIdx.y;
     const int b = blockIdx.z;
@@ -90,11 +92,17 @@ __global__ __launch_bounds__(256) void scan_kernel(
 
     const float bias = dt_bias[d];
     const float Dd = kAgg ? 0.0f : Dskip[d];
-    const int64_t row = (int64_t(b) * D + d) * L;
+    // element t of x, z, y at row[t·ts] (channel-major rows, or token-major with a wave's
+    // 64 channels side by side); Δraw at its own rows
+    const int64_t row = tok ? int64_t(b) * L * D + d : (int64_t(b) * D + d) * L;
+    const int64_t ts = tok ? D : 1;
     const Tin* xr = x + row;
-    const Tin* dr = dt_raw + row;
+    const Tin* dr = dt_raw + int64_t(b) * dtr.sb + d * dtr.sd;
+    const int64_t dts = dtr.ts;
     const Tin* zr = kGate ? z + row : nullptr;
     float* yr = kAgg ? nullptr : y + row;
+    // 8-step vector loads where a tensor's steps are contiguous and 16-byte aligned
+    const bool xvec = vec && ts == 1, dvec = vec && dts == 1;
     const float* bcb = BC + int64_t(b) * L * (2 * N);
     float dsum = 0.0f;
     // checkpoints: the state entering step t for every t % kCkptSteps == 0
@@ -173,16 +181,31 @@ __global__ __launch_bounds__(256) void scan_kernel(
             load_B(t);
             if (!kAgg) load_C(t);
         }
-        if (vec && t + 8 <= t_end) {
+        if ((vec || tok) && t + 8 <= t_end) {
             Tin xr8[8], dr8[8], zr8[8];
             auto load_group = [&](int64_t tt) {
                 constexpr int V = int(8 * sizeof(Tin) / 16);   // uint4 per 8 elements
+                if (xvec) {
 #pragma unroll
-                for (int q = 0; q < V; ++q) {
-                    reinterpret_cast<uint4*>(xr8)[q] = reinterpret_cast<const uint4*>(xr + tt)[q];
-                    reinterpret_cast<uint4*>(dr8)[q] = reinterpret_cast<const uint4*>(dr + tt)[q];
-                    if (kGate && !kAgg)
-                        reinterpret_cast<uint4*>(zr8)[q] = reinterpret_cast<const uint4*>(zr + tt)[q];
+                    for (int q = 0; q < V; ++q) {
+                        reinterpret_cast<uint4*>(xr8)[q] = reinterpret_cast<const uint4*>(xr + tt)[q];
+                        if (kGate && !kAgg)
+                            reinterpret_cast<uint4*>(zr8)[q] = reinterpret_cast<const uint4*>(zr + tt)[q];
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        xr8[i] = xr[(tt + i) * ts];
+                        if (kGate && !kAgg) zr8[i] = zr[(tt + i) * ts];
+                    }
+                }
+                if (dvec) {
+#pragma unroll
+                    for (int q = 0; q < V; ++q)
+                        reinterpret_cast<uint4*>(dr8)[q] = reinterpret_cast<const uint4*>(dr + tt)[q];
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) dr8[i] = dr[(tt + i) * dts];
                 }
             };
             load_group(t);
@@ -198,13 +221,20 @@ __global__ __launch_bounds__(256) void scan_kernel(
                 // rolled: an unrolled body keeps several B/C rows live and spills SGPRs
 #pragma unroll 1
                 for (int i = 0; i < 8; ++i) yv[i] = step(s4d_tag, xv[i], dv[i], zv[i], t + i);
-                if (!kAgg) store8(yr + t, yv);
+                if (!kAgg) {
+                    if (xvec) {
+                        store8(yr + t, yv);
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) yr[(t + i) * ts] = yv[i];
+                    }
+                }
             }
         }
         for (; t < t_end; ++t) {
-            const float zv = (kGate && !kAgg) ? to_f32(zr[t]) : 0.0f;
-            const float r = step(s4d_tag, to_f32(xr[t]), to_f32(dr[t]), zv, t);
-            if (!kAgg) yr[t] = r;
+            const float zv = (kGate && !kAgg) ? to_f32(zr[t * ts]) : 0.0f;
+            const float r = step(s4d_tag, to_f32(xr[t * ts]), to_f32(dr[t * dts]), zv, t);
+            if (!kAgg) yr[t * ts] = r;
         }
     };
     if (fast) run(Tag1{});
@@ -227,10 +257,10 @@ __global__ __launch_bounds__(256) void scan_kernel(
 // ---------------------------------------------------------------------------------------
 template <typename Tin, int N>
 static hipError_t launch_bc_stage_t(const void* Bm, const void* Cm, float* BC, int64_t B,
-                                    int64_t L, hipStream_t s) {
+                                    int64_t L, int tok, hipStream_t s) {
     dim3 grid(unsigned((L + 63) / 64), unsigned(B));
     hipLaunchKernelGGL((bc_stage_kernel<Tin, N>), grid, dim3(256), 0, s,
-                       static_cast<const Tin*>(Bm), static_cast<const Tin*>(Cm), BC, L);
+                       static_cast<const Tin*>(Bm), static_cast<const Tin*>(Cm), BC, L, tok);
     return hipGetLastError();
 }
 
@@ -242,7 +272,7 @@ static hipError_t launch_scan_t(const ScanLaunch& p, hipStream_t s) {
     const Tin* dr = static_cast<const Tin*>(p.dt_raw);
     const Tin* z = static_cast<const Tin*>(p.z);
 #define SS_SCAN_ARGS x, dr, z, p.dt_bias, p.A, p.Dskip, p.BC, p.h_init, p.y, p.h_last, p.h_ckpt, \
-                     p.dsum, p.L, p.D, p.chunk, p.K, p.vec
+                     p.dsum, p.L, p.D, p.chunk, p.K, p.vec, p.tok, p.dtr
     if (p.zoh) {
         if (p.agg)
             hipLaunchKernelGGL((scan_kernel<Tin, N, false, true, true>), grid, dim3(wg), 0, s, SS_SCAN_ARGS);
@@ -274,9 +304,9 @@ static hipError_t launch_scan_t(const ScanLaunch& p, hipStream_t s) {
     }
 
 hipError_t launch_bc_stage(int bf16, int N, const void* Bm, const void* Cm, float* BC, int64_t B,
-                           int64_t L, hipStream_t s) {
-    if (bf16) { SS_DISPATCH_N(launch_bc_stage_t, bf16_t, Bm, Cm, BC, B, L, s) }
-    SS_DISPATCH_N(launch_bc_stage_t, float, Bm, Cm, BC, B, L, s)
+                           int64_t L, int tok, hipStream_t s) {
+    if (bf16) { SS_DISPATCH_N(launch_bc_stage_t, bf16_t, Bm, Cm, BC, B, L, tok, s) }
+    SS_DISPATCH_N(launch_bc_stage_t, float, Bm, Cm, BC, B, L, tok, s)
 }
 
 hipError_t launch_scan(int bf16, int N, const ScanLaunch& p, hipStream_t s) {

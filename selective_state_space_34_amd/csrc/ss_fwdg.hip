@@ -83,6 +83,12 @@ template <int K> struct Raw<bf16_t, K> {
             w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
         }
     }
+    // elements p[0], p[st], ..., p[(K-1)·st] (token-major rows)
+    __device__ __forceinline__ void load_strided(const bf16_t* p, int64_t st) {
+#pragma unroll
+        for (int i = 0; i < K / 2; ++i)
+            w[i] = uint32_t(p[2 * i * st].bits) | (uint32_t(p[(2 * i + 1) * st].bits) << 16);
+    }
     __device__ __forceinline__ void decode(float (&o)[K]) const {
 #pragma unroll
         for (int i = 0; i < K / 2; ++i) {
@@ -104,6 +110,10 @@ template <int K> struct Raw<float, K> {
                 v[q] = a.x; v[q + 1] = a.y; v[q + 2] = a.z; v[q + 3] = a.w;
             }
         }
+    }
+    __device__ __forceinline__ void load_strided(const float* p, int64_t st) {
+#pragma unroll
+        for (int i = 0; i < K; ++i) v[i] = p[i * st];
     }
     __device__ __forceinline__ void decode(float (&o)[K]) const {
 #pragma unroll
@@ -173,7 +183,7 @@ struct GroupLds {
 // below d_hi), chunk k.  lds: GroupLds<G, S>::FLOATS floats, 16-byte aligned.  Requires
 // L % 8 == 0 and chunk % 32 == 0 (or K == 1) for the tiled part; the last < 32 steps of a
 // chunk run a per-step tail.
-template <typename Tin, int G, int S, bool kGate, bool kAgg, bool kZoh>
+template <typename Tin, int G, int S, bool kGate, bool kAgg, bool kZoh, bool kTok>
 __device__ __forceinline__ void scang_body(
     float* __restrict__ lds, int64_t blk, int k, int b, int64_t d_lo, int64_t d_hi,
     const Tin* __restrict__ x, const Tin* __restrict__ dt_raw, const Tin* __restrict__ z,
@@ -181,7 +191,7 @@ __device__ __forceinline__ void scang_body(
     const float* __restrict__ Dskip, const Tin* __restrict__ Bm, const Tin* __restrict__ Cm,
     const float* __restrict__ h_init, float* __restrict__ y, float* __restrict__ h_last,
     float* __restrict__ h_ckpt, float* __restrict__ dsum_out, int64_t L, int64_t D,
-    int64_t chunk, int K) {
+    int64_t chunk, int K, DtRows dtr) {
     using Lay = GroupLds<G, S>;
     constexpr int N = G * S;
     constexpr int CW = 64 / G;                    // channels per wave
@@ -220,11 +230,15 @@ __device__ __forceinline__ void scang_body(
     for (int s = 0; s < S; ++s) h[s] = h_init ? h_init[hidx + s] : 0.0f;
     const float bias = dt_bias[d];
     const float Dd = kAgg ? 0.0f : Dskip[d];
-    const int64_t row = (int64_t(b) * D + d) * L;
+    // channel (b, d): element t of x, z, y at row[t·ts]; Δraw at its own rows (dtr)
+    const int64_t row = kTok ? int64_t(b) * L * D + d : (int64_t(b) * D + d) * L;
+    const int64_t ts = kTok ? D : 1;
     const Tin* xr = x + row;
-    const Tin* dr = dt_raw + row;
+    const Tin* dr = dt_raw + int64_t(b) * dtr.sb + d * dtr.sd;
+    const int64_t dts = dtr.ts;
     const Tin* zr = kGate ? z + row : nullptr;
     float* yr = kAgg ? nullptr : y + row;
+    // B, C of row b: [N, L] (channel-major) or [L, N] (token-major)
     const Tin* Bb = Bm + int64_t(b) * N * L;
     const Tin* Cb = Cm + int64_t(b) * N * L;
     float dsum = 0.0f;
@@ -236,9 +250,11 @@ __device__ __forceinline__ void scang_body(
         for (int s = 0; s < S; ++s) ckr[(t / kCkptSteps) * N + s] = h[s];
     };
 
-    // B/C tile copy: 2·N rows of 32 steps; unit e covers steps 4q..4q+3 of state n of
-    // B (m = 0) or C (m = 1), with n fastest across lanes
+    // B/C tile copy: 2·N rows of 32 steps.  Channel-major: unit e covers steps 4q..4q+3 of
+    // state n of B (m = 0) or C (m = 1), with n fastest across lanes.  Token-major: unit e
+    // covers states 4q..4q+3 of step tt, with q fastest (a step's N states are contiguous).
     constexpr int BC_UNITS = 2 * N * (kTile / 4);
+    constexpr int NQ = N / 4;
     constexpr int BC_PASSES = (BC_UNITS + kThreads - 1) / kThreads;
     Raw4<Tin> bc_next[BC_PASSES];
     Raw<Tin, kH> xn[2], dn[2], zn[2];
@@ -248,16 +264,27 @@ __device__ __forceinline__ void scang_body(
         for (int p = 0; p < BC_PASSES; ++p) {
             const int e = tid + p * kThreads;
             if (BC_UNITS % kThreads == 0 || e < BC_UNITS) {
-                const int n = e % N, q = (e / N) % (kTile / 4), m = e / (N * (kTile / 4));
-                bc_next[p].load((m ? Cb : Bb) + int64_t(n) * L + t0 + 4 * q);
+                if constexpr (kTok) {
+                    const int q = e % NQ, tt = (e / NQ) % kTile, m = e / (NQ * kTile);
+                    bc_next[p].load((m ? Cb : Bb) + (t0 + tt) * N + 4 * q);
+                } else {
+                    const int n = e % N, q = (e / N) % (kTile / 4), m = e / (N * (kTile / 4));
+                    bc_next[p].load((m ? Cb : Bb) + int64_t(n) * L + t0 + 4 * q);
+                }
             }
         }
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             const int64_t te = t0 + kHalf * hh + kH * l;
-            xn[hh].load(xr + te);
-            dn[hh].load(dr + te);
-            if (kGate && !kAgg) zn[hh].load(zr + te);
+            if constexpr (kTok) {
+                xn[hh].load_strided(xr + te * ts, ts);
+                dn[hh].load_strided(dr + te * dts, dts);
+                if (kGate && !kAgg) zn[hh].load_strided(zr + te * ts, ts);
+            } else {
+                xn[hh].load(xr + te);
+                dn[hh].load(dr + te);
+                if (kGate && !kAgg) zn[hh].load(zr + te);
+            }
         }
     };
 
@@ -273,10 +300,17 @@ __device__ __forceinline__ void scang_body(
         for (int p = 0; p < BC_PASSES; ++p) {
             const int e = tid + p * kThreads;
             if (BC_UNITS % kThreads == 0 || e < BC_UNITS) {
-                const int n = e % N, q = (e / N) % (kTile / 4), m = e / (N * (kTile / 4));
-                float* dst = buf + 4 * q * R + m * N + n;
+                if constexpr (kTok) {
+                    const int q = e % NQ, tt = (e / NQ) % kTile, m = e / (NQ * kTile);
+                    *reinterpret_cast<float4*>(buf + tt * R + m * N + 4 * q) =
+                        make_float4(bc_next[p].get(0), bc_next[p].get(1), bc_next[p].get(2),
+                                    bc_next[p].get(3));
+                } else {
+                    const int n = e % N, q = (e / N) % (kTile / 4), m = e / (N * (kTile / 4));
+                    float* dst = buf + 4 * q * R + m * N + n;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) dst[i * R] = bc_next[p].get(i);
+                    for (int i = 0; i < 4; ++i) dst[i * R] = bc_next[p].get(i);
+                }
             }
         }
         float xv[2][kH], dv[2][kH], zv[2][kH];
@@ -365,7 +399,15 @@ __device__ __forceinline__ void scang_body(
                     if (kGate) sv *= silu(zv[hh][i]);
                     out[i] = sv;
                 }
-                if (valid) store_k<kH>(yr + t0 + kHalf * hh + kH * l, out);
+                if (valid) {
+                    const int64_t te = t0 + kHalf * hh + kH * l;
+                    if constexpr (kTok) {
+#pragma unroll
+                        for (int i = 0; i < kH; ++i) yr[(te + i) * ts] = out[i];
+                    } else {
+                        store_k<kH>(yr + te, out);
+                    }
+                }
                 wave_sync();  // gathers done before the next half's rows overwrite the area
             }
         }
@@ -375,8 +417,8 @@ __device__ __forceinline__ void scang_body(
     // prepares the step itself and reads its B/C straight from the inputs
     for (int64_t t = t_tiles_end; t < t_end; ++t) {
         if (ckr && t % kCkptSteps == 0) checkpoint(t);
-        const float xt = to_f32(xr[t]);
-        const float delta = softplus(bias + to_f32(dr[t]));
+        const float xt = to_f32(xr[t * ts]);
+        const float delta = softplus(bias + to_f32(dr[t * dts]));
         const float dxt = delta * xt;
         if (kAgg) dsum += (l == 0) ? delta : 0.0f;
         float acc = 0.0f;
@@ -384,16 +426,17 @@ __device__ __forceinline__ void scang_body(
         for (int s = 0; s < S; ++s) {
             const float t2 = delta * A2[s];
             const float abar = exp2_hw(t2);
-            float bx = (kZoh ? xt : dxt) * to_f32(Bb[int64_t(n0 + s) * L + t]);
+            const int64_t bci = kTok ? t * N + n0 + s : int64_t(n0 + s) * L + t;
+            float bx = (kZoh ? xt : dxt) * to_f32(Bb[bci]);
             if (kZoh) bx *= zoh_gain(t2, abar, delta, iA[s]);
             h[s] = fmaf(abar, h[s], bx);
-            if (!kAgg) acc = fmaf(to_f32(Cb[int64_t(n0 + s) * L + t]), h[s], acc);
+            if (!kAgg) acc = fmaf(to_f32(Cb[bci]), h[s], acc);
         }
         if (!kAgg) {
             acc = group_sum<G>(acc);
             float sv = fmaf(Dd, xt, acc);
-            if (kGate) sv *= silu(to_f32(zr[t]));
-            if (valid && l == 0) yr[t] = sv;
+            if (kGate) sv *= silu(to_f32(zr[t * ts]));
+            if (valid && l == 0) yr[t * ts] = sv;
         }
     }
 
@@ -413,18 +456,18 @@ __device__ __forceinline__ void scang_body(
 }
 
 // grid = (ceil(D / (256/G)), K, B), block = 256.
-template <typename Tin, int G, int S, bool kGate, bool kAgg, bool kZoh>
+template <typename Tin, int G, int S, bool kGate, bool kAgg, bool kZoh, bool kTok>
 __global__ __launch_bounds__(kThreads) void scang_kernel(
     const Tin* __restrict__ x, const Tin* __restrict__ dt_raw, const Tin* __restrict__ z,
     const float* __restrict__ dt_bias, const float* __restrict__ A,
     const float* __restrict__ Dskip, const Tin* __restrict__ Bm, const Tin* __restrict__ Cm,
     const float* __restrict__ h_init, float* __restrict__ y, float* __restrict__ h_last,
     float* __restrict__ h_ckpt, float* __restrict__ dsum_out, int64_t L, int64_t D,
-    int64_t chunk, int K) {
+    int64_t chunk, int K, DtRows dtr) {
     __shared__ __align__(16) float lds[GroupLds<G, S>::FLOATS];
-    scang_body<Tin, G, S, kGate, kAgg, kZoh>(lds, blockIdx.x, blockIdx.y, blockIdx.z, 0, D, x, dt_raw, z,
-                                       dt_bias, A, Dskip, Bm, Cm, h_init, y, h_last, h_ckpt,
-                                       dsum_out, L, D, chunk, K);
+    scang_body<Tin, G, S, kGate, kAgg, kZoh, kTok>(lds, blockIdx.x, blockIdx.y, blockIdx.z, 0, D, x,
+                                                   dt_raw, z, dt_bias, A, Dskip, Bm, Cm, h_init, y,
+                                                   h_last, h_ckpt, dsum_out, L, D, chunk, K, dtr);
 }
 
 // Single pass over every channel with two layouts in one launch: per batch row, channels
@@ -433,26 +476,27 @@ __global__ __launch_bounds__(kThreads) void scang_kernel(
 // four-lane workgroups and then its eight-lane one: whole rounds of four-lane waves per
 // SIMD, the remainder as eight-lane waves that take about half a four-lane wave's time.
 // grid = B * (nb4 + nb8), block = 256.
-template <typename Tin, int N, bool kGate, bool kZoh>
+template <typename Tin, int N, bool kGate, bool kZoh, bool kTok>
 __global__ __launch_bounds__(kThreads) void scang_mixed_kernel(
     const Tin* __restrict__ x, const Tin* __restrict__ dt_raw, const Tin* __restrict__ z,
     const float* __restrict__ dt_bias, const float* __restrict__ A,
     const float* __restrict__ Dskip, const Tin* __restrict__ Bm, const Tin* __restrict__ Cm,
     const float* __restrict__ h_init, float* __restrict__ y, float* __restrict__ h_last,
-    float* __restrict__ h_ckpt, int64_t L, int64_t D, int64_t d4, int nb4, int nb8, int B) {
+    float* __restrict__ h_ckpt, int64_t L, int64_t D, int64_t d4, int nb4, int nb8, int B,
+    DtRows dtr) {
     constexpr int F4 = GroupLds<4, N / 4>::FLOATS, F8 = GroupLds<8, N / 8>::FLOATS;
     __shared__ __align__(16) float lds[F4 > F8 ? F4 : F8];
     const int64_t f = blockIdx.x;
     const int64_t n4 = int64_t(B) * nb4;
     if (f < n4) {
-        scang_body<Tin, 4, N / 4, kGate, false, kZoh>(lds, f % nb4, 0, int(f / nb4), 0, d4, x, dt_raw, z,
-                                                dt_bias, A, Dskip, Bm, Cm, h_init, y, h_last, h_ckpt,
-                                                nullptr, L, D, L, 1);
+        scang_body<Tin, 4, N / 4, kGate, false, kZoh, kTok>(
+            lds, f % nb4, 0, int(f / nb4), 0, d4, x, dt_raw, z, dt_bias, A, Dskip, Bm, Cm, h_init,
+            y, h_last, h_ckpt, nullptr, L, D, L, 1, dtr);
     } else {
         const int64_t g = f - n4;
-        scang_body<Tin, 8, N / 8, kGate, false, kZoh>(lds, g % nb8, 0, int(g / nb8), d4, D, x, dt_raw, z,
-                                                dt_bias, A, Dskip, Bm, Cm, h_init, y, h_last, h_ckpt,
-                                                nullptr, L, D, L, 1);
+        scang_body<Tin, 8, N / 8, kGate, false, kZoh, kTok>(
+            lds, g % nb8, 0, int(g / nb8), d4, D, x, dt_raw, z, dt_bias, A, Dskip, Bm, Cm, h_init,
+            y, h_last, h_ckpt, nullptr, L, D, L, 1, dtr);
     }
 }
 
@@ -465,21 +509,17 @@ static hipError_t launch_scang_mixed_t(const ScanLaunch& p, hipStream_t s) {
     const Tin* z = static_cast<const Tin*>(p.z);
     const Tin* Bm = static_cast<const Tin*>(p.Bm);
     const Tin* Cm = static_cast<const Tin*>(p.Cm);
-#define SS_ARGS x, dr, z, p.dt_bias, p.A, p.Dskip, Bm, Cm, p.h_init, p.y, p.h_last, p.h_ckpt, p.L, \
-                p.D, p.d4, p.nb4, nb8, int(p.B)
-    if (p.zoh) {
-        if (p.z)
-            hipLaunchKernelGGL((scang_mixed_kernel<Tin, N, true, true>), grid, dim3(kThreads), 0, s, SS_ARGS);
-        else
-            hipLaunchKernelGGL((scang_mixed_kernel<Tin, N, false, true>), grid, dim3(kThreads), 0, s, SS_ARGS);
-    } else {
-        if (p.z)
-            hipLaunchKernelGGL((scang_mixed_kernel<Tin, N, true, false>), grid, dim3(kThreads), 0, s, SS_ARGS);
-        else
-            hipLaunchKernelGGL((scang_mixed_kernel<Tin, N, false, false>), grid, dim3(kThreads), 0, s, SS_ARGS);
-    }
-#undef SS_ARGS
-    return hipGetLastError();
+    return with_bool(p.z != nullptr, [&](auto gate) {
+        return with_bool(p.zoh != 0, [&](auto zoh) {
+            return with_bool(p.tok != 0, [&](auto tok) {
+                hipLaunchKernelGGL((scang_mixed_kernel<Tin, N, gate.value, zoh.value, tok.value>),
+                                   grid, dim3(kThreads), 0, s, x, dr, z, p.dt_bias, p.A, p.Dskip,
+                                   Bm, Cm, p.h_init, p.y, p.h_last, p.h_ckpt, p.L, p.D, p.d4, p.nb4,
+                                   nb8, int(p.B), p.dtr);
+                return hipGetLastError();
+            });
+        });
+    });
 }
 
 template <typename Tin, int G, int S>
@@ -491,25 +531,21 @@ static hipError_t launch_scang_t(const ScanLaunch& p, hipStream_t s) {
     const Tin* z = static_cast<const Tin*>(p.z);
     const Tin* Bm = static_cast<const Tin*>(p.Bm);
     const Tin* Cm = static_cast<const Tin*>(p.Cm);
-#define SS_ARGS x, dr, z, p.dt_bias, p.A, p.Dskip, Bm, Cm, p.h_init, p.y, p.h_last, p.h_ckpt, \
-                p.dsum, p.L, p.D, p.chunk, p.K
-    if (p.zoh) {
-        if (p.agg)
-            hipLaunchKernelGGL((scang_kernel<Tin, G, S, false, true, true>), grid, dim3(kThreads), 0, s, SS_ARGS);
-        else if (p.z)
-            hipLaunchKernelGGL((scang_kernel<Tin, G, S, true, false, true>), grid, dim3(kThreads), 0, s, SS_ARGS);
-        else
-            hipLaunchKernelGGL((scang_kernel<Tin, G, S, false, false, true>), grid, dim3(kThreads), 0, s, SS_ARGS);
-    } else {
-        if (p.agg)
-            hipLaunchKernelGGL((scang_kernel<Tin, G, S, false, true, false>), grid, dim3(kThreads), 0, s, SS_ARGS);
-        else if (p.z)
-            hipLaunchKernelGGL((scang_kernel<Tin, G, S, true, false, false>), grid, dim3(kThreads), 0, s, SS_ARGS);
-        else
-            hipLaunchKernelGGL((scang_kernel<Tin, G, S, false, false, false>), grid, dim3(kThreads), 0, s, SS_ARGS);
-    }
-#undef SS_ARGS
-    return hipGetLastError();
+    return with_bool(p.zoh != 0, [&](auto zoh) {
+        return with_bool(p.tok != 0, [&](auto tok) {
+            auto go = [&](auto gate, auto agg) {
+                hipLaunchKernelGGL(
+                    (scang_kernel<Tin, G, S, gate.value, agg.value, zoh.value, tok.value>), grid,
+                    dim3(kThreads), 0, s, x, dr, z, p.dt_bias, p.A, p.Dskip, Bm, Cm, p.h_init, p.y,
+                    p.h_last, p.h_ckpt, p.dsum, p.L, p.D, p.chunk, p.K, p.dtr);
+                return hipGetLastError();
+            };
+            // the aggregate pass has no gate
+            if (p.agg) return go(std::false_type{}, std::true_type{});
+            if (p.z) return go(std::true_type{}, std::false_type{});
+            return go(std::false_type{}, std::false_type{});
+        });
+    });
 }
 
 template <typename Tin>

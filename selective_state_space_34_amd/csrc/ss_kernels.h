@@ -4,10 +4,24 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace ss {
 
 // Steps between the forward's state checkpoints (the backward's tile length).
 constexpr int kCkptSteps = 16;
+
+// Where channel (b, d)'s Δraw values lie: element t at dt_raw[b·sb + d·sd + t·ts].
+//   [B, D, L]: (D·L, L, 1);  [B, L, D]: (L·D, 1, D);  one value per token [B, L]: (L, 0, 1).
+struct DtRows {
+    int64_t sb, sd, ts;
+};
+
+// Calls f(std::integral_constant<bool, v>): a runtime flag as a template argument.
+template <typename F>
+inline hipError_t with_bool(bool v, F&& f) {
+    return v ? f(std::true_type{}) : f(std::false_type{});
+}
 
 struct ScanLaunch {
     const void* x;
@@ -32,6 +46,8 @@ struct ScanLaunch {
     int64_t d4;             // mixed layout: channels [0, d4) on four lanes, [d4, D) on eight
     int nb4;                //               four-lane workgroups per batch row (d4 / 64)
     int zoh;                // 1: exact zero-order-hold B̄
+    int tok;                // 1: token-major x, z, y [B, L, D] and B, C [B, L, N]
+    DtRows dtr;             // Δraw rows
 };
 
 // Affine-pair carry across chunks (one workgroup per channel).  Chunk c's pair is
@@ -88,6 +104,11 @@ struct BwdLaunch {
     int K;
     int vec;
     int stage;
+    int tok;           // 1: token-major x, z, dy, dx, dz [B, L, D] and B, C, dB, dC [B, L, N]
+    DtRows dtr;        // Δraw rows
+    DtRows gdr;        // rows the per-channel Δraw gradient is written to (ddt_raw)
+    float* ddt_shared; // nullable: Δraw shared by the channels; its gradient [B, L]
+    float* ddt_blk;    // with ddt_shared: per-64-channel-block sums [B, ceil(D/64), L]
 };
 
 // Single-token step: x, dt_raw, z [B, D]; Bm, Cm [B, N]; h_in, h_out [B, D, N] (may be equal).
@@ -106,12 +127,14 @@ struct StepLaunch {
     int64_t B, D;
     int N;
     int zoh;                // 1: exact zero-order-hold B̄
+    int dt_shared;          // 1: dt_raw [B], one value per token
 };
 
 hipError_t launch_bc_stage(int bf16, int N, const void* Bm, const void* Cm, float* BC, int64_t B,
-                           int64_t L, hipStream_t s);
+                           int64_t L, int tok, hipStream_t s);
 hipError_t launch_scan(int bf16, int N, const ScanLaunch& p, hipStream_t s);
 // group-split layout: G = 4 (N in {4, 8, 16, 32}) or G = 8 (N in {8, 16, 32}); L % 8 == 0
+// for channel-major inputs
 hipError_t launch_scang(int bf16, int N, int G, const ScanLaunch& p, hipStream_t s);
 // single pass, N in {8, 16, 32}: four lanes for channels [0, d4), eight for [d4, D)
 hipError_t launch_scang_mixed(int bf16, int N, const ScanLaunch& p, hipStream_t s);

@@ -22,8 +22,10 @@ struct Plan {
     int64_t d4;
     int nb4;         // four-lane workgroups per batch row (d4 / 64)
     int zoh;         // exact zero-order-hold input term
+    int tok;         // token-major x, z, y, dy, dx, dz [B, L, D] and B, C, dB, dC [B, L, N]
+    int dt_shared;   // Δraw one value per token [B, L]
     // workspace carving (byte offsets, 256-aligned)
-    size_t off_bc, off_hend, off_dsum, off_hstart, off_gend, off_gstart, off_red;
+    size_t off_bc, off_hend, off_dsum, off_hstart, off_gend, off_gstart, off_red, off_ddt;
     size_t red_bytes;
     size_t ws_total;
 };
@@ -57,6 +59,8 @@ inline int make_plan(const ss_dims& d, bool backward, Plan* out) {
         d.layout != SS_LAYOUT_OCT)
         return SS_ERR_DTYPE;
     if (d.disc != SS_DISC_EULER && d.disc != SS_DISC_ZOH) return SS_ERR_DTYPE;
+    if (d.order != SS_ORDER_BDL && d.order != SS_ORDER_BLD) return SS_ERR_DTYPE;
+    if (d.dt_layout != SS_DT_FULL && d.dt_layout != SS_DT_SHARED) return SS_ERR_DTYPE;
     if (d.batch <= 0 || d.seqlen <= 0 || d.dim <= 0 || d.dstate <= 0) return SS_ERR_DIMS;
     const int64_t N = d.dstate;
     if (N != 1 && N != 2 && N != 4 && N != 8 && N != 16 && N != 32) return SS_ERR_DIMS;
@@ -68,13 +72,16 @@ inline int make_plan(const ss_dims& d, bool backward, Plan* out) {
     if (d.batch > kMaxGridYZ) return SS_ERR_DIMS;
     p.B = d.batch; p.L = d.seqlen; p.D = d.dim; p.N = N; p.in_dtype = d.in_dtype;
     p.zoh = d.disc == SS_DISC_ZOH;
+    p.tok = d.order == SS_ORDER_BLD;
+    p.dt_shared = d.dt_layout == SS_DT_SHARED;
     p.vec = (p.L % 8) == 0;
     // layout: a group of G lanes per channel (G x the waves of one lane per channel).
     // Automatic choice: four lanes wherever they apply.  Measured on MI355X, eight lanes
     // balance the SIMDs better at B*D = 40960 but saturate the LDS (their operand
     // traffic per state-step is higher) and lose on every workload; one lane per channel
     // loses on every workload too.
-    const int gmax = !p.vec ? 0 : N >= 8 ? 8 : N >= 4 ? 4 : 0;
+    // (token-major rows are read element by element, so only channel-major needs L % 8)
+    const int gmax = !(p.vec || p.tok) ? 0 : N >= 8 ? 8 : N >= 4 ? 4 : 0;
     if (d.layout == SS_LAYOUT_LANE) p.group = 0;
     else if (d.layout == SS_LAYOUT_OCT) p.group = gmax;
     else p.group = gmax >= 4 ? 4 : 0;
@@ -141,6 +148,12 @@ inline int make_plan(const ss_dims& d, bool backward, Plan* out) {
             p.red_bytes = bwd_partial_bytes(p);
             p.off_red = off; off = align256(off + p.red_bytes);
         }
+    }
+    // shared Δraw: the backward's per-64-channel-block sums of its gradient [B, ceil(D/64), L]
+    p.off_ddt = 0;
+    if (backward && p.dt_shared) {
+        p.off_ddt = off;
+        off = align256(off + size_t(p.B) * size_t(bwd_reduce_blocks(p)) * size_t(p.L) * sizeof(float));
     }
     p.ws_total = off;
     *out = p;

@@ -5,7 +5,8 @@
 // 알고리즘과 정보의 압축 및 선별", §1.2 softplus step, §2.1 exp discretisation, §1.1
 // readout, §3 of the note for the SiLU gate): for one token per (batch row, channel),
 //   δ = softplus(dt_bias + dt_raw);  h_n ← exp(δ A_n) h_n + δ B_n x;  y = (Σ_n C_n h_n + D x)·silu(z)
-// with the state read and written in place.  Per channel the state is N floats, and it is
+// with the state read and written in place.  Δraw is per (row, channel) [B, D] or one
+// value per token [B] shared by the channels.  Per channel the state is N floats, and it is
 // the whole of the traffic that grows with N: the step is bound by HBM bandwidth.
 //
 // Layout: S = min(N, 4) states per lane, G = N / S lanes per channel, so a wave reads and
@@ -33,7 +34,7 @@ __global__ __launch_bounds__(256) void step_kernel(
     const Tin* __restrict__ x, const Tin* __restrict__ dt_raw, const Tin* __restrict__ z,
     const float* __restrict__ dt_bias, const float* __restrict__ A, const Tin* __restrict__ Bm,
     const Tin* __restrict__ Cm, const float* __restrict__ Dskip, const float* h_in, float* h_out,
-    float* __restrict__ y, int64_t BD, int64_t D) {
+    float* __restrict__ y, int64_t BD, int64_t D, int dt_shared) {
     constexpr int N = S * G;
     const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     const int64_t ch = gid / G;                  // b * D + d
@@ -43,7 +44,7 @@ __global__ __launch_bounds__(256) void step_kernel(
     const int n0 = l * S;
 
     const float xv = to_f32(x[ch]);
-    const float delta = softplus(dt_bias[d] + to_f32(dt_raw[ch]));
+    const float delta = softplus(dt_bias[d] + to_f32(dt_raw[dt_shared ? b : ch]));
     const float dx = delta * xv;
     float h[S];
     const float* hp = h_in + ch * N + n0;
@@ -90,7 +91,8 @@ static hipError_t launch_step_t(const StepLaunch& p, hipStream_t s) {
     const Tin* z = static_cast<const Tin*>(p.z);
     const Tin* Bm = static_cast<const Tin*>(p.Bm);
     const Tin* Cm = static_cast<const Tin*>(p.Cm);
-#define SS_STEP_ARGS x, dr, z, p.dt_bias, p.A, Bm, Cm, p.Dskip, p.h_in, p.h_out, p.y, p.B * p.D, p.D
+#define SS_STEP_ARGS x, dr, z, p.dt_bias, p.A, Bm, Cm, p.Dskip, p.h_in, p.h_out, p.y, p.B * p.D, p.D, \
+                     p.dt_shared
     if (p.zoh) {
         if (z) hipLaunchKernelGGL((step_kernel<Tin, S, G, true, true>), grid, dim3(256), 0, s, SS_STEP_ARGS);
         else hipLaunchKernelGGL((step_kernel<Tin, S, G, false, true>), grid, dim3(256), 0, s, SS_STEP_ARGS);

@@ -37,7 +37,7 @@ def test_exports_match_header(lib):
 
 
 def test_version_and_strerror(lib):
-    assert lib.ss_version() == (0 << 16) | 4
+    assert lib.ss_version() == (0 << 16) | 5
     for code in ss.ERRORS:
         assert len(lib.ss_strerror(code)) > 0
     assert b"unknown" in lib.ss_strerror(12345)
@@ -66,6 +66,8 @@ def test_fwd_validation(lib):
     assert _fwd(lib, ss.make_dims(2, 64, 32, 16, layout=5)) == -3
     assert _fwd(lib, ss.make_dims(2, 64, 32, 16, disc=2)) == -3
     assert _fwd(lib, ss.make_dims(2, 64, 32, 16, disc=-1)) == -3
+    assert _fwd(lib, ss.make_dims(2, 64, 32, 16, order=2)) == -3
+    assert _fwd(lib, ss.make_dims(2, 64, 32, 16, dt_layout=2)) == -3
     # required pointers
     for i in (0, 1, 2, 3, 4, 5, 6, 9):
         p = [ctypes.c_void_p(FAKE)] * 12
@@ -116,6 +118,13 @@ def test_workspace_sizes(lib):
     a256 = lambda v: (v + 255) // 256 * 256
     assert ss.workspace_size(d, backward=True) == (4 * st + a256(8 * K * 5120 * 4)
                                                    + a256(8 * NB * 2048 * 32 * 4) + 8 * K * 5120 * 2 * 4)
+    # a Δraw shared by the channels adds its gradient's per-block sums [B, D/64, L]
+    ds = ss.make_dims(8, 2048, 5120, 16, ss.SS_BF16, dt_layout=ss.SS_DT_SHARED)
+    assert ss.workspace_size(ds, backward=True) == ss.workspace_size(d, backward=True) + 8 * NB * 2048 * 4
+    # token-major: the same plan and workspace
+    dt_ = ss.make_dims(8, 2048, 5120, 16, ss.SS_BF16, order=ss.SS_ORDER_BLD)
+    assert ss.workspace_size(dt_, backward=True) == ss.workspace_size(d, backward=True)
+    assert ss.workspace_size(dt_) == ss.workspace_size(ss.make_dims(8, 2048, 5120, 16, ss.SS_BF16))
     n = ctypes.c_size_t()
     assert lib.ss_fwd_workspace_size(None, ctypes.byref(n)) == -1
     assert lib.ss_fwd_workspace_size(ctypes.byref(d), None) == -1
@@ -173,6 +182,7 @@ def test_step_validation(lib):
     assert call(ss.make_dims(4, 1, 32, 16, layout=1), args) == -3
     assert call(ss.make_dims(4, 1, 32, 16, in_dtype=9), args) == -3
     assert call(ss.make_dims(4, 1, 32, 16, disc=2), args) == -3
+    assert call(ss.make_dims(4, 1, 32, 16, dt_layout=5), args) == -3
     good = ss.make_dims(4, 1, 32, 16)
     for i in (0, 1, 2, 3, 4, 5, 6, 8, 9, 10):
         a = list(args)
