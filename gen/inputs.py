@@ -22,7 +22,8 @@ import numpy as np
 
 from .configs import Workload, seed_of
 
-STREAMS = ("x", "z", "dt_raw", "dt", "eps", "B", "C", "D", "dy", "h0", "dh_final", "spare")
+STREAMS = ("x", "z", "dt_raw", "dt", "eps", "B", "C", "D", "dy", "h0", "dh_final", "spare",
+           "u", "W_in", "W_x")
 
 _CHUNK = 1 << 24  # elements per narrowing pass, bounds temporaries for the 268M-element tensors
 
@@ -135,6 +136,53 @@ def make_inputs(batch: int, seqlen: int, dim: int, dstate: int, *, dtype: str = 
     return S6Inputs(Bn, L, D, N, dtype, x, dt_raw, dt_bias, A, Bm, Cm, Dskip,
                     z=z, h0=h0, dy=dy, dh_final=dh_final, dt_tok=dt_tok,
                     meta=dict(seed=seed, gate=gate, a_perturb=a_perturb, dt_shared=dt_shared))
+
+
+@dataclass
+class BlockInputs:
+    """One case of the block's inputs: u [B, L, D_in] and W_in [2D, D_in] bf16-exact (or
+    float32) values, W_x [1 + 2N, D] float32, and the scan's per-channel parameters."""
+    batch: int
+    seqlen: int
+    d_in: int
+    dim: int
+    dstate: int
+    dtype: str
+    u: np.ndarray
+    W_in: np.ndarray
+    W_x: np.ndarray
+    dt_bias: np.ndarray
+    A: np.ndarray
+    Dskip: np.ndarray
+    h0: Optional[np.ndarray] = None
+
+
+def make_block_inputs(batch: int, seqlen: int, d_in: int, dim: int, dstate: int, *,
+                      dtype: str = "f32", seed: int = 0, a_perturb: bool = True,
+                      with_h0: bool = False, dt_min: float = 1e-3,
+                      dt_max: float = 1e-1) -> BlockInputs:
+    """Draw one seeded case of the block: u ~ N(0,1); W_in ~ N(0, 1/D_in), so x and z are
+    about N(0,1); W_x ~ N(0, 1/D) with its Δraw row scaled by 0.5, so Δraw, B and C follow
+    the scan recipe's scales; dt_bias, A, D and h0 as make_inputs (same streams)."""
+    if dtype not in ("f32", "bf16"):
+        raise ValueError(f"dtype must be 'f32' or 'bf16', got {dtype!r}")
+    kids = np.random.SeedSequence(seed).spawn(len(STREAMS))
+    rng = {name: np.random.Generator(np.random.PCG64(k)) for name, k in zip(STREAMS, kids)}
+    Bn, L, Din, D, N = batch, seqlen, d_in, dim, dstate
+    narrow = round_bf16 if dtype == "bf16" else (lambda a: a)
+    u = narrow(_normal(rng["u"], (Bn, L, Din)))
+    W_in = narrow(_normal(rng["W_in"], (2 * D, Din), 1.0 / np.sqrt(Din)))
+    W_x = _normal(rng["W_x"], (1 + 2 * N, D), 1.0 / np.sqrt(D))
+    W_x[0] *= np.float32(0.5)
+    log_dt = rng["dt"].uniform(np.log(dt_min), np.log(dt_max), size=D)
+    dt_bias = np.log(np.expm1(np.exp(log_dt))).astype(np.float32)
+    base = -np.arange(1, N + 1, dtype=np.float64)[None, :].repeat(D, axis=0)
+    if a_perturb:
+        base = base * np.exp(rng["eps"].normal(0.0, 0.1, size=(D, N)))
+    A = base.astype(np.float32)
+    Dskip = _normal(rng["D"], (D,))
+    h0 = _normal(rng["h0"], (Bn, D, N)) if with_h0 else None
+    return BlockInputs(Bn, L, Din, D, N, dtype, u, W_in, W_x, dt_bias, A, Dskip, h0)
 
 
 def workload_inputs(w: Workload, **overrides) -> S6Inputs:
