@@ -240,6 +240,107 @@ def run_decode(args, w, inp):
     print(json.dumps(out), flush=True)
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+
+
+def block_cpu_baseline(w, inp, budget_s=4.0):
+    """The fp64 block oracle (numpy projections, C scan) timed on a growing prefix of the
+    first batch row's tokens until one run takes about budget_s seconds."""
+    from oracle import block_ref, cref
+    threads = cref.threads(0)
+    n = 16
+    while True:
+        t0 = time.perf_counter()
+        block_ref.block_fwd(inp.u[:1, :n], inp.W_in, inp.W_x, inp.dt_bias, inp.A, inp.Dskip,
+                            impl="c")
+        dt = time.perf_counter() - t0
+        if dt >= budget_s / 4 or n >= w.seqlen:
+            break
+        n = min(w.seqlen, int(n * max(2.0, budget_s / max(dt, 1e-3) / 2)))
+    elems = n * w.dim
+    return {"value": elems / dt, "unit": "elem/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"batch row 0, first {n} of {w.seqlen} tokens, all {w.dim} channels "
+                      f"(B*L*D elements {elems}), {dt:.2f} s wall; numpy float64 matrix products "
+                      f"and the C scan on {threads} OpenMP threads"}
+
+
+def run_block(args, w, inp):
+    """Block workload: K timed ss_block_fwd calls (input projection on the matrix cores,
+    selection projections, gated scan); then K ss_in_proj calls timed alone, the dominant
+    kernel, for the MFMA roofline."""
+    import torch
+    import selective_state_space_34_amd as ss
+    dev = torch.device("cuda:0")
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(torch.bfloat16).to(dev)
+    f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
+    u, W_in = bf(inp.u), bf(inp.W_in)
+    W_x, dtb, A, Dk = f32(inp.W_x), f32(inp.dt_bias), f32(inp.A), f32(inp.Dskip)
+    y = torch.empty((w.batch, w.seqlen, w.dim), dtype=torch.float32, device=dev)
+    dims = ss.make_block_dims(w.batch, w.seqlen, w.d_in, w.dim, w.dstate)
+    ws = torch.empty(ss.block_workspace_size(dims), dtype=torch.uint8, device=dev)
+    xo = torch.empty((w.batch, w.seqlen, w.dim), dtype=torch.float32, device=dev)
+    zo = torch.empty_like(xo)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        ss.ss_block_fwd(u, W_in, W_x, dtb, A, Dk, y=y, workspace=ws, stream=stream)
+
+    def gemm():
+        ss.ss_in_proj(u, W_in, x=xo, z=zo, stream=stream)
+
+    def timed(fn):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for e0, e1 in evs:
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return np.array([e0.elapsed_time(e1) for e0, e1 in evs]) * 1e-3, wall
+
+    for _ in range(args.warmup):
+        step()
+        gemm()
+    torch.cuda.synchronize()
+    calib_copy(args, dev)
+    per, wall = timed(step)
+    gper, _ = timed(gemm)
+    t_avg, tg = float(per.mean()), float(gper.mean())
+    M = w.batch * w.seqlen
+    flops = 2.0 * M * (2 * w.dim) * w.d_in
+    tflops = flops / tg / 1e12
+    elems = M * w.dim
+    log(f"[bench] block step event avg {t_avg * 1e6:.1f} us; input projection alone "
+        f"{tg * 1e6:.1f} us = {tflops:.0f} TFLOP/s ({tflops / MFMA_BF16_PEAK_TFLOPS:.3f} of "
+        f"{MFMA_BF16_PEAK_TFLOPS:.0f}); the rest {(t_avg - tg) * 1e6:.1f} us")
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = block_cpu_baseline(w, inp)
+        log(f"[bench] cpu baseline {cpu['value']:.3e} elem/s ({cpu['sample']})")
+    out = {
+        "metric": "selective-scan block fwd B·L·D elements/s; input projection TFLOP/s vs "
+                  "MI355X bf16 matrix peak",
+        "value": elems * args.steps / wall, "unit": "elem/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": wall / args.steps * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16 x bf16 -> f32 (projection), f32",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: {w.label}", "batch": w.batch, "seqlen": w.seqlen,
+                   "d_in": w.d_in, "dim": w.dim, "dstate": w.dstate},
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
+                     "traffic": None,
+                     "kernel": "gemm_bf16_nt_kernel (ss_in_proj, the block's input projection)",
+                     "launch_us": tg * 1e6, "flops": flops},
+        "block_split": {"step_us": t_avg * 1e6, "in_proj_us": tg * 1e6,
+                        "rest_us": (t_avg - tg) * 1e6},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def calib_copy(args, dev):
     """One device copy of a known size, for scaling the HBM byte counters."""
     import torch
@@ -264,7 +365,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c2",
-                    help="c0..c4 (default c2, D=5120 forward); d1 = decode step")
+                    help="c0..c4 (default c2, D=5120 forward); d1 = decode step; p2 = block")
     ap.add_argument("--plan", type=int, default=0)
     ap.add_argument("--layout", type=int, default=0, help="0 auto, 1 four lanes, 2 one lane, 3 eight lanes per channel")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -299,10 +400,13 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     t0 = time.perf_counter()
-    inp = workload_inputs(w, dt_shared=args.dt_shared)
+    inp = workload_inputs(w) if w.d_in else workload_inputs(w, dt_shared=args.dt_shared)
     log(f"[bench] inputs generated in {time.perf_counter() - t0:.1f}s")
     if w.decode:
         run_decode(args, w, inp)
+        return
+    if w.d_in:
+        run_block(args, w, inp)
         return
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     dev = torch.device("cuda:0")

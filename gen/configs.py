@@ -2,8 +2,10 @@
 
 Each workload is named by what it is.  c0..c4 restate the benchmark configurations this
 library is measured on; d1 is a decode step (one token per sequence, the state carried in
-and out) at the D=5120 width with a serving-size batch.  Nothing here computes any part of
-the scan.
+and out) at the D=5120 width with a serving-size batch; p2 is the block around the scan
+(input projection, selection projections, gated scan) at the D=5120 width with an input
+twice as narrow (the block's usual expansion by 2).  Nothing here computes any part of the
+scan.
 """
 from dataclasses import dataclass
 
@@ -22,6 +24,7 @@ class Workload:
     backward: bool     # workload also exercises the backward pass
     h_final: bool      # final state is an output of the workload
     decode: bool = False  # one token per (batch row, channel) through ss_step, state in place
+    d_in: int = 0         # > 0: the block (projections + gated scan) on input width d_in
 
     @property
     def elems(self) -> int:
@@ -46,6 +49,9 @@ WORKLOADS = (
              4, 4096, 2048, 16, "bf16", True, False, True, False),
     Workload("d1", "S6 decode step (one token, state in place) bf16-in B=256 D=5120 N=16 gate",
              256, 1, 5120, 16, "bf16", True, True, False, True, decode=True),
+    Workload("p2", "S6 block fwd: bf16 u [8, 2048, 2560] x W_in [10240, 2560] on the matrix "
+             "cores, fp32 selection projections, gated scan D=5120 N=16",
+             8, 2048, 5120, 16, "bf16", True, True, False, False, d_in=2560),
 )
 
 BY_NAME = {w.name: w for w in WORKLOADS}

@@ -185,8 +185,12 @@ def make_block_inputs(batch: int, seqlen: int, d_in: int, dim: int, dstate: int,
     return BlockInputs(Bn, L, Din, D, N, dtype, u, W_in, W_x, dt_bias, A, Dskip, h0)
 
 
-def workload_inputs(w: Workload, **overrides) -> S6Inputs:
-    """Inputs of a named workload, seeded with its index."""
+def workload_inputs(w: Workload, **overrides):
+    """Inputs of a named workload, seeded with its index (BlockInputs for a block workload)."""
+    if w.d_in:
+        kw = dict(dtype=w.dtype, seed=seed_of(w), a_perturb=w.a_perturb)
+        kw.update(overrides)
+        return make_block_inputs(w.batch, w.seqlen, w.d_in, w.dim, w.dstate, **kw)
     kw = dict(dtype=w.dtype, seed=seed_of(w), gate=w.gate, a_perturb=w.a_perturb,
               with_dy=w.backward, with_h0=w.decode)
     kw.update(overrides)

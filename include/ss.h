@@ -54,7 +54,7 @@ extern "C" {
 #endif
 
 #define SS_VERSION_MAJOR 0
-#define SS_VERSION_MINOR 5
+#define SS_VERSION_MINOR 6
 
 /* dtype of x, dt_raw, z, Bm, Cm */
 typedef enum { SS_F32 = 0, SS_BF16 = 1 } ss_dtype;
@@ -166,6 +166,40 @@ int ss_bwd(const ss_dims* dims,
            float* dx, float* ddt_raw, float* ddt_bias, float* dA, float* dB, float* dC,
            float* dD, float* dz, float* dh0,
            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Selection projections and gated block around the scan (note "상태공간 모델(SSM)과 Mamba
+ * 아키텍처", §3: the input is projected two ways, one branch through the scan and one through
+ * the SiLU gate; page "3.2 선택적 스캔(Selective Scan) 알고리즘과 정보의 압축 및 선별", §1.2:
+ * B_t, C_t and Δ_t come from linear maps of the token).  Weights are stored (outputs, inputs):
+ *   [x | z]     = u · W_inᵀ         u [B, L, d_in] bf16, W_in [2·dim, d_in] bf16, fp32 accumulate
+ *   [Δraw|B|C]  = x · W_xᵀ          W_x [1 + 2·dstate, dim] float32
+ *   y           = scan of x with Δraw shared by the channels (plus each channel's dt_bias),
+ *                 B, C, gate z, A, Dskip, h0 — token-major, float32 throughout
+ * and y [B, L, dim] float32 (h_final [B, dim, dstate] optional).  x, z [B, L, dim], dt [B, L],
+ * Bm, Cm [B, L, dstate] are float32 outputs when given (else they live in the workspace).
+ * d_in % 8 == 0 and dim % 4 == 0 (else SS_ERR_DIMS); plan and layout as for ss_fwd. */
+typedef struct ss_block_dims {
+    int64_t batch;    /* B >= 1 */
+    int64_t seqlen;   /* L >= 1 */
+    int64_t d_in;     /* input width, multiple of 8 */
+    int64_t dim;      /* D: channels of the scan, multiple of 4 */
+    int64_t dstate;   /* N, one of 1, 2, 4, 8, 16, 32 */
+    int32_t plan;     /* ss_plan of the scan */
+    int32_t layout;   /* ss_layout of the scan */
+} ss_block_dims;
+
+int ss_block_fwd_workspace_size(const ss_block_dims* dims, size_t* bytes);
+
+/* The block's first stage alone: [x | z] = u · W_inᵀ with u [B, L, d_in], W_in [2·dim, d_in]
+ * (bf16) and x, z [B, L, dim] float32 (required).  dstate, plan and layout of dims are not
+ * used.  Needs no workspace. */
+int ss_in_proj(const ss_block_dims* dims, const void* u, const void* W_in, float* x, float* z,
+               hipStream_t stream);
+
+int ss_block_fwd(const ss_block_dims* dims, const void* u, const void* W_in, const float* W_x,
+                 const float* dt_bias, const float* A, const float* Dskip, const float* h0,
+                 float* y, float* h_final, float* x, float* z, float* dt, float* Bm, float* Cm,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Single-token (decode) step: the recurrence carried one token further for every (batch
  * row, channel), as in recurrent inference (note "상태공간 모델(SSM)과 Mamba 아키텍처", §2):

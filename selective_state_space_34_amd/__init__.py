@@ -31,7 +31,8 @@ ERRORS = {0: "SS_OK", -1: "SS_ERR_NULL", -2: "SS_ERR_DIMS", -3: "SS_ERR_DTYPE", 
           -5: "SS_ERR_WORKSPACE", -6: "SS_ERR_HIP", -7: "SS_ERR_UNSUPPORTED"}
 
 EXPORTS = ("ss_fwd", "ss_bwd", "ss_step", "ss_fwd_workspace_size", "ss_bwd_workspace_size",
-           "ss_strerror", "ss_last_hip_error", "ss_version")
+           "ss_block_fwd", "ss_block_fwd_workspace_size", "ss_in_proj", "ss_strerror",
+           "ss_last_hip_error", "ss_version")
 
 
 class ss_dims(ctypes.Structure):
@@ -39,6 +40,12 @@ class ss_dims(ctypes.Structure):
                 ("dstate", ctypes.c_int64), ("in_dtype", ctypes.c_int32), ("plan", ctypes.c_int32),
                 ("chunk", ctypes.c_int64), ("layout", ctypes.c_int32), ("disc", ctypes.c_int32),
                 ("order", ctypes.c_int32), ("dt_layout", ctypes.c_int32)]
+
+
+class ss_block_dims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("d_in", ctypes.c_int64),
+                ("dim", ctypes.c_int64), ("dstate", ctypes.c_int64), ("plan", ctypes.c_int32),
+                ("layout", ctypes.c_int32)]
 
 
 class SSError(RuntimeError):
@@ -74,6 +81,13 @@ def load(path: str = LIB):
     for f in ("ss_fwd_workspace_size", "ss_bwd_workspace_size"):
         getattr(lib, f).argtypes = [D, ctypes.POINTER(ctypes.c_size_t)]
         getattr(lib, f).restype = ctypes.c_int
+    BD = ctypes.POINTER(ss_block_dims)
+    lib.ss_block_fwd.argtypes = [BD] + [P] * 14 + [P, ctypes.c_size_t, P]
+    lib.ss_block_fwd.restype = ctypes.c_int
+    lib.ss_block_fwd_workspace_size.argtypes = [BD, ctypes.POINTER(ctypes.c_size_t)]
+    lib.ss_block_fwd_workspace_size.restype = ctypes.c_int
+    lib.ss_in_proj.argtypes = [BD] + [P] * 5
+    lib.ss_in_proj.restype = ctypes.c_int
     lib.ss_strerror.argtypes = [ctypes.c_int]
     lib.ss_strerror.restype = ctypes.c_char_p
     lib.ss_last_hip_error.restype = ctypes.c_int
@@ -304,3 +318,91 @@ def ss_step(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, h, z=None, *, h_out=None, y=No
     if rc != 0:
         raise SSError(rc, lib)
     return y
+
+
+def make_block_dims(batch, seqlen, d_in, dim, dstate, plan=SS_PLAN_AUTO, layout=SS_LAYOUT_AUTO):
+    return ss_block_dims(batch, seqlen, d_in, dim, dstate, plan, layout)
+
+
+def block_workspace_size(dims) -> int:
+    lib = load()
+    n = ctypes.c_size_t(0)
+    rc = lib.ss_block_fwd_workspace_size(ctypes.byref(dims), ctypes.byref(n))
+    if rc != 0:
+        raise SSError(rc, lib)
+    return n.value
+
+
+def ss_block_fwd(u, W_in, W_x, dt_bias, A, Dskip, h0=None, *, return_final=False,
+                 return_proj=False, y=None, workspace=None, plan=SS_PLAN_AUTO,
+                 layout=SS_LAYOUT_AUTO, stream=None):
+    """Projections and gated scan through the C ABI: u [B, L, d_in] bf16, W_in [2D, d_in]
+    bf16, W_x [1 + 2N, D] float32, dt_bias, Dskip [D], A [D, N], h0 [B, D, N] float32.
+    Returns y [B, L, D] float32; with return_final also h_final [B, D, N]; with return_proj
+    also a dict of the projections x, z [B, L, D], dt [B, L], B, C [B, L, N] (float32)."""
+    import torch
+    lib = load()
+    if u.dim() != 3:
+        raise ValueError(f"u must be [B, L, d_in], got shape {tuple(u.shape)}")
+    Bn, L, Din = u.shape
+    D, N = A.shape
+    dev = u.device
+    f32, bf = torch.float32, torch.bfloat16
+    _check(u, "u", (Bn, L, Din), bf, dev)
+    _check(W_in, "W_in", (2 * D, Din), bf, dev)
+    _check(W_x, "W_x", (1 + 2 * N, D), f32, dev)
+    _check(dt_bias, "dt_bias", (D,), f32, dev)
+    _check(A, "A", (D, N), f32, dev)
+    _check(Dskip, "Dskip", (D,), f32, dev)
+    _check(h0, "h0", (Bn, D, N), f32, dev)
+    dims = make_block_dims(Bn, L, Din, D, N, plan, layout)
+    if y is None:
+        y = torch.empty((Bn, L, D), dtype=f32, device=dev)
+    _check(y, "y", (Bn, L, D), f32, dev)
+    hf = torch.empty((Bn, D, N), dtype=f32, device=dev) if return_final else None
+    proj = None
+    if return_proj:
+        proj = dict(x=torch.empty((Bn, L, D), dtype=f32, device=dev),
+                    z=torch.empty((Bn, L, D), dtype=f32, device=dev),
+                    dt=torch.empty((Bn, L), dtype=f32, device=dev),
+                    B=torch.empty((Bn, L, N), dtype=f32, device=dev),
+                    C=torch.empty((Bn, L, N), dtype=f32, device=dev))
+    need = block_workspace_size(dims)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wbytes = workspace.numel() * workspace.element_size()
+    g = (lambda k: None) if proj is None else (lambda k: _ptr(proj[k]))
+    rc = lib.ss_block_fwd(ctypes.byref(dims), _ptr(u), _ptr(W_in), _ptr(W_x), _ptr(dt_bias),
+                          _ptr(A), _ptr(Dskip), _ptr(h0), _ptr(y), _ptr(hf), g("x"), g("z"),
+                          g("dt"), g("B"), g("C"), _ptr(workspace), wbytes, _stream(stream))
+    if rc != 0:
+        raise SSError(rc, lib)
+    out = (y,)
+    if return_final:
+        out += (hf,)
+    if return_proj:
+        out += (proj,)
+    return out if len(out) > 1 else y
+
+
+def ss_in_proj(u, W_in, *, x=None, z=None, stream=None):
+    """[x | z] = u · W_inᵀ through the C ABI: u [B, L, d_in] bf16, W_in [2D, d_in] bf16;
+    returns x, z [B, L, D] float32."""
+    import torch
+    lib = load()
+    Bn, L, Din = u.shape
+    D = W_in.shape[0] // 2
+    dev = u.device
+    _check(u, "u", (Bn, L, Din), torch.bfloat16, dev)
+    _check(W_in, "W_in", (2 * D, Din), torch.bfloat16, dev)
+    if x is None:
+        x = torch.empty((Bn, L, D), dtype=torch.float32, device=dev)
+    if z is None:
+        z = torch.empty((Bn, L, D), dtype=torch.float32, device=dev)
+    _check(x, "x", (Bn, L, D), torch.float32, dev)
+    _check(z, "z", (Bn, L, D), torch.float32, dev)
+    dims = make_block_dims(Bn, L, Din, D, 1)
+    rc = lib.ss_in_proj(ctypes.byref(dims), _ptr(u), _ptr(W_in), _ptr(x), _ptr(z), _stream(stream))
+    if rc != 0:
+        raise SSError(rc, lib)
+    return x, z

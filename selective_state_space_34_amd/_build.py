@@ -15,7 +15,8 @@ OBJDIR = os.path.join(ROOT, "_build")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libss.so")
 
-SOURCES = ["ss_api.cpp", "ss_fwd.hip", "ss_fwdg.hip", "ss_carry.hip", "ss_bwd.hip", "ss_step.hip"]
+SOURCES = ["ss_api.cpp", "ss_fwd.hip", "ss_fwdg.hip", "ss_carry.hip", "ss_bwd.hip", "ss_step.hip",
+           "ss_block.hip"]
 HEADERS = ["ss_device.h", "ss_kernels.h", "ss_plan.h"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -35,6 +35,45 @@ ss::DtRows dt_rows(const ss::Plan& p) {
     return p.dt_shared ? ss::DtRows{p.L, 0, 1} : seq_rows(p);
 }
 
+// Workspace carving of ss_block_fwd: every intermediate, the projection partials and the
+// scan's own workspace.  Depends on the dims alone.
+struct BlockPlan {
+    int64_t M, Din, D, N, S;
+    ss_dims sd;                 // the scan: float32, token-major, Δraw shared
+    size_t off_x, off_z, off_dt, off_B, off_C, off_part, off_scan, scan_ws, total;
+};
+
+int make_block_plan(const ss_block_dims& bd, BlockPlan* out) {
+    BlockPlan bp{};
+    if (bd.batch <= 0 || bd.seqlen <= 0 || bd.d_in <= 0 || bd.dim <= 0 || bd.dstate <= 0)
+        return SS_ERR_DIMS;
+    if (bd.d_in % 8 != 0 || bd.dim % 4 != 0) return SS_ERR_DIMS;
+    const int64_t lim = int64_t(1) << 40;
+    if (bd.batch > lim / bd.seqlen) return SS_ERR_DIMS;
+    bp.M = bd.batch * bd.seqlen; bp.Din = bd.d_in; bp.D = bd.dim; bp.N = bd.dstate;
+    if (bp.M > lim / bp.Din || bp.M > lim / (2 * bp.D)) return SS_ERR_DIMS;
+    bp.sd = ss_dims{bd.batch, bd.seqlen, bd.dim, bd.dstate, SS_F32, bd.plan, 0, bd.layout,
+                    SS_DISC_EULER, SS_ORDER_BLD, SS_DT_SHARED};
+    ss::Plan p;
+    const int rc = ss::make_plan(bp.sd, false, &p);
+    if (rc != SS_OK) return rc;
+    bp.S = ss::xproj_splits(bp.M, bp.D, int(bp.N));
+    const size_t f = sizeof(float);
+    const size_t MD = size_t(bp.M) * size_t(bp.D), MN = size_t(bp.M) * size_t(bp.N);
+    size_t off = 0;
+    bp.off_x = off; off = ss::align256(off + MD * f);
+    bp.off_z = off; off = ss::align256(off + MD * f);
+    bp.off_dt = off; off = ss::align256(off + size_t(bp.M) * f);
+    bp.off_B = off; off = ss::align256(off + MN * f);
+    bp.off_C = off; off = ss::align256(off + MN * f);
+    bp.off_part = off;
+    off = ss::align256(off + size_t(bp.S) * size_t(bp.M) * size_t(1 + 2 * bp.N) * f);
+    bp.off_scan = off; bp.scan_ws = p.ws_total; off = ss::align256(off + p.ws_total);
+    bp.total = off;
+    *out = bp;
+    return SS_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -243,6 +282,66 @@ int ss_bwd(const ss_dims* dims, const void* x, const void* dt_raw, const float* 
     e = ss::launch_bwd_reduce(bl, stream);
     if (e != hipSuccess) return hip_fail(e);
     return SS_OK;
+}
+
+int ss_in_proj(const ss_block_dims* dims, const void* u, const void* W_in, float* x, float* z,
+               hipStream_t stream) {
+    if (!dims) return SS_ERR_NULL;
+    BlockPlan bp;
+    const int rc = make_block_plan(*dims, &bp);
+    if (rc != SS_OK) return rc;
+    if (!u || !W_in || !x || !z) return SS_ERR_NULL;
+    if (!aligned16(u) || !aligned16(W_in) || !aligned16(x) || !aligned16(z)) return SS_ERR_ALIGN;
+    const hipError_t e = ss::launch_gemm_bf16_nt(u, W_in, x, z, bp.M, 2 * bp.D, bp.Din, bp.D,
+                                                 bp.D, bp.D, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    return SS_OK;
+}
+
+int ss_block_fwd_workspace_size(const ss_block_dims* dims, size_t* bytes) {
+    if (!dims || !bytes) return SS_ERR_NULL;
+    BlockPlan bp;
+    const int rc = make_block_plan(*dims, &bp);
+    if (rc != SS_OK) return rc;
+    *bytes = bp.total;
+    return SS_OK;
+}
+
+int ss_block_fwd(const ss_block_dims* dims, const void* u, const void* W_in, const float* W_x,
+                 const float* dt_bias, const float* A, const float* Dskip, const float* h0,
+                 float* y, float* h_final, float* x, float* z, float* dt, float* Bm, float* Cm,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!dims) return SS_ERR_NULL;
+    BlockPlan bp;
+    const int rc = make_block_plan(*dims, &bp);
+    if (rc != SS_OK) return rc;
+    if (!u || !W_in || !W_x || !dt_bias || !A || !Dskip || !y) return SS_ERR_NULL;
+    const void* req[] = {u, W_in, W_x, dt_bias, A, Dskip, y};
+    for (const void* q : req)
+        if (!aligned16(q)) return SS_ERR_ALIGN;
+    const void* opt[] = {h0, h_final, x, z, dt, Bm, Cm};
+    for (const void* q : opt)
+        if (q && !aligned16(q)) return SS_ERR_ALIGN;
+    if (!workspace || workspace_bytes < bp.total) return SS_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return SS_ERR_ALIGN;
+
+    char* ws = static_cast<char*>(workspace);
+    float* xb = x ? x : reinterpret_cast<float*>(ws + bp.off_x);
+    float* zb = z ? z : reinterpret_cast<float*>(ws + bp.off_z);
+    float* dtb = dt ? dt : reinterpret_cast<float*>(ws + bp.off_dt);
+    float* Bb = Bm ? Bm : reinterpret_cast<float*>(ws + bp.off_B);
+    float* Cb = Cm ? Cm : reinterpret_cast<float*>(ws + bp.off_C);
+    float* part = reinterpret_cast<float*>(ws + bp.off_part);
+    // 1. [x | z] = u · W_inᵀ on the matrix cores
+    hipError_t e = ss::launch_gemm_bf16_nt(u, W_in, xb, zb, bp.M, 2 * bp.D, bp.Din, bp.D, bp.D,
+                                           bp.D, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    // 2. [Δraw | B | C] = x · W_xᵀ
+    e = ss::launch_xproj(xb, W_x, part, dtb, Bb, Cb, bp.M, bp.D, int(bp.N), stream);
+    if (e != hipSuccess) return hip_fail(e);
+    // 3. the gated scan, token-major with the shared Δraw
+    return ss_fwd(&bp.sd, xb, dtb, dt_bias, A, Bb, Cb, Dskip, zb, h0, y, h_final, nullptr,
+                  ws + bp.off_scan, bp.scan_ws, stream);
 }
 
 }  // extern "C"

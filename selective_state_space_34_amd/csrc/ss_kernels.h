@@ -143,4 +143,16 @@ hipError_t launch_step(int bf16, const StepLaunch& p, hipStream_t s);
 hipError_t launch_bwd(int bf16, const BwdLaunch& p, hipStream_t s);
 hipError_t launch_bwd_reduce(const BwdLaunch& p, hipStream_t s);
 
+// Block projections (ss_block.hip).  C0 | C1 = A [M, K] · W [Nc, K]ᵀ (bf16 in, fp32 out),
+// split at column nsplit; K % 8 == 0, 16-byte aligned rows.
+hipError_t launch_gemm_bf16_nt(const void* A, const void* W, float* C0, float* C1, int64_t M,
+                               int64_t Nc, int64_t K, int64_t nsplit, int64_t ld0, int64_t ld1,
+                               hipStream_t s);
+// [Δ | B | C] = x [M, D] · Wx [1 + 2N, D]ᵀ (fp32) through split-K partials part
+// [S, M, 1 + 2N] (S = xproj_splits); D % 4 == 0.
+int64_t xproj_splits(int64_t M, int64_t D, int N);
+int64_t xproj_split_len(int64_t D, int64_t S);
+hipError_t launch_xproj(const float* x, const float* Wx, float* part, float* dt, float* Bm,
+                        float* Cm, int64_t M, int64_t D, int N, hipStream_t s);
+
 }  // namespace ss

@@ -37,7 +37,7 @@ def test_exports_match_header(lib):
 
 
 def test_version_and_strerror(lib):
-    assert lib.ss_version() == (0 << 16) | 5
+    assert lib.ss_version() == (0 << 16) | 6
     for code in ss.ERRORS:
         assert len(lib.ss_strerror(code)) > 0
     assert b"unknown" in lib.ss_strerror(12345)
@@ -192,3 +192,36 @@ def test_step_validation(lib):
         a = list(args)
         a[i] = ctypes.c_void_p(FAKE + 4)
         assert call(good, a) == -4, i
+
+
+def test_block_validation(lib):
+    """ss_block_fwd checks dims, pointers, alignment and workspace before any launch."""
+    F = ctypes.c_void_p(FAKE)
+    # u W_in W_x dt_bias A Dskip | h0 | y | h_final x z dt Bm Cm
+    args = [F] * 6 + [None] + [F] + [None] * 6
+
+    def call(dims, a, ws=None, wbytes=0):
+        return lib.ss_block_fwd(None if dims is None else ctypes.byref(dims), *a, ws,
+                                ctypes.c_size_t(wbytes), None)
+    good = ss.make_block_dims(2, 64, 64, 128, 16)
+    assert call(None, args) == -1
+    for bad in (ss.make_block_dims(0, 64, 64, 128, 16), ss.make_block_dims(2, 64, 60, 128, 16),
+                ss.make_block_dims(2, 64, 64, 126, 16), ss.make_block_dims(2, 64, 64, 128, 5),
+                ss.make_block_dims(2, 64, 64, 128, 64)):
+        assert call(bad, args) == -2
+    assert call(ss.make_block_dims(2, 64, 64, 128, 16, plan=7), args) == -3
+    for i in (0, 1, 2, 3, 4, 5, 7):
+        a = list(args)
+        a[i] = None
+        assert call(good, a) == -1, i
+    for i in range(14):
+        a = list(args)
+        a[i] = ctypes.c_void_p(FAKE + 4)
+        assert call(good, a) == -4, i
+    need = ss.block_workspace_size(good)
+    # x, z [M, D], dt [M], B, C [M, N], the projection partials, then the scan's workspace
+    M, D, N = 128, 128, 16
+    assert need >= (2 * M * D + M + 2 * M * N) * 4
+    assert call(good, args) == -5
+    assert call(good, args, ws=F, wbytes=need - 1) == -5
+    assert call(good, args, ws=ctypes.c_void_p(FAKE + 8), wbytes=need) == -4

@@ -46,7 +46,7 @@ def test_recipe():
 
 def test_workloads_table():
     names = [w.name for w in WORKLOADS]
-    assert names == ["c0", "c1", "c2", "c3", "c4", "d1"]
+    assert names == ["c0", "c1", "c2", "c3", "c4", "d1", "p2"]
     c2 = WORKLOADS[2]
     assert (c2.batch, c2.seqlen, c2.dim, c2.dstate, c2.dtype, c2.gate) == (8, 2048, 5120, 16, "bf16", True)
     assert WORKLOADS[3].seqlen == 1048576 and WORKLOADS[4].backward
