@@ -148,40 +148,87 @@ __global__ __launch_bounds__(kGThreads) void gemm_bf16_nt_kernel(
 }
 
 // ---- selection projections -----------------------------------------------------------------
-// part[s, m, o] = Σ_{k in split s} x[m, k] · Wx[o, k], o < P = 1 + 2N.  One token per thread;
-// the split's slice of Wx sits in LDS and every lane reads the same 16 bytes (broadcast).
-// grid = (ceil(M / 256), S), block = 256.  kc (split length) is a multiple of 4, D % 4 == 0.
+// part[s, m, o] = Σ_{k in split s} x[m, k] · Wx[o, k], o < P = 1 + 2N: a product with few
+// columns, register-tiled on the vector ALUs.  Thread (token group tg, output group og) owns
+// 4 tokens x 4 outputs (16 accumulators); per K step it reads 4 x values and 4 weights as two
+// 16-byte LDS reads for 16 FMAs.  A workgroup covers TM = 4·TG tokens and all outputs, and
+// one split of K, staged 32 steps at a time: x rows are read coalesced (8 threads per 128-byte
+// row piece) and stored transposed, [k][token], so a thread's 4 tokens are adjacent.
+// grid = (ceil(M / TM), S), block = TG·OG threads.  D % 4 == 0.
+template <int P>
+struct XprojShape {
+    static constexpr int OG = (P + 3) / 4;           // output groups of 4
+    static constexpr int TG = 256 / OG;              // token groups of 4
+    static constexpr int TM = 4 * TG;                // tokens per workgroup
+    static constexpr int THREADS = TG * OG;
+    static constexpr int KT = 32;                    // K steps per LDS stage
+    static constexpr int XS = TM + 4;                // row stride of the transposed x tile
+    static constexpr int WS = 4 * OG;                // row stride of the weight tile
+};
+
 template <int P>
 __global__ __launch_bounds__(256) void xproj_partial_kernel(
     const float* __restrict__ x, const float* __restrict__ Wx, float* __restrict__ part,
     int64_t M, int64_t D, int64_t kc) {
-    extern __shared__ __align__(16) float wl[];   // [P][kc]
+    using Sh = XprojShape<P>;
+    __shared__ __align__(16) float xs[Sh::KT * Sh::XS];
+    __shared__ __align__(16) float wsh[Sh::KT * Sh::WS];
+    const int tid = threadIdx.x;
+    const int tg = tid % Sh::TG, og = tid / Sh::TG;
     const int s = blockIdx.y;
+    const int64_t m0 = int64_t(blockIdx.x) * Sh::TM;
     const int64_t k0 = int64_t(s) * kc;
     const int64_t k1 = (k0 + kc < D) ? k0 + kc : D;
-    const int64_t nk = k1 - k0;
-    for (int64_t e = threadIdx.x; e < int64_t(P) * nk; e += 256) {
-        const int64_t o = e / nk, k = e % nk;
-        wl[o * kc + k] = Wx[o * D + k0 + k];
-    }
-    __syncthreads();
-    const int64_t m = int64_t(blockIdx.x) * 256 + threadIdx.x;
-    if (m >= M) return;
-    float acc[P];
+
+    float acc[4][4];
 #pragma unroll
-    for (int o = 0; o < P; ++o) acc[o] = 0.0f;
-    const float* xr = x + m * D + k0;
-    for (int64_t k = 0; k < nk; k += 4) {
-        const float4 xv = *reinterpret_cast<const float4*>(xr + k);
+    for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int o = 0; o < P; ++o) {
-            const float4 w = *reinterpret_cast<const float4*>(wl + o * kc + k);
-            acc[o] = fmaf(xv.x, w.x, fmaf(xv.y, w.y, fmaf(xv.z, w.z, fmaf(xv.w, w.w, acc[o]))));
+        for (int c = 0; c < 4; ++c) acc[a][c] = 0.0f;
+
+    for (int64_t kb = k0; kb < k1; kb += Sh::KT) {
+        const int nk = int((k1 - kb < Sh::KT) ? k1 - kb : Sh::KT);   // a multiple of 4
+        __syncthreads();                                               // previous stage read
+        for (int e = tid; e < Sh::TM * (Sh::KT / 4); e += Sh::THREADS) {
+            const int tok = e / (Sh::KT / 4), q = e % (Sh::KT / 4);
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (m0 + tok < M && 4 * q < nk) v = *reinterpret_cast<const float4*>(x + (m0 + tok) * D + kb + 4 * q);
+            xs[(4 * q + 0) * Sh::XS + tok] = v.x;
+            xs[(4 * q + 1) * Sh::XS + tok] = v.y;
+            xs[(4 * q + 2) * Sh::XS + tok] = v.z;
+            xs[(4 * q + 3) * Sh::XS + tok] = v.w;
+        }
+        for (int e = tid; e < Sh::WS * (Sh::KT / 4); e += Sh::THREADS) {
+            const int o = e / (Sh::KT / 4), q = e % (Sh::KT / 4);
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (o < P && 4 * q < nk) v = *reinterpret_cast<const float4*>(Wx + int64_t(o) * D + kb + 4 * q);
+            wsh[(4 * q + 0) * Sh::WS + o] = v.x;
+            wsh[(4 * q + 1) * Sh::WS + o] = v.y;
+            wsh[(4 * q + 2) * Sh::WS + o] = v.z;
+            wsh[(4 * q + 3) * Sh::WS + o] = v.w;
+        }
+        __syncthreads();
+#pragma unroll 8
+        for (int k = 0; k < Sh::KT; ++k) {
+            const float4 xv = *reinterpret_cast<const float4*>(xs + k * Sh::XS + 4 * tg);
+            const float4 wv = *reinterpret_cast<const float4*>(wsh + k * Sh::WS + 4 * og);
+            const float xa[4] = {xv.x, xv.y, xv.z, xv.w};
+            const float wa[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) acc[a][c] = fmaf(xa[a], wa[c], acc[a][c]);
         }
     }
-    float* pr = part + (int64_t(s) * M + m) * P;
 #pragma unroll
-    for (int o = 0; o < P; ++o) pr[o] = acc[o];
+    for (int a = 0; a < 4; ++a) {
+        const int64_t m = m0 + 4 * tg + a;
+        if (m >= M) continue;
+        float* pr = part + (int64_t(s) * M + m) * P;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            if (4 * og + c < P) pr[4 * og + c] = acc[a][c];
+    }
 }
 
 // Σ over the S splits -> Δraw [M], B [M, N], C [M, N].  One thread per (m, o).
@@ -212,16 +259,23 @@ hipError_t launch_gemm_bf16_nt(const void* A, const void* W, float* C0, float* C
     return hipGetLastError();
 }
 
+static int xproj_tile_tokens(int N) {
+    switch (N) {
+        case 1: return XprojShape<3>::TM;
+        case 2: return XprojShape<5>::TM;
+        case 4: return XprojShape<9>::TM;
+        case 8: return XprojShape<17>::TM;
+        case 16: return XprojShape<33>::TM;
+        default: return XprojShape<65>::TM;
+    }
+}
+
 int64_t xproj_splits(int64_t M, int64_t D, int N) {
-    // enough workgroups for the part (about 2048), each split a multiple of 4 elements and
-    // its slice of W_x within 64 KB of LDS
-    const int64_t P = 1 + 2 * N;
-    const int64_t mb = (M + 255) / 256;
-    int64_t S = (2048 + mb - 1) / mb;
-    const int64_t kmax = ((16384 / P) / 4) * 4;
-    if ((D + S - 1) / S > kmax) S = (D + kmax - 1) / kmax;
-    if (S > D / 4) S = D / 4 > 0 ? D / 4 : 1;
-    return S;
+    // about 1024 workgroups in all, each split at least 64 steps of K
+    const int64_t mb = (M + xproj_tile_tokens(N) - 1) / xproj_tile_tokens(N);
+    int64_t S = (1024 + mb - 1) / mb;
+    if (S > D / 64) S = D / 64;
+    return S < 1 ? 1 : S;
 }
 
 int64_t xproj_split_len(int64_t D, int64_t S) { return ((D + S - 1) / S + 3) / 4 * 4; }
@@ -229,9 +283,10 @@ int64_t xproj_split_len(int64_t D, int64_t S) { return ((D + S - 1) / S + 3) / 4
 template <int P>
 static hipError_t launch_xproj_p(const float* x, const float* Wx, float* part, int64_t M,
                                  int64_t D, int64_t S, int64_t kc, hipStream_t s) {
-    const size_t lds = size_t(P) * size_t(kc) * sizeof(float);
-    hipLaunchKernelGGL((xproj_partial_kernel<P>), dim3(unsigned((M + 255) / 256), unsigned(S)),
-                       dim3(256), lds, s, x, Wx, part, M, D, kc);
+    using Sh = XprojShape<P>;
+    hipLaunchKernelGGL((xproj_partial_kernel<P>),
+                       dim3(unsigned((M + Sh::TM - 1) / Sh::TM), unsigned(S)), dim3(Sh::THREADS),
+                       0, s, x, Wx, part, M, D, kc);
     return hipGetLastError();
 }
 

@@ -90,7 +90,9 @@ def test_block_full_size_sampled(gpu):
     assert_close(ycm[chans], ref["y"], TOL, "y (sampled channels)")
 
 
-@pytest.mark.parametrize("shape", [(1, 100, 40, 36), (2, 256, 128, 128), (1, 517, 264, 200)],
+# the last shape spans many tiles and is ragged in M, 2D and d_in
+@pytest.mark.parametrize("shape", [(1, 100, 40, 36), (2, 256, 128, 128), (1, 517, 264, 200),
+                                   (1, 4100, 264, 4100)],
                          ids=lambda s: "B{}L{}Din{}D{}".format(*s))
 def test_in_proj(gpu, shape):
     """The block's first stage alone (ss_in_proj): every element of x and z."""
