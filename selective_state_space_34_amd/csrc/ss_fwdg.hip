@@ -83,11 +83,12 @@ template <int K> struct Raw<bf16_t, K> {
             w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
         }
     }
-    // elements p[0], p[st], ..., p[(K-1)·st] (token-major rows)
-    __device__ __forceinline__ void load_strided(const bf16_t* p, int64_t st) {
+    // elements base[off], base[off + st], ..., base[off + (K-1)·st] (token-major rows); 32-bit
+    // offsets from a base shared by the wave, so each load takes one offset register
+    __device__ __forceinline__ void load_strided(const bf16_t* base, uint32_t off, uint32_t st) {
 #pragma unroll
         for (int i = 0; i < K / 2; ++i)
-            w[i] = uint32_t(p[2 * i * st].bits) | (uint32_t(p[(2 * i + 1) * st].bits) << 16);
+            w[i] = uint32_t(base[off + 2 * i * st].bits) | (uint32_t(base[off + (2 * i + 1) * st].bits) << 16);
     }
     __device__ __forceinline__ void decode(float (&o)[K]) const {
 #pragma unroll
@@ -111,9 +112,9 @@ template <int K> struct Raw<float, K> {
             }
         }
     }
-    __device__ __forceinline__ void load_strided(const float* p, int64_t st) {
+    __device__ __forceinline__ void load_strided(const float* base, uint32_t off, uint32_t st) {
 #pragma unroll
-        for (int i = 0; i < K; ++i) v[i] = p[i * st];
+        for (int i = 0; i < K; ++i) v[i] = base[off + i * st];
     }
     __device__ __forceinline__ void decode(float (&o)[K]) const {
 #pragma unroll
@@ -238,6 +239,14 @@ __device__ __forceinline__ void scang_body(
     const int64_t dts = dtr.ts;
     const Tin* zr = kGate ? z + row : nullptr;
     float* yr = kAgg ? nullptr : y + row;
+    // token-major: the batch row's bases (uniform) and 32-bit element offsets (L·D < 2^31)
+    const int64_t brow = int64_t(b) * L * D;
+    const Tin* xb = x + brow;
+    const Tin* zb = kGate ? z + brow : nullptr;
+    float* yb = kAgg ? nullptr : y + brow;
+    const Tin* db = dt_raw + int64_t(b) * dtr.sb;
+    const uint32_t dofs = uint32_t(d * dtr.sd), d32 = uint32_t(d), D32 = uint32_t(D);
+    const uint32_t dts32 = uint32_t(dtr.ts);
     // B, C of row b: [N, L] (channel-major) or [L, N] (token-major)
     const Tin* Bb = Bm + int64_t(b) * N * L;
     const Tin* Cb = Cm + int64_t(b) * N * L;
@@ -277,9 +286,10 @@ __device__ __forceinline__ void scang_body(
         for (int hh = 0; hh < 2; ++hh) {
             const int64_t te = t0 + kHalf * hh + kH * l;
             if constexpr (kTok) {
-                xn[hh].load_strided(xr + te * ts, ts);
-                dn[hh].load_strided(dr + te * dts, dts);
-                if (kGate && !kAgg) zn[hh].load_strided(zr + te * ts, ts);
+                const uint32_t t32 = uint32_t(te);
+                xn[hh].load_strided(xb, t32 * D32 + d32, D32);
+                dn[hh].load_strided(db, t32 * dts32 + dofs, dts32);
+                if (kGate && !kAgg) zn[hh].load_strided(zb, t32 * D32 + d32, D32);
             } else {
                 xn[hh].load(xr + te);
                 dn[hh].load(dr + te);
@@ -402,8 +412,9 @@ __device__ __forceinline__ void scang_body(
                 if (valid) {
                     const int64_t te = t0 + kHalf * hh + kH * l;
                     if constexpr (kTok) {
+                        const uint32_t o = uint32_t(te) * D32 + d32;
 #pragma unroll
-                        for (int i = 0; i < kH; ++i) yr[(te + i) * ts] = out[i];
+                        for (int i = 0; i < kH; ++i) yb[o + uint32_t(i) * D32] = out[i];
                     } else {
                         store_k<kH>(yr + te, out);
                     }

@@ -80,8 +80,10 @@ inline int make_plan(const ss_dims& d, bool backward, Plan* out) {
     // balance the SIMDs better at B*D = 40960 but saturate the LDS (their operand
     // traffic per state-step is higher) and lose on every workload; one lane per channel
     // loses on every workload too.
-    // (token-major rows are read element by element, so only channel-major needs L % 8)
-    const int gmax = !(p.vec || p.tok) ? 0 : N >= 8 ? 8 : N >= 4 ? 4 : 0;
+    // (token-major rows are read element by element, so only channel-major needs L % 8;
+    // token-major offsets within a batch row are 32-bit: L·D < 2^31)
+    const bool tile_ok = p.tok ? p.L * p.D < (int64_t(1) << 31) : p.vec != 0;
+    const int gmax = !tile_ok ? 0 : N >= 8 ? 8 : N >= 4 ? 4 : 0;
     if (d.layout == SS_LAYOUT_LANE) p.group = 0;
     else if (d.layout == SS_LAYOUT_OCT) p.group = gmax;
     else p.group = gmax >= 4 ? 4 : 0;
