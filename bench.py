@@ -45,12 +45,12 @@ STEP_SOURCES = ["ss_step.hip", "ss_device.h", "ss_plan.h", "ss_api.cpp", "ss_ker
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 MEASURED_TRAFFIC = {
     # (workload, disc): first-order (0) or exact zero-order hold (1)
-    ("c2", 0): {"sources": FWD_SOURCES, "fetch_kib": 323075, "write_kib": 399107,
-                "sources_sha256": "3057dccd95a97f3bcdb62bf8373fab26d1937509dc6b0e01cafdeebdc4e111df"},
-    ("c2", 1): {"sources": FWD_SOURCES, "fetch_kib": 329492, "write_kib": 396194,
-                "sources_sha256": "3057dccd95a97f3bcdb62bf8373fab26d1937509dc6b0e01cafdeebdc4e111df"},
-    ("d1", 0): {"sources": STEP_SOURCES, "fetch_kib": 45071, "write_kib": 87040,
-                "sources_sha256": "df0ce1f23149492f9a50e44a13847060c50e27f296b1f498e20474f70e01c9a5"},
+    ("c2", 0): {"sources": FWD_SOURCES, "fetch_kib": 341866, "write_kib": 398425,
+                "sources_sha256": "ee791002627c79e9536b6c0c70d0728e96789ed0518b1cba170b9edb69dd86b5"},
+    ("c2", 1): {"sources": FWD_SOURCES, "fetch_kib": 354264, "write_kib": 396125,
+                "sources_sha256": "ee791002627c79e9536b6c0c70d0728e96789ed0518b1cba170b9edb69dd86b5"},
+    ("d1", 0): {"sources": STEP_SOURCES, "fetch_kib": 45070, "write_kib": 87040,
+                "sources_sha256": "68c1384fea7a5b4a5bae0bbe377cce036e36926baefd928b2ced842c429c5cf0"},
 }
 
 
