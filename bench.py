@@ -188,6 +188,9 @@ def run_decode(args, w, inp):
     def step():
         ss.ss_step(x, dtr, dtb, A, Bm, Cm, Dk, h, z=z, y=y, disc=args.disc, stream=stream)
 
+    if args.graph:
+        return run_decode_graph(args, w, step_graphable=lambda s: ss.ss_step(
+            x, dtr, dtb, A, Bm, Cm, Dk, h, z=z, y=y, disc=args.disc, stream=s))
     # the state (B*D*N*4 bytes) fits in the 256 MB Infinity Cache: an untimed 1 GiB write
     # between steps evicts it, so each timed step reads and writes HBM
     flush = torch.empty(args.flush_mib << 20, dtype=torch.uint8, device=dev) if args.flush_mib else None
@@ -341,6 +344,58 @@ def run_block(args, w, inp):
     print(json.dumps(out), flush=True)
 
 
+def run_decode_graph(args, w, step_graphable):
+    """Decode as a serving loop: `steps` consecutive ss_step calls captured in one HIP graph
+    and replayed; the state stays warm between steps, as it does between tokens."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _ in range(args.warmup):
+            step_graphable(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for _ in range(args.steps):
+            step_graphable(s)
+    torch.cuda.current_stream().wait_stream(s)
+    g.replay()
+    torch.cuda.synchronize()
+    reps = 5
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_step = e0.elapsed_time(e1) * 1e-3 / (reps * args.steps)
+    s_in = 2 if w.dtype == "bf16" else 4
+    mb = step_min_bytes(w, s_in, args.dt_shared)
+    gbps = mb / t_step / 1e9
+    elems = w.batch * w.dim
+    log(f"[bench] decode loop in one graph: {args.steps} steps x {reps} replays, "
+        f"{t_step * 1e6:.2f} us per step; {gbps:.0f} GB/s of minimum bytes (state warm)")
+    out = {
+        "metric": "selective-scan decode step B·D channel-steps/s (graph-replayed loop, state warm)",
+        "value": elems / t_step, "unit": "elem/s", "n_gpus": 1, "steps": args.steps * reps,
+        "warmup": args.warmup, "ms_per_step": t_step * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{w.name}: {w.label}", "batch": w.batch, "seqlen": 1,
+                   "dim": w.dim, "dstate": w.dstate, "in_dtype": w.dtype, "gate": w.gate,
+                   "graph": True, "cache_flush_mib": 0,
+                   "disc": "zoh" if args.disc else "first-order",
+                   "wall_s": wall},
+        "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": gbps / HBM_PEAK_GBPS, "traffic": None,
+                     "kernel": "ss_step (step_kernel, graph replay)",
+                     "launch_us": t_step * 1e6, "traffic_algorithmic_bytes": mb},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def calib_copy(args, dev):
     """One device copy of a known size, for scaling the HBM byte counters."""
     import torch
@@ -377,6 +432,8 @@ def main():
                     help="0 first-order input term (δ·B·x), 1 exact zero-order hold (forward only)")
     ap.add_argument("--no-ckpt", action="store_true",
                     help="fwd+bwd: recompute chunk start states instead of using checkpoints")
+    ap.add_argument("--graph", action="store_true",
+                    help="decode: capture the timed steps in one HIP graph and replay it")
     ap.add_argument("--flush-mib", type=int, default=1024,
                     help="decode, and forwards under 512 MB: untimed write of this many MiB "
                          "before each timed step (0 = none)")

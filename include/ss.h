@@ -33,7 +33,9 @@
  *     ss_dims pointer, which is a host pointer read during the call only.
  *   - The caller owns every buffer and the workspace; the library never
  *     allocates, frees or synchronises.  All work is enqueued on `stream`
- *     (0 = the null stream) and the call returns without waiting.
+ *     (0 = the null stream) and the call returns without waiting.  Calls only
+ *     launch kernels (no memset, no copy), so they can be captured in a HIP graph
+ *     and replayed.
  *   - Outputs are overwritten, never accumulated into (the reduced gradients
  *     dA, dB, dC, dD, ddt_bias included).  Inputs and outputs must not alias.
  *   - The library keeps no state between calls and is re-entrant; concurrent
