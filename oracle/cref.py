@@ -38,7 +38,7 @@ def load():
         lib.s6o_threads.restype = ctypes.c_int
         lib.s6o_fwd.argtypes = [I, I, I, I] + [P] * 9 + [P, I, P, P, ctypes.c_int]
         lib.s6o_fwd.restype = ctypes.c_int
-        lib.s6o_bwd.argtypes = [I, I, I, I] + [P] * 11 + [P] * 9
+        lib.s6o_bwd.argtypes = [I, I, I, I] + [P] * 11 + [P] * 9 + [ctypes.c_int]
         lib.s6o_bwd.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -86,8 +86,9 @@ def fwd(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, z=None, h0=None, chans=None, want_
     return y, hf
 
 
-def bwd(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, dy, z=None, h0=None, dh_final=None):
-    """Backward over all channels.  Returns the same dict as oracle.ss_ref.ss_bwd."""
+def bwd(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, dy, z=None, h0=None, dh_final=None, zoh=False):
+    """Backward over all channels.  Returns the same dict as oracle.ss_ref.ss_bwd.
+    zoh: gradients of the exact zero-order-hold forward."""
     lib = load()
     x, dt_raw, dt_bias, A, Bm, Cm, Dskip, dy, z, h0, dh_final = map(
         _f32, (x, dt_raw, dt_bias, A, Bm, Cm, Dskip, dy, z, h0, dh_final))
@@ -101,7 +102,7 @@ def bwd(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, dy, z=None, h0=None, dh_final=None
     rc = lib.s6o_bwd(Bn, L, D, N, _p(x), _p(dt_raw), _p(dt_bias), _p(A), _p(Bm), _p(Cm),
                      _p(Dskip), _p(z), _p(h0), _p(dy), _p(dh_final),
                      _p(out["dx"]), _p(out["ddt_raw"]), _p(out["dz"]), _p(out["ddt_bias"]),
-                     _p(out["dA"]), _p(out["dB"]), _p(out["dC"]), _p(out["dD"]), _p(out["dh0"]))
+                     _p(out["dA"]), _p(out["dB"]), _p(out["dC"]), _p(out["dD"]), _p(out["dh0"]), int(bool(zoh)))
     if rc != 0:
         raise RuntimeError(f"s6o_bwd failed: {rc}")
     return out

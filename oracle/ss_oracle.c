@@ -100,13 +100,31 @@ int s6o_fwd(int64_t B, int64_t L, int64_t D, int64_t N,
  * dA [D,N]; dB, dC [B,N,L]; dD [D]; dh0 [B,D,N] (required iff h0).
  * Forward states are stored for the whole sequence of the channel, then the
  * adjoint g = ∂/∂h_t is swept from t = L-1 to 0 (see oracle/ss_ref.py).
+ * zoh = 1: gradients of the exact zero-order-hold forward, whose input factor
+ * f = expm1(δA)/A has ∂f/∂δ = Ā and ∂f/∂A = (δĀ - f)/A (series below |δA| = 1e-2).
  */
+/* ∂f/∂A of the exact-hold factor: δ² Σ_k (k+1) u^k/(k+2)!, u = δA, for |u| < 1e-2
+ * (ten terms), else the closed form (δ e^u - expm1(u)/A)/A. */
+static double zoh_dfda(double delta, double an) {
+    double u = delta * an;
+    if (fabs(u) < 1e-2) {
+        double sum = 0.0, fact = 2.0, pw = 1.0;
+        for (int k = 0; k < 10; ++k) {
+            sum += (k + 1) * pw / fact;
+            pw *= u;
+            fact *= k + 3;
+        }
+        return delta * delta * sum;
+    }
+    return (delta * exp(u) - expm1(u) / an) / an;
+}
+
 int s6o_bwd(int64_t B, int64_t L, int64_t D, int64_t N,
             const float* x, const float* dt_raw, const float* dt_bias, const float* A,
             const float* Bm, const float* Cm, const float* Dskip, const float* z, const float* h0,
             const float* dy, const float* dh_final,
             double* dx, double* ddt_raw, double* dz, double* ddt_bias, double* dA,
-            double* dB, double* dC, double* dD, double* dh0) {
+            double* dB, double* dC, double* dD, double* dh0, int zoh) {
     if (B <= 0 || L <= 0 || D <= 0 || N <= 0) return -1;
     if ((z && !dz) || (h0 && !dh0)) return -1;
     int nth = 1;
@@ -153,8 +171,10 @@ int s6o_bwd(int64_t B, int64_t L, int64_t D, int64_t N,
             double delta = softplus_d(bias + (double)dr[t]);
             double s = 0.0;
             for (int64_t n = 0; n < N; ++n) {
-                double abar = exp(delta * (double)A[d * N + n]);
-                double hn = abar * hs[t * N + n] + delta * (double)Br[n * L + t] * xt;
+                double an = (double)A[d * N + n];
+                double abar = exp(delta * an);
+                double fb = (zoh && an != 0.0) ? expm1(delta * an) / an : delta;
+                double hn = abar * hs[t * N + n] + fb * (double)Br[n * L + t] * xt;
                 hs[(t + 1) * N + n] = hn;
                 s += (double)Cr[n * L + t] * hn;
             }
@@ -181,12 +201,19 @@ int s6o_bwd(int64_t B, int64_t L, int64_t D, int64_t N,
                 double an = (double)A[d * N + n];
                 double abar = exp(delta * an);
                 double hprev = hs[t * N + n];
+                /* input factor f and its partials: (δ, 1, 0) first order */
+                double fb = delta, dfd = 1.0, dfa = 0.0;
+                if (zoh) {
+                    fb = an != 0.0 ? expm1(delta * an) / an : delta;
+                    dfd = abar;
+                    dfa = zoh_dfda(delta, an);
+                }
                 g[n] += ds * Ct;
                 myC[n * L + t] += ds * hs[(t + 1) * N + n];
-                myB[n * L + t] += g[n] * delta * xt;
-                dxt += g[n] * delta * Bt;
-                ddel += g[n] * (an * abar * hprev + Bt * xt);
-                myA[n] += g[n] * delta * abar * hprev;
+                myB[n * L + t] += g[n] * fb * xt;
+                dxt += g[n] * fb * Bt;
+                ddel += g[n] * (an * abar * hprev + dfd * Bt * xt);
+                myA[n] += g[n] * (delta * abar * hprev + dfa * Bt * xt);
                 g[n] *= abar;
             }
             dx[c * L + t] = dxt;

@@ -72,6 +72,31 @@ def bbar_factor(dl, A, zoh):
     return np.where(A == 0.0, dl * np.ones_like(A), num / safe)
 
 
+def bbar_factor_grads(dl, A, zoh):
+    """Partial derivatives (∂f/∂δ, ∂f/∂A) of the factor f of bbar_factor.
+
+    First order, f = δ: (1, 0).  Exact hold, f = (e^{δA} - 1)/A:
+      ∂f/∂δ = e^{δA} = Ā
+      ∂f/∂A = (δĀ - f)/A = δ² Σ_{k>=0} (k+1)(δA)^k/(k+2)!   (term-by-term derivative of
+              f = δ Σ_k (δA)^k/(k+1)!), the closed form where |δA| >= 1e-2 and the series,
+              ten terms, below that, where the closed form would cancel.
+    """
+    ones = np.ones_like(dl * A)
+    if not zoh:
+        return ones, np.zeros_like(ones)
+    u = dl * A
+    abar = np.exp(u)
+    small = np.abs(u) < 1e-2
+    series = np.zeros_like(u)
+    fact = 2.0                                                   # (k+2)!
+    for k in range(10):
+        series = series + (k + 1) * u ** k / fact
+        fact *= k + 3
+    safe = np.where(small, 1.0, A * ones)
+    closed = (dl * abar - np.expm1(u) / safe) / safe
+    return abar, np.where(small, dl * dl * series, closed)
+
+
 def ss_fwd(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, z=None, h0=None, zoh=False):
     """Forward scan.  Returns (y [B,D,L], h_final [B,D,N]) in float64.
 
@@ -98,7 +123,7 @@ def ss_fwd(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, z=None, h0=None, zoh=False):
     return y, h
 
 
-def ss_bwd(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, dy, z=None, h0=None, dh_final=None):
+def ss_bwd(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, dy, z=None, h0=None, dh_final=None, zoh=False):
     """Gradients of sum(dy*y) + sum(dh_final*h_final) with respect to every input.
 
     Returns a dict of float64 arrays: dx, ddt_raw, dz (None without gate) [B,D,L];
@@ -113,6 +138,10 @@ def ss_bwd(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, dy, z=None, h0=None, dh_final=N
       dδ_t  = Σ_n g (A Ā_t h_{t-1} + B_t x_t) ;  dA += g δ_t Ā_t h_{t-1}
       ddt_raw_t = dδ_t σ(u_t) ;  ddt_bias += ddt_raw_t
       g     = Ā_t ⊙ g                              (after t = 0 this is dh0)
+    With zoh=True the input term is f B x with f = (Ā - 1)/A (bbar_factor) in place of δ B x:
+      dB_t += g f x ;  dx_t = ds_t D + Σ_n g f B_t
+      dδ_t  = Σ_n g (A Ā_t h_{t-1} + Ā_t B_t x_t)   (∂f/∂δ = Ā)
+      dA   += g (δ_t Ā_t h_{t-1} + ∂f/∂A B_t x_t)
     """
     x, dt_raw, dt_bias, A, Bm, Cm, Dskip, dy, z, h0, dh_final = map(
         _f64, (x, dt_raw, dt_bias, A, Bm, Cm, Dskip, dy, z, h0, dh_final))
@@ -130,7 +159,8 @@ def ss_bwd(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, dy, z=None, h0=None, dh_final=N
         dl = delta[:, :, t, None]
         abar = np.exp(dl * A[None])
         abar_all[t] = abar
-        hs[t + 1] = abar * hs[t] + dl * Bm[:, None, :, t] * x[:, :, t, None]
+        fb = bbar_factor(dl, A[None], zoh)
+        hs[t + 1] = abar * hs[t] + fb * Bm[:, None, :, t] * x[:, :, t, None]
         s_all[:, :, t] = (Cm[:, None, :, t] * hs[t + 1]).sum(-1) + Dskip[None, :] * x[:, :, t]
 
     dx = np.empty((Bn, D, L))
@@ -154,12 +184,15 @@ def ss_bwd(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, dy, z=None, h0=None, dh_final=N
         g = g + ds[:, :, None] * Cm[:, None, :, t]
         dC[:, :, t] += np.einsum("bd,bdn->bn", ds, hs[t + 1])
         dD += (ds * xt).sum(axis=0)
-        dB[:, :, t] += np.einsum("bdn,bd->bn", g, dl * xt)
-        dx[:, :, t] = ds * Dskip[None, :] + (g * Bm[:, None, :, t]).sum(-1) * dl
+        fb = bbar_factor(dl[:, :, None], A[None], zoh)             # [B,D,N]
+        dfd, dfa = bbar_factor_grads(dl[:, :, None], A[None], zoh)
+        bx = Bm[:, None, :, t] * xt[:, :, None]                    # B_t x_t  [B,D,N]
+        dB[:, :, t] += np.einsum("bdn,bdn->bn", g, fb * xt[:, :, None])
+        dx[:, :, t] = ds * Dskip[None, :] + (g * fb * Bm[:, None, :, t]).sum(-1)
         abar = abar_all[t]
         hprev = hs[t]
-        ddelta = (g * (A[None] * abar * hprev + Bm[:, None, :, t] * xt[:, :, None])).sum(-1)
-        dA += (g * dl[:, :, None] * abar * hprev).sum(axis=0)
+        ddelta = (g * (A[None] * abar * hprev + dfd * bx)).sum(-1)
+        dA += (g * (dl[:, :, None] * abar * hprev + dfa * bx)).sum(axis=0)
         ddt_raw[:, :, t] = ddelta * sig_u[:, :, t]
         g = abar * g
     ddt_bias = ddt_raw.sum(axis=(0, 2))
