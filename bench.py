@@ -119,18 +119,21 @@ def alu_slots_per_elem(w, disc=0):
     return per_state + elem
 
 
-def bwd_alu_slots_per_elem(w):
+def bwd_alu_slots_per_elem(w, disc=0):
     """Algorithmic VALU lane-slots per element of the backward (transcendental = 2 slots).
     Per state: recompute h (δ·A, exp 2, δx·B, FMA: 5); adjoint g += ds·C (1), dC term ds·h (1),
     dB term g·δx (1), Σ g·B (1), g·Ā·h_prev (2), dA FMA (1), Σ A·g·Ā·h_prev (1), g *= Ā (1);
-    the channel sums of dB and dC (2) -> 17 x N.  Per element: softplus 9, sigmoid(u) 4,
-    dx 2, dΔ 2, dD 1, with a gate sigmoid(z) 4 + ds 2 + dz 5; bf16 widening per bf16 input."""
+    the channel sums of dB and dC (2) -> 17 x N.  The exact zero-order hold adds per state its
+    gain in the recompute and again in the adjoint (3 + 3, as in the forward), ∂g/∂A from the
+    gain (2), x·g (1), g·B apart from its sum (1), g·B·x (1) and its FMAs into dA and dδ (2)
+    -> 30 x N.  Per element: softplus 9, sigmoid(u) 4, dx 2, dΔ 2, dD 1, with a gate
+    sigmoid(z) 4 + ds 2 + dz 5; bf16 widening per bf16 input."""
     elem = 9 + 4 + 2 + 2 + 1
     if w.gate:
         elem += 4 + 2 + 5
     if w.dtype == "bf16":
         elem += 3 if w.gate else 2
-    return 17 * w.dstate + elem
+    return (30 if disc else 17) * w.dstate + elem
 
 
 def cpu_baseline(w, inp, budget_s=4.0, disc=0):
@@ -453,10 +456,6 @@ def main():
 
     w = workload(args.workload)
     log(f"[bench] workload {w.name}: {w.label}")
-    if args.disc and w.backward:
-        print("bench.py: the exact zero-order hold has no backward (ss_bwd rejects it)",
-              file=sys.stderr)
-        sys.exit(2)
     t0 = time.perf_counter()
     inp = workload_inputs(w) if w.d_in else workload_inputs(w, dt_shared=args.dt_shared)
     log(f"[bench] inputs generated in {time.perf_counter() - t0:.1f}s")
@@ -489,7 +488,7 @@ def main():
     if w.backward:
         dy = t32(np.ascontiguousarray(lay(inp.dy)))
         wsb = torch.empty(ss.workspace_size(dims, backward=True), dtype=torch.uint8, device=dev)
-        grads = ss.ss_bwd(x, dtr, dtb, A, Bm, Cm, Dk, dy, z=z, order=args.order)
+        grads = ss.ss_bwd(x, dtr, dtb, A, Bm, Cm, Dk, dy, z=z, order=args.order, disc=args.disc)
         # training use: the forward keeps its 16-step state checkpoints for the backward
         if not args.no_ckpt:
             nck = (w.seqlen + ss.CKPT_STEPS - 1) // ss.CKPT_STEPS
@@ -502,7 +501,7 @@ def main():
 
     def bwd_call():
         ss.ss_bwd(x, dtr, dtb, A, Bm, Cm, Dk, dy, z=z, h_ckpt=hck, workspace=wsb, out=grads,
-                  order=args.order, stream=stream)
+                  order=args.order, disc=args.disc, stream=stream)
 
     def step():
         fwd_call()
@@ -559,7 +558,8 @@ def main():
     mb = min_bytes(w, s_in, args.dt_shared)
     t_avg = float(per.mean())
     value = elems * args.steps / wall
-    slots_pe = alu_slots_per_elem(w, args.disc) + (bwd_alu_slots_per_elem(w) if w.backward else 0)
+    slots_pe = alu_slots_per_elem(w, args.disc) + (bwd_alu_slots_per_elem(w, args.disc)
+                                                    if w.backward else 0)
     slots = elems * slots_pe
     alu_achieved = slots / t_avg / 1e12
     hbm_achieved = mb / t_avg / 1e9

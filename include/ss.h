@@ -85,8 +85,8 @@ typedef enum { SS_LAYOUT_AUTO = 0, SS_LAYOUT_QUAD = 1, SS_LAYOUT_LANE = 2, SS_LA
 /* Discretisation of the input term (page "3.2 선택적 스캔(Selective Scan) 알고리즘과 정보의
  * 압축 및 선별", §2.1; Ā = exp(δA) in both).
  *   SS_DISC_EULER — B̄x = δ·B·x, the first-order form of the hold (the default).
- *   SS_DISC_ZOH   — B̄x = (exp(δA) - 1)/A · B·x, the exact zero-order hold (forward and
- *                   ss_step; ss_bwd returns SS_ERR_UNSUPPORTED). */
+ *   SS_DISC_ZOH   — B̄x = (exp(δA) - 1)/A · B·x, the exact zero-order hold (ss_fwd, ss_bwd
+ *                   and ss_step). */
 typedef enum { SS_DISC_EULER = 0, SS_DISC_ZOH = 1 } ss_disc;
 
 /* Memory order of the sequence tensors (the pages write x as (B, L, D)).
@@ -153,7 +153,9 @@ int ss_fwd(const ss_dims* dims,
            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Backward: gradients of sum(dy·y) + sum(dh_final·h_final) with respect to every
- * input, recomputing the states from the inputs (§3.3) instead of storing them.
+ * input, recomputing the states from the inputs (§3.3) instead of storing them.  With
+ * dims->disc = SS_DISC_ZOH they are the gradients of the exact hold (its gain
+ * g = (exp(δA) - 1)/A has ∂g/∂δ = exp(δA) and ∂g/∂A = (δ·exp(δA) - g)/A).
  *   Inputs as ss_fwd; dy required; dh_final NULL = zero.
  *   h_ckpt : NULL = the chunk start states are recomputed here; else the checkpoints an
  *            ss_fwd call on these same inputs (and h0) wrote, from which every 16-step

@@ -234,15 +234,16 @@ def ss_fwd(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, z=None, h0=None, *, return_fina
 
 
 def ss_bwd(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, dy, z=None, h0=None, dh_final=None, *,
-           h_ckpt=None, workspace=None, chunk=0, order=SS_ORDER_BDL, out=None, stream=None):
+           h_ckpt=None, workspace=None, chunk=0, order=SS_ORDER_BDL, disc=SS_DISC_EULER,
+           out=None, stream=None):
     """Backward through the C ABI.  Returns a dict dx, ddt_raw, ddt_bias, dA, dB, dC, dD,
     dz (None without gate), dh0 (None without h0); all float32, each shaped like its input
     (order as in ss_fwd).  h_ckpt: the checkpoints of an ss_fwd call on the same inputs
-    (optional)."""
+    (optional; made with the same disc).  disc: the discretisation the forward used."""
     import torch
     lib = load()
     _check_inputs(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, z, h0, order)
-    dims = _dims_of(x, A, dt_raw, SS_PLAN_CHUNKED, chunk, order=order)
+    dims = _dims_of(x, A, dt_raw, SS_PLAN_CHUNKED, chunk, disc=disc, order=order)
     Bn, D, L = _seq_shape(x, order)
     N = A.shape[1]
     dev = x.device

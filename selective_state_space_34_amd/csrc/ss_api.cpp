@@ -226,8 +226,6 @@ int ss_bwd(const ss_dims* dims, const void* x, const void* dt_raw, const float* 
     const void* opt[] = {z, h0, dh_final, dz, dh0, h_ckpt};
     for (const void* q : opt)
         if (q && !aligned16(q)) return SS_ERR_ALIGN;
-    // the adjoint kernels implement the first-order input term only
-    if (p.zoh) return SS_ERR_UNSUPPORTED;
     if (!workspace || workspace_bytes < p.ws_total) return SS_ERR_WORKSPACE;
     if (!aligned16(workspace)) return SS_ERR_ALIGN;
 
@@ -249,6 +247,7 @@ int ss_bwd(const ss_dims* dims, const void* x, const void* dt_raw, const float* 
     bl.B = p.B; bl.L = p.L; bl.D = p.D; bl.N = p.N; bl.chunk = p.chunk; bl.K = int(p.K);
     bl.vec = p.vec;
     bl.tok = p.tok;
+    bl.zoh = p.zoh;
     bl.dtr = dt_rows(p);
     bl.gdr = seq_rows(p);
     bl.ddt_shared = nullptr;

@@ -185,7 +185,7 @@ __device__ __forceinline__ void load_chunk_bc(float* __restrict__ lds, const Tin
 // ---------------------------------------------------------------------------------------
 // 1. chunk aggregates.  grid (ceil(D/64), K, B), 256 threads.
 // ---------------------------------------------------------------------------------------
-template <typename Tin, int S, bool kGate, bool kFwd>
+template <typename Tin, int S, bool kGate, bool kFwd, bool kZoh>
 __global__ __launch_bounds__(kBThreads) void bwd_agg_kernel(
     const Tin* __restrict__ x, const Tin* __restrict__ dt_raw, const Tin* __restrict__ z,
     const float* __restrict__ dy, const float* __restrict__ dt_bias, const float* __restrict__ A,
@@ -210,11 +210,13 @@ __global__ __launch_bounds__(kBThreads) void bwd_agg_kernel(
     const int ntiles = (nsteps + kBT - 1) / kBT;
     load_chunk_bc<Tin, NP>(bc_lds, Bm, Cm, b, Nr, L, t0c, nsteps, tid, tok);
 
-    float A2[S], h[S], P[S], Rv[S];
+    float A2[S], iA[S], h[S], P[S], Rv[S];
 #pragma unroll
     for (int s = 0; s < S; ++s) {
         const int n = n0 + s;
-        A2[s] = (n < Nr) ? A[d * Nr + n] * kLog2e : 0.0f;
+        const float a = (n < Nr) ? A[d * Nr + n] : 0.0f;
+        A2[s] = a * kLog2e;
+        if (kZoh && kFwd) iA[s] = 1.0f / a;
         h[s] = 0.0f; P[s] = 1.0f; Rv[s] = 0.0f;
     }
     const float bias = dt_bias[d];
@@ -240,7 +242,9 @@ __global__ __launch_bounds__(kBThreads) void bwd_agg_kernel(
             const float dl = ok ? softplus(bias + dv[i]) : 0.0f;
             const float ds = ok ? (kGate ? gv[i] * silu(zv[i]) : gv[i]) : 0.0f;
             dsum += dl;
-            *reinterpret_cast<float4*>(myrow + 4 * (kBPer * j + i)) = make_float4(dl, dl * xv[i], ds, 0.0f);
+            // (δ, δ·x) or, with the exact hold, (δ, x): its gain depends on the state
+            *reinterpret_cast<float4*>(myrow + 4 * (kBPer * j + i)) =
+                make_float4(dl, kZoh ? xv[i] : dl * xv[i], ds, 0.0f);
         }
         wave_sync();
         const float* bt = bc_lds + tb * R;
@@ -260,8 +264,13 @@ __global__ __launch_bounds__(kBThreads) void bwd_agg_kernel(
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int s = 0; s < S; ++s) {
-                const float a = exp2_hw(rc.x * A2[s]);
-                if (kFwd) h[s] = fmaf(a, h[s], rc.y * bc.v[s]);
+                const float t2 = rc.x * A2[s];
+                const float a = exp2_hw(t2);
+                if (kFwd) {
+                    float bx = rc.y * bc.v[s];
+                    if (kZoh) bx *= zoh_gain(t2, a, rc.x, iA[s]);
+                    h[s] = fmaf(a, h[s], bx);
+                }
                 P[s] *= a;
                 Rv[s] = fmaf(P[s], rc.z * cc.v[s], Rv[s]);
             }
@@ -293,7 +302,7 @@ __global__ __launch_bounds__(kBThreads) void bwd_agg_kernel(
 // ---------------------------------------------------------------------------------------
 // Two waves per SIMD: the tile's 16 recomputed states per lane and the per-step Σ_n
 // partials take most of the 256 registers a wave then has.
-template <typename Tin, int S, bool kGate, bool kCk>
+template <typename Tin, int S, bool kGate, bool kCk, bool kZoh>
 __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_chunk_kernel(
     const Tin* __restrict__ x, const Tin* __restrict__ dt_raw, const Tin* __restrict__ z,
     const float* __restrict__ dy, const float* __restrict__ dt_bias, const float* __restrict__ A,
@@ -372,7 +381,7 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     };
     if (kCk) load_tile(ntiles - 1);
     load_chunk_bc<Tin, NP>(bc_lds, Bm, Cm, b, Nr, L, t0c, nsteps, tid, tok);
-    float A2[S], An[S], g[S], dA[S];
+    float A2[S], An[S], iA[S], g[S], dA[S];
     float ck[kCk ? 1 : kBMaxTiles][S];          // state entering each tile (uniform index)
 #pragma unroll
     for (int s = 0; s < S; ++s) {
@@ -380,6 +389,7 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
         const bool ok = n < Nr;
         An[s] = ok ? A[d * Nr + n] : 0.0f;
         A2[s] = An[s] * kLog2e;
+        if (kZoh) iA[s] = 1.0f / An[s];
         g[s] = ok ? q[sidx + n] : 0.0f;
         dA[s] = 0.0f;
         if (!kCk) ck[0][s] = ok ? h_start[sidx + n] : 0.0f;
@@ -409,7 +419,8 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
 #pragma unroll
             for (int i = 0; i < kBPer; ++i) {
                 const float dl = softplus(bias + dv[i]);  // every step of a non-last tile is real
-                *reinterpret_cast<float2*>(myrow + 4 * (kBPer * j + i)) = make_float2(dl, dl * xv[i]);
+                *reinterpret_cast<float2*>(myrow + 4 * (kBPer * j + i)) =
+                    make_float2(dl, kZoh ? xv[i] : dl * xv[i]);
             }
             wave_sync();
             const float* bt = bc_lds + tb * R;
@@ -425,7 +436,13 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
                 }
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int s = 0; s < S; ++s) h[s] = fmaf(exp2_hw(rc.x * A2[s]), h[s], rc.y * bc.v[s]);
+                for (int s = 0; s < S; ++s) {
+                    const float t2 = rc.x * A2[s];
+                    const float ab = exp2_hw(t2);
+                    float bx = rc.y * bc.v[s];
+                    if (kZoh) bx *= zoh_gain(t2, ab, rc.x, iA[s]);
+                    h[s] = fmaf(ab, h[s], bx);
+                }
             }
 #pragma unroll
             for (int s = 0; s < S; ++s) ck[tile + 1][s] = h[s];
@@ -494,7 +511,10 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
                 float acc = 0.0f;
 #pragma unroll
                 for (int s = 0; s < S; ++s) {
-                    h[s] = fmaf(exp2_hw(rc.x * A2[s]), h[s], dxr * bc.v[s]);
+                    const float t2 = rc.x * A2[s];
+                    const float ab = exp2_hw(t2);
+                    const float bx = kZoh ? rc.y * bc.v[s] * zoh_gain(t2, ab, rc.x, iA[s]) : dxr * bc.v[s];
+                    h[s] = fmaf(ab, h[s], bx);
                     hs[t][s] = h[s];
                     if (kGate) acc = fmaf(cc.v[s], h[s], acc);
                 }
@@ -545,11 +565,29 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
 #pragma unroll
                 for (int s = 0; s < S; ++s) {
                     const float hp = (t > 0) ? hs[t > 0 ? t - 1 : 0][s] : hc[s];
+                    const float t2 = rc.x * A2[s];
+                    const float ab = exp2_hw(t2);
                     g[s] = fmaf(rc.z, cc.v[s], g[s]);
                     cC[s] = rc.z * hs[t][s];
-                    cB[s] = g[s] * dxr;
-                    pxa = fmaf(g[s], bc.v[s], pxa);
-                    g[s] *= exp2_hw(rc.x * A2[s]);
+                    if (kZoh) {
+                        // input term f·B·x, f the state's gain: dB += g f x, Σ_n g f B for dx,
+                        // dA += g (∂f/∂A) B x, and ∂f/∂δ = Ā puts (Ā g) B x into dδ
+                        const float f = zoh_gain(t2, ab, rc.x, iA[s]);
+                        const float gB = g[s] * bc.v[s];
+                        const float gBx = gB * rc.y;
+                        cB[s] = g[s] * (rc.y * f);
+                        pxa = fmaf(gB, f, pxa);
+                        dA[s] = fmaf(zoh_gain_da(t2, ab, rc.x, iA[s], f), gBx, dA[s]);
+                        // dA has no use inside the tile: without this empty register constraint
+                        // the compiler sinks every step's ∂f/∂A term to the tile's end and holds
+                        // all their operands live (it emits no instruction)
+                        asm volatile("" : "+v"(dA[s]));
+                        pda = fmaf(ab, gBx, pda);
+                    } else {
+                        cB[s] = g[s] * dxr;
+                        pxa = fmaf(g[s], bc.v[s], pxa);
+                    }
+                    g[s] *= ab;
                     const float w = g[s] * hp;
                     dA[s] = fmaf(w, rc.x, dA[s]);
                     pda = fmaf(w, An[s], pda);
@@ -597,8 +635,9 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
                 const float4 rw = *reinterpret_cast<const float4*>(myrow + 4 * tj);  // (δ, x, ds, σ)
                 const int64_t tg = t0c + tb + tj;
                 const bool ok = tg < t1c;
-                const float ox = fmaf(rw.z, Dd, rw.x * PX);
-                const float od = fmaf(rw.y, PX, PD) * rw.w;
+                // exact hold: PX already carries the gain and PD the input term of dδ
+                const float ox = fmaf(rw.z, Dd, kZoh ? PX : rw.x * PX);
+                const float od = (kZoh ? PD : fmaf(rw.y, PX, PD)) * rw.w;
                 accD += ok ? rw.z * rw.y : 0.0f;
                 accT += ok ? od : 0.0f;
                 // park (dx, dΔraw) in the step's row, which no later batch reads: the tile's
@@ -774,17 +813,21 @@ static void launch_bwd_g(const BwdLaunch& p, dim3 grid, hipStream_t s) {
     const Tin* Bm = static_cast<const Tin*>(p.Bm);
     const Tin* Cm = static_cast<const Tin*>(p.Cm);
     with_bool(p.h_ckpt != nullptr, [&](auto ck) {
+      return with_bool(p.zoh != 0, [&](auto zoh) {
         if (p.stage == 0)
-            hipLaunchKernelGGL((bwd_agg_kernel<Tin, S, kGate, !ck.value>), grid, dim3(kBThreads), 0,
+            hipLaunchKernelGGL((bwd_agg_kernel<Tin, S, kGate, !ck.value, zoh.value && !ck.value>),
+                               grid, dim3(kBThreads), 0,
                                s, x, dr, z, p.dy, p.dt_bias, p.A, Bm, Cm, p.h_end, p.rev_end, p.dsum,
                                p.L, p.D, int(p.N), p.chunk, p.K, p.vec, p.tok, p.dtr);
         else
-            hipLaunchKernelGGL((bwd_chunk_kernel<Tin, S, kGate, ck.value>), grid, dim3(kBThreads), 0,
+            hipLaunchKernelGGL((bwd_chunk_kernel<Tin, S, kGate, ck.value, zoh.value>), grid,
+                               dim3(kBThreads), 0,
                                s, x, dr, z, p.dy, p.dt_bias, p.A, p.Dskip, Bm, Cm, p.h_ckpt, p.h_end,
                                p.rev_end, p.dx, p.ddt_raw, p.dz, p.dbc_part, p.ddt_part,
                                p.ddt_shared ? p.ddt_blk : nullptr, p.L, p.D, int(p.N), p.chunk,
                                p.K, p.vec, p.tok, p.dtr, p.gdr);
         return hipSuccess;
+      });
     });
 }
 

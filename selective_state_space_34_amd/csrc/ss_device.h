@@ -52,6 +52,24 @@ __device__ __forceinline__ float zoh_gain(float t2, float abar, float delta, flo
     return fabsf(t2) < kZohSwitch2 ? delta * p : q;
 }
 
+// ∂g/∂A of the same gain, for the backward: δ²·ψ(u) with ψ(u) = Σ_k (k+1)u^k/(k+2)!, the
+// term-by-term derivative of φ.  For |u| < 1/8, the degree-4 series in t2 (truncation below
+// 7.3e-8 relative); elsewhere the closed form (δĀ - g)·(1/A), g the caller's zoh_gain value,
+// whose cancellation costs at most a factor 16 over the error of g (at |u| = 1/8).
+constexpr float kZohD1 = 0.23104906018664842f;    // (k+1) ln2^k / (k+2)!
+constexpr float kZohD2 = 0.06005662673977517f;
+constexpr float kZohD3 = 0.011100821732964315f;
+constexpr float kZohD4 = 0.0016030215179380794f;
+__device__ __forceinline__ float zoh_gain_da(float t2, float abar, float delta, float inv_a,
+                                             float gain) {
+    float p = fmaf(t2, kZohD4, kZohD3);
+    p = fmaf(t2, p, kZohD2);
+    p = fmaf(t2, p, kZohD1);
+    p = fmaf(t2, p, 0.5f);
+    const float q = fmaf(delta, abar, -gain) * inv_a;
+    return fabsf(t2) < kZohSwitch2 ? (delta * delta) * p : q;
+}
+
 // sigmoid(z) = 1 / (1 + e^{-z}); e^{-z} = inf for z << 0 gives exactly 0.
 __device__ __forceinline__ float sigmoid(float z) { return rcp_hw(1.0f + exp2_hw(-z * kLog2e)); }
 

@@ -107,6 +107,7 @@ struct BwdLaunch {
     int tok;           // 1: token-major x, z, dy, dx, dz [B, L, D] and B, C, dB, dC [B, L, N]
     DtRows dtr;        // Δraw rows
     DtRows gdr;        // rows the per-channel Δraw gradient is written to (ddt_raw)
+    int zoh;           // 1: gradients of the exact zero-order hold
     float* ddt_shared; // nullable: Δraw shared by the channels; its gradient [B, L]
     float* ddt_blk;    // with ddt_shared: per-64-channel-block sums [B, ceil(D/64), L]
 };

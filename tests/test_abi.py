@@ -163,8 +163,9 @@ def test_bwd_validation(lib):
     a[11] = ctypes.c_void_p(FAKE + 4)
     assert call(good, a) == -4
     assert call(good, args) == -5
-    # the exact zero-order hold has no backward; an unknown disc is rejected as an enum
-    assert call(ss.make_dims(2, 64, 32, 16, ss.SS_F32, disc=ss.SS_DISC_ZOH), args) == -7
+    # the exact zero-order hold passes validation (then needs its workspace); an unknown
+    # disc is rejected as an enum
+    assert call(ss.make_dims(2, 64, 32, 16, ss.SS_F32, disc=ss.SS_DISC_ZOH), args) == -5
     assert call(ss.make_dims(2, 64, 32, 16, ss.SS_F32, disc=3), args) == -3
 
 
