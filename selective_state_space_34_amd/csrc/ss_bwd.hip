@@ -231,8 +231,8 @@ __global__ __launch_bounds__(kBThreads) void bwd_agg_kernel(
     for (int tile = 0; tile < ntiles; ++tile) {
         const int tb = tile * kBT;
         const int64_t te = t0c + tb + kBPer * j;
-        float xv[4], dv[4], gv[4], zv[4];
-        load4(x + row, te, t1c, vec, ts, xv);
+        float xv[4] = {0.0f, 0.0f, 0.0f, 0.0f}, dv[4], gv[4], zv[4];
+        if (kFwd) load4(x + row, te, t1c, vec, ts, xv);   // only the forward pair uses x
         load4(drr, te, t1c, vec, dtr.ts, dv);
         load4(dy + row, te, t1c, vec, ts, gv);
         if (kGate) load4(z + row, te, t1c, vec, ts, zv);
@@ -590,6 +590,7 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
                     g[s] *= ab;
                     const float w = g[s] * hp;
                     dA[s] = fmaf(w, rc.x, dA[s]);
+                    asm volatile("" : "+v"(dA[s]));
                     pda = fmaf(w, An[s], pda);
                 }
                 pxb[i] = pxa;
