@@ -53,6 +53,12 @@ __device__ __forceinline__ float qsum(float v) {
     return v;
 }
 
+// v from lane O of this lane's quad (DPP quad permutation)
+template <int O>
+__device__ __forceinline__ float quad_bcast(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), O * 0x55, 0xf, 0xf, false));
+}
+
 __device__ __forceinline__ void wave_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -195,9 +201,7 @@ __global__ __launch_bounds__(kBThreads) void bwd_agg_kernel(
     constexpr int NP = 4 * S;
     constexpr int R = 2 * NP + 4;
     __shared__ __align__(16) float bc_lds[kBMaxSteps * R];
-    __shared__ __align__(16) float rows[4 * 16 * kRW];
     const int tid = threadIdx.x;
-    const int lane = tid & 63;
     const int j = tid & 3;
     const int n0 = j * S;
     const int64_t d_raw = int64_t(blockIdx.x) * kBChan + (tid >> 2);
@@ -208,7 +212,52 @@ __global__ __launch_bounds__(kBThreads) void bwd_agg_kernel(
     const int64_t t1c = (t0c + chunk < L) ? t0c + chunk : L;
     const int nsteps = int(t1c - t0c);
     const int ntiles = (nsteps + kBT - 1) / kBT;
-    load_chunk_bc<Tin, NP>(bc_lds, Bm, Cm, b, Nr, L, t0c, nsteps, tid, tok);
+    // element t of channel (b, d) at row[t·ts]; Δraw at its own rows
+    const int64_t row = tok ? int64_t(b) * L * D + d : (int64_t(b) * D + d) * L;
+    const int64_t ts = tok ? D : 1;
+    const Tin* drr = dt_raw + int64_t(b) * dtr.sb + d * dtr.sd;
+    const float bias = dt_bias[d];
+
+    // Lane j of a channel owns the 16 steps [16 j, 16 j + 16) of the chunk: the four lanes
+    // read the chunk's whole run of each input at once (a 64-step bf16 run is one 128-byte
+    // line), before anything waits, and each lane forms δ, ds (and the input term) of its
+    // own steps.  Steps past the chunk's end are identities (δ = 0, ds = 0).
+    const int64_t tl = t0c + kBT * j;
+    float dl[kBT], dsv[kBT], xin[kFwd ? kBT : 1];
+    float dsum = 0.0f;
+    {
+        float xv[kBT], dv[kBT], gv[kBT], zv[kBT];
+#pragma unroll
+        for (int q = 0; q < kBT / 4; ++q) {
+            float t4[4];
+            load4(drr, tl + 4 * q, t1c, vec, dtr.ts, t4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dv[4 * q + i] = t4[i];
+            load4(dy + row, tl + 4 * q, t1c, vec, ts, t4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) gv[4 * q + i] = t4[i];
+            if (kGate) {
+                load4(z + row, tl + 4 * q, t1c, vec, ts, t4);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) zv[4 * q + i] = t4[i];
+            }
+            if (kFwd) {
+                load4(x + row, tl + 4 * q, t1c, vec, ts, t4);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) xv[4 * q + i] = t4[i];
+            }
+        }
+        load_chunk_bc<Tin, NP>(bc_lds, Bm, Cm, b, Nr, L, t0c, nsteps, tid, tok);
+#pragma unroll
+        for (int i = 0; i < kBT; ++i) {
+            const bool ok = tl + i < t1c;
+            dl[i] = ok ? softplus(bias + dv[i]) : 0.0f;
+            dsv[i] = ok ? (kGate ? gv[i] * silu(zv[i]) : gv[i]) : 0.0f;
+            dsum += dl[i];
+            // δ·x, or x with the exact hold (its gain depends on the state)
+            if (kFwd) xin[i] = kZoh ? xv[i] : dl[i] * xv[i];
+        }
+    }
 
     float A2[S], iA[S], h[S], P[S], Rv[S];
 #pragma unroll
@@ -219,64 +268,42 @@ __global__ __launch_bounds__(kBThreads) void bwd_agg_kernel(
         if (kZoh && kFwd) iA[s] = 1.0f / a;
         h[s] = 0.0f; P[s] = 1.0f; Rv[s] = 0.0f;
     }
-    const float bias = dt_bias[d];
-    // element t of channel (b, d) at row[t·ts]; Δraw at its own rows
-    const int64_t row = tok ? int64_t(b) * L * D + d : (int64_t(b) * D + d) * L;
-    const int64_t ts = tok ? D : 1;
-    const Tin* drr = dt_raw + int64_t(b) * dtr.sb + d * dtr.sd;
-    float* myrow = rows + (tid >> 6) * 16 * kRW + (lane >> 2) * kRW;
-    float dsum = 0.0f;
     __syncthreads();
 
-    for (int tile = 0; tile < ntiles; ++tile) {
-        const int tb = tile * kBT;
-        const int64_t te = t0c + tb + kBPer * j;
-        float xv[4] = {0.0f, 0.0f, 0.0f, 0.0f}, dv[4], gv[4], zv[4];
-        if (kFwd) load4(x + row, te, t1c, vec, ts, xv);   // only the forward pair uses x
-        load4(drr, te, t1c, vec, dtr.ts, dv);
-        load4(dy + row, te, t1c, vec, ts, gv);
-        if (kGate) load4(z + row, te, t1c, vec, ts, zv);
+    // tile T's steps sit in lane T of each quad: broadcast each step's values to the quad
+    auto tile = [&](auto tc) {
+        constexpr int T = decltype(tc)::value;
+        const float* bt = bc_lds + T * kBT * R;
 #pragma unroll
-        for (int i = 0; i < kBPer; ++i) {
-            const bool ok = te + i < t1c;
-            const float dl = ok ? softplus(bias + dv[i]) : 0.0f;
-            const float ds = ok ? (kGate ? gv[i] * silu(zv[i]) : gv[i]) : 0.0f;
-            dsum += dl;
-            // (δ, δ·x) or, with the exact hold, (δ, x): its gain depends on the state
-            *reinterpret_cast<float4*>(myrow + 4 * (kBPer * j + i)) =
-                make_float4(dl, kZoh ? xv[i] : dl * xv[i], ds, 0.0f);
-        }
-        wave_sync();
-        const float* bt = bc_lds + tb * R;
-        float4 rc, rn = *reinterpret_cast<const float4*>(myrow);
-        Vec<S> bc, cc, bn, cn;
-        if (kFwd) bn.load(bt + n0);
-        cn.load(bt + NP + n0);
-#pragma unroll
-        for (int t = 0; t < kBT; ++t) {
-            rc = rn; cc = cn;
-            if (kFwd) bc = bn;
-            if (t + 1 < kBT) {
-                rn = *reinterpret_cast<const float4*>(myrow + 4 * (t + 1));
-                if (kFwd) bn.load(bt + (t + 1) * R + n0);
-                cn.load(bt + (t + 1) * R + NP + n0);
+        for (int i = 0; i < kBT; ++i) {
+            const float dlt = quad_bcast<T>(dl[i]);
+            const float dst = quad_bcast<T>(dsv[i]);
+            Vec<S> bc, cc;
+            cc.load(bt + i * R + NP + n0);
+            float xt = 0.0f;
+            if (kFwd) {
+                xt = quad_bcast<T>(xin[i]);
+                bc.load(bt + i * R + n0);
             }
-            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int s = 0; s < S; ++s) {
-                const float t2 = rc.x * A2[s];
+                const float t2 = dlt * A2[s];
                 const float a = exp2_hw(t2);
                 if (kFwd) {
-                    float bx = rc.y * bc.v[s];
-                    if (kZoh) bx *= zoh_gain(t2, a, rc.x, iA[s]);
+                    float bx = xt * bc.v[s];
+                    if (kZoh) bx *= zoh_gain(t2, a, dlt, iA[s]);
                     h[s] = fmaf(a, h[s], bx);
                 }
                 P[s] *= a;
-                Rv[s] = fmaf(P[s], rc.z * cc.v[s], Rv[s]);
+                Rv[s] = fmaf(P[s], dst * cc.v[s], Rv[s]);
             }
         }
-        wave_sync();
-    }
+    };
+    static_assert(kBMaxSteps == 4 * kBT, "one tile per lane of a channel");
+    tile(std::integral_constant<int, 0>{});
+    if (ntiles > 1) tile(std::integral_constant<int, 1>{});
+    if (ntiles > 2) tile(std::integral_constant<int, 2>{});
+    if (ntiles > 3) tile(std::integral_constant<int, 3>{});
     dsum = qsum(dsum);
     if (valid) {
         const int64_t aidx = (int64_t(b) * D + d) * K + k;
