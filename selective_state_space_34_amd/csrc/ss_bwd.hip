@@ -9,6 +9,10 @@
 //   g += ds·C_t;  dC_t += ds·h_t;  dB_t += g·δ·x;  dx = ds·D + δ Σ_n g B_t
 //   g ← Ā_t g;  w = g·h_{t-1};  dA += δ w;  dδ = Σ_n A w + x Σ_n g B_t (g before ← Ā_t g)
 //   ddt_raw = dδ σ(u)   (after t = 0, g is dh0)
+// With the exact zero-order hold of §2.1 (kZoh) the input term is f·B_t·x with the per-state
+// gain f = (e^{δA} - 1)/A, whose partials are ∂f/∂δ = Ā and ∂f/∂A = (δĀ - f)/A:
+//   dB_t += g·f·x;  dx = ds·D + Σ_n g f B_t;  dδ = Σ_n A w + x Σ_n (Ā g) B_t;
+//   dA += δ w + (∂f/∂A)·g·B_t·x   (g before ← Ā_t g, w after)
 //
 // Plan (sequence split into chunks of 16..64 steps; the N states of a channel on four
 // lanes, 16 channels per wave, 64 per workgroup):
