@@ -1,5 +1,6 @@
 """Seeded input generator: reproducibility, per-tensor streams, bf16 rounding, recipe."""
 import numpy as np
+import pytest
 import torch
 
 from gen import WORKLOADS, bf16_bits, bits_to_f32, make_inputs, round_bf16
@@ -52,3 +53,33 @@ def test_workloads_table():
     assert WORKLOADS[3].seqlen == 1048576 and WORKLOADS[4].backward
     d1 = WORKLOADS[5]
     assert d1.decode and d1.seqlen == 1 and (d1.batch, d1.dim, d1.dstate) == (256, 5120, 16)
+
+
+@pytest.mark.parametrize("order", [0, 1])
+def test_device_inputs_channel_rows(order):
+    """gen.device (run here on the CPU device): a channel's host case holds exactly that
+    channel's rows of the drawn tensors, and the per-channel parameters equal make_inputs'."""
+    import torch
+    from gen.device import make_device_inputs
+    B, L, D, N = 2, 40, 5, 4
+    c = make_device_inputs(B, L, D, N, dtype="bf16", seed=3, gate=True, order=order,
+                           with_dy=True, with_h0=True, device="cpu")
+    seq = (B, D, L) if order == 0 else (B, L, D)
+    assert tuple(c.x.shape) == seq and c.x.dtype == torch.bfloat16
+    assert tuple(c.Bm.shape) == ((B, N, L) if order == 0 else (B, L, N))
+    ref = make_inputs(1, 1, D, N, seed=3, a_perturb=True)
+    assert np.array_equal(c.dt_bias, ref.dt_bias) and np.array_equal(c.A, ref.A)
+    assert np.array_equal(c.Dskip, ref.Dskip)
+    h = c.channel(1, 3)
+    xs = c.x.float().numpy()
+    want = xs[1, 3, :] if order == 0 else xs[1, :, 3]
+    assert np.array_equal(h.x[0, 0], want)
+    bs = c.Bm.float().numpy()
+    assert np.array_equal(h.Bm[0], bs[1] if order == 0 else bs[1].T)
+    assert np.array_equal(h.h0[0, 0], c.h0[1, 3].numpy())
+    assert h.A.shape == (1, N) and h.dt_bias.shape == (1,)
+    # values are bf16-exact and the draws are seeded
+    assert np.array_equal(round_bf16(h.x), h.x)
+    c2 = make_device_inputs(B, L, D, N, dtype="bf16", seed=3, gate=True, order=order,
+                            device="cpu")
+    assert torch.equal(c2.x, c.x) and torch.equal(c2.Cm, c.Cm)
