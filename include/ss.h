@@ -56,7 +56,7 @@ extern "C" {
 #endif
 
 #define SS_VERSION_MAJOR 0
-#define SS_VERSION_MINOR 6
+#define SS_VERSION_MINOR 7
 
 /* dtype of x, dt_raw, z, Bm, Cm */
 typedef enum { SS_F32 = 0, SS_BF16 = 1 } ss_dtype;
@@ -108,7 +108,10 @@ typedef struct ss_dims {
     int64_t batch;    /* B  >= 1 */
     int64_t seqlen;   /* L  >= 1 */
     int64_t dim;      /* D  >= 1 */
-    int64_t dstate;   /* N, one of 1, 2, 4, 8, 16, 32 */
+    int64_t dstate;   /* N, one of 1, 2, 4, 8, 16, 32, 64.  N = 64: ss_fwd on the eight-lane
+                         layout only (layout AUTO or OCT; channel-major rows need L % 8 == 0,
+                         token-major L·D < 2^31) and ss_step; ss_bwd, and the layouts and rows
+                         the eight-lane kernel cannot take, return SS_ERR_UNSUPPORTED */
     int32_t in_dtype; /* ss_dtype */
     int32_t plan;     /* ss_plan */
     int64_t chunk;    /* chunk length of the chunked plan (multiple of 8; backward: multiple
@@ -187,7 +190,7 @@ typedef struct ss_block_dims {
     int64_t seqlen;   /* L >= 1 */
     int64_t d_in;     /* input width, multiple of 8 */
     int64_t dim;      /* D: channels of the scan, multiple of 4 */
-    int64_t dstate;   /* N, one of 1, 2, 4, 8, 16, 32 */
+    int64_t dstate;   /* N, one of 1, 2, 4, 8, 16, 32, 64 (as ss_dims) */
     int32_t plan;     /* ss_plan of the scan */
     int32_t layout;   /* ss_layout of the scan */
 } ss_block_dims;

@@ -55,7 +55,7 @@ int make_block_plan(const ss_block_dims& bd, BlockPlan* out) {
     bp.sd = ss_dims{bd.batch, bd.seqlen, bd.dim, bd.dstate, SS_F32, bd.plan, 0, bd.layout,
                     SS_DISC_EULER, SS_ORDER_BLD, SS_DT_SHARED};
     ss::Plan p;
-    const int rc = ss::make_plan(bp.sd, false, &p);
+    const int rc = ss::make_plan(bp.sd, ss::kPlanFwd, &p);
     if (rc != SS_OK) return rc;
     bp.S = ss::xproj_splits(bp.M, bp.D, int(bp.N));
     const size_t f = sizeof(float);
@@ -99,7 +99,7 @@ const char* ss_strerror(int code) {
 int ss_fwd_workspace_size(const ss_dims* dims, size_t* bytes) {
     if (!dims || !bytes) return SS_ERR_NULL;
     ss::Plan p;
-    const int rc = ss::make_plan(*dims, /*backward=*/false, &p);
+    const int rc = ss::make_plan(*dims, ss::kPlanFwd, &p);
     if (rc != SS_OK) return rc;
     *bytes = p.ws_total;
     return SS_OK;
@@ -108,7 +108,7 @@ int ss_fwd_workspace_size(const ss_dims* dims, size_t* bytes) {
 int ss_bwd_workspace_size(const ss_dims* dims, size_t* bytes) {
     if (!dims || !bytes) return SS_ERR_NULL;
     ss::Plan p;
-    const int rc = ss::make_plan(*dims, /*backward=*/true, &p);
+    const int rc = ss::make_plan(*dims, ss::kPlanBwd, &p);
     if (rc != SS_OK) return rc;
     *bytes = p.ws_total;
     return SS_OK;
@@ -120,7 +120,7 @@ int ss_fwd(const ss_dims* dims, const void* x, const void* dt_raw, const float* 
            size_t workspace_bytes, hipStream_t stream) {
     if (!dims) return SS_ERR_NULL;
     ss::Plan p;
-    int rc = ss::make_plan(*dims, false, &p);
+    int rc = ss::make_plan(*dims, ss::kPlanFwd, &p);
     if (rc != SS_OK) return rc;
     if (!x || !dt_raw || !dt_bias || !A || !Bm || !Cm || !Dskip || !y) return SS_ERR_NULL;
     const void* ptrs[] = {x, dt_raw, dt_bias, A, Bm, Cm, Dskip, y};
@@ -188,7 +188,7 @@ int ss_step(const ss_dims* dims, const void* x, const void* dt_raw, const float*
     if (dims->plan != SS_PLAN_AUTO || dims->layout != SS_LAYOUT_AUTO) return SS_ERR_DTYPE;
     if (dims->seqlen != 1 || dims->chunk != 0) return SS_ERR_DIMS;
     ss::Plan p;
-    const int rc = ss::make_plan(*dims, false, &p);
+    const int rc = ss::make_plan(*dims, ss::kPlanStep, &p);
     if (rc != SS_OK) return rc;
     if (!x || !dt_raw || !dt_bias || !A || !Bm || !Cm || !Dskip || !h_in || !h_out || !y)
         return SS_ERR_NULL;
@@ -214,7 +214,7 @@ int ss_bwd(const ss_dims* dims, const void* x, const void* dt_raw, const float* 
            void* workspace, size_t workspace_bytes, hipStream_t stream) {
     if (!dims) return SS_ERR_NULL;
     ss::Plan p;
-    const int rc = ss::make_plan(*dims, true, &p);
+    const int rc = ss::make_plan(*dims, ss::kPlanBwd, &p);
     if (rc != SS_OK) return rc;
     if (!x || !dt_raw || !dt_bias || !A || !Bm || !Cm || !Dskip || !dy) return SS_ERR_NULL;
     if (!dx || !ddt_raw || !ddt_bias || !dA || !dB || !dC || !dD) return SS_ERR_NULL;

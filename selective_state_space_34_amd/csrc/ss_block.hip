@@ -266,7 +266,8 @@ static int xproj_tile_tokens(int N) {
         case 4: return XprojShape<9>::TM;
         case 8: return XprojShape<17>::TM;
         case 16: return XprojShape<33>::TM;
-        default: return XprojShape<65>::TM;
+        case 32: return XprojShape<65>::TM;
+        default: return XprojShape<129>::TM;
     }
 }
 
@@ -302,6 +303,7 @@ hipError_t launch_xproj(const float* x, const float* Wx, float* part, float* dt,
         case 8: e = launch_xproj_p<17>(x, Wx, part, M, D, S, kc, s); break;
         case 16: e = launch_xproj_p<33>(x, Wx, part, M, D, S, kc, s); break;
         case 32: e = launch_xproj_p<65>(x, Wx, part, M, D, S, kc, s); break;
+        case 64: e = launch_xproj_p<129>(x, Wx, part, M, D, S, kc, s); break;
         default: return hipErrorInvalidValue;
     }
     if (e != hipSuccess) return e;

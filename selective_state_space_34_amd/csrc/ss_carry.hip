@@ -191,7 +191,9 @@ static hipError_t launch_carry_t(const CarryLaunch& p, hipStream_t s) {
 
 hipError_t launch_carry(int N, const CarryLaunch& p, hipStream_t s) {
     const int64_t BDN = p.B * p.D * N;
-    if (p.K <= kSeqMaxK && BDN >= 16384) {
+    // one thread per (channel, state) walking the chunks; also every N = 64 carry, whose
+    // per-channel kernel would hold 4 x 64 values per thread
+    if ((p.K <= kSeqMaxK && BDN >= 16384) || N == 64) {
         const CarrySet s0{p.h_end, p.h_in, p.h_start, p.h_out, p.reverse};
         const CarrySet s1{p.h_end2, p.h_in2, p.h_start2, p.h_out2, p.reverse2};
         dim3 grid(unsigned((BDN + 255) / 256), p.dual ? 2u : 1u);

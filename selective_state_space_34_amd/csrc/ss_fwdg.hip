@@ -575,6 +575,7 @@ static hipError_t launch_scang_dt(int N, int G, const ScanLaunch& p, hipStream_t
             case 8: return launch_scang_t<Tin, 8, 1>(p, s);
             case 16: return launch_scang_t<Tin, 8, 2>(p, s);
             case 32: return launch_scang_t<Tin, 8, 4>(p, s);
+            case 64: return launch_scang_t<Tin, 8, 8>(p, s);
             default: return hipErrorInvalidValue;
         }
     }

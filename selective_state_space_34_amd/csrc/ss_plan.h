@@ -50,7 +50,12 @@ constexpr int64_t kSimds = 1024;
 int64_t bwd_reduce_blocks(const Plan& p);
 size_t bwd_partial_bytes(const Plan& p);
 
-inline int make_plan(const ss_dims& d, bool backward, Plan* out) {
+// What the plan is for: the sequence forward, the backward, or the single-token step (which
+// uses only the validated sizes and flags, none of the sequence kernels' tiling).
+enum PlanFor { kPlanFwd, kPlanBwd, kPlanStep };
+
+inline int make_plan(const ss_dims& d, PlanFor what, Plan* out) {
+    const bool backward = what == kPlanBwd;
     Plan p{};
     if (d.in_dtype != SS_F32 && d.in_dtype != SS_BF16) return SS_ERR_DTYPE;
     if (d.plan != SS_PLAN_AUTO && d.plan != SS_PLAN_SINGLE && d.plan != SS_PLAN_CHUNKED)
@@ -63,7 +68,12 @@ inline int make_plan(const ss_dims& d, bool backward, Plan* out) {
     if (d.dt_layout != SS_DT_FULL && d.dt_layout != SS_DT_SHARED) return SS_ERR_DTYPE;
     if (d.batch <= 0 || d.seqlen <= 0 || d.dim <= 0 || d.dstate <= 0) return SS_ERR_DIMS;
     const int64_t N = d.dstate;
-    if (N != 1 && N != 2 && N != 4 && N != 8 && N != 16 && N != 32) return SS_ERR_DIMS;
+    if (N != 1 && N != 2 && N != 4 && N != 8 && N != 16 && N != 32 && N != 64) return SS_ERR_DIMS;
+    // N = 64: the forward on eight lanes of eight states only (one lane per channel or four
+    // lanes would hold 64 or 16 states and their B/C operands per lane), no backward (its
+    // tile of 16 recomputed states per lane would need 256 registers)
+    if (N == 64 && (backward || d.layout == SS_LAYOUT_LANE || d.layout == SS_LAYOUT_QUAD))
+        return SS_ERR_UNSUPPORTED;
     if (d.chunk < 0 || (d.chunk % 8) != 0) return SS_ERR_DIMS;
     const int64_t lim = int64_t(1) << 40;  // element count bound of any one array
     if (!mul_ok(d.batch, d.dim, lim) || !mul_ok(d.batch * d.dim, d.seqlen, lim) ||
@@ -85,8 +95,11 @@ inline int make_plan(const ss_dims& d, bool backward, Plan* out) {
     const bool tile_ok = p.tok ? p.L * p.D < (int64_t(1) << 31) : p.vec != 0;
     const int gmax = !tile_ok ? 0 : N >= 8 ? 8 : N >= 4 ? 4 : 0;
     if (d.layout == SS_LAYOUT_LANE) p.group = 0;
-    else if (d.layout == SS_LAYOUT_OCT) p.group = gmax;
+    else if (d.layout == SS_LAYOUT_OCT || N == 64) p.group = gmax;
     else p.group = gmax >= 4 ? 4 : 0;
+    // N = 64 rows the eight-lane kernel cannot tile (channel-major L % 8 != 0, token-major
+    // L·D >= 2^31) would need the one-lane kernel
+    if (N == 64 && p.group != 8 && what != kPlanStep) return SS_ERR_UNSUPPORTED;
     const int64_t waves = p.group ? (p.B * p.D * p.group + 63) / 64 : (p.B * p.D + 63) / 64;
     int chunked = backward ? 1 : 0;
     if (!backward) {

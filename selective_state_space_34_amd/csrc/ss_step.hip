@@ -113,6 +113,7 @@ static hipError_t launch_step_dt(const StepLaunch& p, hipStream_t s) {
         case 8: return launch_step_t<Tin, 4, 2>(p, s);
         case 16: return launch_step_t<Tin, 4, 4>(p, s);
         case 32: return launch_step_t<Tin, 4, 8>(p, s);
+        case 64: return launch_step_t<Tin, 4, 16>(p, s);
         default: return hipErrorInvalidValue;
     }
 }

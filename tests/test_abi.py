@@ -37,7 +37,7 @@ def test_exports_match_header(lib):
 
 
 def test_version_and_strerror(lib):
-    assert lib.ss_version() == (0 << 16) | 6
+    assert lib.ss_version() == (0 << 16) | 7
     for code in ss.ERRORS:
         assert len(lib.ss_strerror(code)) > 0
     assert b"unknown" in lib.ss_strerror(12345)
@@ -57,7 +57,7 @@ def test_fwd_validation(lib):
     good = ss.make_dims(2, 64, 32, 16, ss.SS_F32, ss.SS_PLAN_CHUNKED, 32)
     assert _fwd(lib, None) == -1
     for bad in (ss.make_dims(0, 64, 32, 16), ss.make_dims(2, 0, 32, 16), ss.make_dims(2, 64, -1, 16),
-                ss.make_dims(2, 64, 32, 3), ss.make_dims(2, 64, 32, 64), ss.make_dims(2, 64, 32, 0),
+                ss.make_dims(2, 64, 32, 3), ss.make_dims(2, 64, 32, 128), ss.make_dims(2, 64, 32, 0),
                 ss.make_dims(2, 64, 32, 16, chunk=12), ss.make_dims(2, 64, 32, 16, chunk=-8),
                 ss.make_dims(1 << 20, 1 << 20, 1 << 20, 16)):
         assert _fwd(lib, bad) == -2
@@ -68,6 +68,20 @@ def test_fwd_validation(lib):
     assert _fwd(lib, ss.make_dims(2, 64, 32, 16, disc=-1)) == -3
     assert _fwd(lib, ss.make_dims(2, 64, 32, 16, order=2)) == -3
     assert _fwd(lib, ss.make_dims(2, 64, 32, 16, dt_layout=2)) == -3
+    # N = 64: eight lanes only (automatic or OCT layout, rows the eight-lane kernel tiles)
+    n64 = ss.make_dims(2, 64, 32, 64, ss.SS_F32, ss.SS_PLAN_CHUNKED, 32)
+    assert _fwd(lib, n64, ws=None, wbytes=0) == -5
+    assert _fwd(lib, ss.make_dims(2, 64, 32, 64, ss.SS_F32, ss.SS_PLAN_CHUNKED, 32,
+                                  ss.SS_LAYOUT_OCT), ws=None, wbytes=0) == -5
+    for lay in (ss.SS_LAYOUT_LANE, ss.SS_LAYOUT_QUAD):
+        assert _fwd(lib, ss.make_dims(2, 64, 32, 64, layout=lay)) == -7
+    assert _fwd(lib, ss.make_dims(2, 63, 32, 64)) == -7            # channel-major L % 8 != 0
+    # token-major rows take any L (chunked, so the call stops at the workspace check)
+    assert _fwd(lib, ss.make_dims(2, 63, 32, 64, ss.SS_F32, ss.SS_PLAN_CHUNKED, 32,
+                                  order=ss.SS_ORDER_BLD), ws=None, wbytes=0) == -5
+    n = ctypes.c_size_t()
+    assert lib.ss_bwd_workspace_size(ctypes.byref(ss.make_dims(2, 64, 32, 64)), ctypes.byref(n)) == -7
+    assert lib.ss_fwd_workspace_size(ctypes.byref(n64), ctypes.byref(n)) == 0
     # required pointers
     for i in (0, 1, 2, 3, 4, 5, 6, 9):
         p = [ctypes.c_void_p(FAKE)] * 12
@@ -208,8 +222,9 @@ def test_block_validation(lib):
     assert call(None, args) == -1
     for bad in (ss.make_block_dims(0, 64, 64, 128, 16), ss.make_block_dims(2, 64, 60, 128, 16),
                 ss.make_block_dims(2, 64, 64, 126, 16), ss.make_block_dims(2, 64, 64, 128, 5),
-                ss.make_block_dims(2, 64, 64, 128, 64)):
+                ss.make_block_dims(2, 64, 64, 128, 128)):
         assert call(bad, args) == -2
+    assert call(ss.make_block_dims(2, 64, 64, 128, 64), args) == -5   # N = 64: valid
     assert call(ss.make_block_dims(2, 64, 64, 128, 16, plan=7), args) == -3
     for i in (0, 1, 2, 3, 4, 5, 7):
         a = list(args)
