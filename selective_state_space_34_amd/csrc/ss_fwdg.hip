@@ -364,7 +364,8 @@ __device__ __forceinline__ void scang_body(
                     if (!kAgg) cnxt.load(bh + (t + 1) * R + N + n0);
                     dnxt = *reinterpret_cast<const float2*>(dd_row + 2 * (t + 1));
                 }
-                __builtin_amdgcn_sched_barrier(0);  // keep the next step's reads issued here
+                // the next step's LDS reads stay issued here; arithmetic may move across
+                __builtin_amdgcn_sched_barrier(0x7);
                 float acc = 0.0f;
 #pragma unroll
                 for (int s = 0; s < S; ++s) {
