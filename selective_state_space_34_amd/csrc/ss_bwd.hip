@@ -63,6 +63,16 @@ __device__ __forceinline__ float quad_bcast(float v) {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), O * 0x55, 0xf, 0xf, false));
 }
 
+// element t % 4 of v from quad lane t / 4 (t a constant after unrolling)
+__device__ __forceinline__ float quad_bcast_i(const float (&v)[4], int t) {
+    switch (t >> 2) {
+        case 0: return quad_bcast<0>(v[t & 3]);
+        case 1: return quad_bcast<1>(v[t & 3]);
+        case 2: return quad_bcast<2>(v[t & 3]);
+        default: return quad_bcast<3>(v[t & 3]);
+    }
+}
+
 __device__ __forceinline__ void wave_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -497,6 +507,10 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
         for (int s = 0; s < S; ++s) hc[s] = kCk ? ckn[s] : ck[kCk ? 0 : tt][s];
         if (kCk && tt > 0) load_tile(tt - 1);
         float sz[4];
+        // this lane's steps 4j..4j+3: (δ, x, ds) stay in registers, and the sweeps take each
+        // step's values from the quad lane that formed them (DPP broadcast); the LDS row
+        // (δ, x, ds, σ(u)) serves the per-step finishing below
+        float rdl[kBPer], rx[kBPer], rds[kBPer];
 #pragma unroll
         for (int i = 0; i < kBPer; ++i) {
             const bool ok = te + i < t1c;
@@ -509,10 +523,13 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
             } else {
                 ds = ok ? gv[i] : 0.0f;
             }
-            // step row (δ, x, ds, σ(u)); channels past D compute on a clamped copy and must
-            // add nothing to dB, dC: their x and ds are zero
+            // channels past D compute on a clamped copy and must add nothing to dB, dC:
+            // their x and ds are zero
+            rdl[i] = dl;
+            rx[i] = valid ? xv[i] : 0.0f;
+            rds[i] = valid ? ds : 0.0f;
             *reinterpret_cast<float4*>(myrow + 4 * (kBPer * j + i)) =
-                make_float4(dl, valid ? xv[i] : 0.0f, valid ? ds : 0.0f, sigmoid(u));
+                make_float4(dl, rx[i], rds[i], sigmoid(u));
         }
         wave_sync();
         const float* bt = bc_lds + tb * R;
@@ -522,7 +539,6 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
         {
             float sp[kBT];
             float h[S];
-            float4 rc, rn = *reinterpret_cast<const float4*>(myrow);
             Vec<S> bc, cc, bn, cn;
             bn.load(bt + n0);
             if (kGate) cn.load(bt + NP + n0);
@@ -530,10 +546,12 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
             for (int s = 0; s < S; ++s) h[s] = hc[s];
 #pragma unroll
             for (int t = 0; t < kBT; ++t) {
-                rc = rn; bc = bn;
+                float2 rc;
+                rc.x = quad_bcast_i(rdl, t);
+                rc.y = quad_bcast_i(rx, t);
+                bc = bn;
                 if (kGate) cc = cn;
                 if (t + 1 < kBT) {
-                    rn = *reinterpret_cast<const float4*>(myrow + 4 * (t + 1));
                     bn.load(bt + (t + 1) * R + n0);
                     if (kGate) cn.load(bt + (t + 1) * R + NP + n0);
                 }
@@ -586,7 +604,10 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
 #pragma unroll
             for (int i = kBB - 1; i >= 0; --i) {
                 const int t = bi * kBB + i;
-                const float4 rc = *reinterpret_cast<const float4*>(myrow + 4 * t);
+                float4 rc;
+                rc.x = quad_bcast_i(rdl, t);
+                rc.y = quad_bcast_i(rx, t);
+                rc.z = quad_bcast_i(rds, t);
                 Vec<S> bc, cc;
                 bc.load(bt + t * R + n0);
                 cc.load(bt + t * R + NP + n0);
