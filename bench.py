@@ -604,7 +604,8 @@ def main():
                      "kernel": ("ss_fwd + ss_bwd step (every kernel of both calls)" if w.backward
                                 else "ss_fwd (scang_kernel, one launch per call)"
                                 if dims_plan_single(ss, dims) else "ss_fwd (all passes)"),
-                     "launch_us": t_avg * 1e6, "slots_per_elem": slots_pe,
+                     "launch_us": t_avg * 1e6, "launch_us_median": float(np.median(per)) * 1e6,
+                     "slots_per_elem": slots_pe,
                      "traffic_algorithmic_bytes": mb if not w.backward else None},
         "hbm": {"min_bytes": mb, "achieved_gbps": hbm_achieved, "peak_gbps": HBM_PEAK_GBPS,
                 "frac": hbm_achieved / HBM_PEAK_GBPS},

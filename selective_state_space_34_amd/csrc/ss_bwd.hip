@@ -29,9 +29,10 @@
 //      channels by an LDS transpose and over the workgroup's 4 waves once per tile;
 //   4. reduce kernels sum the partials into dB, dC, dA, dD, ddt_bias.
 // Both sweeping kernels copy the chunk's B and C from the [B, N, L] inputs into LDS
-// (float32, zero past the chunk's end and past N), and broadcast each step's (δ, δ·x, ds)
-// to the four lanes of a channel through a per-wave LDS row.  Steps past the end of the
-// sequence run as identities (δ = 0, ds = 0), so the sweeps carry no per-step branches.
+// (float32, zero past the chunk's end and past N).  Each lane of a channel forms the step
+// values (δ, x or δ·x, ds) of its own steps, and the four lanes of the channel take each
+// step's values from the lane that formed them by a DPP quad broadcast.  Steps past the end
+// of the sequence run as identities (δ = 0, ds = 0), so the sweeps carry no per-step branches.
 #include "ss_device.h"
 #include "ss_kernels.h"
 #include "ss_plan.h"
@@ -47,8 +48,8 @@ constexpr int kBChan = 64;
 constexpr int kBT = kCkptSteps;
 constexpr int kBPer = 4;
 constexpr int kBMaxTiles = kBMaxSteps / kBT;
-// floats per channel in a wave's step rows: steps x (δ, δ·x, ds, 0), +4 so that the
-// rows of different channels start on different banks
+// floats per channel in a wave's step rows of the final pass: steps x (δ, x, ds, σ(u)), +4 so
+// that the rows of different channels start on different banks
 constexpr int kRW = 4 * kBT + 4;
 
 __device__ __forceinline__ float qsum(float v) {
@@ -457,24 +458,23 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
                 ax.load(xr, ta, t1c, vec, ts);
                 ad.load(drr, ta, t1c, vec, dts);
             }
+            // (δ, δ·x) of this lane's steps (x with the exact hold), broadcast per step
+            float fdl[kBPer], fxi[kBPer];
 #pragma unroll
             for (int i = 0; i < kBPer; ++i) {
-                const float dl = softplus(bias + dv[i]);  // every step of a non-last tile is real
-                *reinterpret_cast<float2*>(myrow + 4 * (kBPer * j + i)) =
-                    make_float2(dl, kZoh ? xv[i] : dl * xv[i]);
+                fdl[i] = softplus(bias + dv[i]);  // every step of a non-last tile is real
+                fxi[i] = kZoh ? xv[i] : fdl[i] * xv[i];
             }
-            wave_sync();
             const float* bt = bc_lds + tb * R;
-            float2 rc, rn = *reinterpret_cast<const float2*>(myrow);
             Vec<S> bc, bn;
             bn.load(bt + n0);
 #pragma unroll
             for (int t = 0; t < kBT; ++t) {
-                rc = rn; bc = bn;
-                if (t + 1 < kBT) {
-                    rn = *reinterpret_cast<const float2*>(myrow + 4 * (t + 1));
-                    bn.load(bt + (t + 1) * R + n0);
-                }
+                float2 rc;
+                rc.x = quad_bcast_i(fdl, t);
+                rc.y = quad_bcast_i(fxi, t);
+                bc = bn;
+                if (t + 1 < kBT) bn.load(bt + (t + 1) * R + n0);
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int s = 0; s < S; ++s) {
@@ -487,7 +487,6 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
             }
 #pragma unroll
             for (int s = 0; s < S; ++s) ck[tile + 1][s] = h[s];
-            wave_sync();
         }
     }
 
