@@ -45,12 +45,12 @@ STEP_SOURCES = ["ss_step.hip", "ss_device.h", "ss_plan.h", "ss_api.cpp", "ss_ker
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 MEASURED_TRAFFIC = {
     # (workload, disc): first-order (0) or exact zero-order hold (1)
-    ("c2", 0): {"sources": FWD_SOURCES, "fetch_kib": 341866, "write_kib": 398425,
-                "sources_sha256": "ee791002627c79e9536b6c0c70d0728e96789ed0518b1cba170b9edb69dd86b5"},
-    ("c2", 1): {"sources": FWD_SOURCES, "fetch_kib": 354264, "write_kib": 396125,
-                "sources_sha256": "ee791002627c79e9536b6c0c70d0728e96789ed0518b1cba170b9edb69dd86b5"},
-    ("d1", 0): {"sources": STEP_SOURCES, "fetch_kib": 45070, "write_kib": 87040,
-                "sources_sha256": "68c1384fea7a5b4a5bae0bbe377cce036e36926baefd928b2ced842c429c5cf0"},
+    ("c2", 0): {"sources": FWD_SOURCES, "fetch_kib": 326182, "write_kib": 397420,
+                "sources_sha256": "949c6812d50cc83cbf77fe135384a1869bdcb036aee52c8e3567f5ad02a8e420"},
+    ("c2", 1): {"sources": FWD_SOURCES, "fetch_kib": 339539, "write_kib": 412589,
+                "sources_sha256": "949c6812d50cc83cbf77fe135384a1869bdcb036aee52c8e3567f5ad02a8e420"},
+    ("d1", 0): {"sources": STEP_SOURCES, "fetch_kib": 45071, "write_kib": 87040,
+                "sources_sha256": "49ad91af5f7733a2fd6aafabaa0a4dba71ac4d8dc2779d982edfa22be3ed12b0"},
 }
 
 
@@ -315,6 +315,16 @@ def run_block(args, w, inp):
     per, wall = timed(step)
     gper, _ = timed(gemm)
     t_avg, tg = float(per.mean()), float(gper.mean())
+    vendor = None
+    if args.vendor_gemm:
+        # the same product by the vendor GEMM torch.matmul calls (bf16 result: torch has no
+        # bf16 x bf16 -> float32 product), a reference point for the projection kernel only
+        u2, Wt = u.reshape(-1, w.d_in), W_in.t()
+        o16 = torch.empty((u2.shape[0], 2 * w.dim), dtype=torch.bfloat16, device=dev)
+        for _ in range(args.warmup):
+            torch.matmul(u2, Wt, out=o16)
+        vper, _ = timed(lambda: torch.matmul(u2, Wt, out=o16))
+        vendor = float(vper.mean())
     M = w.batch * w.seqlen
     flops = 2.0 * M * (2 * w.dim) * w.d_in
     tflops = flops / tg / 1e12
@@ -322,6 +332,9 @@ def run_block(args, w, inp):
     log(f"[bench] block step event avg {t_avg * 1e6:.1f} us; input projection alone "
         f"{tg * 1e6:.1f} us = {tflops:.0f} TFLOP/s ({tflops / MFMA_BF16_PEAK_TFLOPS:.3f} of "
         f"{MFMA_BF16_PEAK_TFLOPS:.0f}); the rest {(t_avg - tg) * 1e6:.1f} us")
+    if vendor is not None:
+        log(f"[bench] vendor GEMM (torch.matmul, bf16 result) on the same product: "
+            f"{vendor * 1e6:.1f} us = {flops / vendor / 1e12:.0f} TFLOP/s")
     cpu = None
     if not args.no_cpu_baseline:
         cpu = block_cpu_baseline(w, inp)
@@ -342,6 +355,7 @@ def run_block(args, w, inp):
                      "launch_us": tg * 1e6, "flops": flops},
         "block_split": {"step_us": t_avg * 1e6, "in_proj_us": tg * 1e6,
                         "rest_us": (t_avg - tg) * 1e6},
+        "vendor_gemm_bf16_out_us": None if vendor is None else vendor * 1e6,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
@@ -440,6 +454,9 @@ def main():
     ap.add_argument("--flush-mib", type=int, default=1024,
                     help="decode, and forwards under 512 MB: untimed write of this many MiB "
                          "before each timed step (0 = none)")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="block workload: also time the vendor GEMM (torch.matmul) on the input "
+                         "projection's product, for reference")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also launch one device copy of this many MiB (HBM counter calibration)")
     args = ap.parse_args()
