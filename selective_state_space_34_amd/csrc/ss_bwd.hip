@@ -285,7 +285,10 @@ __global__ __launch_bounds__(kBThreads) void bwd_agg_kernel(
     }
     __syncthreads();
 
-    // tile T's steps sit in lane T of each quad: broadcast each step's values to the quad
+    // tile T's steps sit in lane T of each quad: broadcast each step's values to the quad.
+    // Without the forward pair no step needs its own Ā: the cumulative product is taken as
+    // 2^(A·log2(e)·Σδ) from the running sum of δ, one exponential and no product per state.
+    float cum = 0.0f;
     auto tile = [&](auto tc) {
         constexpr int T = decltype(tc)::value;
         const float* bt = bc_lds + T * kBT * R;
@@ -300,16 +303,19 @@ __global__ __launch_bounds__(kBThreads) void bwd_agg_kernel(
                 xt = quad_bcast<T>(xin[i]);
                 bc.load(bt + i * R + n0);
             }
+            if constexpr (!kFwd) cum += dlt;
 #pragma unroll
             for (int s = 0; s < S; ++s) {
-                const float t2 = dlt * A2[s];
-                const float a = exp2_hw(t2);
-                if (kFwd) {
+                if constexpr (kFwd) {
+                    const float t2 = dlt * A2[s];
+                    const float a = exp2_hw(t2);
                     float bx = xt * bc.v[s];
                     if (kZoh) bx *= zoh_gain(t2, a, dlt, iA[s]);
                     h[s] = fmaf(a, h[s], bx);
+                    P[s] *= a;
+                } else {
+                    P[s] = exp2_hw(cum * A2[s]);
                 }
-                P[s] *= a;
                 Rv[s] = fmaf(P[s], dst * cc.v[s], Rv[s]);
             }
         }

@@ -16,7 +16,8 @@
 //   4. wave_shr:1 turns the inclusive prefix into each lane's entering state, and
 //      the lane walks its run again writing every chunk's start state.
 // With few chunks and many channels a plain sequential walk per (channel, state) is
-// faster (carry_seq_kernel): the scan's depth is then small and its lanes mostly idle.
+// faster (carry_seq_kernel): the scan's depth is then small and its lanes mostly idle.  At
+// N = 64 the walk is always used: the per-channel scan would hold 4 x 64 values per lane.
 #include "ss_device.h"
 #include "ss_kernels.h"
 

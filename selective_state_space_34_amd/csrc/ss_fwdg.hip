@@ -8,7 +8,10 @@
 // 64-lane wave covers 64/G channels and B*D channels yield B*D*G/64 waves.  G = 8
 // gives five waves per SIMD at B*D = 40960, where G = 4 leaves the SIMDs unevenly
 // loaded (2.5 waves each), but it moves more operand bytes through LDS per state-step
-// and is LDS-issue bound on gfx950 (measured slower); G = 4 is the default.
+// and is LDS-issue bound on gfx950 (measured slower); G = 4 is the default.  A single pass
+// whose last round of four-lane waves would be at most half full runs its remaining
+// channels on eight lanes in the same launch (scang_mixed_kernel), which evens out the
+// SIMDs; N = 64 runs on eight lanes of eight states.
 //
 // Per 32-step tile:
 //   - the workgroup copies the tile's B and C ([B, N, L] inputs, N rows of 32 steps
