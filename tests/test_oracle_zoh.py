@@ -111,8 +111,37 @@ def pin_zoh_large_step(fwd, seed=24, L=16, D=3, N=4):
     return rel_err(hf[0], ref)
 
 
+def pin_zoh_golden(fwd):
+    """Hand-unrolled exact-hold cases (tests/golden/hand_unrolled_zoh.json): δ = ln 2 makes
+    the gains 1/2 (A = -1) and 3/8 (A = -2), and ln 2 itself at A = 0."""
+    import json
+    import math
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden", "hand_unrolled_zoh.json")) as f:
+        cases = json.load(f)["cases"]
+    ln2 = math.log(2.0)
+    worst = 0.0
+    for c in cases:
+        L, N = c["L"], c["N"]
+        x = np.array(c["x"], np.float32).reshape(1, 1, L)
+        dtr = np.array(c["dt_raw"], np.float32).reshape(1, 1, L)
+        dtb = np.array([c["dt_bias"]], np.float32)
+        A = np.array(c["A"], np.float32).reshape(1, N)
+        Bm = np.array(c["B"], np.float32).reshape(1, N, L)
+        Cm = np.array(c["C"], np.float32).reshape(1, N, L)
+        Dk = np.array([c["D"]], np.float32)
+        h0 = None if c["h0"] is None else np.array(c["h0"], np.float32).reshape(1, 1, N)
+        y, hf = fwd(x, dtr, dtb, A, Bm, Cm, Dk, h0=h0, zoh=True)
+        y_exp = np.array([p + q * ln2 for p, q in c["y"]])
+        h_exp = np.array([p + q * ln2 for p, q in c["h_final"]])
+        worst = max(worst, rel_err(np.asarray(y).reshape(-1), y_exp),
+                    rel_err(np.asarray(hf).reshape(-1), h_exp))
+    return worst
+
+
 PINS = {"zoh_lti": (pin_zoh_lti, 1e-12), "zoh_ode": (pin_zoh_ode, 1e-10),
-        "zoh_small_step": (pin_zoh_small_step, 1e-10), "zoh_large_step": (pin_zoh_large_step, 1e-12)}
+        "zoh_small_step": (pin_zoh_small_step, 1e-10), "zoh_large_step": (pin_zoh_large_step, 1e-12),
+        "zoh_golden": (pin_zoh_golden, 1e-12)}
 
 
 @pytest.mark.parametrize("pin", sorted(PINS))
@@ -176,6 +205,8 @@ def test_zoh_pins_catch_planted_mistakes(kind):
     for name, (f, tol) in PINS.items():
         if name == "zoh_ode":
             continue  # slow; the other pins suffice for these mutants
-        if f(bad) > tol:
+        with np.errstate(divide="ignore", invalid="ignore"):
+            err = f(bad)
+        if not err <= tol:        # a NaN error (0/0 of a planted form) counts as caught
             caught.append(name)
     assert caught, f"no pin caught mutant {kind}"
