@@ -171,15 +171,36 @@ __device__ __forceinline__ void wave_sync() {
 
 }  // namespace
 
+// Token-major staging of one 32-step tile of x, Δraw and z for the CW channels of a wave:
+// the wave reads each step's CW elements as 16-byte pieces (one per lane per tensor for
+// bf16 at G = 4) and stores them, in the element type, as rows of its exchange area; each
+// lane then reads its own steps of its channel from there.  Rows are padded so that the
+// lanes of one read (G lane groups, kH rows apart) fall on distinct banks.
+template <int G, typename Tin>
+struct TokStage {
+    static constexpr int CW = 64 / G;
+    static constexpr int ELEM = int(sizeof(Tin));
+    static constexpr int PIECE = 16 / ELEM;              // elements per 16-byte piece
+    static constexpr int ROWB = CW * ELEM;               // bytes of a step's CW elements
+    static constexpr int PPR = ROWB / 16;                // pieces per step
+    static constexpr int RSB = ROWB + (ROWB >= 32 ? 16 : 0);  // row stride, bytes
+    static constexpr int PIECES = kTile * PPR;           // pieces per tensor per wave
+    static constexpr int PL = (PIECES + 63) / 64;        // pieces per lane per tensor
+    static constexpr int TBYTES = kTile * RSB;           // bytes per tensor
+    static constexpr int FLOATS = 3 * TBYTES / 4;
+};
+
 // LDS floats the body of a G-lane workgroup needs: a double-buffered B/C tile, then the
-// four waves' exchange areas
-template <int G, int S>
+// four waves' exchange areas (large enough for the token-major staging)
+template <int G, int S, typename Tin = float, bool kTok = false>
 struct GroupLds {
     static constexpr int N = G * S;
     static constexpr int CW = 64 / G;
     static constexpr int R = 2 * N + 4;           // B_t | C_t row, padded by 4 floats
     static constexpr int TILE_F = kTile * R;
-    static constexpr int WAREA = (64 * kPS > CW * kDS) ? 64 * kPS : CW * kDS;
+    static constexpr int WAREA0 = (64 * kPS > CW * kDS) ? 64 * kPS : CW * kDS;
+    static constexpr int WAREA = (kTok && TokStage<G, Tin>::FLOATS > WAREA0)
+                                     ? TokStage<G, Tin>::FLOATS : WAREA0;
     static constexpr int FLOATS = 2 * TILE_F + 4 * WAREA;
 };
 
@@ -196,7 +217,8 @@ __device__ __forceinline__ void scang_body(
     const float* __restrict__ h_init, float* __restrict__ y, float* __restrict__ h_last,
     float* __restrict__ h_ckpt, float* __restrict__ dsum_out, int64_t L, int64_t D,
     int64_t chunk, int K, DtRows dtr) {
-    using Lay = GroupLds<G, S>;
+    using Lay = GroupLds<G, S, Tin, kTok>;
+    using TS = TokStage<G, Tin>;
     constexpr int N = G * S;
     constexpr int CW = 64 / G;                    // channels per wave
     constexpr int CB = 4 * CW;                    // channels per block
@@ -270,6 +292,33 @@ __device__ __forceinline__ void scang_body(
     constexpr int BC_PASSES = (BC_UNITS + kThreads - 1) / kThreads;
     Raw4<Tin> bc_next[BC_PASSES];
     Raw<Tin, kH> xn[2], dn[2], zn[2];
+    // token-major: the wave's 16-byte pieces of the next tile (x, Δraw, z).  A Δraw shared
+    // by the channels is not staged: each lane reads its own steps of the row, both halves'
+    // kH elements packed into the same registers (2·kH elements fit in TS::PL pieces)
+    uint4 px[kTok ? TS::PL : 1], pd[kTok ? TS::PL : 1], pz[kTok ? TS::PL : 1];
+    static_assert(!kTok || 2 * kH * int(sizeof(Tin)) <= 16 * TS::PL, "shared Δraw steps fit");
+    const int64_t dw0 = d_lo + blk * CB + (tid >> 6) * CW;   // the wave's first channel
+    const bool dt_full = dtr.sd != 0;
+    // 16-byte pieces need every row's start on a piece boundary
+    const bool pieces_aligned = (D % TS::PIECE) == 0;
+    auto load_piece = [&](const Tin* base, uint32_t off, int64_t ch0) -> uint4 {
+        // elements [off, off + PIECE) of a row (32-bit offset from the batch row's base):
+        // channels ch0 .. ch0 + PIECE - 1, those at or past d_hi read as zero
+        if (pieces_aligned && ch0 + TS::PIECE <= d_hi)
+            return *reinterpret_cast<const uint4*>(base + off);
+        uint32_t w[4] = {0u, 0u, 0u, 0u};
+        if constexpr (sizeof(Tin) == 2) {
+#pragma unroll
+            for (int e = 0; e < TS::PIECE; ++e)
+                if (ch0 + e < d_hi)
+                    w[e >> 1] |= uint32_t(reinterpret_cast<const uint16_t*>(base)[off + e]) << (16 * (e & 1));
+        } else {
+#pragma unroll
+            for (int e = 0; e < TS::PIECE; ++e)
+                if (ch0 + e < d_hi) w[e] = __float_as_uint(reinterpret_cast<const float*>(base)[off + e]);
+        }
+        return make_uint4(w[0], w[1], w[2], w[3]);
+    };
 
     auto issue_loads = [&](int64_t t0) {
 #pragma unroll
@@ -285,15 +334,40 @@ __device__ __forceinline__ void scang_body(
                 }
             }
         }
+        if constexpr (kTok) {
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-            const int64_t te = t0 + kHalf * hh + kH * l;
-            if constexpr (kTok) {
-                const uint32_t t32 = uint32_t(te);
-                xn[hh].load_strided(xb, t32 * D32 + d32, D32);
-                dn[hh].load_strided(db, t32 * dts32 + dofs, dts32);
-                if (kGate && !kAgg) zn[hh].load_strided(zb, t32 * D32 + d32, D32);
-            } else {
+            for (int j = 0; j < TS::PL; ++j) {
+                const int q = lane + 64 * j;
+                if (TS::PIECES % 64 == 0 || q < TS::PIECES) {
+                    const int row = q / TS::PPR, pc = q % TS::PPR;
+                    const int64_t ch0 = dw0 + pc * TS::PIECE;
+                    const uint32_t off = uint32_t(t0 + row) * D32 + uint32_t(ch0);
+                    px[j] = load_piece(xb, off, ch0);
+                    if (dt_full) pd[j] = load_piece(db, off, ch0);
+                    if (kGate && !kAgg) pz[j] = load_piece(zb, off, ch0);
+                }
+            }
+            if (!dt_full) {
+                uint32_t* w = reinterpret_cast<uint32_t*>(pd);
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const uint32_t o = uint32_t(t0 + kHalf * hh + kH * l) * dts32 + dofs;
+#pragma unroll
+                    for (int i = 0; i < kH; ++i) {
+                        const int e = hh * kH + i;           // element of the packed run
+                        if constexpr (sizeof(Tin) == 2) {
+                            const uint32_t v = uint32_t(reinterpret_cast<const uint16_t*>(db)[o + i * dts32]);
+                            w[e >> 1] = (e & 1) ? (w[e >> 1] | (v << 16)) : v;
+                        } else {
+                            w[e] = __float_as_uint(reinterpret_cast<const float*>(db)[o + i * dts32]);
+                        }
+                    }
+                }
+            }
+        } else {
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const int64_t te = t0 + kHalf * hh + kH * l;
                 xn[hh].load(xr + te);
                 dn[hh].load(dr + te);
                 if (kGate && !kAgg) zn[hh].load(zr + te);
@@ -327,11 +401,60 @@ __device__ __forceinline__ void scang_body(
             }
         }
         float xv[2][kH], dv[2][kH], zv[2][kH];
+        if constexpr (kTok) {
+            // the wave's pieces into its own area as rows, then each lane's kH steps of its
+            // channel from there (the area is free: the last sweep's gathers are done)
+            char* st = reinterpret_cast<char*>(wa);
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-            xn[hh].decode(xv[hh]);
-            dn[hh].decode(dv[hh]);
-            if (kGate && !kAgg) zn[hh].decode(zv[hh]);
+            for (int j = 0; j < TS::PL; ++j) {
+                const int q = lane + 64 * j;
+                if (TS::PIECES % 64 == 0 || q < TS::PIECES) {
+                    const int row = q / TS::PPR, pc = q % TS::PPR;
+                    char* dst = st + row * TS::RSB + pc * 16;
+                    *reinterpret_cast<uint4*>(dst) = px[j];
+                    if (dt_full) *reinterpret_cast<uint4*>(dst + TS::TBYTES) = pd[j];
+                    if (kGate && !kAgg) *reinterpret_cast<uint4*>(dst + 2 * TS::TBYTES) = pz[j];
+                }
+            }
+            wave_sync();
+            const char* src = st + c * TS::ELEM;
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+                for (int i = 0; i < kH; ++i) {
+                    const char* e = src + (kHalf * hh + kH * l + i) * TS::RSB;
+                    if constexpr (sizeof(Tin) == 2) {
+                        xv[hh][i] = __uint_as_float(uint32_t(*reinterpret_cast<const uint16_t*>(e)) << 16);
+                        if (dt_full)
+                            dv[hh][i] = __uint_as_float(
+                                uint32_t(*reinterpret_cast<const uint16_t*>(e + TS::TBYTES)) << 16);
+                        if (kGate && !kAgg)
+                            zv[hh][i] = __uint_as_float(
+                                uint32_t(*reinterpret_cast<const uint16_t*>(e + 2 * TS::TBYTES)) << 16);
+                    } else {
+                        xv[hh][i] = *reinterpret_cast<const float*>(e);
+                        if (dt_full) dv[hh][i] = *reinterpret_cast<const float*>(e + TS::TBYTES);
+                        if (kGate && !kAgg) zv[hh][i] = *reinterpret_cast<const float*>(e + 2 * TS::TBYTES);
+                    }
+                }
+                if (!dt_full) {
+                    const uint32_t* w = reinterpret_cast<const uint32_t*>(pd);
+#pragma unroll
+                    for (int i = 0; i < kH; ++i) {
+                        const int e = hh * kH + i;
+                        dv[hh][i] = (sizeof(Tin) == 2)
+                                        ? __uint_as_float((e & 1) ? (w[e >> 1] & 0xffff0000u) : (w[e >> 1] << 16))
+                                        : __uint_as_float(w[e]);
+                    }
+                }
+            }
+        } else {
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                xn[hh].decode(xv[hh]);
+                dn[hh].decode(dv[hh]);
+                if (kGate && !kAgg) zn[hh].decode(zv[hh]);
+            }
         }
         if (it + 1 < n_tiles) issue_loads(t0 + kTile);
         __syncthreads();
@@ -479,7 +602,7 @@ __global__ __launch_bounds__(kThreads) void scang_kernel(
     const float* __restrict__ h_init, float* __restrict__ y, float* __restrict__ h_last,
     float* __restrict__ h_ckpt, float* __restrict__ dsum_out, int64_t L, int64_t D,
     int64_t chunk, int K, DtRows dtr) {
-    __shared__ __align__(16) float lds[GroupLds<G, S>::FLOATS];
+    __shared__ __align__(16) float lds[GroupLds<G, S, Tin, kTok>::FLOATS];
     scang_body<Tin, G, S, kGate, kAgg, kZoh, kTok>(lds, blockIdx.x, blockIdx.y, blockIdx.z, 0, D, x,
                                                    dt_raw, z, dt_bias, A, Dskip, Bm, Cm, h_init, y,
                                                    h_last, h_ckpt, dsum_out, L, D, chunk, K, dtr);
@@ -499,7 +622,7 @@ __global__ __launch_bounds__(kThreads) void scang_mixed_kernel(
     const float* __restrict__ h_init, float* __restrict__ y, float* __restrict__ h_last,
     float* __restrict__ h_ckpt, int64_t L, int64_t D, int64_t d4, int nb4, int nb8, int B,
     DtRows dtr) {
-    constexpr int F4 = GroupLds<4, N / 4>::FLOATS, F8 = GroupLds<8, N / 8>::FLOATS;
+    constexpr int F4 = GroupLds<4, N / 4, Tin, kTok>::FLOATS, F8 = GroupLds<8, N / 8, Tin, kTok>::FLOATS;
     __shared__ __align__(16) float lds[F4 > F8 ? F4 : F8];
     const int64_t f = blockIdx.x;
     const int64_t n4 = int64_t(B) * nb4;
