@@ -52,16 +52,25 @@ constexpr int kBMaxTiles = kBMaxSteps / kBT;
 // that the rows of different channels start on different banks
 constexpr int kRW = 4 * kBT + 4;
 
+// DPP quad permutations.  Every lane of a quad is a valid source and every lane is active
+// where these run, so bound_ctrl with a zero old value gives the same result as a plain move;
+// that form lets the compiler fold the permutation into the VOP2 instruction that consumes it
+// (v_mul_f32_dpp, v_add_f32_dpp) instead of issuing a separate v_mov_b32_dpp.
+template <int Ctrl>
+__device__ __forceinline__ float qperm(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), Ctrl, 0xf, 0xf, true));
+}
+
 __device__ __forceinline__ float qsum(float v) {
-    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xf, 0xf, false));
-    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xf, 0xf, false));
+    v += qperm<0xB1>(v);
+    v += qperm<0x4E>(v);
     return v;
 }
 
-// v from lane O of this lane's quad (DPP quad permutation)
+// v from lane O of this lane's quad
 template <int O>
 __device__ __forceinline__ float quad_bcast(float v) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), O * 0x55, 0xf, 0xf, false));
+    return qperm<O * 0x55>(v);
 }
 
 // element t % 4 of v from quad lane t / 4 (t a constant after unrolling)
@@ -554,6 +563,10 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
                 float2 rc;
                 rc.x = quad_bcast_i(rdl, t);
                 rc.y = quad_bcast_i(rx, t);
+                // with the exact hold, keep these steps' values apart from the reverse sweep's:
+                // shared, the gains and exponentials of all 16 steps would stay live between
+                // the two sweeps and spill
+                if constexpr (kZoh) asm volatile("" : "+v"(rc.x));
                 bc = bn;
                 if (kGate) cc = cn;
                 if (t + 1 < kBT) {

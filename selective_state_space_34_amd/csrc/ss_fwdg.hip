@@ -162,6 +162,22 @@ __device__ __forceinline__ float group_sum(float v) {
     return v;
 }
 
+// element t % 4 of v from lane t / 4 of this lane's quad (t a constant after unrolling).
+// Every lane of the quad is a valid source and all lanes are active where this runs, so
+// bound_ctrl with a zero old value equals a plain move, and in that form the compiler folds
+// the permutation into the multiply that consumes it (v_mul_f32_dpp): no extra instruction.
+template <int K>
+__device__ __forceinline__ float quad_step(const float (&v)[K], int t) {
+    static_assert(K == 4, "four steps per lane of a quad");
+    const int i = __float_as_int(v[t & 3]);
+    switch (t >> 2) {
+        case 0: return __int_as_float(__builtin_amdgcn_update_dpp(0, i, 0x00, 0xf, 0xf, true));
+        case 1: return __int_as_float(__builtin_amdgcn_update_dpp(0, i, 0x55, 0xf, 0xf, true));
+        case 2: return __int_as_float(__builtin_amdgcn_update_dpp(0, i, 0xAA, 0xf, 0xf, true));
+        default: return __int_as_float(__builtin_amdgcn_update_dpp(0, i, 0xFF, 0xf, 0xf, true));
+    }
+}
+
 // order LDS traffic of one wave: everything before is visible to the wave's lanes after
 __device__ __forceinline__ void wave_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -223,6 +239,11 @@ __device__ __forceinline__ void scang_body(
     constexpr int CW = 64 / G;                    // channels per wave
     constexpr int CB = 4 * CW;                    // channels per block
     constexpr int kH = kHalf / G;                 // steps per lane per half
+    // four lanes, first order: step t's (δ, δ·x) stay in quad lane t / 4, which formed them,
+    // and reach the other three by DPP (folded into the multiplies that use them) instead of
+    // through the channel's LDS row; the exact hold's gain uses δ in fused multiply-adds,
+    // which take no DPP operand, so it keeps the row
+    constexpr bool kDpp = (G == 4) && !kZoh;
     // LDS tile row per step: B_t (N floats) then C_t (N floats), padded by 4 floats so
     // the transposing writes of a wave fall on at most two lanes per bank
     constexpr int R = Lay::R;
@@ -462,15 +483,20 @@ __device__ __forceinline__ void scang_body(
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             if (ckr) checkpoint(t0 + kHalf * hh);      // sweeps start on multiples of 16
-            // this lane's kH steps of the half: (δ, δ·x) into the channel's row
+            // this lane's kH steps of the half: (δ, δ·x) into the channel's row (or kept in
+            // registers for the quad broadcast)
+            float qdl[kH], qdx[kH];
 #pragma unroll
             for (int i = 0; i < kH; ++i) {
                 const float dl = softplus(bias + dv[hh][i]);
                 if (kAgg) dsum += dl;
-                *reinterpret_cast<float2*>(dd_row + 2 * (kH * l + i)) =
-                    make_float2(dl, kZoh ? xv[hh][i] : dl * xv[hh][i]);
+                qdl[i] = dl;
+                qdx[i] = dl * xv[hh][i];
+                if constexpr (!kDpp)
+                    *reinterpret_cast<float2*>(dd_row + 2 * (kH * l + i)) =
+                        make_float2(dl, kZoh ? xv[hh][i] : qdx[i]);
             }
-            wave_sync();
+            if constexpr (!kDpp) wave_sync();
 
             // recurrence over the half; operands of step t+1 are read during step t
             const float* bh = buf + kHalf * hh * R;
@@ -479,16 +505,21 @@ __device__ __forceinline__ void scang_body(
             float2 dcur, dnxt;
             bnxt.load(bh + n0);
             if (!kAgg) cnxt.load(bh + N + n0);
-            dnxt = *reinterpret_cast<const float2*>(dd_row);
+            if constexpr (!kDpp) dnxt = *reinterpret_cast<const float2*>(dd_row);
 #pragma unroll
             for (int t = 0; t < kHalf; ++t) {
                 bcur = bnxt;
                 if (!kAgg) ccur = cnxt;
-                dcur = dnxt;
+                if constexpr (kDpp) {
+                    dcur.x = quad_step(qdl, t);
+                    dcur.y = quad_step(qdx, t);
+                } else {
+                    dcur = dnxt;
+                }
                 if (t + 1 < kHalf) {
                     bnxt.load(bh + (t + 1) * R + n0);
                     if (!kAgg) cnxt.load(bh + (t + 1) * R + N + n0);
-                    dnxt = *reinterpret_cast<const float2*>(dd_row + 2 * (t + 1));
+                    if constexpr (!kDpp) dnxt = *reinterpret_cast<const float2*>(dd_row + 2 * (t + 1));
                 }
                 // the next step's LDS reads stay issued here; arithmetic may move across
                 __builtin_amdgcn_sched_barrier(0x7);
@@ -505,7 +536,8 @@ __device__ __forceinline__ void scang_body(
                 }
                 part[t] = acc;
             }
-            wave_sync();  // every lane's reads of the rows are done before partials land
+            // every lane's reads of the rows are done before partials land
+            if constexpr (!kDpp) wave_sync();
 
             if (!kAgg) {
                 // partial readouts through the wave's area: each lane writes its 16, then
