@@ -597,12 +597,17 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
         if (kGate) {
             // readout partials -> owner lanes (steps 4j..4j+3 of lane j); dz right away
             wave_sync();
-            float stot[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            // sums start from the first source (a 0 + x add is not folded: signed zeros)
+            float stot[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int src = (j + r) & 3;
                 const float4 v = *reinterpret_cast<const float4*>(wx + (qb + src) * LS + kBPer * j);
-                stot[0] += v.x; stot[1] += v.y; stot[2] += v.z; stot[3] += v.w;
+                if (r == 0) {
+                    stot[0] = v.x; stot[1] = v.y; stot[2] = v.z; stot[3] = v.w;
+                } else {
+                    stot[0] += v.x; stot[1] += v.y; stot[2] += v.z; stot[3] += v.w;
+                }
             }
             float dzv[4];
 #pragma unroll
@@ -686,9 +691,9 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
                     const int ty = (e / (4 * S)) % 2;
                     const int st = e / (8 * S);
                     const float* col = wx + jp * LS + ty * kBB * S + st * S + sp_;
-                    float tot = 0.0f;
+                    float tot = col[0];
 #pragma unroll
-                    for (int c = 0; c < 16; ++c) tot += col[c * 4 * LS];
+                    for (int c = 1; c < 16; ++c) tot += col[c * 4 * LS];
                     cbuf[(bi * kBB + st) * 2 * NP + ty * NP + jp * S + sp_] = tot;
                 }
             }
@@ -696,9 +701,9 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
                 // lane j finishes step 4 bi + j of its channel: Σ_n over the quad's partials
                 // of that step, then dx and dΔ from the step's row
                 const int tj = bi * kBB + j;
-                float PX = 0.0f, PD = 0.0f;
+                float PX = wx[qb * LS + PXO + j], PD = wx[qb * LS + PXO + j + 4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
+                for (int r = 1; r < 4; ++r) {
                     const float* src = wx + (qb + r) * LS + PXO + j;
                     PX += src[0];
                     PD += src[4];

@@ -548,18 +548,16 @@ __device__ __forceinline__ void scang_body(
                         make_float4(part[q], part[q + 1], part[q + 2], part[q + 3]);
                 wave_sync();
                 float sum[kH];
-#pragma unroll
-                for (int i = 0; i < kH; ++i) sum[i] = 0.0f;
                 const int gbase = lane & ~(G - 1);
                 // lane l starts at source l (rotation): lanes served together read
-                // different source rows
+                // different source rows; the first row starts the sums (no 0 + x)
 #pragma unroll
                 for (int r = 0; r < G; ++r) {
                     const int src = (l + r) & (G - 1);
                     Row<kH> pr;
                     pr.load(wa + (gbase + src) * kPS + kH * l);
 #pragma unroll
-                    for (int i = 0; i < kH; ++i) sum[i] += pr.v[i];
+                    for (int i = 0; i < kH; ++i) sum[i] = r ? sum[i] + pr.v[i] : pr.v[i];
                 }
                 float out[kH];
 #pragma unroll
