@@ -550,6 +550,7 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
 
         // recompute the tile's states (and, with the gate, the readout for dz)
         float hs[kBT][S];
+        Vec<S> rbn, rcn;                        // B, C of the reverse sweep's next step
         {
             float sp[kBT];
             float h[S];
@@ -587,6 +588,10 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
                 }
                 sp[t] = acc;
             }
+            // the reverse sweep's first step (the tile's last) reads in flight during the dz
+            // section
+            rbn.load(bt + (kBT - 1) * R + n0);
+            rcn.load(bt + (kBT - 1) * R + NP + n0);
             if (kGate) {
 #pragma unroll
                 for (int i = 0; i < kBT; i += 4)
@@ -619,7 +624,9 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
             wave_sync();
         }
 
-        // reverse sweep over the tile, in batches of kBB steps
+        // reverse sweep over the tile, in batches of kBB steps.  B and C of the step after
+        // are read one step ahead (issued before this step's exchange-area stores, which the
+        // compiler cannot prove disjoint from them and would otherwise wait behind)
         float* cbuf = comb + wave * OUTW;
 #pragma unroll
         for (int bi = kNBat - 1; bi >= 0; --bi) {
@@ -631,9 +638,13 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
                 rc.x = quad_bcast_i(rdl, t);
                 rc.y = quad_bcast_i(rx, t);
                 rc.z = quad_bcast_i(rds, t);
-                Vec<S> bc, cc;
-                bc.load(bt + t * R + n0);
-                cc.load(bt + t * R + NP + n0);
+                const Vec<S> bc = rbn, cc = rcn;
+                if (t > 0) {
+                    rbn.load(bt + (t - 1) * R + n0);
+                    rcn.load(bt + (t - 1) * R + NP + n0);
+                }
+                // those reads stay issued at the step's start, ahead of its arithmetic
+                __builtin_amdgcn_sched_barrier(0);
                 const float dxr = rc.x * rc.y;
                 float pxa = 0.0f, pda = 0.0f;
                 float cB[S], cC[S];
