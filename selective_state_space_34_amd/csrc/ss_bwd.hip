@@ -692,33 +692,50 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
             *reinterpret_cast<float4*>(mine + PXO + 4) = make_float4(pdb[0], pdb[1], pdb[2], pdb[3]);
             wave_sync();
             // sum over the wave's 16 channels: output e -> (state sp_, lane group jp, type
-            // ty, step st)
+            // ty, step st).  Every read of the lane's outputs and of its Σ_n partials below
+            // is issued before the first sum (one LDS round trip instead of a chain of them),
+            // then the 16 terms are added as a tree.
+            constexpr int NOUT = (2 * kBB * NP + 63) / 64;
+            float tv[NOUT][16];
 #pragma unroll
-            for (int r = 0; r < (2 * kBB * NP + 63) / 64; ++r) {
+            for (int r = 0; r < NOUT; ++r) {
+                const int e = lane + 64 * r;
+                const int sp_ = e % S;
+                const int jp = (e / S) % 4;
+                const int ty = (e / (4 * S)) % 2;
+                const int st = (e / (8 * S)) % kBB;
+                const float* col = wx + jp * LS + ty * kBB * S + st * S + sp_;
+#pragma unroll
+                for (int c = 0; c < 16; ++c) tv[r][c] = col[c * 4 * LS];
+            }
+            float pv[2][4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float* src = wx + (qb + r) * LS + PXO + j;
+                pv[0][r] = src[0];
+                pv[1][r] = src[4];
+            }
+#pragma unroll
+            for (int r = 0; r < NOUT; ++r) {
                 const int e = lane + 64 * r;
                 if (e < 2 * kBB * NP) {
                     const int sp_ = e % S;
                     const int jp = (e / S) % 4;
                     const int ty = (e / (4 * S)) % 2;
                     const int st = e / (8 * S);
-                    const float* col = wx + jp * LS + ty * kBB * S + st * S + sp_;
-                    float tot = col[0];
 #pragma unroll
-                    for (int c = 1; c < 16; ++c) tot += col[c * 4 * LS];
-                    cbuf[(bi * kBB + st) * 2 * NP + ty * NP + jp * S + sp_] = tot;
+                    for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+                        for (int c = 0; c < w; ++c) tv[r][c] += tv[r][c + w];
+                    cbuf[(bi * kBB + st) * 2 * NP + ty * NP + jp * S + sp_] = tv[r][0];
                 }
             }
             {
                 // lane j finishes step 4 bi + j of its channel: Σ_n over the quad's partials
                 // of that step, then dx and dΔ from the step's row
                 const int tj = bi * kBB + j;
-                float PX = wx[qb * LS + PXO + j], PD = wx[qb * LS + PXO + j + 4];
-#pragma unroll
-                for (int r = 1; r < 4; ++r) {
-                    const float* src = wx + (qb + r) * LS + PXO + j;
-                    PX += src[0];
-                    PD += src[4];
-                }
+                const float PX = (pv[0][0] + pv[0][1]) + (pv[0][2] + pv[0][3]);
+                const float PD = (pv[1][0] + pv[1][1]) + (pv[1][2] + pv[1][3]);
                 const float4 rw = *reinterpret_cast<const float4*>(myrow + 4 * tj);  // (δ, x, ds, σ)
                 const int64_t tg = t0c + tb + tj;
                 const bool ok = tg < t1c;
