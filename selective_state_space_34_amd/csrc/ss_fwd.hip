@@ -267,7 +267,10 @@ static hipError_t launch_bc_stage_t(const void* Bm, const void* Cm, float* BC, i
 template <typename Tin, int N>
 static hipError_t launch_scan_t(const ScanLaunch& p, hipStream_t s) {
     const int wg = p.D >= 256 ? 256 : int((p.D + 63) / 64) * 64;
-    dim3 grid(unsigned((p.D + wg - 1) / wg), unsigned(p.K), unsigned(p.B));
+    // the last chunk's aggregate has no successor: the carry reads it only into values it
+    // never stores (the final state comes from the output pass), so it is not computed
+    const unsigned kg = unsigned((p.agg && p.K > 1) ? p.K - 1 : p.K);
+    dim3 grid(unsigned((p.D + wg - 1) / wg), kg, unsigned(p.B));
     const Tin* x = static_cast<const Tin*>(p.x);
     const Tin* dr = static_cast<const Tin*>(p.dt_raw);
     const Tin* z = static_cast<const Tin*>(p.z);

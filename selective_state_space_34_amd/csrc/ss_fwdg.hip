@@ -693,7 +693,10 @@ static hipError_t launch_scang_mixed_t(const ScanLaunch& p, hipStream_t s) {
 template <typename Tin, int G, int S>
 static hipError_t launch_scang_t(const ScanLaunch& p, hipStream_t s) {
     constexpr int CB = 4 * 64 / G;
-    dim3 grid(unsigned((p.D + CB - 1) / CB), unsigned(p.K), unsigned(p.B));
+    // the last chunk's aggregate has no successor: the carry reads it only into values it
+    // never stores (the final state comes from the output pass), so it is not computed
+    const unsigned kg = unsigned((p.agg && p.K > 1) ? p.K - 1 : p.K);
+    dim3 grid(unsigned((p.D + CB - 1) / CB), kg, unsigned(p.B));
     const Tin* x = static_cast<const Tin*>(p.x);
     const Tin* dr = static_cast<const Tin*>(p.dt_raw);
     const Tin* z = static_cast<const Tin*>(p.z);
