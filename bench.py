@@ -45,10 +45,10 @@ STEP_SOURCES = ["ss_step.hip", "ss_device.h", "ss_plan.h", "ss_api.cpp", "ss_ker
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 MEASURED_TRAFFIC = {
     # (workload, disc): first-order (0) or exact zero-order hold (1)
-    ("c2", 0): {"sources": FWD_SOURCES, "fetch_kib": 316865, "write_kib": 397083,
-                "sources_sha256": "b4d8ad5863a0e41040486c81c57d588ab9cb74329d61aa14f3169db4831f93c2"},
-    ("c2", 1): {"sources": FWD_SOURCES, "fetch_kib": 336547, "write_kib": 415388,
-                "sources_sha256": "b4d8ad5863a0e41040486c81c57d588ab9cb74329d61aa14f3169db4831f93c2"},
+    ("c2", 0): {"sources": FWD_SOURCES, "fetch_kib": 318863, "write_kib": 399174,
+                "sources_sha256": "0ea80df27192f7fcc1fc6ce8393157fa34700a8252c7f4bc8122077e84877175"},
+    ("c2", 1): {"sources": FWD_SOURCES, "fetch_kib": 336294, "write_kib": 415446,
+                "sources_sha256": "0ea80df27192f7fcc1fc6ce8393157fa34700a8252c7f4bc8122077e84877175"},
     ("d1", 0): {"sources": STEP_SOURCES, "fetch_kib": 45071, "write_kib": 87040,
                 "sources_sha256": "49ad91af5f7733a2fd6aafabaa0a4dba71ac4d8dc2779d982edfa22be3ed12b0"},
 }

@@ -20,11 +20,13 @@
 //     halves h of the tile (kH = 16/G): widening, δ = softplus(dt_bias + dt_raw), δ·x.
 //     No element is prepared twice.
 // Per 16-step half:
-//   - the lanes write their (δ, δ·x) pairs into a per-wave LDS row of their channel;
-//   - the recurrence walks the 16 steps; each step reads its (δ, δ·x) pair from that
-//     row and B_t, C_t for the lane's S states from the tile, one step ahead, as
-//     broadcast reads (no VALU work moves operands between lanes); under the exact
-//     zero-order hold the pair is (δ, x) and each state forms its own gain;
+//   - four lanes, first-order hold: step t's (δ, δ·x) stays in quad lane t / 4, which
+//     formed it, and reaches the quad by a DPP broadcast folded into the multiplies that
+//     use it; otherwise (eight lanes, or the exact zero-order hold, whose pair is (δ, x)
+//     and whose per-state gain uses δ in fused multiply-adds) the lanes write their pairs
+//     into a per-wave LDS row of their channel and each step reads its pair from there;
+//   - the recurrence walks the 16 steps, reading B_t, C_t for the lane's S states from
+//     the tile, one step ahead, as broadcast LDS reads;
 //   - each lane's partial readouts (its S states, 16 steps) go to the same per-wave
 //     area; lane l sums the G partials of its own kH steps, adds D·x, applies the
 //     gate and stores kH outputs.
