@@ -27,7 +27,9 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // of that instruction (lane l, element e of 8): A row l % 32, k = 8·(l / 32) + e; B column
 // l % 32, same k; accumulator element r: row 8·(r / 4) + 4·(l / 32) + r % 4, column l % 32.
 // One LDS stage with the next K tile prefetched into registers: load(k+1) -> MFMAs on the
-// LDS copy of k -> barrier -> registers to LDS -> barrier.  LDS rows are padded by 8
+// LDS copy of k -> barrier -> registers to LDS -> barrier.  Inside a K tile each 16-deep
+// step's fragments are read while the previous step's MFMAs run (two fragment sets; the
+// accumulators then sit in arch VGPRs, 254 in all, still two waves per SIMD).  LDS rows are padded by 8
 // elements (144 bytes), which keeps the 16-byte fragment reads of 16 lanes on disjoint banks.
 constexpr int kGM = 256, kGN = 128, kGK = 64;
 constexpr int kGPad = kGK + 8;                   // LDS row stride (elements)
@@ -46,7 +48,7 @@ __device__ __forceinline__ uint4 load16_or_zero(const bf16_t* base, int64_t row,
 // C0 / C1 [M, ·] = (A [M, K] · W [Nc, K]ᵀ) split at column nsplit: columns [0, nsplit) go to
 // C0 (row stride ld0), [nsplit, Nc) to C1 at column - nsplit (row stride ld1).  K % 8 == 0.
 // grid = ceil(M / 256) · ceil(Nc / 128) (one dimension, remapped below), block = 256.
-__global__ __launch_bounds__(kGThreads) void gemm_bf16_nt_kernel(
+__global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_bf16_nt_kernel(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ W, float* __restrict__ C0,
     float* __restrict__ C1, int64_t M, int64_t Nc, int64_t K, int64_t nsplit, int64_t ld0,
     int64_t ld1, int tiles_m, int tiles_n) {
@@ -105,22 +107,27 @@ __global__ __launch_bounds__(kGThreads) void gemm_bf16_nt_kernel(
     load_tile(0);
     store_tile();
     __syncthreads();
+    // fragments of K step ks + 16 are read while the MFMAs of step ks run
+    auto read_frag = [&](int ks, bf16x8 (&af)[4], bf16x8 (&bfr)[2]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            af[i] = *reinterpret_cast<const bf16x8*>(As + (wm * 128 + 32 * i + lr) * kGPad + ks + lk);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            bfr[j] = *reinterpret_cast<const bf16x8*>(Ws + (wn * 64 + 32 * j + lr) * kGPad + ks + lk);
+    };
     for (int64_t kt = 0; kt < nk; ++kt) {
         if (kt + 1 < nk) load_tile((kt + 1) * kGK);
+        bf16x8 fa[2][4], fb[2][2];
+        read_frag(0, fa[0], fb[0]);
 #pragma unroll
-        for (int ks = 0; ks < kGK; ks += 16) {
-            bf16x8 af[4], bfr[2];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                af[i] = *reinterpret_cast<const bf16x8*>(As + (wm * 128 + 32 * i + lr) * kGPad + ks + lk);
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-                bfr[j] = *reinterpret_cast<const bf16x8*>(Ws + (wn * 64 + 32 * j + lr) * kGPad + ks + lk);
+        for (int q = 0; q < kGK / 16; ++q) {
+            if (q + 1 < kGK / 16) read_frag(16 * (q + 1), fa[(q + 1) & 1], fb[(q + 1) & 1]);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[q & 1][i], fb[q & 1][j], acc[i][j], 0, 0, 0);
         }
         if (kt + 1 < nk) {
             __syncthreads();
