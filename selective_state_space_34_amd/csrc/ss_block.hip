@@ -155,87 +155,120 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
 }
 
 // ---- selection projections -----------------------------------------------------------------
-// part[s, m, o] = Σ_{k in split s} x[m, k] · Wx[o, k], o < P = 1 + 2N: a product with few
-// columns, register-tiled on the vector ALUs.  Thread (token group tg, output group og) owns
-// 4 tokens x 4 outputs (16 accumulators); per K step it reads 4 x values and 4 weights as two
-// 16-byte LDS reads for 16 FMAs.  A workgroup covers TM = 4·TG tokens and all outputs, and
-// one split of K, staged 32 steps at a time: x rows are read coalesced (8 threads per 128-byte
-// row piece) and stored transposed, [k][token], so a thread's 4 tokens are adjacent.
-// grid = (ceil(M / TM), S), block = TG·OG threads.  D % 4 == 0.
-template <int P>
-struct XprojShape {
-    static constexpr int OG = (P + 3) / 4;           // output groups of 4
-    static constexpr int TG = 256 / OG;              // token groups of 4
-    static constexpr int TM = 4 * TG;                // tokens per workgroup
-    static constexpr int THREADS = TG * OG;
-    static constexpr int KT = 32;                    // K steps per LDS stage
-    static constexpr int XS = TM + 4;                // row stride of the transposed x tile
-    static constexpr int WS = 4 * OG;                // row stride of the weight tile
-};
+// part[s, m, o] = Σ_{k in split s} x[m, k] · Wx[o, k], o < P = 1 + 2N: a dense contraction over
+// K = D with few columns, run on the fp32 matrix cores (v_mfma_f32_16x16x4f32: 16 x 16 output,
+// K = 4; operand a of lane l is A[l % 16][l / 16], operand b is B[l / 16][l % 16], and the
+// accumulator's element v is C[4·(l / 16) + v][l % 16]).  A wave owns MT tiles of 16 tokens
+// and NT tiles of 16 outputs over one K split.  Per 16-deep K chunk lane (r, g) = (l % 16,
+// l / 16) loads one 16-byte run of each of its tokens' x rows, x[m + r][kc + 4g .. kc + 4g + 3],
+// and the same run of each output tile's weight row; MFMA j of the chunk takes element j of
+// both runs, so it sums the products at k = kc + 4g + j over g: the four MFMAs cover the
+// chunk's 16 steps (the order of k inside a chunk is permuted the same way for both operands).
+// No LDS: x runs are 64 bytes per token row per chunk, coalesced, and the weights (P·D floats)
+// stay in L2.  Up to three chunks after the current one are in flight while its MFMAs run.
+// Workgroup = 4 waves = 64·MT tokens.
+// grid = (ceil(M / (64·MT)), S), block = 256.  D % 4 == 0; split lengths are multiples of 16.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+// 16-token tiles per wave (MT): each weight run loaded feeds MT MFMAs.  Two tiles measured
+// 1.7 % faster on the block step than one at N = 16, four no faster than two at half the
+// occupancy; above three output tiles (N > 16) one token tile keeps the registers in reach.
+static inline int xproj_mt(int N) { return N <= 16 ? 2 : 1; }
 
-template <int P>
-__global__ __launch_bounds__(256) void xproj_partial_kernel(
+template <int NT, int MT>
+__global__ __launch_bounds__(256) void xproj_mfma_kernel(
     const float* __restrict__ x, const float* __restrict__ Wx, float* __restrict__ part,
-    int64_t M, int64_t D, int64_t kc) {
-    using Sh = XprojShape<P>;
-    __shared__ __align__(16) float xs[Sh::KT * Sh::XS];
-    __shared__ __align__(16) float wsh[Sh::KT * Sh::WS];
-    const int tid = threadIdx.x;
-    const int tg = tid % Sh::TG, og = tid / Sh::TG;
+    int64_t M, int64_t D, int P, int64_t kc) {
+    // chunk slots per wave (PD - 1 chunks in flight): a chunk's 4·NT·MT MFMAs cover less than
+    // a global load's latency; wider tiles hold more registers per slot
+    constexpr int PD = (NT + MT) <= 4 ? 4 : (NT + MT) <= 6 ? 3 : 2;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r = lane & 15, g = lane >> 4;
     const int s = blockIdx.y;
-    const int64_t m0 = int64_t(blockIdx.x) * Sh::TM;
+    const int64_t m0 = (int64_t(blockIdx.x) * 4 + wave) * (16 * MT);
     const int64_t k0 = int64_t(s) * kc;
     const int64_t k1 = (k0 + kc < D) ? k0 + kc : D;
+    const int64_t nch = (k1 > k0) ? (k1 - k0 + 15) / 16 : 0;
+    // rows past M read the last row and rows past P the last weight row (in bounds); their
+    // results are dropped, resp. zeroed
+    const float* xr[MT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+        const int64_t m = m0 + 16 * i + r;
+        xr[i] = x + (m < M ? m : M - 1) * D;
+    }
+    const float* wr[NT];
+    bool wok[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const int o = 16 * t + r;
+        wok[t] = o < P;
+        wr[t] = Wx + int64_t(wok[t] ? o : P - 1) * D;
+    }
+    f32x4 acc[MT][NT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[i][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    float acc[4][4];
+    // chunk c of the split: this lane's runs start at k0 + 16c + 4g.  k1 and the runs are
+    // multiples of 4, so a run is wholly inside the split or wholly past it; a run past it
+    // (also every run of a chunk c >= nch) loads the split's first run (in bounds) and its
+    // weights are zeroed where the MFMA takes them (a select next to the load would make the
+    // wave wait for the load right there).  Loads and MFMAs are unconditional (chunks past the
+    // end add zeros), so the loop body is straight-line code and the chunks in flight are
+    // plain vmcnt steps.
+    float4 xb[PD][MT], wb[PD][NT];
+    bool inb[PD];
+    auto load = [&](int64_t c, float4 (&xa)[MT], float4 (&w)[NT], bool& in) {
+        const int64_t k = k0 + 16 * c + 4 * g;
+        in = k < k1;
+        const int64_t kk = in ? k : k0;
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+        for (int i = 0; i < MT; ++i) xa[i] = *reinterpret_cast<const float4*>(xr[i] + kk);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) acc[a][c] = 0.0f;
-
-    for (int64_t kb = k0; kb < k1; kb += Sh::KT) {
-        const int nk = int((k1 - kb < Sh::KT) ? k1 - kb : Sh::KT);   // a multiple of 4
-        __syncthreads();                                               // previous stage read
-        for (int e = tid; e < Sh::TM * (Sh::KT / 4); e += Sh::THREADS) {
-            const int tok = e / (Sh::KT / 4), q = e % (Sh::KT / 4);
-            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (m0 + tok < M && 4 * q < nk) v = *reinterpret_cast<const float4*>(x + (m0 + tok) * D + kb + 4 * q);
-            xs[(4 * q + 0) * Sh::XS + tok] = v.x;
-            xs[(4 * q + 1) * Sh::XS + tok] = v.y;
-            xs[(4 * q + 2) * Sh::XS + tok] = v.z;
-            xs[(4 * q + 3) * Sh::XS + tok] = v.w;
-        }
-        for (int e = tid; e < Sh::WS * (Sh::KT / 4); e += Sh::THREADS) {
-            const int o = e / (Sh::KT / 4), q = e % (Sh::KT / 4);
-            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (o < P && 4 * q < nk) v = *reinterpret_cast<const float4*>(Wx + int64_t(o) * D + kb + 4 * q);
-            wsh[(4 * q + 0) * Sh::WS + o] = v.x;
-            wsh[(4 * q + 1) * Sh::WS + o] = v.y;
-            wsh[(4 * q + 2) * Sh::WS + o] = v.z;
-            wsh[(4 * q + 3) * Sh::WS + o] = v.w;
-        }
-        __syncthreads();
-#pragma unroll 8
-        for (int k = 0; k < Sh::KT; ++k) {
-            const float4 xv = *reinterpret_cast<const float4*>(xs + k * Sh::XS + 4 * tg);
-            const float4 wv = *reinterpret_cast<const float4*>(wsh + k * Sh::WS + 4 * og);
-            const float xa[4] = {xv.x, xv.y, xv.z, xv.w};
-            const float wa[4] = {wv.x, wv.y, wv.z, wv.w};
+        for (int t = 0; t < NT; ++t) w[t] = *reinterpret_cast<const float4*>(wr[t] + kk);
+    };
+    if (nch > 0) {
 #pragma unroll
-            for (int a = 0; a < 4; ++a)
+        for (int u = 0; u < PD - 1; ++u) load(u, xb[u], wb[u], inb[u]);
+        for (int64_t c = 0; c < nch; c += PD) {
 #pragma unroll
-                for (int c = 0; c < 4; ++c) acc[a][c] = fmaf(xa[a], wa[c], acc[a][c]);
+            for (int u = 0; u < PD; ++u) {
+                // chunk c + u + PD - 1 into the slot chunk c + u - 1 has freed
+                load(c + u + PD - 1, xb[(u + PD - 1) % PD], wb[(u + PD - 1) % PD], inb[(u + PD - 1) % PD]);
+                // the loads stay issued here, PD - 1 chunks ahead of their use
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int t = 0; t < NT; ++t) {
+                        const float4& wv = wb[u][t];
+                        const float bv = j == 0 ? wv.x : j == 1 ? wv.y : j == 2 ? wv.z : wv.w;
+                        // a run past the split's end, or a weight row past P, contributes 0
+                        // (zeroing the weight suffices: the x run read instead is finite data)
+                        const float bz = (inb[u] && wok[t]) ? bv : 0.0f;
+#pragma unroll
+                        for (int i = 0; i < MT; ++i) {
+                            const float4& xa = xb[u][i];
+                            const float av = j == 0 ? xa.x : j == 1 ? xa.y : j == 2 ? xa.z : xa.w;
+                            acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bz, acc[i][t], 0, 0, 0);
+                        }
+                    }
+            }
         }
     }
+    // element v of tile (i, t): token m0 + 16i + 4g + v, output 16t + r
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-        const int64_t m = m0 + 4 * tg + a;
-        if (m >= M) continue;
-        float* pr = part + (int64_t(s) * M + m) * P;
+    for (int i = 0; i < MT; ++i)
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-            if (4 * og + c < P) pr[4 * og + c] = acc[a][c];
-    }
+        for (int v = 0; v < 4; ++v) {
+            const int64_t m = m0 + 16 * i + 4 * g + v;
+            if (m >= M) continue;
+            float* pr = part + (int64_t(s) * M + m) * P;
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                if (16 * t + r < P) pr[16 * t + r] = acc[i][t][v];
+        }
 }
 
 // Σ over the S splits -> Δraw [M], B [M, N], C [M, N].  One thread per (m, o).
@@ -266,35 +299,25 @@ hipError_t launch_gemm_bf16_nt(const void* A, const void* W, float* C0, float* C
     return hipGetLastError();
 }
 
-static int xproj_tile_tokens(int N) {
-    switch (N) {
-        case 1: return XprojShape<3>::TM;
-        case 2: return XprojShape<5>::TM;
-        case 4: return XprojShape<9>::TM;
-        case 8: return XprojShape<17>::TM;
-        case 16: return XprojShape<33>::TM;
-        case 32: return XprojShape<65>::TM;
-        default: return XprojShape<129>::TM;
-    }
-}
-
 int64_t xproj_splits(int64_t M, int64_t D, int N) {
-    // about 1024 workgroups in all, each split at least 64 steps of K
-    const int64_t mb = (M + xproj_tile_tokens(N) - 1) / xproj_tile_tokens(N);
+    // about 1024 workgroups in all (one round of four waves per SIMD at the kernel's register
+    // use for N = 16), each split at least 64 steps of K
+    const int64_t tok = 64 * xproj_mt(N);        // tokens per workgroup
+    const int64_t mb = (M + tok - 1) / tok;
     int64_t S = (1024 + mb - 1) / mb;
     if (S > D / 64) S = D / 64;
     return S < 1 ? 1 : S;
 }
 
-int64_t xproj_split_len(int64_t D, int64_t S) { return ((D + S - 1) / S + 3) / 4 * 4; }
+// split length: a multiple of the 16-step chunk
+int64_t xproj_split_len(int64_t D, int64_t S) { return ((D + S - 1) / S + 15) / 16 * 16; }
 
-template <int P>
-static hipError_t launch_xproj_p(const float* x, const float* Wx, float* part, int64_t M,
-                                 int64_t D, int64_t S, int64_t kc, hipStream_t s) {
-    using Sh = XprojShape<P>;
-    hipLaunchKernelGGL((xproj_partial_kernel<P>),
-                       dim3(unsigned((M + Sh::TM - 1) / Sh::TM), unsigned(S)), dim3(Sh::THREADS),
-                       0, s, x, Wx, part, M, D, kc);
+template <int NT, int MT>
+static hipError_t launch_xproj_t(const float* x, const float* Wx, float* part, int64_t M,
+                                 int64_t D, int P, int64_t S, int64_t kc, hipStream_t s) {
+    const int64_t tok = 64 * MT;
+    hipLaunchKernelGGL((xproj_mfma_kernel<NT, MT>), dim3(unsigned((M + tok - 1) / tok), unsigned(S)),
+                       dim3(256), 0, s, x, Wx, part, M, D, P, kc);
     return hipGetLastError();
 }
 
@@ -302,15 +325,14 @@ hipError_t launch_xproj(const float* x, const float* Wx, float* part, float* dt,
                         float* Cm, int64_t M, int64_t D, int N, hipStream_t s) {
     const int64_t S = xproj_splits(M, D, N);
     const int64_t kc = xproj_split_len(D, S);
+    const int P = 1 + 2 * N;
     hipError_t e;
-    switch (N) {
-        case 1: e = launch_xproj_p<3>(x, Wx, part, M, D, S, kc, s); break;
-        case 2: e = launch_xproj_p<5>(x, Wx, part, M, D, S, kc, s); break;
-        case 4: e = launch_xproj_p<9>(x, Wx, part, M, D, S, kc, s); break;
-        case 8: e = launch_xproj_p<17>(x, Wx, part, M, D, S, kc, s); break;
-        case 16: e = launch_xproj_p<33>(x, Wx, part, M, D, S, kc, s); break;
-        case 32: e = launch_xproj_p<65>(x, Wx, part, M, D, S, kc, s); break;
-        case 64: e = launch_xproj_p<129>(x, Wx, part, M, D, S, kc, s); break;
+    switch (N) {   // ceil(P / 16) output tiles; token tiles per wave as xproj_mt(N)
+        case 1: case 2: case 4: e = launch_xproj_t<1, 2>(x, Wx, part, M, D, P, S, kc, s); break;
+        case 8: e = launch_xproj_t<2, 2>(x, Wx, part, M, D, P, S, kc, s); break;
+        case 16: e = launch_xproj_t<3, 2>(x, Wx, part, M, D, P, S, kc, s); break;
+        case 32: e = launch_xproj_t<5, 1>(x, Wx, part, M, D, P, S, kc, s); break;
+        case 64: e = launch_xproj_t<9, 1>(x, Wx, part, M, D, P, S, kc, s); break;
         default: return hipErrorInvalidValue;
     }
     if (e != hipSuccess) return e;
