@@ -158,12 +158,15 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
 // part[s, m, o] = Σ_{k in split s} x[m, k] · Wx[o, k], o < P = 1 + 2N: a dense contraction over
 // K = D with few columns, run on the fp32 matrix cores (v_mfma_f32_16x16x4f32: 16 x 16 output,
 // K = 4; operand a of lane l is A[l % 16][l / 16], operand b is B[l / 16][l % 16], and the
-// accumulator's element v is C[4·(l / 16) + v][l % 16]).  A wave owns MT tiles of 16 tokens
-// and NT tiles of 16 outputs over one K split.  Per 16-deep K chunk lane (r, g) = (l % 16,
-// l / 16) loads one 16-byte run of each of its tokens' x rows, x[m + r][kc + 4g .. kc + 4g + 3],
-// and the same run of each output tile's weight row; MFMA j of the chunk takes element j of
+// accumulator's element v is C[4·(l / 16) + v][l % 16]).  P = 1 + 2N: the 2N outputs of B and
+// C fill whole 16-wide tiles for N >= 8, and output 0 (Δraw) is a dot product per lane on the
+// vector ALUs instead of a third, mostly empty tile.  A wave owns MT tiles of 16 tokens and the
+// NT output tiles over one K split.  Per 16-deep K chunk lane (r, g) = (l % 16, l / 16) loads
+// one 16-byte run of each of its tokens' x rows, x[m + r][kc + 4g .. kc + 4g + 3], and the same
+// run of each output tile's weight row and of row 0; MFMA j of the chunk takes element j of
 // both runs, so it sums the products at k = kc + 4g + j over g: the four MFMAs cover the
-// chunk's 16 steps (the order of k inside a chunk is permuted the same way for both operands).
+// chunk's 16 steps (the order of k inside a chunk is permuted the same way for both operands),
+// and output 0's four-term partials are summed over the four lanes g of a token at the end.
 // No LDS: x runs are 64 bytes per token row per chunk, coalesced, and the weights (P·D floats)
 // stay in L2.  Up to three chunks after the current one are in flight while its MFMAs run.
 // Workgroup = 4 waves = 64·MT tokens.
@@ -196,19 +199,26 @@ __global__ __launch_bounds__(256) void xproj_mfma_kernel(
         const int64_t m = m0 + 16 * i + r;
         xr[i] = x + (m < M ? m : M - 1) * D;
     }
+    // MFMA tile t holds outputs 1 + 16t .. 16 + 16t (the 2N rows of B and C: whole tiles for
+    // N >= 8); output 0, the Δraw row, is a per-lane dot product on the vector ALUs, summed
+    // over the four lanes of a token at the end
     const float* wr[NT];
     bool wok[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-        const int o = 16 * t + r;
+        const int o = 1 + 16 * t + r;
         wok[t] = o < P;
         wr[t] = Wx + int64_t(wok[t] ? o : P - 1) * D;
     }
+    const float* w0r = Wx;
     f32x4 acc[MT][NT];
+    float dacc[MT];
 #pragma unroll
-    for (int i = 0; i < MT; ++i)
+    for (int i = 0; i < MT; ++i) {
+        dacc[i] = 0.0f;
 #pragma unroll
         for (int t = 0; t < NT; ++t) acc[i][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
 
     // chunk c of the split: this lane's runs start at k0 + 16c + 4g.  k1 and the runs are
     // multiples of 4, so a run is wholly inside the split or wholly past it; a run past it
@@ -217,9 +227,9 @@ __global__ __launch_bounds__(256) void xproj_mfma_kernel(
     // wave wait for the load right there).  Loads and MFMAs are unconditional (chunks past the
     // end add zeros), so the loop body is straight-line code and the chunks in flight are
     // plain vmcnt steps.
-    float4 xb[PD][MT], wb[PD][NT];
+    float4 xb[PD][MT], wb[PD][NT], w0b[PD];
     bool inb[PD];
-    auto load = [&](int64_t c, float4 (&xa)[MT], float4 (&w)[NT], bool& in) {
+    auto load = [&](int64_t c, float4 (&xa)[MT], float4 (&w)[NT], float4& w0, bool& in) {
         const int64_t k = k0 + 16 * c + 4 * g;
         in = k < k1;
         const int64_t kk = in ? k : k0;
@@ -227,15 +237,17 @@ __global__ __launch_bounds__(256) void xproj_mfma_kernel(
         for (int i = 0; i < MT; ++i) xa[i] = *reinterpret_cast<const float4*>(xr[i] + kk);
 #pragma unroll
         for (int t = 0; t < NT; ++t) w[t] = *reinterpret_cast<const float4*>(wr[t] + kk);
+        w0 = *reinterpret_cast<const float4*>(w0r + kk);
     };
     if (nch > 0) {
 #pragma unroll
-        for (int u = 0; u < PD - 1; ++u) load(u, xb[u], wb[u], inb[u]);
+        for (int u = 0; u < PD - 1; ++u) load(u, xb[u], wb[u], w0b[u], inb[u]);
         for (int64_t c = 0; c < nch; c += PD) {
 #pragma unroll
             for (int u = 0; u < PD; ++u) {
                 // chunk c + u + PD - 1 into the slot chunk c + u - 1 has freed
-                load(c + u + PD - 1, xb[(u + PD - 1) % PD], wb[(u + PD - 1) % PD], inb[(u + PD - 1) % PD]);
+                load(c + u + PD - 1, xb[(u + PD - 1) % PD], wb[(u + PD - 1) % PD], w0b[(u + PD - 1) % PD],
+                     inb[(u + PD - 1) % PD]);
                 // the loads stay issued here, PD - 1 chunks ahead of their use
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -254,10 +266,17 @@ __global__ __launch_bounds__(256) void xproj_mfma_kernel(
                             acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bz, acc[i][t], 0, 0, 0);
                         }
                     }
+#pragma unroll
+                for (int i = 0; i < MT; ++i) {
+                    const float4& xa = xb[u][i];
+                    const float4& w0 = w0b[u];
+                    const float d4 = fmaf(xa.w, w0.w, fmaf(xa.z, w0.z, fmaf(xa.y, w0.y, xa.x * w0.x)));
+                    dacc[i] += inb[u] ? d4 : 0.0f;
+                }
             }
         }
     }
-    // element v of tile (i, t): token m0 + 16i + 4g + v, output 16t + r
+    // element v of tile (i, t): token m0 + 16i + 4g + v, output 1 + 16t + r
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
@@ -267,8 +286,17 @@ __global__ __launch_bounds__(256) void xproj_mfma_kernel(
             float* pr = part + (int64_t(s) * M + m) * P;
 #pragma unroll
             for (int t = 0; t < NT; ++t)
-                if (16 * t + r < P) pr[16 * t + r] = acc[i][t][v];
+                if (1 + 16 * t + r < P) pr[1 + 16 * t + r] = acc[i][t][v];
         }
+    // output 0: the four lanes g of token m0 + 16i + r hold partial dot products
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+        float d = dacc[i];
+        d += __shfl_xor(d, 16, 64);
+        d += __shfl_xor(d, 32, 64);
+        const int64_t m = m0 + 16 * i + r;
+        if (g == 0 && m < M) part[(int64_t(s) * M + m) * P] = d;
+    }
 }
 
 // Σ over the S splits -> Δraw [M], B [M, N], C [M, N].  One thread per (m, o).
@@ -327,12 +355,11 @@ hipError_t launch_xproj(const float* x, const float* Wx, float* part, float* dt,
     const int64_t kc = xproj_split_len(D, S);
     const int P = 1 + 2 * N;
     hipError_t e;
-    switch (N) {   // ceil(P / 16) output tiles; token tiles per wave as xproj_mt(N)
-        case 1: case 2: case 4: e = launch_xproj_t<1, 2>(x, Wx, part, M, D, P, S, kc, s); break;
-        case 8: e = launch_xproj_t<2, 2>(x, Wx, part, M, D, P, S, kc, s); break;
-        case 16: e = launch_xproj_t<3, 2>(x, Wx, part, M, D, P, S, kc, s); break;
-        case 32: e = launch_xproj_t<5, 1>(x, Wx, part, M, D, P, S, kc, s); break;
-        case 64: e = launch_xproj_t<9, 1>(x, Wx, part, M, D, P, S, kc, s); break;
+    switch (N) {   // ceil(2N / 16) output tiles; token tiles per wave as xproj_mt(N)
+        case 1: case 2: case 4: case 8: e = launch_xproj_t<1, 2>(x, Wx, part, M, D, P, S, kc, s); break;
+        case 16: e = launch_xproj_t<2, 2>(x, Wx, part, M, D, P, S, kc, s); break;
+        case 32: e = launch_xproj_t<4, 1>(x, Wx, part, M, D, P, S, kc, s); break;
+        case 64: e = launch_xproj_t<8, 1>(x, Wx, part, M, D, P, S, kc, s); break;
         default: return hipErrorInvalidValue;
     }
     if (e != hipSuccess) return e;
