@@ -7,8 +7,9 @@
 //   [x | z]    = u · W_inᵀ        u [M, K] bf16, W_in [2D, K] bf16: a dense contraction,
 //                                  run on the matrix cores (gemm_bf16_nt_kernel)
 //   [Δ | B | C] = x · W_xᵀ        x [M, D] fp32, W_x [1 + 2N, D] fp32: 1 + 2N outputs per
-//                                  token, a skinny product kept in fp32 on the vector ALUs
-//                                  (xproj_partial_kernel, xproj_reduce_kernel)
+//                                  token, a skinny contraction kept in fp32: B and C on the
+//                                  fp32 matrix cores, Δ as a vector dot product beside them
+//                                  (xproj_mfma_kernel, xproj_reduce_kernel)
 // M = B·L tokens.  x and z stay float32, so the scan that follows sees the projections
 // at float32 accuracy.
 #include "ss_device.h"
