@@ -162,56 +162,78 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
 // accumulator's element v is C[4·(l / 16) + v][l % 16]).  P = 1 + 2N: the 2N outputs of B and
 // C fill whole 16-wide tiles for N >= 8, and output 0 (Δraw) is a dot product per lane on the
 // vector ALUs instead of a third, mostly empty tile.  A wave owns MT tiles of 16 tokens and the
-// NT output tiles over one K split.  Per 16-deep K chunk lane (r, g) = (l % 16, l / 16) loads
-// one 16-byte run of each of its tokens' x rows, x[m + r][kc + 4g .. kc + 4g + 3], and the same
-// run of each output tile's weight row and of row 0; MFMA j of the chunk takes element j of
-// both runs, so it sums the products at k = kc + 4g + j over g: the four MFMAs cover the
-// chunk's 16 steps (the order of k inside a chunk is permuted the same way for both operands),
-// and output 0's four-term partials are summed over the four lanes g of a token at the end.
-// No LDS: x runs are 64 bytes per token row per chunk, coalesced, and the weights (P·D floats)
-// stay in L2.  Up to three chunks after the current one are in flight while its MFMAs run.
-// Workgroup = 4 waves = 64·MT tokens.
-// grid = (ceil(M / (64·MT)), S), block = 256.  D % 4 == 0; split lengths are multiples of 16.
+// NT output tiles over one K split.  The workgroup stages 64-step tiles of its tokens' x rows
+// and of the weight rows in LDS, each global load covering 256-byte runs of a row (reading x
+// straight into the MFMA operands instead scattered 64-byte pieces over 16 rows per load and
+// ran at a third of the DRAM rate), the next tile prefetched into registers.  Per 16-deep
+// chunk lane (r, g) = (l % 16, l / 16) reads one 16-byte run of each of its tokens' x rows,
+// x[m + r][kc + 4g .. kc + 4g + 3], and the same run of each output tile's weight row and of
+// row 0; MFMA j of the chunk takes element j of both runs, so it sums the products at
+// k = kc + 4g + j over g: the four MFMAs cover the chunk's 16 steps (the order of k inside a
+// chunk is permuted the same way for both operands), and output 0's four-term partials are
+// summed over the four lanes g of a token at the end.  Workgroup = 4 waves = 64·MT tokens.
+// grid = (ceil(M / (64·MT)), S), block = 256.  D % 4 == 0; split lengths are multiples of 64.
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 // 16-token tiles per wave (MT): each weight run loaded feeds MT MFMAs.  Two tiles measured
 // 1.7 % faster on the block step than one at N = 16, four no faster than two at half the
 // occupancy; above three output tiles (N > 16) one token tile keeps the registers in reach.
 static inline int xproj_mt(int N) { return N <= 16 ? 2 : 1; }
 
+// K steps per LDS tile and the tiles' row stride (floats; 4 of padding)
+constexpr int kXK = 64;
+constexpr int kXRS = kXK + 4;
+
 template <int NT, int MT>
 __global__ __launch_bounds__(256) void xproj_mfma_kernel(
     const float* __restrict__ x, const float* __restrict__ Wx, float* __restrict__ part,
     int64_t M, int64_t D, int P, int64_t kc) {
-    // chunk slots per wave (PD - 1 chunks in flight): a chunk's 4·NT·MT MFMAs cover less than
-    // a global load's latency; wider tiles hold more registers per slot
-    constexpr int PD = (NT + MT) <= 4 ? 4 : (NT + MT) <= 6 ? 3 : 2;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    constexpr int XT = 64 * MT;                  // tokens per workgroup
+    constexpr int XQ = XT * (kXK / 4) / 256;     // x float4 pieces per thread per tile
+    constexpr int PR = 1 + 16 * NT;              // weight rows staged (P <= PR)
+    constexpr int WQ = (PR * (kXK / 4) + 255) / 256;
+    __shared__ __align__(16) float xs[XT * kXRS];
+    __shared__ __align__(16) float ws[PR * kXRS];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
     const int r = lane & 15, g = lane >> 4;
     const int s = blockIdx.y;
-    const int64_t m0 = (int64_t(blockIdx.x) * 4 + wave) * (16 * MT);
+    const int64_t m0 = int64_t(blockIdx.x) * XT;
     const int64_t k0 = int64_t(s) * kc;
     const int64_t k1 = (k0 + kc < D) ? k0 + kc : D;
-    const int64_t nch = (k1 > k0) ? (k1 - k0 + 15) / 16 : 0;
-    // rows past M read the last row and rows past P the last weight row (in bounds); their
-    // results are dropped, resp. zeroed
-    const float* xr[MT];
+    const int64_t nt = (k1 > k0) ? (k1 - k0 + kXK - 1) / kXK : 0;
+
+    // staging: 16 consecutive threads cover one row's 64 steps (256 bytes); steps at or past
+    // k1 and rows past M or P load nothing and stage zeros
+    float4 px[XQ], pw[WQ];
+    auto load_tile = [&](int64_t kt) {
 #pragma unroll
-    for (int i = 0; i < MT; ++i) {
-        const int64_t m = m0 + 16 * i + r;
-        xr[i] = x + (m < M ? m : M - 1) * D;
-    }
-    // MFMA tile t holds outputs 1 + 16t .. 16 + 16t (the 2N rows of B and C: whole tiles for
-    // N >= 8); output 0, the Δraw row, is a per-lane dot product on the vector ALUs, summed
-    // over the four lanes of a token at the end
-    const float* wr[NT];
-    bool wok[NT];
+        for (int q = 0; q < XQ; ++q) {
+            const int e = tid + 256 * q, row = e >> 4, c4 = e & 15;
+            const int64_t k = kt + 4 * c4, m = m0 + row;
+            px[q] = (m < M && k < k1) ? *reinterpret_cast<const float4*>(x + m * D + k)
+                                      : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-        const int o = 1 + 16 * t + r;
-        wok[t] = o < P;
-        wr[t] = Wx + int64_t(wok[t] ? o : P - 1) * D;
-    }
-    const float* w0r = Wx;
+        for (int q = 0; q < WQ; ++q) {
+            const int e = tid + 256 * q, row = e >> 4, c4 = e & 15;
+            const int64_t k = kt + 4 * c4;
+            pw[q] = (row < P && k < k1) ? *reinterpret_cast<const float4*>(Wx + int64_t(row) * D + k)
+                                        : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    };
+    auto store_tile = [&]() {
+#pragma unroll
+        for (int q = 0; q < XQ; ++q) {
+            const int e = tid + 256 * q;
+            *reinterpret_cast<float4*>(xs + (e >> 4) * kXRS + 4 * (e & 15)) = px[q];
+        }
+#pragma unroll
+        for (int q = 0; q < WQ; ++q) {
+            const int e = tid + 256 * q;
+            if (e < PR * (kXK / 4)) *reinterpret_cast<float4*>(ws + (e >> 4) * kXRS + 4 * (e & 15)) = pw[q];
+        }
+    };
+
     f32x4 acc[MT][NT];
     float dacc[MT];
 #pragma unroll
@@ -220,82 +242,65 @@ __global__ __launch_bounds__(256) void xproj_mfma_kernel(
 #pragma unroll
         for (int t = 0; t < NT; ++t) acc[i][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
-
-    // chunk c of the split: this lane's runs start at k0 + 16c + 4g.  k1 and the runs are
-    // multiples of 4, so a run is wholly inside the split or wholly past it; a run past it
-    // (also every run of a chunk c >= nch) loads the split's first run (in bounds) and its
-    // weights are zeroed where the MFMA takes them (a select next to the load would make the
-    // wave wait for the load right there).  Loads and MFMAs are unconditional (chunks past the
-    // end add zeros), so the loop body is straight-line code and the chunks in flight are
-    // plain vmcnt steps.
-    float4 xb[PD][MT], wb[PD][NT], w0b[PD];
-    bool inb[PD];
-    auto load = [&](int64_t c, float4 (&xa)[MT], float4 (&w)[NT], float4& w0, bool& in) {
-        const int64_t k = k0 + 16 * c + 4 * g;
-        in = k < k1;
-        const int64_t kk = in ? k : k0;
+    if (nt > 0) {
+        load_tile(k0);
+        store_tile();
+        __syncthreads();
+    }
+    for (int64_t it = 0; it < nt; ++it) {
+        if (it + 1 < nt) load_tile(k0 + (it + 1) * kXK);
 #pragma unroll
-        for (int i = 0; i < MT; ++i) xa[i] = *reinterpret_cast<const float4*>(xr[i] + kk);
+        for (int cc = 0; cc < kXK / 16; ++cc) {
+            // chunk cc: lane (r, g) takes the runs at steps 16cc + 4g .. 16cc + 4g + 3
+            const int kl = 16 * cc + 4 * g;
+            float4 xa[MT], wb[NT];
 #pragma unroll
-        for (int t = 0; t < NT; ++t) w[t] = *reinterpret_cast<const float4*>(wr[t] + kk);
-        w0 = *reinterpret_cast<const float4*>(w0r + kk);
-    };
-    if (nch > 0) {
+            for (int i = 0; i < MT; ++i)
+                xa[i] = *reinterpret_cast<const float4*>(xs + (wave * 16 * MT + 16 * i + r) * kXRS + kl);
 #pragma unroll
-        for (int u = 0; u < PD - 1; ++u) load(u, xb[u], wb[u], w0b[u], inb[u]);
-        for (int64_t c = 0; c < nch; c += PD) {
+            for (int t = 0; t < NT; ++t)
+                wb[t] = *reinterpret_cast<const float4*>(ws + (1 + 16 * t + r) * kXRS + kl);
+            const float4 w0 = *reinterpret_cast<const float4*>(ws + kl);
 #pragma unroll
-            for (int u = 0; u < PD; ++u) {
-                // chunk c + u + PD - 1 into the slot chunk c + u - 1 has freed
-                load(c + u + PD - 1, xb[(u + PD - 1) % PD], wb[(u + PD - 1) % PD], w0b[(u + PD - 1) % PD],
-                     inb[(u + PD - 1) % PD]);
-                // the loads stay issued here, PD - 1 chunks ahead of their use
-                __builtin_amdgcn_sched_barrier(0);
+            for (int j = 0; j < 4; ++j)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+                for (int t = 0; t < NT; ++t) {
+                    const float bv = j == 0 ? wb[t].x : j == 1 ? wb[t].y : j == 2 ? wb[t].z : wb[t].w;
 #pragma unroll
-                    for (int t = 0; t < NT; ++t) {
-                        const float4& wv = wb[u][t];
-                        const float bv = j == 0 ? wv.x : j == 1 ? wv.y : j == 2 ? wv.z : wv.w;
-                        // a run past the split's end, or a weight row past P, contributes 0
-                        // (zeroing the weight suffices: the x run read instead is finite data)
-                        const float bz = (inb[u] && wok[t]) ? bv : 0.0f;
-#pragma unroll
-                        for (int i = 0; i < MT; ++i) {
-                            const float4& xa = xb[u][i];
-                            const float av = j == 0 ? xa.x : j == 1 ? xa.y : j == 2 ? xa.z : xa.w;
-                            acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bz, acc[i][t], 0, 0, 0);
-                        }
+                    for (int i = 0; i < MT; ++i) {
+                        const float av = j == 0 ? xa[i].x : j == 1 ? xa[i].y : j == 2 ? xa[i].z : xa[i].w;
+                        acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc[i][t], 0, 0, 0);
                     }
-#pragma unroll
-                for (int i = 0; i < MT; ++i) {
-                    const float4& xa = xb[u][i];
-                    const float4& w0 = w0b[u];
-                    const float d4 = fmaf(xa.w, w0.w, fmaf(xa.z, w0.z, fmaf(xa.y, w0.y, xa.x * w0.x)));
-                    dacc[i] += inb[u] ? d4 : 0.0f;
                 }
-            }
+#pragma unroll
+            for (int i = 0; i < MT; ++i)
+                dacc[i] += fmaf(xa[i].w, w0.w, fmaf(xa[i].z, w0.z, fmaf(xa[i].y, w0.y, xa[i].x * w0.x)));
+        }
+        if (it + 1 < nt) {
+            __syncthreads();
+            store_tile();
+            __syncthreads();
         }
     }
-    // element v of tile (i, t): token m0 + 16i + 4g + v, output 1 + 16t + r
+    // element v of tile (i, t): token m0 + 16(MT·wave + i) + 4g + v, output 1 + 16t + r
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-            const int64_t m = m0 + 16 * i + 4 * g + v;
+            const int64_t m = m0 + 16 * (MT * wave + i) + 4 * g + v;
             if (m >= M) continue;
             float* pr = part + (int64_t(s) * M + m) * P;
 #pragma unroll
             for (int t = 0; t < NT; ++t)
                 if (1 + 16 * t + r < P) pr[1 + 16 * t + r] = acc[i][t][v];
         }
-    // output 0: the four lanes g of token m0 + 16i + r hold partial dot products
+    // output 0: the four lanes g of token m0 + 16(MT·wave + i) + r hold partial dot products
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
         float d = dacc[i];
         d += __shfl_xor(d, 16, 64);
         d += __shfl_xor(d, 32, 64);
-        const int64_t m = m0 + 16 * i + r;
+        const int64_t m = m0 + 16 * (MT * wave + i) + r;
         if (g == 0 && m < M) part[(int64_t(s) * M + m) * P] = d;
     }
 }
@@ -329,17 +334,17 @@ hipError_t launch_gemm_bf16_nt(const void* A, const void* W, float* C0, float* C
 }
 
 int64_t xproj_splits(int64_t M, int64_t D, int N) {
-    // about 1024 workgroups in all (one round of four waves per SIMD at the kernel's register
-    // use for N = 16), each split at least 64 steps of K
+    // about 768 workgroups in all (one round at three workgroups per CU, which the kernel's
+    // LDS tiles and registers allow for N = 16), each split at least 64 steps of K
     const int64_t tok = 64 * xproj_mt(N);        // tokens per workgroup
     const int64_t mb = (M + tok - 1) / tok;
-    int64_t S = (1024 + mb - 1) / mb;
+    int64_t S = (768 + mb - 1) / mb;
     if (S > D / 64) S = D / 64;
     return S < 1 ? 1 : S;
 }
 
-// split length: a multiple of the 16-step chunk
-int64_t xproj_split_len(int64_t D, int64_t S) { return ((D + S - 1) / S + 15) / 16 * 16; }
+// split length: whole 64-step LDS tiles
+int64_t xproj_split_len(int64_t D, int64_t S) { return ((D + S - 1) / S + kXK - 1) / kXK * kXK; }
 
 template <int NT, int MT>
 static hipError_t launch_xproj_t(const float* x, const float* Wx, float* part, int64_t M,
