@@ -162,9 +162,8 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
 // accumulator's element v is C[4·(l / 16) + v][l % 16]).  P = 1 + 2N: the 2N outputs of B and
 // C fill whole 16-wide tiles for N >= 8, and output 0 (Δraw) is a dot product per lane on the
 // vector ALUs instead of a third, mostly empty tile.  A wave owns MT tiles of 16 tokens and the
-// NT output tiles over one K split.  The workgroup stages 64- or 128-step tiles of its tokens'
-// x rows and of the weight rows in LDS, each global load covering 256- or 512-byte runs of a
-// row (reading x
+// NT output tiles over one K split.  The workgroup stages 64-step tiles of its tokens' x rows
+// and of the weight rows in LDS, each global load covering 256-byte runs of a row (reading x
 // straight into the MFMA operands instead scattered 64-byte pieces over 16 rows per load and
 // ran at a third of the DRAM rate), the next tile prefetched into registers.  Per 16-deep
 // chunk lane (r, g) = (l % 16, l / 16) reads one 16-byte run of each of its tokens' x rows,
@@ -173,20 +172,21 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
 // k = kc + 4g + j over g: the four MFMAs cover the chunk's 16 steps (the order of k inside a
 // chunk is permuted the same way for both operands), and output 0's four-term partials are
 // summed over the four lanes g of a token at the end.  Workgroup = 4 waves = 64·MT tokens.
-// grid = (ceil(M / (64·MT)), S), block = 256.  D % 4 == 0; split lengths are multiples of 128.
+// grid = (ceil(M / (64·MT)), S), block = 256.  D % 4 == 0; split lengths are multiples of 64.
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-// Shapes per N: one 16-token tile per wave (MT = 1); LDS tiles of KT = 128 steps (512-byte row
-// runs per global load) up to N = 16, 64 above (the wider output tiles need the registers and
-// LDS).  At N = 16, 128-step tiles with one token tile per wave measured 2.8 % faster on the
-// block step than 64-step tiles with two.
-static inline int xproj_kt(int N) { return N <= 16 ? 128 : 64; }
-}
+// 16-token tiles per wave (MT): each weight run loaded feeds MT MFMAs.  Two tiles measured
+// 1.7 % faster on the block step than one at N = 16, four no faster than two at half the
+// occupancy; above three output tiles (N > 16) one token tile keeps the registers in reach.
+static inline int xproj_mt(int N) { return N <= 16 ? 2 : 1; }
 
-template <int NT, int MT, int kXK>
+// K steps per LDS tile and the tiles' row stride (floats; 4 of padding)
+constexpr int kXK = 64;
+constexpr int kXRS = kXK + 4;
+
+template <int NT, int MT>
 __global__ __launch_bounds__(256) void xproj_mfma_kernel(
     const float* __restrict__ x, const float* __restrict__ Wx, float* __restrict__ part,
     int64_t M, int64_t D, int P, int64_t kc) {
-    constexpr int kXRS = kXK + 4;                // LDS row stride (floats; 4 of padding)
     constexpr int XT = 64 * MT;                  // tokens per workgroup
     constexpr int XQ = XT * (kXK / 4) / 256;     // x float4 pieces per thread per tile
     constexpr int PR = 1 + 16 * NT;              // weight rows staged (P <= PR)
@@ -202,20 +202,20 @@ __global__ __launch_bounds__(256) void xproj_mfma_kernel(
     const int64_t k1 = (k0 + kc < D) ? k0 + kc : D;
     const int64_t nt = (k1 > k0) ? (k1 - k0 + kXK - 1) / kXK : 0;
 
-    // staging: kXK / 4 consecutive threads cover one row's tile steps; steps at or past
+    // staging: 16 consecutive threads cover one row's 64 steps (256 bytes); steps at or past
     // k1 and rows past M or P load nothing and stage zeros
     float4 px[XQ], pw[WQ];
     auto load_tile = [&](int64_t kt) {
 #pragma unroll
         for (int q = 0; q < XQ; ++q) {
-            const int e = tid + 256 * q, row = e / (kXK / 4), c4 = e % (kXK / 4);
+            const int e = tid + 256 * q, row = e >> 4, c4 = e & 15;
             const int64_t k = kt + 4 * c4, m = m0 + row;
             px[q] = (m < M && k < k1) ? *reinterpret_cast<const float4*>(x + m * D + k)
                                       : make_float4(0.f, 0.f, 0.f, 0.f);
         }
 #pragma unroll
         for (int q = 0; q < WQ; ++q) {
-            const int e = tid + 256 * q, row = e / (kXK / 4), c4 = e % (kXK / 4);
+            const int e = tid + 256 * q, row = e >> 4, c4 = e & 15;
             const int64_t k = kt + 4 * c4;
             pw[q] = (row < P && k < k1) ? *reinterpret_cast<const float4*>(Wx + int64_t(row) * D + k)
                                         : make_float4(0.f, 0.f, 0.f, 0.f);
@@ -225,13 +225,12 @@ __global__ __launch_bounds__(256) void xproj_mfma_kernel(
 #pragma unroll
         for (int q = 0; q < XQ; ++q) {
             const int e = tid + 256 * q;
-            *reinterpret_cast<float4*>(xs + (e / (kXK / 4)) * kXRS + 4 * (e % (kXK / 4))) = px[q];
+            *reinterpret_cast<float4*>(xs + (e >> 4) * kXRS + 4 * (e & 15)) = px[q];
         }
 #pragma unroll
         for (int q = 0; q < WQ; ++q) {
             const int e = tid + 256 * q;
-            if (e < PR * (kXK / 4))
-                *reinterpret_cast<float4*>(ws + (e / (kXK / 4)) * kXRS + 4 * (e % (kXK / 4))) = pw[q];
+            if (e < PR * (kXK / 4)) *reinterpret_cast<float4*>(ws + (e >> 4) * kXRS + 4 * (e & 15)) = pw[q];
         }
     };
 
@@ -335,24 +334,23 @@ hipError_t launch_gemm_bf16_nt(const void* A, const void* W, float* C0, float* C
 }
 
 int64_t xproj_splits(int64_t M, int64_t D, int N) {
-    // about 768 workgroups, each split at least 64 steps of K.  The kernel waits on memory:
-    // at N = 16 this (1.5 rounds at two workgroups per CU) measured 3.6 % faster on the block
-    // step than exactly one round (512 workgroups, longer splits)
-    (void)N;
-    const int64_t mb = (M + 63) / 64;            // 64 tokens per workgroup
+    // about 768 workgroups in all (one round at three workgroups per CU, which the kernel's
+    // LDS tiles and registers allow for N = 16), each split at least 64 steps of K
+    const int64_t tok = 64 * xproj_mt(N);        // tokens per workgroup
+    const int64_t mb = (M + tok - 1) / tok;
     int64_t S = (768 + mb - 1) / mb;
     if (S > D / 64) S = D / 64;
     return S < 1 ? 1 : S;
 }
 
-// split length: whole 128-step LDS tiles (a multiple of either tile length)
-int64_t xproj_split_len(int64_t D, int64_t S) { return ((D + S - 1) / S + 127) / 128 * 128; }
+// split length: whole 64-step LDS tiles
+int64_t xproj_split_len(int64_t D, int64_t S) { return ((D + S - 1) / S + kXK - 1) / kXK * kXK; }
 
-template <int NT, int MT, int KT>
+template <int NT, int MT>
 static hipError_t launch_xproj_t(const float* x, const float* Wx, float* part, int64_t M,
                                  int64_t D, int P, int64_t S, int64_t kc, hipStream_t s) {
     const int64_t tok = 64 * MT;
-    hipLaunchKernelGGL((xproj_mfma_kernel<NT, MT, KT>), dim3(unsigned((M + tok - 1) / tok), unsigned(S)),
+    hipLaunchKernelGGL((xproj_mfma_kernel<NT, MT>), dim3(unsigned((M + tok - 1) / tok), unsigned(S)),
                        dim3(256), 0, s, x, Wx, part, M, D, P, kc);
     return hipGetLastError();
 }
@@ -363,11 +361,11 @@ hipError_t launch_xproj(const float* x, const float* Wx, float* part, float* dt,
     const int64_t kc = xproj_split_len(D, S);
     const int P = 1 + 2 * N;
     hipError_t e;
-    switch (N) {   // ceil(2N / 16) output tiles, one token tile per wave, tile steps xproj_kt(N)
-        case 1: case 2: case 4: case 8: e = launch_xproj_t<1, 1, 128>(x, Wx, part, M, D, P, S, kc, s); break;
-        case 16: e = launch_xproj_t<2, 1, 128>(x, Wx, part, M, D, P, S, kc, s); break;
-        case 32: e = launch_xproj_t<4, 1, 64>(x, Wx, part, M, D, P, S, kc, s); break;
-        case 64: e = launch_xproj_t<8, 1, 64>(x, Wx, part, M, D, P, S, kc, s); break;
+    switch (N) {   // ceil(2N / 16) output tiles; token tiles per wave as xproj_mt(N)
+        case 1: case 2: case 4: case 8: e = launch_xproj_t<1, 2>(x, Wx, part, M, D, P, S, kc, s); break;
+        case 16: e = launch_xproj_t<2, 2>(x, Wx, part, M, D, P, S, kc, s); break;
+        case 32: e = launch_xproj_t<4, 1>(x, Wx, part, M, D, P, S, kc, s); break;
+        case 64: e = launch_xproj_t<8, 1>(x, Wx, part, M, D, P, S, kc, s); break;
         default: return hipErrorInvalidValue;
     }
     if (e != hipSuccess) return e;
