@@ -825,8 +825,15 @@ __global__ __launch_bounds__(256) void bwd_reduce_bc_kernel(const float* __restr
     const int64_t LR = L * R;
     if (f >= LR) return;
     const float* p = part + int64_t(b) * NB * LR + f;
-    float acc = 0.0f;
-    for (int gi = 0; gi < NB; ++gi) acc += p[int64_t(gi) * LR];
+    // eight independent partial sums: eight loads in flight per thread instead of a chain
+    float a[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+    int gi = 0;
+    for (; gi + 8 <= NB; gi += 8) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) a[u] += p[int64_t(gi + u) * LR];
+    }
+    for (; gi < NB; ++gi) a[0] += p[int64_t(gi) * LR];
+    const float acc = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
     const int64_t t = f / R;
     const int v = int(f % R);
     const int n = v < Nr ? v : v - Nr;
@@ -862,12 +869,19 @@ __global__ __launch_bounds__(256) void bwd_reduce_params_kernel(
     const int KN = K * Nr;
     // thread tid accumulates entries e = tid + 256 i of the K*N block; Nr divides 256,
     // so every entry a thread touches has state n = tid % Nr
-    float acc = 0.0f;
+    // four independent partial sums (loads in flight instead of a chain); every entry a
+    // thread touches still has state n = tid % Nr
+    float ac[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     for (int b = 0; b < Bn; ++b) {
         const float* p = dA_part + (int64_t(b) * D + d) * KN;
-        for (int e = tid; e < KN; e += 256) acc += p[e];
+        int e = tid;
+        for (; e + 3 * 256 < KN; e += 4 * 256) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) ac[u] += p[e + 256 * u];
+        }
+        for (; e < KN; e += 256) ac[0] += p[e];
     }
-    red[tid] = acc;
+    red[tid] = (ac[0] + ac[1]) + (ac[2] + ac[3]);
     __syncthreads();
     if (tid < Nr) {
         float t = 0.0f;
