@@ -49,8 +49,8 @@ MEASURED_TRAFFIC = {
                 "sources_sha256": "0ea80df27192f7fcc1fc6ce8393157fa34700a8252c7f4bc8122077e84877175"},
     ("c2", 1): {"sources": FWD_SOURCES, "fetch_kib": 336294, "write_kib": 415446,
                 "sources_sha256": "0ea80df27192f7fcc1fc6ce8393157fa34700a8252c7f4bc8122077e84877175"},
-    ("d1", 0): {"sources": STEP_SOURCES, "fetch_kib": 45071, "write_kib": 87040,
-                "sources_sha256": "49ad91af5f7733a2fd6aafabaa0a4dba71ac4d8dc2779d982edfa22be3ed12b0"},
+    ("d1", 0): {"sources": STEP_SOURCES, "fetch_kib": 45068, "write_kib": 87040,
+                "sources_sha256": "fb704a2f5e74dc3510a1b8b4d9350cdbb9fe0159c47a80c5718f05dc8357e747"},
 }
 
 

@@ -28,6 +28,9 @@ __device__ __forceinline__ float group_sum(float v) {
 
 }  // namespace
 
+// four floats as a native vector (the nontemporal builtins take no struct types)
+typedef float ntf4 __attribute__((ext_vector_type(4)));
+
 // one thread per (batch row, channel, lane of the channel's group); grid = ceil(B·D·G / 256)
 template <typename Tin, int S, int G, bool kGate, bool kZoh>
 __global__ __launch_bounds__(256) void step_kernel(
@@ -48,8 +51,9 @@ __global__ __launch_bounds__(256) void step_kernel(
     const float dx = delta * xv;
     float h[S];
     const float* hp = h_in + ch * N + n0;
+    // the state streams through once per step: nontemporal load and store (cache hint only)
     if constexpr (S == 4) {
-        const float4 v = *reinterpret_cast<const float4*>(hp);
+        const ntf4 v = __builtin_nontemporal_load(reinterpret_cast<const ntf4*>(hp));
         h[0] = v.x; h[1] = v.y; h[2] = v.z; h[3] = v.w;
     } else {
 #pragma unroll
@@ -69,7 +73,7 @@ __global__ __launch_bounds__(256) void step_kernel(
     }
     float* ho = h_out + ch * N + n0;             // may be h_in: this lane read its states above
     if constexpr (S == 4) {
-        *reinterpret_cast<float4*>(ho) = make_float4(h[0], h[1], h[2], h[3]);
+        __builtin_nontemporal_store(ntf4{h[0], h[1], h[2], h[3]}, reinterpret_cast<ntf4*>(ho));
     } else {
 #pragma unroll
         for (int s = 0; s < S; ++s) ho[s] = h[s];
