@@ -73,6 +73,19 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def emit(out, value_key="value"):
+    """Print the one JSON line: adds the library's build identity (the SHA-256 of the sources
+    it was built from; load() has already refused any other) and, when the CPU oracle was
+    timed, the GPU/CPU throughput ratio inside cpu_baseline (vs_baseline stays null: the pages
+    publish no number for this metric)."""
+    import selective_state_space_34_amd as ss
+    out["build_id"] = ss.load().ss_build_id().decode()
+    cpu = out.get("cpu_baseline")
+    if cpu:
+        cpu["gpu_over_cpu"] = out[value_key] / cpu["value"]
+    emit(out)
+
+
 def min_bytes(w, s_in, dt_shared=False):
     """Algorithmic HBM bytes of one forward: read x, dt_raw (, z), B, C and parameters,
     write y (the (B,L,D,N) state and Ā/B̄ are never materialised).  A shared Δraw is
@@ -243,7 +256,7 @@ def run_decode(args, w, inp):
                      "launch_us": t_avg * 1e6, "traffic_algorithmic_bytes": mb},
         "cpu_baseline": cpu,
     }
-    print(json.dumps(out), flush=True)
+    emit(out)
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
@@ -358,7 +371,7 @@ def run_block(args, w, inp):
         "vendor_gemm_bf16_out_us": None if vendor is None else vendor * 1e6,
         "cpu_baseline": cpu,
     }
-    print(json.dumps(out), flush=True)
+    emit(out)
 
 
 def run_decode_graph(args, w, step_graphable):
@@ -410,7 +423,7 @@ def run_decode_graph(args, w, step_graphable):
                      "launch_us": t_step * 1e6, "traffic_algorithmic_bytes": mb},
         "cpu_baseline": None,
     }
-    print(json.dumps(out), flush=True)
+    emit(out)
 
 
 def calib_copy(args, dev):
@@ -630,7 +643,7 @@ def main():
     }
     if split:
         out["fwd_bwd_split"] = split
-    print(json.dumps(out), flush=True)
+    emit(out)
 
 
 if __name__ == "__main__":

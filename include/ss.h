@@ -236,6 +236,13 @@ int ss_last_hip_error(void);
 /* (SS_VERSION_MAJOR << 16) | SS_VERSION_MINOR */
 int ss_version(void);
 
+/* Identity of the sources this library was built from: a NUL-terminated string of 64
+ * lowercase hex digits, the SHA-256 over every file of the kernel source directory (name
+ * and bytes, in name order), this header and the code-generation flags, fixed at compile
+ * time.  A loader compares it with the same digest of the sources it expects, so results
+ * are never taken from a library built from other sources.  Static storage; never NULL. */
+const char* ss_build_id(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -18,7 +18,7 @@ everything else is float32.
 import ctypes
 import os
 
-from ._build import LIB, build, stale  # noqa: F401
+from ._build import LIB, build, stale, tree_id  # noqa: F401
 
 SS_F32, SS_BF16 = 0, 1
 SS_PLAN_AUTO, SS_PLAN_SINGLE, SS_PLAN_CHUNKED = 0, 1, 2
@@ -32,7 +32,7 @@ ERRORS = {0: "SS_OK", -1: "SS_ERR_NULL", -2: "SS_ERR_DIMS", -3: "SS_ERR_DTYPE", 
 
 EXPORTS = ("ss_fwd", "ss_bwd", "ss_step", "ss_fwd_workspace_size", "ss_bwd_workspace_size",
            "ss_block_fwd", "ss_block_fwd_workspace_size", "ss_in_proj", "ss_strerror",
-           "ss_last_hip_error", "ss_version")
+           "ss_last_hip_error", "ss_version", "ss_build_id")
 
 
 class ss_dims(ctypes.Structure):
@@ -62,14 +62,22 @@ class SSError(RuntimeError):
 _lib = None
 
 
-def load(path: str = LIB):
-    """Load libss.so (built in-tree by ``build()``).  Raises if it is missing."""
+def load(path: str = LIB, expect: str = None):
+    """Load libss.so (built in-tree by ``build()``).  Raises if it is missing, or if its build
+    identity (ss_build_id) differs from ``expect`` (default: the digest of the sources in this
+    tree, ``tree_id()``): a library built from other sources is never used."""
     global _lib
-    if _lib is not None:
+    if _lib is not None and expect is None and path == LIB:
         return _lib
     if not os.path.exists(path):
         raise RuntimeError(f"HIP library not built: {path} (run selective_state_space_34_amd.build())")
     lib = ctypes.CDLL(path)
+    lib.ss_build_id.restype = ctypes.c_char_p
+    got = lib.ss_build_id().decode()
+    want = tree_id() if expect is None else expect
+    if got != want:
+        raise RuntimeError(f"{path} was built from other sources (library id {got[:16]}..., "
+                           f"expected {want[:16]}...): rebuild it with build()")
     P = ctypes.c_void_p
     D = ctypes.POINTER(ss_dims)
     lib.ss_fwd.argtypes = [D] + [P] * 12 + [P, ctypes.c_size_t, P]
@@ -92,7 +100,8 @@ def load(path: str = LIB):
     lib.ss_strerror.restype = ctypes.c_char_p
     lib.ss_last_hip_error.restype = ctypes.c_int
     lib.ss_version.restype = ctypes.c_int
-    _lib = lib
+    if expect is None and path == LIB:
+        _lib = lib
     return lib
 
 

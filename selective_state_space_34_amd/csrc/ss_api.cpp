@@ -13,6 +13,10 @@
 #include "ss_kernels.h"
 #include "ss_plan.h"
 
+#ifndef SS_BUILD_ID
+#error "SS_BUILD_ID (the SHA-256 of the sources, 64 hex digits) must be defined by the build"
+#endif
+
 namespace {
 
 thread_local int g_last_hip_error = 0;
@@ -80,6 +84,8 @@ extern "C" {
 
 int ss_version(void) { return (SS_VERSION_MAJOR << 16) | SS_VERSION_MINOR; }
 
+const char* ss_build_id(void) { return SS_BUILD_ID; }
+
 int ss_last_hip_error(void) { return g_last_hip_error; }
 
 const char* ss_strerror(int code) {
@@ -129,8 +135,11 @@ int ss_fwd(const ss_dims* dims, const void* x, const void* dt_raw, const float* 
     if ((z && !aligned16(z)) || (h0 && !aligned16(h0)) || (h_final && !aligned16(h_final)) ||
         (h_ckpt && !aligned16(h_ckpt)))
         return SS_ERR_ALIGN;
-    // the group kernel checkpoints at its 16-step sweep starts, which need chunk % 16 == 0
-    if (h_ckpt && p.group && p.chunked && p.chunk % ss::kCkptSteps != 0) return SS_ERR_UNSUPPORTED;
+    // the group kernel checkpoints at its 16-step sweep starts, which are multiples of 16 when
+    // every chunk starts on one: chunk % 16 == 0, or a single chunk (its sweeps start at 0, its
+    // per-step tail checkpoints at t % 16 == 0)
+    if (h_ckpt && p.group && p.chunked && p.K > 1 && p.chunk % ss::kCkptSteps != 0)
+        return SS_ERR_UNSUPPORTED;
     if (p.ws_total > 0 && (!workspace || workspace_bytes < p.ws_total)) return SS_ERR_WORKSPACE;
     if (workspace && !aligned16(workspace)) return SS_ERR_ALIGN;
 

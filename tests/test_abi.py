@@ -36,6 +36,33 @@ def test_exports_match_header(lib):
         assert hasattr(lib, n), f"missing export {n}"
 
 
+def test_build_id_matches_tree(lib):
+    ident = lib.ss_build_id()
+    assert isinstance(ident, bytes) and re.fullmatch(rb"[0-9a-f]{64}", ident), ident
+    assert ident.decode() == _build.tree_id()
+    assert not _build.stale()
+
+
+def test_stale_library_refused(lib, tmp_path):
+    """A library whose build identity is not the digest of the sources under test is refused:
+    here the digest of a copy of the tree with one kernel source changed by one byte."""
+    import shutil
+    csrc = tmp_path / "csrc"
+    inc = tmp_path / "include"
+    shutil.copytree(_build.CSRC, csrc)
+    shutil.copytree(_build.INCLUDE, inc)
+    src = csrc / "ss_fwdg.hip"
+    src.write_bytes(src.read_bytes() + b"\n")
+    other = _build.tree_id(str(csrc), str(inc))
+    assert other != _build.tree_id()
+    copy = tmp_path / "libss_copy.so"
+    shutil.copyfile(_build.LIB, copy)
+    with pytest.raises(RuntimeError, match="built from other sources"):
+        ss.load(str(copy), expect=other)
+    # the same library with the tree's own digest loads
+    assert ss.load(str(copy), expect=_build.tree_id()) is not None
+
+
 def test_version_and_strerror(lib):
     assert lib.ss_version() == (0 << 16) | 7
     for code in ss.ERRORS:
@@ -96,6 +123,8 @@ def test_fwd_validation(lib):
     assert _fwd(lib, ss.make_dims(2, 80, 32, 16, ss.SS_F32, ss.SS_PLAN_CHUNKED, 40)) == -7
     lane40 = ss.make_dims(2, 80, 32, 16, ss.SS_F32, ss.SS_PLAN_CHUNKED, 40, ss.SS_LAYOUT_LANE)
     assert _fwd(lib, lane40) == -5
+    # ... unless there is a single chunk (chunk 104 = L): then the call reaches the workspace
+    assert _fwd(lib, ss.make_dims(1, 104, 20, 16, ss.SS_F32, ss.SS_PLAN_CHUNKED, 0)) == -5
     # alignment
     for i in range(12):
         p = [ctypes.c_void_p(FAKE)] * 12

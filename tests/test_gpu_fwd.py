@@ -210,6 +210,7 @@ CKPT_CASES = [
     (1, 333, 20, 16, "bf16", True, True, 2, 40, 2),     # one lane per channel, chunk 40
     (3, 64, 9, 2, "f32", True, False, 0, 0, 0),         # N = 2: one-lane kernel
     (1, 64, 24576, 16, "bf16", True, True, 0, 0, 0),    # mixed four/eight-lane launch
+    (1, 104, 20, 16, "f32", True, True, 2, 0, 0),       # chunked, one chunk of 104 steps
 ]
 
 
