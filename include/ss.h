@@ -146,8 +146,9 @@ int ss_bwd_workspace_size(const ss_dims* dims, size_t* bytes);
  *   h_final : NULL = final state not written.
  *   h_ckpt  : NULL = not written; else the state entering steps 0, 16, 32, ... (entry i is
  *             the state before step 16·i; entry 0 is h0 or 0): the checkpoints ss_bwd can
- *             take instead of recomputing chunk start states.  With a user-chosen chunk
- *             that is not a multiple of 16 on the four-lane layout: SS_ERR_UNSUPPORTED.
+ *             take instead of recomputing chunk start states.  A chunked plan of two or
+ *             more chunks on the four- or eight-lane layout whose chunk is no multiple of 16
+ *             (a user-chosen chunk) returns SS_ERR_UNSUPPORTED.
  *   workspace / workspace_bytes : at least ss_fwd_workspace_size bytes of device memory. */
 int ss_fwd(const ss_dims* dims,
            const void* x, const void* dt_raw, const float* dt_bias, const float* A,
