@@ -131,7 +131,8 @@ enum {
     SS_ERR_ALIGN = -4,       /* a base pointer is not 16-byte aligned */
     SS_ERR_WORKSPACE = -5,   /* workspace NULL while needed, or workspace_bytes too small */
     SS_ERR_HIP = -6,         /* a HIP call failed; see ss_last_hip_error() */
-    SS_ERR_UNSUPPORTED = -7  /* valid arguments this build does not handle */
+    SS_ERR_UNSUPPORTED = -7, /* valid arguments this build does not handle */
+    SS_ERR_SCRATCH = -8      /* ss_fwd_noalloc: the plan needs more than its static scratch */
 };
 
 /* Workspace bytes ss_fwd / ss_bwd need for these dims (written to *bytes).
@@ -208,6 +209,26 @@ int ss_block_fwd(const ss_block_dims* dims, const void* u, const void* W_in, con
                  const float* dt_bias, const float* A, const float* Dskip, const float* h0,
                  float* y, float* h_final, float* x, float* z, float* dt, float* Bm, float* Cm,
                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Forward without a workspace argument, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same computation, arguments (minus workspace / workspace_bytes), kernels and results as
+ * ss_fwd.  The scratch the chunked and one-lane plans need (ss_fwd_workspace_size bytes) comes
+ * from a static device array of SS_NOALLOC_SCRATCH_MIB MiB inside the library, one per GPU,
+ * held from the first use on that GPU until the process ends; dims whose workspace size
+ * exceeds it return SS_ERR_SCRATCH before anything happens.  The call allocates nothing and
+ * calls no allocating routine.  The first call on a GPU that needs scratch looks up the
+ * array's device address once (hipGetSymbolAddress, the stream's device made current for it,
+ * then restored); a HIP failure there returns SS_ERR_HIP.
+ * Every call on one GPU uses the same array: calls that overlap on one GPU (concurrent
+ * streams, or several host threads) race on it and give undefined results; calls ordered on
+ * one stream are safe.  Nothing in the array needs to start at zero (each call writes every
+ * value it reads), so the previous call's contents do no harm. */
+#define SS_NOALLOC_SCRATCH_MIB 32
+int ss_fwd_noalloc(const ss_dims* dims,
+                   const void* x, const void* dt_raw, const float* dt_bias, const float* A,
+                   const void* Bm, const void* Cm, const float* Dskip, const void* z,
+                   const float* h0, float* y, float* h_final, float* h_ckpt, hipStream_t stream);
 
 /* Single-token (decode) step: the recurrence carried one token further for every (batch
  * row, channel), as in recurrent inference (note "상태공간 모델(SSM)과 Mamba 아키텍처", §2):

@@ -28,11 +28,11 @@ SS_ORDER_BDL, SS_ORDER_BLD = 0, 1
 SS_DT_FULL, SS_DT_SHARED = 0, 1
 
 ERRORS = {0: "SS_OK", -1: "SS_ERR_NULL", -2: "SS_ERR_DIMS", -3: "SS_ERR_DTYPE", -4: "SS_ERR_ALIGN",
-          -5: "SS_ERR_WORKSPACE", -6: "SS_ERR_HIP", -7: "SS_ERR_UNSUPPORTED"}
+          -5: "SS_ERR_WORKSPACE", -6: "SS_ERR_HIP", -7: "SS_ERR_UNSUPPORTED", -8: "SS_ERR_SCRATCH"}
 
 EXPORTS = ("ss_fwd", "ss_bwd", "ss_step", "ss_fwd_workspace_size", "ss_bwd_workspace_size",
            "ss_block_fwd", "ss_block_fwd_workspace_size", "ss_in_proj", "ss_strerror",
-           "ss_last_hip_error", "ss_version", "ss_build_id")
+           "ss_last_hip_error", "ss_version", "ss_build_id", "ss_fwd_noalloc")
 
 
 class ss_dims(ctypes.Structure):
@@ -84,6 +84,8 @@ def load(path: str = LIB, expect: str = None):
     lib.ss_fwd.restype = ctypes.c_int
     lib.ss_bwd.argtypes = [D] + [P] * 9 + [P, P, P] + [P] * 9 + [P, ctypes.c_size_t, P]
     lib.ss_bwd.restype = ctypes.c_int
+    lib.ss_fwd_noalloc.argtypes = [D] + [P] * 12 + [P]
+    lib.ss_fwd_noalloc.restype = ctypes.c_int
     lib.ss_step.argtypes = [D] + [P] * 12
     lib.ss_step.restype = ctypes.c_int
     for f in ("ss_fwd_workspace_size", "ss_bwd_workspace_size"):
@@ -240,6 +242,33 @@ def ss_fwd(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, z=None, h0=None, *, return_fina
     if h_ckpt is not None:
         out += (h_ckpt,)
     return out if len(out) > 1 else y
+
+
+def ss_fwd_noalloc(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, y, z=None, h0=None, *, h_final=None,
+                   h_ckpt=None, plan=SS_PLAN_AUTO, chunk=0, layout=SS_LAYOUT_AUTO,
+                   disc=SS_DISC_EULER, order=SS_ORDER_BDL, stream=None):
+    """ss_fwd without a workspace: the library's static scratch (SS_NOALLOC_SCRATCH_MIB MiB per
+    GPU) serves the chunked and one-lane plans, and nothing is allocated, here or in the
+    library.  The caller passes every output (y, and h_final / h_ckpt if wanted).  Calls that
+    overlap on one GPU share that scratch and race; calls ordered on one stream do not."""
+    import torch
+    lib = load()
+    _check_inputs(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, z, h0, order)
+    dims = _dims_of(x, A, dt_raw, plan, chunk, layout, disc, order)
+    Bn, D, L = _seq_shape(x, order)
+    N = A.shape[1]
+    if y is None:
+        raise ValueError("y is required")
+    _check(y, "y", _seq(Bn, D, L, order), torch.float32, x.device)
+    _check(h_final, "h_final", (Bn, D, N), torch.float32, x.device)
+    nck = (L + CKPT_STEPS - 1) // CKPT_STEPS
+    _check(h_ckpt, "h_ckpt", (Bn, D, nck, N), torch.float32, x.device)
+    rc = lib.ss_fwd_noalloc(ctypes.byref(dims), _ptr(x), _ptr(dt_raw), _ptr(dt_bias), _ptr(A),
+                            _ptr(Bm), _ptr(Cm), _ptr(Dskip), _ptr(z), _ptr(h0), _ptr(y),
+                            _ptr(h_final), _ptr(h_ckpt), _stream(stream))
+    if rc != 0:
+        raise SSError(rc, lib)
+    return y
 
 
 def ss_bwd(x, dt_raw, dt_bias, A, Bm, Cm, Dskip, dy, z=None, h0=None, dh_final=None, *,

@@ -10,8 +10,17 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "ss_kernels.h"
 #include "ss_plan.h"
+
+// Scratch of ss_fwd_noalloc: a fixed device array instead of a caller's workspace.  Each GPU
+// the library runs on holds its own copy (allocated with the code object, kept until the
+// process ends).  In host code `scratch` names a host-side stand-in, never the device memory:
+// every host use goes through the address hipGetSymbolAddress returns for the device.
+constexpr size_t kScratchBytes = size_t(SS_NOALLOC_SCRATCH_MIB) << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
 
 #ifndef SS_BUILD_ID
 #error "SS_BUILD_ID (the SHA-256 of the sources, 64 hex digits) must be defined by the build"
@@ -27,6 +36,37 @@ int hip_fail(hipError_t e) {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the device that runs `stream`, looked up once per device with
+// that device current (the caller's current device is restored).
+int scratch_for_stream(hipStream_t stream, void** out) {
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return hip_fail(e);
+    int dev = cur;
+    if (stream) {
+        e = hipStreamGetDevice(stream, &dev);
+        if (e != hipSuccess) return hip_fail(e);
+    }
+    if (dev < 0 || dev >= kMaxDevices) return SS_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return hip_fail(e);
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        const hipError_t r = (dev != cur) ? hipSetDevice(cur) : hipSuccess;
+        if (e != hipSuccess) return hip_fail(e);
+        if (r != hipSuccess) return hip_fail(r);
+        if (!p) return hip_fail(hipErrorInvalidSymbol);
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return SS_OK;
+}
 
 // Rows of a [B, D, L] (channel-major) or [B, L, D] (token-major) tensor: element (b, d, t) at
 // b·sb + d·sd + t·ts.
@@ -98,6 +138,7 @@ const char* ss_strerror(int code) {
         case SS_ERR_WORKSPACE: return "workspace missing or too small";
         case SS_ERR_HIP: return "a HIP runtime call failed";
         case SS_ERR_UNSUPPORTED: return "unsupported by this build";
+        case SS_ERR_SCRATCH: return "the call needs more scratch than ss_fwd_noalloc's static buffer holds";
         default: return "unknown error code";
     }
 }
@@ -120,12 +161,16 @@ int ss_bwd_workspace_size(const ss_dims* dims, size_t* bytes) {
     return SS_OK;
 }
 
-int ss_fwd(const ss_dims* dims, const void* x, const void* dt_raw, const float* dt_bias,
-           const float* A, const void* Bm, const void* Cm, const float* Dskip, const void* z,
-           const float* h0, float* y, float* h_final, float* h_ckpt, void* workspace,
-           size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks of the forward, in order; nothing is launched.  Fills the plan.
+int fwd_validate(const ss_dims* dims, const void* x, const void* dt_raw, const float* dt_bias,
+                 const float* A, const void* Bm, const void* Cm, const float* Dskip, const void* z,
+                 const float* h0, float* y, float* h_final, float* h_ckpt, ss::Plan* plan) {
     if (!dims) return SS_ERR_NULL;
-    ss::Plan p;
+    ss::Plan& p = *plan;
     int rc = ss::make_plan(*dims, ss::kPlanFwd, &p);
     if (rc != SS_OK) return rc;
     if (!x || !dt_raw || !dt_bias || !A || !Bm || !Cm || !Dskip || !y) return SS_ERR_NULL;
@@ -140,10 +185,14 @@ int ss_fwd(const ss_dims* dims, const void* x, const void* dt_raw, const float* 
     // per-step tail checkpoints at t % 16 == 0)
     if (h_ckpt && p.group && p.chunked && p.K > 1 && p.chunk % ss::kCkptSteps != 0)
         return SS_ERR_UNSUPPORTED;
-    if (p.ws_total > 0 && (!workspace || workspace_bytes < p.ws_total)) return SS_ERR_WORKSPACE;
-    if (workspace && !aligned16(workspace)) return SS_ERR_ALIGN;
+    return SS_OK;
+}
 
-    char* ws = static_cast<char*>(workspace);
+// The forward's launches on a validated plan; ws holds at least p.ws_total bytes.
+int fwd_launch(const ss::Plan& p, const void* x, const void* dt_raw, const float* dt_bias,
+               const float* A, const void* Bm, const void* Cm, const float* Dskip, const void* z,
+               const float* h0, float* y, float* h_final, float* h_ckpt, char* ws,
+               hipStream_t stream) {
     const int bf16 = p.in_dtype == SS_BF16;
     hipError_t e = hipSuccess;
     // the group kernel tiles B/C from the inputs; the one-lane kernel reads a [B, L, 2N] copy
@@ -188,6 +237,44 @@ int ss_fwd(const ss_dims* dims, const void* x, const void* dt_raw, const float* 
     e = p.group ? ss::launch_scang(bf16, int(p.N), p.group, s, stream) : ss::launch_scan(bf16, int(p.N), s, stream);
     if (e != hipSuccess) return hip_fail(e);
     return SS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ss_fwd(const ss_dims* dims, const void* x, const void* dt_raw, const float* dt_bias,
+           const float* A, const void* Bm, const void* Cm, const float* Dskip, const void* z,
+           const float* h0, float* y, float* h_final, float* h_ckpt, void* workspace,
+           size_t workspace_bytes, hipStream_t stream) {
+    ss::Plan p;
+    const int rc = fwd_validate(dims, x, dt_raw, dt_bias, A, Bm, Cm, Dskip, z, h0, y, h_final,
+                                h_ckpt, &p);
+    if (rc != SS_OK) return rc;
+    if (p.ws_total > 0 && (!workspace || workspace_bytes < p.ws_total)) return SS_ERR_WORKSPACE;
+    if (workspace && !aligned16(workspace)) return SS_ERR_ALIGN;
+    return fwd_launch(p, x, dt_raw, dt_bias, A, Bm, Cm, Dskip, z, h0, y, h_final, h_ckpt,
+                      static_cast<char*>(workspace), stream);
+}
+
+int ss_fwd_noalloc(const ss_dims* dims, const void* x, const void* dt_raw, const float* dt_bias,
+                   const float* A, const void* Bm, const void* Cm, const float* Dskip,
+                   const void* z, const float* h0, float* y, float* h_final, float* h_ckpt,
+                   hipStream_t stream) {
+    ss::Plan p;
+    int rc = fwd_validate(dims, x, dt_raw, dt_bias, A, Bm, Cm, Dskip, z, h0, y, h_final, h_ckpt,
+                          &p);
+    if (rc != SS_OK) return rc;
+    if (p.ws_total > kScratchBytes) return SS_ERR_SCRATCH;
+    // nothing needs to start at zero: every scratch value the kernels read was written earlier
+    // in the same call (the aggregates, then the carry's start states)
+    void* ws = nullptr;
+    if (p.ws_total > 0) {
+        rc = scratch_for_stream(stream, &ws);
+        if (rc != SS_OK) return rc;
+    }
+    return fwd_launch(p, x, dt_raw, dt_bias, A, Bm, Cm, Dskip, z, h0, y, h_final, h_ckpt,
+                      static_cast<char*>(ws), stream);
 }
 
 int ss_step(const ss_dims* dims, const void* x, const void* dt_raw, const float* dt_bias,

@@ -63,6 +63,29 @@ def test_stale_library_refused(lib, tmp_path):
     assert ss.load(str(copy), expect=_build.tree_id()) is not None
 
 
+def test_fwd_noalloc_validation(lib):
+    """ss_fwd_noalloc checks its arguments like ss_fwd and refuses a plan whose workspace
+    exceeds its static scratch, before any HIP call."""
+    def call(dims, ptrs=None):
+        p = [ctypes.c_void_p(FAKE)] * 12 if ptrs is None else ptrs
+        return lib.ss_fwd_noalloc(None if dims is None else ctypes.byref(dims), *p, None)
+    assert call(None) == -1
+    assert call(ss.make_dims(0, 64, 32, 16)) == -2
+    assert call(ss.make_dims(2, 64, 32, 16, plan=9)) == -3
+    big = ss.make_dims(1, 65536, 256, 16, ss.SS_BF16, ss.SS_PLAN_CHUNKED, 32)
+    n = ctypes.c_size_t(0)
+    assert lib.ss_fwd_workspace_size(ctypes.byref(big), ctypes.byref(n)) == 0
+    assert n.value > (32 << 20)
+    assert call(big) == -8
+    p = [ctypes.c_void_p(FAKE)] * 12
+    p[0] = None
+    assert call(big, p) == -1
+    p = [ctypes.c_void_p(FAKE)] * 12
+    p[3] = ctypes.c_void_p(FAKE + 4)
+    assert call(big, p) == -4
+    assert b"scratch" in lib.ss_strerror(-8)
+
+
 def test_version_and_strerror(lib):
     assert lib.ss_version() == (0 << 16) | 7
     for code in ss.ERRORS:
