@@ -32,6 +32,8 @@
 //     gate and stores kH outputs.
 // All global loads of the next tile (x, dt_raw, z, B/C) are issued before the current
 // tile's arithmetic.  The state never leaves VGPRs (§3.2).
+#include <type_traits>
+
 #include "ss_device.h"
 #include "ss_kernels.h"
 
@@ -226,7 +228,7 @@ struct GroupLds {
 // below d_hi), chunk k.  lds: GroupLds<G, S>::FLOATS floats, 16-byte aligned.  Requires
 // L % 8 == 0 and chunk % 32 == 0 (or K == 1) for the tiled part; the last < 32 steps of a
 // chunk run a per-step tail.
-template <typename Tin, int G, int S, bool kGate, bool kAgg, bool kZoh, bool kTok>
+template <typename Tin, int G, int S, bool kGate, bool kAgg, bool kZoh, bool kTok, bool kMayPow = true>
 __device__ __forceinline__ void scang_body(
     float* __restrict__ lds, int64_t blk, int k, int b, int64_t d_lo, int64_t d_hi,
     const Tin* __restrict__ x, const Tin* __restrict__ dt_raw, const Tin* __restrict__ z,
@@ -268,12 +270,20 @@ __device__ __forceinline__ void scang_body(
     const int n0 = l * S;
 
     float A2[S], iA[S], h[S];
+    bool pow_lane = true;
 #pragma unroll
     for (int s = 0; s < S; ++s) {
         const float a = A[d * N + n0 + s];
         A2[s] = a * kLog2e;
         if (kZoh) iA[s] = 1.0f / a;
+        pow_lane = pow_lane && (a == -float(n0 + s + 1));
     }
+    // A[d, n] = -(n + 1) for every state of every channel of the wave (the S4D-real A): then
+    // Ā_n = r^(n+1) with r = e^{-δ}, so a lane forms its first state's Ā = 2^(δ·A_{n0}·log2 e)
+    // with one exponential and the next S - 1 by multiplying with r, which the lane that
+    // prepared the step broadcasts with (δ, δ·x) (four lanes, first-order hold only).  The
+    // chain carries at most S ulp of relative error.  The vote is uniform over the wave.
+    const bool pow_path = kDpp && kMayPow && __builtin_amdgcn_readfirstlane(int(__all(pow_lane))) != 0;
     const int64_t hidx = ((int64_t(b) * D + d) * K + k) * N + n0;
 #pragma unroll
     for (int s = 0; s < S; ++s) h[s] = h_init ? h_init[hidx + s] : 0.0f;
@@ -403,184 +413,212 @@ __device__ __forceinline__ void scang_body(
     float* dd_row = wa + c * kDS;                 // (δ, δ·x) of this lane's channel
     float* mine = wa + lane * kPS;                // this lane's partial readouts
 
-    for (int64_t it = 0; it < n_tiles; ++it) {
-        const int64_t t0 = t_begin + it * kTile;
-        float* buf = lds + (it & 1) * TILE_F;
+    // the tile loop in two copies, the power path and the general one, chosen once per wave
+    // (separate copies keep either one's registers to what it needs alone)
+    auto run_tiles = [&](auto pw) {
+        constexpr bool kPow = decltype(pw)::value && kDpp;
+        for (int64_t it = 0; it < n_tiles; ++it) {
+            const int64_t t0 = t_begin + it * kTile;
+            float* buf = lds + (it & 1) * TILE_F;
 #pragma unroll
-        for (int p = 0; p < BC_PASSES; ++p) {
-            const int e = tid + p * kThreads;
-            if (BC_UNITS % kThreads == 0 || e < BC_UNITS) {
-                if constexpr (kTok) {
-                    const int q = e % NQ, tt = (e / NQ) % kTile, m = e / (NQ * kTile);
-                    *reinterpret_cast<float4*>(buf + tt * R + m * N + 4 * q) =
-                        make_float4(bc_next[p].get(0), bc_next[p].get(1), bc_next[p].get(2),
-                                    bc_next[p].get(3));
-                } else {
-                    const int n = e % N, q = (e / N) % (kTile / 4), m = e / (N * (kTile / 4));
-                    float* dst = buf + 4 * q * R + m * N + n;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) dst[i * R] = bc_next[p].get(i);
-                }
-            }
-        }
-        float xv[2][kH], dv[2][kH], zv[2][kH];
-        if constexpr (kTok) {
-            // the wave's pieces into its own area as rows, then each lane's kH steps of its
-            // channel from there (the area is free: the last sweep's gathers are done)
-            char* st = reinterpret_cast<char*>(wa);
-#pragma unroll
-            for (int j = 0; j < TS::PL; ++j) {
-                const int q = lane + 64 * j;
-                if (TS::PIECES % 64 == 0 || q < TS::PIECES) {
-                    const int row = q / TS::PPR, pc = q % TS::PPR;
-                    char* dst = st + row * TS::RSB + pc * 16;
-                    *reinterpret_cast<uint4*>(dst) = px[j];
-                    if (dt_full) *reinterpret_cast<uint4*>(dst + TS::TBYTES) = pd[j];
-                    if (kGate && !kAgg) *reinterpret_cast<uint4*>(dst + 2 * TS::TBYTES) = pz[j];
-                }
-            }
-            wave_sync();
-            const char* src = st + c * TS::ELEM;
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-                for (int i = 0; i < kH; ++i) {
-                    const char* e = src + (kHalf * hh + kH * l + i) * TS::RSB;
-                    if constexpr (sizeof(Tin) == 2) {
-                        xv[hh][i] = __uint_as_float(uint32_t(*reinterpret_cast<const uint16_t*>(e)) << 16);
-                        if (dt_full)
-                            dv[hh][i] = __uint_as_float(
-                                uint32_t(*reinterpret_cast<const uint16_t*>(e + TS::TBYTES)) << 16);
-                        if (kGate && !kAgg)
-                            zv[hh][i] = __uint_as_float(
-                                uint32_t(*reinterpret_cast<const uint16_t*>(e + 2 * TS::TBYTES)) << 16);
+            for (int p = 0; p < BC_PASSES; ++p) {
+                const int e = tid + p * kThreads;
+                if (BC_UNITS % kThreads == 0 || e < BC_UNITS) {
+                    if constexpr (kTok) {
+                        const int q = e % NQ, tt = (e / NQ) % kTile, m = e / (NQ * kTile);
+                        *reinterpret_cast<float4*>(buf + tt * R + m * N + 4 * q) =
+                            make_float4(bc_next[p].get(0), bc_next[p].get(1), bc_next[p].get(2),
+                                        bc_next[p].get(3));
                     } else {
-                        xv[hh][i] = *reinterpret_cast<const float*>(e);
-                        if (dt_full) dv[hh][i] = *reinterpret_cast<const float*>(e + TS::TBYTES);
-                        if (kGate && !kAgg) zv[hh][i] = *reinterpret_cast<const float*>(e + 2 * TS::TBYTES);
+                        const int n = e % N, q = (e / N) % (kTile / 4), m = e / (N * (kTile / 4));
+                        float* dst = buf + 4 * q * R + m * N + n;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) dst[i * R] = bc_next[p].get(i);
                     }
                 }
-                if (!dt_full) {
-                    const uint32_t* w = reinterpret_cast<const uint32_t*>(pd);
+            }
+            float xv[2][kH], dv[2][kH], zv[2][kH];
+            if constexpr (kTok) {
+                // the wave's pieces into its own area as rows, then each lane's kH steps of its
+                // channel from there (the area is free: the last sweep's gathers are done)
+                char* st = reinterpret_cast<char*>(wa);
+#pragma unroll
+                for (int j = 0; j < TS::PL; ++j) {
+                    const int q = lane + 64 * j;
+                    if (TS::PIECES % 64 == 0 || q < TS::PIECES) {
+                        const int row = q / TS::PPR, pc = q % TS::PPR;
+                        char* dst = st + row * TS::RSB + pc * 16;
+                        *reinterpret_cast<uint4*>(dst) = px[j];
+                        if (dt_full) *reinterpret_cast<uint4*>(dst + TS::TBYTES) = pd[j];
+                        if (kGate && !kAgg) *reinterpret_cast<uint4*>(dst + 2 * TS::TBYTES) = pz[j];
+                    }
+                }
+                wave_sync();
+                const char* src = st + c * TS::ELEM;
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
                     for (int i = 0; i < kH; ++i) {
-                        const int e = hh * kH + i;
-                        dv[hh][i] = (sizeof(Tin) == 2)
-                                        ? __uint_as_float((e & 1) ? (w[e >> 1] & 0xffff0000u) : (w[e >> 1] << 16))
-                                        : __uint_as_float(w[e]);
+                        const char* e = src + (kHalf * hh + kH * l + i) * TS::RSB;
+                        if constexpr (sizeof(Tin) == 2) {
+                            xv[hh][i] = __uint_as_float(uint32_t(*reinterpret_cast<const uint16_t*>(e)) << 16);
+                            if (dt_full)
+                                dv[hh][i] = __uint_as_float(
+                                    uint32_t(*reinterpret_cast<const uint16_t*>(e + TS::TBYTES)) << 16);
+                            if (kGate && !kAgg)
+                                zv[hh][i] = __uint_as_float(
+                                    uint32_t(*reinterpret_cast<const uint16_t*>(e + 2 * TS::TBYTES)) << 16);
+                        } else {
+                            xv[hh][i] = *reinterpret_cast<const float*>(e);
+                            if (dt_full) dv[hh][i] = *reinterpret_cast<const float*>(e + TS::TBYTES);
+                            if (kGate && !kAgg) zv[hh][i] = *reinterpret_cast<const float*>(e + 2 * TS::TBYTES);
+                        }
+                    }
+                    if (!dt_full) {
+                        const uint32_t* w = reinterpret_cast<const uint32_t*>(pd);
+#pragma unroll
+                        for (int i = 0; i < kH; ++i) {
+                            const int e = hh * kH + i;
+                            dv[hh][i] = (sizeof(Tin) == 2)
+                                            ? __uint_as_float((e & 1) ? (w[e >> 1] & 0xffff0000u) : (w[e >> 1] << 16))
+                                            : __uint_as_float(w[e]);
+                        }
                     }
                 }
+            } else {
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    xn[hh].decode(xv[hh]);
+                    dn[hh].decode(dv[hh]);
+                    if (kGate && !kAgg) zn[hh].decode(zv[hh]);
+                }
             }
-        } else {
+            if (it + 1 < n_tiles) issue_loads(t0 + kTile);
+            __syncthreads();
+
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
-                xn[hh].decode(xv[hh]);
-                dn[hh].decode(dv[hh]);
-                if (kGate && !kAgg) zn[hh].decode(zv[hh]);
-            }
-        }
-        if (it + 1 < n_tiles) issue_loads(t0 + kTile);
-        __syncthreads();
-
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-            if (ckr) checkpoint(t0 + kHalf * hh);      // sweeps start on multiples of 16
-            // this lane's kH steps of the half: (δ, δ·x) into the channel's row (or kept in
-            // registers for the quad broadcast)
-            float qdl[kH], qdx[kH];
-#pragma unroll
-            for (int i = 0; i < kH; ++i) {
-                const float dl = softplus(bias + dv[hh][i]);
-                if (kAgg) dsum += dl;
-                qdl[i] = dl;
-                qdx[i] = dl * xv[hh][i];
-                if constexpr (!kDpp)
-                    *reinterpret_cast<float2*>(dd_row + 2 * (kH * l + i)) =
-                        make_float2(dl, kZoh ? xv[hh][i] : qdx[i]);
-            }
-            if constexpr (!kDpp) wave_sync();
-
-            // recurrence over the half; operands of step t+1 are read during step t
-            const float* bh = buf + kHalf * hh * R;
-            float part[kHalf];
-            Row<S> bcur, ccur, bnxt, cnxt;
-            float2 dcur, dnxt;
-            bnxt.load(bh + n0);
-            if (!kAgg) cnxt.load(bh + N + n0);
-            if constexpr (!kDpp) dnxt = *reinterpret_cast<const float2*>(dd_row);
-#pragma unroll
-            for (int t = 0; t < kHalf; ++t) {
-                bcur = bnxt;
-                if (!kAgg) ccur = cnxt;
-                if constexpr (kDpp) {
-                    dcur.x = quad_step(qdl, t);
-                    dcur.y = quad_step(qdx, t);
-                } else {
-                    dcur = dnxt;
-                }
-                if (t + 1 < kHalf) {
-                    bnxt.load(bh + (t + 1) * R + n0);
-                    if (!kAgg) cnxt.load(bh + (t + 1) * R + N + n0);
-                    if constexpr (!kDpp) dnxt = *reinterpret_cast<const float2*>(dd_row + 2 * (t + 1));
-                }
-                // the next step's LDS reads stay issued here; arithmetic may move across
-                __builtin_amdgcn_sched_barrier(0x7);
-                float acc = 0.0f;
-#pragma unroll
-                for (int s = 0; s < S; ++s) {
-                    const float t2 = dcur.x * A2[s];
-                    const float abar = exp2_hw(t2);
-                    // first order: dcur.y = δ·x; exact hold: dcur.y = x, times the gain
-                    float bx = dcur.y * bcur.v[s];
-                    if (kZoh) bx *= zoh_gain(t2, abar, dcur.x, iA[s]);
-                    h[s] = fmaf(abar, h[s], bx);
-                    if (!kAgg) acc = fmaf(ccur.v[s], h[s], acc);
-                }
-                part[t] = acc;
-            }
-            // every lane's reads of the rows are done before partials land
-            if constexpr (!kDpp) wave_sync();
-
-            if (!kAgg) {
-                // partial readouts through the wave's area: each lane writes its 16, then
-                // gathers the G partials of its own kH steps
-#pragma unroll
-                for (int q = 0; q < kHalf; q += 4)
-                    *reinterpret_cast<float4*>(mine + q) =
-                        make_float4(part[q], part[q + 1], part[q + 2], part[q + 3]);
-                wave_sync();
-                float sum[kH];
-                const int gbase = lane & ~(G - 1);
-                // lane l starts at source l (rotation): lanes served together read
-                // different source rows; the first row starts the sums (no 0 + x)
-#pragma unroll
-                for (int r = 0; r < G; ++r) {
-                    const int src = (l + r) & (G - 1);
-                    Row<kH> pr;
-                    pr.load(wa + (gbase + src) * kPS + kH * l);
-#pragma unroll
-                    for (int i = 0; i < kH; ++i) sum[i] = r ? sum[i] + pr.v[i] : pr.v[i];
-                }
-                float out[kH];
+                if (ckr) checkpoint(t0 + kHalf * hh);      // sweeps start on multiples of 16
+                // this lane's kH steps of the half: (δ, δ·x) into the channel's row (or kept in
+                // registers for the quad broadcast)
+                float qdl[kH], qdx[kH], qr[kH];
 #pragma unroll
                 for (int i = 0; i < kH; ++i) {
-                    float sv = fmaf(Dd, xv[hh][i], sum[i]);
-                    if (kGate) sv *= silu(zv[hh][i]);
-                    out[i] = sv;
+                    const float dl = softplus(bias + dv[hh][i]);
+                    if (kAgg) dsum += dl;
+                    qdl[i] = dl;
+                    qdx[i] = dl * xv[hh][i];
+                    if constexpr (!kDpp)
+                        *reinterpret_cast<float2*>(dd_row + 2 * (kH * l + i)) =
+                            make_float2(dl, kZoh ? xv[hh][i] : qdx[i]);
                 }
-                if (valid) {
-                    const int64_t te = t0 + kHalf * hh + kH * l;
-                    if constexpr (kTok) {
-                        const uint32_t o = uint32_t(te) * D32 + d32;
+                if constexpr (kPow) {
 #pragma unroll
-                        for (int i = 0; i < kH; ++i) yb[o + uint32_t(i) * D32] = out[i];
-                    } else {
-                        store_k<kH>(yr + te, out);
+                    for (int i = 0; i < kH; ++i) qr[i] = exp2_hw(-qdl[i] * kLog2e);   // e^{-δ}
+                }
+                if constexpr (!kDpp) wave_sync();
+
+                // recurrence over the half; operands of step t+1 are read during step t
+                const float* bh = buf + kHalf * hh * R;
+                float part[kHalf];
+                {
+                    Row<S> bcur, ccur, bnxt, cnxt;
+                    float2 dcur, dnxt;
+                    bnxt.load(bh + n0);
+                    if (!kAgg) cnxt.load(bh + N + n0);
+                    if constexpr (!kDpp) dnxt = *reinterpret_cast<const float2*>(dd_row);
+#pragma unroll
+                    for (int t = 0; t < kHalf; ++t) {
+                        bcur = bnxt;
+                        if (!kAgg) ccur = cnxt;
+                        if constexpr (kDpp) {
+                            dcur.x = quad_step(qdl, t);
+                            dcur.y = quad_step(qdx, t);
+                        } else {
+                            dcur = dnxt;
+                        }
+                        if (t + 1 < kHalf) {
+                            bnxt.load(bh + (t + 1) * R + n0);
+                            if (!kAgg) cnxt.load(bh + (t + 1) * R + N + n0);
+                            if constexpr (!kDpp) dnxt = *reinterpret_cast<const float2*>(dd_row + 2 * (t + 1));
+                        }
+                        // the next step's LDS reads stay issued here; arithmetic may move across
+                        __builtin_amdgcn_sched_barrier(0x7);
+                        float acc = 0.0f;
+                        if constexpr (kPow) {
+                            const float rt = quad_step(qr, t);
+                            float abar = exp2_hw(dcur.x * A2[0]);     // r^(n0+1)
+#pragma unroll
+                            for (int s = 0; s < S; ++s) {
+                                h[s] = fmaf(abar, h[s], dcur.y * bcur.v[s]);
+                                if (!kAgg) acc = fmaf(ccur.v[s], h[s], acc);
+                                if (s + 1 < S) abar *= rt;
+                            }
+                        } else {
+#pragma unroll
+                            for (int s = 0; s < S; ++s) {
+                                const float t2 = dcur.x * A2[s];
+                                const float abar = exp2_hw(t2);
+                                // first order: dcur.y = δ·x; exact hold: dcur.y = x, times the gain
+                                float bx = dcur.y * bcur.v[s];
+                                if (kZoh) bx *= zoh_gain(t2, abar, dcur.x, iA[s]);
+                                h[s] = fmaf(abar, h[s], bx);
+                                if (!kAgg) acc = fmaf(ccur.v[s], h[s], acc);
+                            }
+                        }
+                        part[t] = acc;
                     }
                 }
-                wave_sync();  // gathers done before the next half's rows overwrite the area
+                // every lane's reads of the rows are done before partials land
+                if constexpr (!kDpp) wave_sync();
+
+                if (!kAgg) {
+                    // partial readouts through the wave's area: each lane writes its 16, then
+                    // gathers the G partials of its own kH steps
+#pragma unroll
+                    for (int q = 0; q < kHalf; q += 4)
+                        *reinterpret_cast<float4*>(mine + q) =
+                            make_float4(part[q], part[q + 1], part[q + 2], part[q + 3]);
+                    wave_sync();
+                    float sum[kH];
+                    const int gbase = lane & ~(G - 1);
+                    // lane l starts at source l (rotation): lanes served together read
+                    // different source rows; the first row starts the sums (no 0 + x)
+#pragma unroll
+                    for (int r = 0; r < G; ++r) {
+                        const int src = (l + r) & (G - 1);
+                        Row<kH> pr;
+                        pr.load(wa + (gbase + src) * kPS + kH * l);
+#pragma unroll
+                        for (int i = 0; i < kH; ++i) sum[i] = r ? sum[i] + pr.v[i] : pr.v[i];
+                    }
+                    float out[kH];
+#pragma unroll
+                    for (int i = 0; i < kH; ++i) {
+                        float sv = fmaf(Dd, xv[hh][i], sum[i]);
+                        if (kGate) sv *= silu(zv[hh][i]);
+                        out[i] = sv;
+                    }
+                    if (valid) {
+                        const int64_t te = t0 + kHalf * hh + kH * l;
+                        if constexpr (kTok) {
+                            const uint32_t o = uint32_t(te) * D32 + d32;
+#pragma unroll
+                            for (int i = 0; i < kH; ++i) yb[o + uint32_t(i) * D32] = out[i];
+                        } else {
+                            store_k<kH>(yr + te, out);
+                        }
+                    }
+                    wave_sync();  // gathers done before the next half's rows overwrite the area
+                }
             }
         }
+    };
+    if constexpr (kDpp && kMayPow) {
+        if (pow_path) run_tiles(std::true_type{});
+        else run_tiles(std::false_type{});
+    } else {
+        run_tiles(std::false_type{});
     }
 
     // tail: the last (t_end - t_tiles_end) < 32 steps, one step at a time; every lane
@@ -659,7 +697,7 @@ __global__ __launch_bounds__(kThreads) void scang_mixed_kernel(
     const int64_t f = blockIdx.x;
     const int64_t n4 = int64_t(B) * nb4;
     if (f < n4) {
-        scang_body<Tin, 4, N / 4, kGate, false, kZoh, kTok>(
+        scang_body<Tin, 4, N / 4, kGate, false, kZoh, kTok, false>(
             lds, f % nb4, 0, int(f / nb4), 0, d4, x, dt_raw, z, dt_bias, A, Dskip, Bm, Cm, h_init,
             y, h_last, h_ckpt, nullptr, L, D, L, 1, dtr);
     } else {

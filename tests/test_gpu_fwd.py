@@ -143,15 +143,18 @@ def test_plans_agree_and_deterministic(gpu, a_perturb):
     assert_close(y1, yr, tol_for(inp), "y")
 
 
-def test_s4d_detection_per_wave(gpu):
-    """A = -(n+1) except for one channel: waves holding it take the general path, the
-    others the power path; every channel matches the oracle either way."""
-    inp = make_inputs(1, 512, 200, 16, seed=12, gate=True, with_h0=True)
-    inp.A[77, 5] *= 1.01
-    note("s4d detection")
+@pytest.mark.parametrize("N", [8, 16, 32])
+@pytest.mark.parametrize("plan", [1, 2], ids=["single", "chunked"])
+def test_s4d_detection_per_wave(gpu, N, plan):
+    """A = -(n+1) except for one state of one channel: the wave holding it takes the general
+    path, the others the power path (one exponential and a chain of products per lane); every
+    channel matches the oracle either way, on the one-, four- and eight-lane layouts."""
+    inp = make_inputs(1, 512, 200, N, seed=12, gate=True, with_h0=True)
+    inp.A[77, N // 2 - 1] *= 1.01
+    yr, hr = oracle_fwd(inp)
     for layout in (2, 1, 3):
-        y, hf = gpu_fwd(gpu, inp, plan=2, chunk=128, layout=layout)
-        yr, hr = oracle_fwd(inp)
+        note(f"s4d detection N={N} plan={plan} layout={layout}")
+        y, hf = gpu_fwd(gpu, inp, plan=plan, chunk=128 if plan == 2 else 0, layout=layout)
         assert_close(y, yr, 1e-4, f"y layout {layout}")
         assert_close(hf, hr, 1e-4, f"h_final layout {layout}")
 
