@@ -116,14 +116,26 @@ def bwd_min_bytes(w, s_in, dt_shared=False):
     return rd + wr
 
 
+def pow_a(w):
+    """The workload's A is -(n+1) for every channel (unperturbed), so Ā_n = r^(n+1), r = e^{-δ}."""
+    return not w.a_perturb
+
+
 def alu_slots_per_elem(w, disc=0):
     """Algorithmic VALU lane-slots per (b,t,d) element (transcendental = 2 slots).
     Per state: exp (2) + δ·A, δx·B, state fma, readout fma (4)  -> 6 x N.
+    With A = -(n+1) (first-order hold) each Ā is one product of the previous one and
+    r = e^{-δ}: per state 4 (Ā product, δx·B, state fma, readout fma), per element r (3).
     The exact zero-order hold adds, at its cheapest, Ā - 1, x/A_n and one product per state
     (3; 1/A_n is a per-channel constant) -> 9 x N.
     Per element: softplus 5 VALU + 2 trans; δ·x 1; D·x fma 1; gate 4 VALU + 2 trans (if any);
     bf16 widening 1 per bf16 input tensor."""
-    per_state = (9 if disc else 6) * w.dstate
+    if disc:
+        per_state = 9 * w.dstate
+    elif pow_a(w):
+        per_state = 4 * w.dstate + 3
+    else:
+        per_state = 6 * w.dstate
     elem = 5 + 2 * 2 + 1 + 1
     if w.gate:
         elem += 4 + 2 * 2
@@ -140,13 +152,19 @@ def bwd_alu_slots_per_elem(w, disc=0):
     gain in the recompute and again in the adjoint (3 + 3, as in the forward), ∂g/∂A from the
     gain (2), x·g (1), g·B apart from its sum (1), g·B·x (1) and its FMAs into dA and dδ (2)
     -> 30 x N.  Per element: softplus 9, sigmoid(u) 4, dx 2, dΔ 2, dD 1, with a gate
-    sigmoid(z) 4 + ds 2 + dz 5; bf16 widening per bf16 input."""
+    sigmoid(z) 4 + ds 2 + dz 5; bf16 widening per bf16 input.  With A = -(n+1) (first-order
+    hold) the recompute forms each Ā as one product of the previous one and r = e^{-δ}: 15 per
+    state, plus r (3) per element."""
     elem = 9 + 4 + 2 + 2 + 1
     if w.gate:
         elem += 4 + 2 + 5
     if w.dtype == "bf16":
         elem += 3 if w.gate else 2
-    return (30 if disc else 17) * w.dstate + elem
+    if disc:
+        return 30 * w.dstate + elem
+    if pow_a(w):
+        return 15 * w.dstate + 3 + elem
+    return 17 * w.dstate + elem
 
 
 def cpu_baseline(w, inp, budget_s=4.0, disc=0):

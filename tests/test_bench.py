@@ -34,15 +34,19 @@ def test_forward_algorithmic_bytes():
 
 
 def test_alu_slot_counts():
-    """118 slots per element for the gated bf16 forward at N = 16 (6 per state element plus
-    22 per element), 166 with the exact hold; the gated bf16 backward 17 (30 with the exact
-    hold) per state element plus 32 per element (18, the gate's 11, three bf16 widenings)."""
-    c2, c4 = workload("c2"), workload("c4")
+    """118 slots per element for the gated bf16 forward at N = 16 with a general A (6 per
+    state element plus 22 per element), 166 with the exact hold; with A = -(n+1) each Ā is one
+    product of the previous one and e^{-δ} (4 per state element, 3 per element for e^{-δ}).
+    The gated bf16 backward: 17 per state element (15 with A = -(n+1), plus e^{-δ}; 30 with the
+    exact hold) plus 32 per element (18, the gate's 11, three bf16 widenings)."""
+    c2, c3, c4 = workload("c2"), workload("c3"), workload("c4")
     assert bench.alu_slots_per_elem(c2) == 16 * 6 + 22 == 118
     assert bench.alu_slots_per_elem(c2, 1) == 16 * 9 + 22 == 166
-    assert bench.bwd_alu_slots_per_elem(c4) == 17 * 16 + 32 == 304
+    assert bench.alu_slots_per_elem(c3) == 16 * 4 + 3 + 13 == 80
+    assert bench.alu_slots_per_elem(c4) == 16 * 4 + 3 + 22 == 89
+    assert bench.bwd_alu_slots_per_elem(c4) == 15 * 16 + 3 + 32 == 275
     assert bench.bwd_alu_slots_per_elem(c4, 1) == 30 * 16 + 32 == 512
-    assert bench.alu_slots_per_elem(c4) + bench.bwd_alu_slots_per_elem(c4) == 422
+    assert bench.alu_slots_per_elem(c4) + bench.bwd_alu_slots_per_elem(c4) == 364
     assert bench.alu_slots_per_elem(c4, 1) + bench.bwd_alu_slots_per_elem(c4, 1) == 678
 
 

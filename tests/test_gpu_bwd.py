@@ -118,3 +118,18 @@ def test_c4_full_backward(gpu, ckpt):
     ref = oracle_bwd(inp, True, False, False)
     errs = compare(got, ref)
     print("c4 gradient errors:", {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+
+
+@pytest.mark.parametrize("ckpt", [False, True], ids=["recompute", "ckpt"])
+@pytest.mark.parametrize("N", [8, 16, 32])
+def test_bwd_s4d_detection_per_wave(gpu, N, ckpt):
+    """A = -(n+1) except for one state of one channel: the wave holding that channel runs the
+    general exponentials, the others the power path (one exponential and a chain of products
+    per lane) in the aggregate and final passes; every gradient matches the oracle."""
+    inp = make_inputs(2, 300, 200, N, dtype="f32", seed=40 + N, gate=True, with_h0=True,
+                      with_dy=True, with_dh_final=True)
+    inp.A[77, N // 2 - 1] *= 1.01
+    note(f"bwd s4d detection N={N} ckpt={ckpt}")
+    got = gpu_bwd(gpu, inp, True, True, True, ckpt=ckpt)
+    ref = oracle_bwd(inp, True, True, True)
+    compare(got, ref)
