@@ -79,45 +79,6 @@ ss::DtRows dt_rows(const ss::Plan& p) {
     return p.dt_shared ? ss::DtRows{p.L, 0, 1} : seq_rows(p);
 }
 
-// Workspace carving of ss_block_fwd: every intermediate, the projection partials and the
-// scan's own workspace.  Depends on the dims alone.
-struct BlockPlan {
-    int64_t M, Din, D, N, S;
-    ss_dims sd;                 // the scan: float32, token-major, Δraw shared
-    size_t off_x, off_z, off_dt, off_B, off_C, off_part, off_scan, scan_ws, total;
-};
-
-int make_block_plan(const ss_block_dims& bd, BlockPlan* out) {
-    BlockPlan bp{};
-    if (bd.batch <= 0 || bd.seqlen <= 0 || bd.d_in <= 0 || bd.dim <= 0 || bd.dstate <= 0)
-        return SS_ERR_DIMS;
-    if (bd.d_in % 8 != 0 || bd.dim % 4 != 0) return SS_ERR_DIMS;
-    const int64_t lim = int64_t(1) << 40;
-    if (bd.batch > lim / bd.seqlen) return SS_ERR_DIMS;
-    bp.M = bd.batch * bd.seqlen; bp.Din = bd.d_in; bp.D = bd.dim; bp.N = bd.dstate;
-    if (bp.M > lim / bp.Din || bp.M > lim / (2 * bp.D)) return SS_ERR_DIMS;
-    bp.sd = ss_dims{bd.batch, bd.seqlen, bd.dim, bd.dstate, SS_F32, bd.plan, 0, bd.layout,
-                    SS_DISC_EULER, SS_ORDER_BLD, SS_DT_SHARED};
-    ss::Plan p;
-    const int rc = ss::make_plan(bp.sd, ss::kPlanFwd, &p);
-    if (rc != SS_OK) return rc;
-    bp.S = ss::xproj_splits(bp.M, bp.D, int(bp.N));
-    const size_t f = sizeof(float);
-    const size_t MD = size_t(bp.M) * size_t(bp.D), MN = size_t(bp.M) * size_t(bp.N);
-    size_t off = 0;
-    bp.off_x = off; off = ss::align256(off + MD * f);
-    bp.off_z = off; off = ss::align256(off + MD * f);
-    bp.off_dt = off; off = ss::align256(off + size_t(bp.M) * f);
-    bp.off_B = off; off = ss::align256(off + MN * f);
-    bp.off_C = off; off = ss::align256(off + MN * f);
-    bp.off_part = off;
-    off = ss::align256(off + size_t(bp.S) * size_t(bp.M) * size_t(1 + 2 * bp.N) * f);
-    bp.off_scan = off; bp.scan_ws = p.ws_total; off = ss::align256(off + p.ws_total);
-    bp.total = off;
-    *out = bp;
-    return SS_OK;
-}
-
 }  // namespace
 
 extern "C" {
@@ -335,9 +296,8 @@ int ss_bwd(const ss_dims* dims, const void* x, const void* dt_raw, const float* 
     bl.h_end = reinterpret_cast<float*>(ws + p.off_hend);
     bl.rev_end = reinterpret_cast<float*>(ws + p.off_gend);
     bl.dsum = reinterpret_cast<float*>(ws + p.off_dsum);
-    bl.dbc_part = reinterpret_cast<float*>(ws + p.off_red);
-    bl.ddt_part = reinterpret_cast<float*>(ws + p.off_red + ss::align256(
-        size_t(p.B) * size_t(ss::bwd_reduce_blocks(p)) * size_t(p.L) * size_t(2 * p.N) * 4));
+    bl.dbc_part = reinterpret_cast<float*>(ws + p.off_bcpart);
+    bl.ddt_part = reinterpret_cast<float*>(ws + p.off_dtpart);
     bl.dx = dx; bl.ddt_raw = ddt_raw; bl.dz = dz; bl.dA = dA; bl.dB = dB; bl.dC = dC; bl.dD = dD;
     bl.ddt_bias = ddt_bias;
     bl.B = p.B; bl.L = p.L; bl.D = p.D; bl.N = p.N; bl.chunk = p.chunk; bl.K = int(p.K);
@@ -382,8 +342,8 @@ int ss_bwd(const ss_dims* dims, const void* x, const void* dt_raw, const float* 
 int ss_in_proj(const ss_block_dims* dims, const void* u, const void* W_in, float* x, float* z,
                hipStream_t stream) {
     if (!dims) return SS_ERR_NULL;
-    BlockPlan bp;
-    const int rc = make_block_plan(*dims, &bp);
+    ss::BlockPlan bp;
+    const int rc = ss::make_block_plan(*dims, &bp);
     if (rc != SS_OK) return rc;
     if (!u || !W_in || !x || !z) return SS_ERR_NULL;
     if (!aligned16(u) || !aligned16(W_in) || !aligned16(x) || !aligned16(z)) return SS_ERR_ALIGN;
@@ -395,8 +355,8 @@ int ss_in_proj(const ss_block_dims* dims, const void* u, const void* W_in, float
 
 int ss_block_fwd_workspace_size(const ss_block_dims* dims, size_t* bytes) {
     if (!dims || !bytes) return SS_ERR_NULL;
-    BlockPlan bp;
-    const int rc = make_block_plan(*dims, &bp);
+    ss::BlockPlan bp;
+    const int rc = ss::make_block_plan(*dims, &bp);
     if (rc != SS_OK) return rc;
     *bytes = bp.total;
     return SS_OK;
@@ -407,8 +367,8 @@ int ss_block_fwd(const ss_block_dims* dims, const void* u, const void* W_in, con
                  float* y, float* h_final, float* x, float* z, float* dt, float* Bm, float* Cm,
                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
     if (!dims) return SS_ERR_NULL;
-    BlockPlan bp;
-    const int rc = make_block_plan(*dims, &bp);
+    ss::BlockPlan bp;
+    const int rc = ss::make_block_plan(*dims, &bp);
     if (rc != SS_OK) return rc;
     if (!u || !W_in || !W_x || !dt_bias || !A || !Dskip || !y) return SS_ERR_NULL;
     const void* req[] = {u, W_in, W_x, dt_bias, A, Dskip, y};

@@ -14,6 +14,7 @@
 // at float32 accuracy.
 #include "ss_device.h"
 #include "ss_kernels.h"
+#include "ss_plan.h"
 
 namespace ss {
 
@@ -177,7 +178,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // 16-token tiles per wave (MT): each weight run loaded feeds MT MFMAs.  Two tiles measured
 // 1.7 % faster on the block step than one at N = 16, four no faster than two at half the
 // occupancy; above three output tiles (N > 16) one token tile keeps the registers in reach.
-static inline int xproj_mt(int N) { return N <= 16 ? 2 : 1; }
 
 // K steps per LDS tile and the tiles' row stride (floats; 4 of padding)
 constexpr int kXK = 64;
@@ -332,19 +332,6 @@ hipError_t launch_gemm_bf16_nt(const void* A, const void* W, float* C0, float* C
                        Nc, K, nsplit, ld0, ld1, int(tm), int(tn));
     return hipGetLastError();
 }
-
-int64_t xproj_splits(int64_t M, int64_t D, int N) {
-    // about 768 workgroups in all (one round at three workgroups per CU, which the kernel's
-    // LDS tiles and registers allow for N = 16), each split at least 64 steps of K
-    const int64_t tok = 64 * xproj_mt(N);        // tokens per workgroup
-    const int64_t mb = (M + tok - 1) / tok;
-    int64_t S = (768 + mb - 1) / mb;
-    if (S > D / 64) S = D / 64;
-    return S < 1 ? 1 : S;
-}
-
-// split length: whole 64-step LDS tiles
-int64_t xproj_split_len(int64_t D, int64_t S) { return ((D + S - 1) / S + kXK - 1) / kXK * kXK; }
 
 template <int NT, int MT>
 static hipError_t launch_xproj_t(const float* x, const float* Wx, float* part, int64_t M,

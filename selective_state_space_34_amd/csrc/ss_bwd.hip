@@ -45,7 +45,7 @@ namespace {
 
 constexpr int kBMaxSteps = 64;                // chunk <= 64 steps
 constexpr int kBThreads = 256;                // 4 waves x 16 channels x 4 lanes
-constexpr int kBChan = 64;
+constexpr int kBChan = int(kBwdChan);
 // 16-step tiles (the forward's checkpoint interval), 4 steps prepared per lane
 constexpr int kBT = kCkptSteps;
 constexpr int kBPer = 4;
@@ -1015,15 +1015,6 @@ __global__ __launch_bounds__(256) void bwd_reduce_params_kernel(
 // ---------------------------------------------------------------------------------------
 // plan helpers and launchers
 // ---------------------------------------------------------------------------------------
-int64_t bwd_reduce_blocks(const Plan& p) { return (p.D + kBChan - 1) / kBChan; }
-
-size_t bwd_partial_bytes(const Plan& p) {
-    // dB|dC per-block partials + dD/ddt_bias per-chunk partials
-    const size_t bc = size_t(p.B) * size_t(bwd_reduce_blocks(p)) * size_t(p.L) * size_t(2 * p.N) * 4;
-    const size_t dt = size_t(p.B) * size_t(p.K) * size_t(p.D) * 2 * 4;
-    return align256(bc) + dt;
-}
-
 template <typename Tin, int S, bool kGate>
 static void launch_bwd_g(const BwdLaunch& p, dim3 grid, hipStream_t s) {
     const Tin* x = static_cast<const Tin*>(p.x);

@@ -150,9 +150,7 @@ hipError_t launch_gemm_bf16_nt(const void* A, const void* W, float* C0, float* C
                                int64_t Nc, int64_t K, int64_t nsplit, int64_t ld0, int64_t ld1,
                                hipStream_t s);
 // [Δ | B | C] = x [M, D] · Wx [1 + 2N, D]ᵀ (fp32) through split-K partials part
-// [S, M, 1 + 2N] (S = xproj_splits); D % 4 == 0.
-int64_t xproj_splits(int64_t M, int64_t D, int N);
-int64_t xproj_split_len(int64_t D, int64_t S);
+// [S, M, 1 + 2N] (S = xproj_splits, ss_plan.h); D % 4 == 0.
 hipError_t launch_xproj(const float* x, const float* Wx, float* part, float* dt, float* Bm,
                         float* Cm, int64_t M, int64_t D, int N, hipStream_t s);
 

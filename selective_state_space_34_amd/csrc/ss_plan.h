@@ -25,10 +25,20 @@ struct Plan {
     int tok;         // token-major x, z, y, dy, dx, dz [B, L, D] and B, C, dB, dC [B, L, N]
     int dt_shared;   // Δraw one value per token [B, L]
     // workspace carving (byte offsets, 256-aligned)
-    size_t off_bc, off_hend, off_dsum, off_hstart, off_gend, off_gstart, off_red, off_ddt;
-    size_t red_bytes;
+    //   forward:  off_bc    [B, L, 2N] B|C staging (one-lane kernel)
+    //             off_hend  [B, D, K, N] chunk end states, off_dsum [B, D, K] Σδ per chunk,
+    //             off_hstart [B, D, K, N] chunk start states (chunked plan)
+    //   backward: off_hend  forward pairs -> start states -> dA partials, off_dsum,
+    //             off_gend  [B, D, K, N] reverse pairs -> adjoints entering from the right,
+    //             off_bcpart [B, NB, L, 2N] dB|dC partials of NB = ceil(D / 64) channel blocks,
+    //             off_dtpart [B, D, K, 2] dD, ddt_bias partials,
+    //             off_ddt   [B, NB, L] block sums of a shared Δraw's gradient
+    size_t off_bc, off_hend, off_dsum, off_hstart, off_gend, off_bcpart, off_dtpart, off_ddt;
     size_t ws_total;
 };
+
+// Channels per workgroup of the backward kernels (16 per wave, four waves).
+constexpr int64_t kBwdChan = 64;
 
 constexpr int64_t kMaxGridYZ = 65535;
 
@@ -45,10 +55,8 @@ constexpr int64_t kSingleWaves = 2048;
 // SIMDs of the part (256 CUs x 4): one round of waves
 constexpr int64_t kSimds = 1024;
 
-// Number of workgroups the reduction of the backward's per-block partials uses
-// (see ss_bwd.hip); the partial buffers are sized from it.
-int64_t bwd_reduce_blocks(const Plan& p);
-size_t bwd_partial_bytes(const Plan& p);
+// Channel blocks of the backward (each leaves one row of dB|dC partials per batch row).
+inline int64_t bwd_reduce_blocks(const Plan& p) { return (p.D + kBwdChan - 1) / kBwdChan; }
 
 // What the plan is for: the sequence forward, the backward, or the single-token step (which
 // uses only the validated sizes and flags, none of the sequence kernels' tiling).
@@ -149,19 +157,21 @@ inline int make_plan(const ss_dims& d, PlanFor what, Plan* out) {
     p.off_bc = off;
     // [B, L, 2N] float32 copy of B and C: the one-lane forward kernel only
     if (!backward && !p.group) off = align256(off + size_t(p.B) * size_t(p.L) * size_t(2 * N) * sizeof(float));
-    p.off_hend = p.off_dsum = p.off_hstart = p.off_gend = p.off_gstart = p.off_red = 0;
-    p.red_bytes = 0;
+    p.off_hend = p.off_dsum = p.off_hstart = p.off_gend = p.off_bcpart = p.off_dtpart = 0;
     if (chunked) {
         const size_t st = size_t(p.B) * size_t(p.K) * size_t(p.D) * size_t(N) * sizeof(float);
         const size_t sm = size_t(p.B) * size_t(p.K) * size_t(p.D) * sizeof(float);
         p.off_hend = off; off = align256(off + st);
         p.off_dsum = off; off = align256(off + sm);
-        p.off_hstart = off; off = align256(off + st);
         if (backward) {
+            // the carries run in place: no separate start-state buffers
             p.off_gend = off; off = align256(off + st);
-            p.off_gstart = off; off = align256(off + st);
-            p.red_bytes = bwd_partial_bytes(p);
-            p.off_red = off; off = align256(off + p.red_bytes);
+            p.off_bcpart = off;
+            off = align256(off + size_t(p.B) * size_t(bwd_reduce_blocks(p)) * size_t(p.L) *
+                                     size_t(2 * N) * sizeof(float));
+            p.off_dtpart = off; off = align256(off + size_t(p.B) * size_t(p.K) * size_t(p.D) * 2 * sizeof(float));
+        } else {
+            p.off_hstart = off; off = align256(off + st);
         }
     }
     // shared Δraw: the backward's per-64-channel-block sums of its gradient [B, ceil(D/64), L]
@@ -172,6 +182,62 @@ inline int make_plan(const ss_dims& d, PlanFor what, Plan* out) {
     }
     p.ws_total = off;
     *out = p;
+    return SS_OK;
+}
+
+// Selection projection of the block ([Δ | B | C] = x · W_xᵀ): token tiles per wave, splits of
+// the K = D sum over workgroups and their length (whole 64-step LDS tiles).
+constexpr int64_t kXprojK = 64;
+inline int xproj_mt(int N) { return N <= 16 ? 2 : 1; }
+inline int64_t xproj_splits(int64_t M, int64_t D, int N) {
+    // about 768 workgroups in all (one round at three workgroups per CU, which the kernel's
+    // LDS tiles and registers allow for N = 16), each split at least 64 steps of K
+    const int64_t tok = 64 * xproj_mt(N);        // tokens per workgroup
+    const int64_t mb = (M + tok - 1) / tok;
+    int64_t S = (768 + mb - 1) / mb;
+    if (S > D / 64) S = D / 64;
+    return S < 1 ? 1 : S;
+}
+inline int64_t xproj_split_len(int64_t D, int64_t S) {
+    return ((D + S - 1) / S + kXprojK - 1) / kXprojK * kXprojK;
+}
+
+// Workspace carving of ss_block_fwd: every intermediate, the projection partials and the
+// scan's own workspace.  Depends on the dims alone.
+struct BlockPlan {
+    int64_t M, Din, D, N, S;
+    ss_dims sd;                 // the scan: float32, token-major, Δraw shared
+    size_t off_x, off_z, off_dt, off_B, off_C, off_part, off_scan, scan_ws, total;
+};
+
+inline int make_block_plan(const ss_block_dims& bd, BlockPlan* out) {
+    BlockPlan bp{};
+    if (bd.batch <= 0 || bd.seqlen <= 0 || bd.d_in <= 0 || bd.dim <= 0 || bd.dstate <= 0)
+        return SS_ERR_DIMS;
+    if (bd.d_in % 8 != 0 || bd.dim % 4 != 0) return SS_ERR_DIMS;
+    const int64_t lim = int64_t(1) << 40;
+    if (bd.batch > lim / bd.seqlen) return SS_ERR_DIMS;
+    bp.M = bd.batch * bd.seqlen; bp.Din = bd.d_in; bp.D = bd.dim; bp.N = bd.dstate;
+    if (bp.M > lim / bp.Din || bp.M > lim / (2 * bp.D)) return SS_ERR_DIMS;
+    bp.sd = ss_dims{bd.batch, bd.seqlen, bd.dim, bd.dstate, SS_F32, bd.plan, 0, bd.layout,
+                    SS_DISC_EULER, SS_ORDER_BLD, SS_DT_SHARED};
+    Plan p;
+    const int rc = make_plan(bp.sd, kPlanFwd, &p);
+    if (rc != SS_OK) return rc;
+    bp.S = xproj_splits(bp.M, bp.D, int(bp.N));
+    const size_t f = sizeof(float);
+    const size_t MD = size_t(bp.M) * size_t(bp.D), MN = size_t(bp.M) * size_t(bp.N);
+    size_t off = 0;
+    bp.off_x = off; off = align256(off + MD * f);
+    bp.off_z = off; off = align256(off + MD * f);
+    bp.off_dt = off; off = align256(off + size_t(bp.M) * f);
+    bp.off_B = off; off = align256(off + MN * f);
+    bp.off_C = off; off = align256(off + MN * f);
+    bp.off_part = off;
+    off = align256(off + size_t(bp.S) * size_t(bp.M) * size_t(1 + 2 * bp.N) * f);
+    bp.off_scan = off; bp.scan_ws = p.ws_total; off = align256(off + p.ws_total);
+    bp.total = off;
+    *out = bp;
     return SS_OK;
 }
 

@@ -176,13 +176,13 @@ def test_workspace_sizes(lib):
     st = 1 * K * 256 * 16 * 4
     assert ss.workspace_size(d) == 2 * st + K * 256 * 4
     assert ss.workspace_size(d) == ss.workspace_size(d)
-    # the backward: chunk state buffers (forward and reverse pairs), chunk sums, dB|dC
-    # partials per 64-channel block and dD / ddt_bias partials per chunk
+    # the backward: chunk state buffers (forward and reverse pairs, carried in place), chunk
+    # sums, dB|dC partials per 64-channel block and dD / ddt_bias partials per chunk
     d = ss.make_dims(8, 2048, 5120, 16, ss.SS_BF16)
     K, NB = 2048 // 64, 5120 // 64
     st = 8 * K * 5120 * 16 * 4
     a256 = lambda v: (v + 255) // 256 * 256
-    assert ss.workspace_size(d, backward=True) == (4 * st + a256(8 * K * 5120 * 4)
+    assert ss.workspace_size(d, backward=True) == (2 * st + a256(8 * K * 5120 * 4)
                                                    + a256(8 * NB * 2048 * 32 * 4) + 8 * K * 5120 * 2 * 4)
     # a Δraw shared by the channels adds its gradient's per-block sums [B, D/64, L]
     ds = ss.make_dims(8, 2048, 5120, 16, ss.SS_BF16, dt_layout=ss.SS_DT_SHARED)
