@@ -31,7 +31,9 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 # ALU roof: 256 CUs x 4 SIMDs x 16 fp32 lanes x 2.4 GHz = 39.32e12 VALU lane-slots/s
-# (packed fp32 is not used; transcendentals issue at half rate = 2 slots each).
+# (packed fp32 is not used).  Measured on the part: a wave64 v_fma_f32 occupies its SIMD for
+# one issue unit (full rate), a v_exp_f32 for two (half rate, 2 slots), and the two never
+# overlap (active VALU units = FMAs + 2 x exps, VALU 100 % busy, in every mix).
 ALU_PEAK_TSLOTS = 256 * 4 * 16 * 2.4e9 / 1e12
 
 
