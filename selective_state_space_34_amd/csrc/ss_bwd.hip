@@ -85,6 +85,24 @@ __device__ __forceinline__ float quad_bcast_i(const float (&v)[4], int t) {
     }
 }
 
+// Reduce-scatter over the quad: lane j of each quad gets Σ_q v_q[j], the sum over the quad's
+// four lanes of their element j.  Two exchange stages (DPP quad permutations xor 1, xor 2, each
+// folded into its add): at each, a lane keeps the half of its values whose index bit matches
+// its lane bit and adds the partner's matching half.
+__device__ __forceinline__ float quad_reduce_scatter(const float (&v)[4], int j) {
+    const bool b0 = j & 1, b1 = j & 2;
+    float r[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const float keep = b0 ? v[2 * k + 1] : v[2 * k];
+        const float send = b0 ? v[2 * k] : v[2 * k + 1];
+        r[k] = keep + qperm<0xB1>(send);              // quad_perm [1, 0, 3, 2]
+    }
+    const float keep = b1 ? r[1] : r[0];
+    const float send = b1 ? r[0] : r[1];
+    return keep + qperm<0x4E>(send);                  // quad_perm [2, 3, 0, 1]
+}
+
 // Sums across lanes for the dB|dC channel reduction.  gfx950's v_permlane32_swap exchanges
 // the upper 32 lanes of its first operand with the lower 32 of its second, v_permlane16_swap
 // the odd 16-lane rows of the first with the even rows of the second.  Applied to a pair (a, b)
@@ -454,12 +472,10 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(S >= 
     // lane that owns a batch's elements finishes their gradients right after the batch
     constexpr int kBB = kBPer;
     constexpr int kNBat = kBT / kBB;
-    // per-wave exchange area, per lane: a batch's Σ_n partials (kBB x 2) and the readout
-    // partials of a tile (kBT) share it in turn; the lane stride is an odd multiple of 4
-    // floats, so 16-byte writes of 8 consecutive lanes hit disjoint banks
-    constexpr int XW = (2 * kBB > kBT) ? 2 * kBB : kBT;
+    // per-wave exchange area, per lane: the readout partials of a tile (kBT); the lane stride
+    // is an odd multiple of 4 floats, so 16-byte writes of 8 consecutive lanes hit disjoint banks
+    constexpr int XW = kBT;
     constexpr int LS = ((XW + 4) / 8) * 8 + 4;
-    constexpr int PXO = 0;                      // offset of the Σ_n partials in a lane's area
     constexpr int OUTW = kBT * 2 * NP;          // dB|dC sums of one tile for one wave
     constexpr int CW = (S + 1) / 2;             // channel sums a lane holds per step
     __shared__ __align__(16) float bc_lds[kBMaxSteps * R];
@@ -738,6 +754,10 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(S >= 
 #pragma unroll
             for (int bi = kNBat - 1; bi >= 0; --bi) {
                 float pxb[kBB], pdb[kBB];
+                // the row (δ, x, ds, σ(u)) of step 4 bi + j, which this lane finishes after the
+                // batch: written before the recompute sweep, read now so it is in by then
+                const int tj = bi * kBB + j;
+                const float4 rw = *reinterpret_cast<const float4*>(myrow + 4 * tj);
 #pragma unroll
                 for (int i = kBB - 1; i >= 0; --i) {
                     const int t = bi * kBB + i;
@@ -814,23 +834,11 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(S >= 
                         }
                     }
                 }
-                *reinterpret_cast<float4*>(mine + PXO) = make_float4(pxb[0], pxb[1], pxb[2], pxb[3]);
-                *reinterpret_cast<float4*>(mine + PXO + 4) = make_float4(pdb[0], pdb[1], pdb[2], pdb[3]);
-                wave_sync();
-                float pv[2][4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float* src = wx + (qb + r) * LS + PXO + j;
-                    pv[0][r] = src[0];
-                    pv[1][r] = src[4];
-                }
                 {
                     // lane j finishes step 4 bi + j of its channel: Σ_n over the quad's partials
-                    // of that step, then dx and dΔ from the step's row
-                    const int tj = bi * kBB + j;
-                    const float PX = (pv[0][0] + pv[0][1]) + (pv[0][2] + pv[0][3]);
-                    const float PD = (pv[1][0] + pv[1][1]) + (pv[1][2] + pv[1][3]);
-                    const float4 rw = *reinterpret_cast<const float4*>(myrow + 4 * tj);  // (δ, x, ds, σ)
+                    // of that step (a reduce-scatter in registers), then dx and dΔ from its row
+                    const float PX = quad_reduce_scatter(pxb, j);
+                    const float PD = quad_reduce_scatter(pdb, j);
                     const int64_t tg = t0c + tb + tj;
                     const bool ok = tg < t1c;
                     // exact hold: PX already carries the gain and PD the input term of dδ
@@ -842,8 +850,8 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(S >= 
                     // outputs leave in 16-byte runs per lane once the sweep is done
                     *reinterpret_cast<float2*>(myrow + 4 * tj) = make_float2(ox, od);
                 }
-                wave_sync();
             }
+            wave_sync();   // every lane's parked (dx, dΔraw) visible to the lane that stores it
 
             // dx, dΔraw of the lane's own 4 steps, from the rows.  A Δraw shared by the channels
             // (ddt_blk) takes the sum over the block's channels instead: each wave parks its 16

@@ -66,7 +66,7 @@ def test_c2_sampled(gpu):
 
 
 def test_c3_sampled(gpu):
-    _sampled(workload("c3"), 6, 3, h_final=True)
+    _sampled(workload("c3"), 64, 3, h_final=True)
 
 
 def test_c4_fwd_sampled(gpu):
