@@ -103,6 +103,29 @@ __device__ __forceinline__ float quad_reduce_scatter(const float (&v)[4], int j)
     return keep + qperm<0x4E>(send);                  // quad_perm [2, 3, 0, 1]
 }
 
+// The same over a tile's 16 per-step values, steps 4q..4q+3 owned by quad lane q: lane j gets
+// Σ_q v_q[4j + i] for i < 4, the quad's totals of its own four steps.
+__device__ __forceinline__ void quad_reduce_scatter16(const float (&v)[16], int j, float (&out)[4]) {
+    const bool b0 = j & 1, b1 = j & 2;
+    float r[8];                                       // [hi][i]: step 4 (2 hi + b0) + i
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float a = v[8 * hi + i], c = v[8 * hi + 4 + i];
+            const float keep = b0 ? c : a;
+            const float send = b0 ? a : c;
+            r[4 * hi + i] = keep + qperm<0xB1>(send);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float keep = b1 ? r[4 + i] : r[i];
+        const float send = b1 ? r[i] : r[4 + i];
+        out[i] = keep + qperm<0x4E>(send);
+    }
+}
+
 // Sums across lanes for the dB|dC channel reduction.  gfx950's v_permlane32_swap exchanges
 // the upper 32 lanes of its first operand with the lower 32 of its second, v_permlane16_swap
 // the odd 16-lane rows of the first with the even rows of the second.  Applied to a pair (a, b)
@@ -472,15 +495,12 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(S >= 
     // lane that owns a batch's elements finishes their gradients right after the batch
     constexpr int kBB = kBPer;
     constexpr int kNBat = kBT / kBB;
-    // per-wave exchange area, per lane: the readout partials of a tile (kBT); the lane stride
-    // is an odd multiple of 4 floats, so 16-byte writes of 8 consecutive lanes hit disjoint banks
-    constexpr int XW = kBT;
-    constexpr int LS = ((XW + 4) / 8) * 8 + 4;
     constexpr int OUTW = kBT * 2 * NP;          // dB|dC sums of one tile for one wave
     constexpr int CW = (S + 1) / 2;             // channel sums a lane holds per step
     __shared__ __align__(16) float bc_lds[kBMaxSteps * R];
     __shared__ __align__(16) float rows[4 * 16 * kRW];
-    __shared__ __align__(16) float xch[4 * 64 * LS];
+    // a shared Δraw's gradient of a tile: [wave][channel][step], summed over the block
+    __shared__ __align__(16) float dtx[4 * 16 * kBT];
     __shared__ __align__(16) float comb[4 * OUTW];   // the wave sums of a tile
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -496,8 +516,7 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(S >= 
     const int nsteps = int(t1c - t0c);
     const int ntiles = (nsteps + kBT - 1) / kBT;
     const int64_t NB = (D + kBChan - 1) / kBChan;
-    float* wx = xch + wave * 64 * LS;           // this wave's exchange area
-    float* mine = wx + lane * LS;
+    float* wdt = dtx + wave * 16 * kBT;         // this wave's shared-Δraw gradient rows
     float* myrow = rows + wave * 16 * kRW + (lane >> 2) * kRW;
 
     const int64_t sidx = ((int64_t(b) * D + d) * K + k) * Nr;
@@ -712,40 +731,23 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(S >= 
                 rbn.load(bt + (kBT - 1) * R + n0);
                 rcn.load(bt + (kBT - 1) * R + NP + n0);
                 if (kGate) {
+                    // readout partials -> quad totals of the owner lane's steps (4j..4j+3 of
+                    // lane j), by a reduce-scatter in registers; dz right away
+                    float stot[4];
+                    quad_reduce_scatter16(sp, j, stot);
+                    float dzv[4];
 #pragma unroll
-                    for (int i = 0; i < kBT; i += 4)
-                        *reinterpret_cast<float4*>(mine + i) = make_float4(sp[i], sp[i + 1], sp[i + 2], sp[i + 3]);
-                }
-            }
-            const int qb = lane & ~3;
-            if (kGate) {
-                // readout partials -> owner lanes (steps 4j..4j+3 of lane j); dz right away
-                wave_sync();
-                // sums start from the first source (a 0 + x add is not folded: signed zeros)
-                float stot[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int src = (j + r) & 3;
-                    const float4 v = *reinterpret_cast<const float4*>(wx + (qb + src) * LS + kBPer * j);
-                    if (r == 0) {
-                        stot[0] = v.x; stot[1] = v.y; stot[2] = v.z; stot[3] = v.w;
-                    } else {
-                        stot[0] += v.x; stot[1] += v.y; stot[2] += v.z; stot[3] += v.w;
+                    for (int i = 0; i < 4; ++i) {
+                        const float sv = fmaf(Dd, xv[i], stot[i]);
+                        dzv[i] = gv[i] * sv * sz[i] * fmaf(zv[i], 1.0f - sz[i], 1.0f);
                     }
+                    if (valid) store4(dzo + row, te, t1c, vec, ts, dzv);
                 }
-                float dzv[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float sv = fmaf(Dd, xv[i], stot[i]);
-                    dzv[i] = gv[i] * sv * sz[i] * fmaf(zv[i], 1.0f - sz[i], 1.0f);
-                }
-                if (valid) store4(dzo + row, te, t1c, vec, ts, dzv);
-                wave_sync();
             }
 
             // reverse sweep over the tile, in batches of kBB steps.  B and C of the step after
-            // are read one step ahead (issued before this step's exchange-area stores, which the
-            // compiler cannot prove disjoint from them and would otherwise wait behind)
+            // are read one step ahead (issued before this step's LDS stores of channel sums, which
+            // the compiler cannot prove disjoint from them and would otherwise wait behind)
             float* cbuf = comb + wave * OUTW;
             // which channel sums this lane holds after chan_sum, and whether it stores them
             const int cs_type = (lane >> 5) & 1, cs_half = (lane >> 4) & 1;
@@ -855,7 +857,7 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(S >= 
 
             // dx, dΔraw of the lane's own 4 steps, from the rows.  A Δraw shared by the channels
             // (ddt_blk) takes the sum over the block's channels instead: each wave parks its 16
-            // channels' values in its own exchange area (its sweep is over), summed below.
+            // channels' values in its own rows of dtx, summed below.
             {
                 float ox[4], od[4];
 #pragma unroll
@@ -866,7 +868,7 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(S >= 
                 }
                 if (valid) store4(dxo + row, te, t1c, vec, ts, ox);
                 if (ddt_blk) {
-                    *reinterpret_cast<float4*>(wx + (lane >> 2) * kBT + kBPer * j) =
+                    *reinterpret_cast<float4*>(wdt + (lane >> 2) * kBT + kBPer * j) =
                         valid ? make_float4(od[0], od[1], od[2], od[3]) : make_float4(0.f, 0.f, 0.f, 0.f);
                 } else if (valid) {
                     store4(ddr, te, t1c, vec, gdr.ts, od);
@@ -879,7 +881,7 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(S >= 
                 // Σ over the block's 64 channels of dΔraw at step tb + tid
                 float sdt = 0.0f;
                 for (int w = 0; w < 4; ++w)
-                    for (int cl = 0; cl < 16; ++cl) sdt += xch[w * 64 * LS + cl * kBT + tid];
+                    for (int cl = 0; cl < 16; ++cl) sdt += dtx[(w * 16 + cl) * kBT + tid];
                 const int64_t t = t0c + tb + tid;
                 if (t < t1c) ddt_blk[(int64_t(b) * NB + blockIdx.x) * L + t] = sdt;
             }
