@@ -472,6 +472,8 @@ def main():
     ap.add_argument("--workload", default="c2",
                     help="c0..c4 (default c2, D=5120 forward); d1 = decode step; p2 = block")
     ap.add_argument("--plan", type=int, default=0)
+    ap.add_argument("--chunk", type=int, default=0,
+                    help="chunk length of the chunked forward plan (0 = the plan's choice)")
     ap.add_argument("--layout", type=int, default=0, help="0 auto, 1 four lanes, 2 one lane, 3 eight lanes per channel")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--order", type=int, default=0,
@@ -529,7 +531,7 @@ def main():
     y = torch.empty(yshape, dtype=torch.float32, device=dev)
     hf = torch.empty((w.batch, w.dim, w.dstate), dtype=torch.float32, device=dev) if w.h_final else None
     dims = ss.make_dims(w.batch, w.seqlen, w.dim, w.dstate,
-                        ss.SS_BF16 if w.dtype == "bf16" else ss.SS_F32, args.plan, 0, args.layout,
+                        ss.SS_BF16 if w.dtype == "bf16" else ss.SS_F32, args.plan, args.chunk, args.layout,
                         args.disc, args.order,
                         ss.SS_DT_SHARED if args.dt_shared else ss.SS_DT_FULL)
     ws = torch.empty(max(ss.workspace_size(dims), 1), dtype=torch.uint8, device=dev)
@@ -546,8 +548,8 @@ def main():
 
     def fwd_call():
         ss.ss_fwd(x, dtr, dtb, A, Bm, Cm, Dk, z=z, y=y, h_final=hf, h_ckpt=hck, workspace=ws,
-                  plan=args.plan, layout=args.layout, disc=args.disc, order=args.order,
-                  stream=stream)
+                  plan=args.plan, chunk=args.chunk, layout=args.layout, disc=args.disc,
+                  order=args.order, stream=stream)
 
     def bwd_call():
         ss.ss_bwd(x, dtr, dtb, A, Bm, Cm, Dk, dy, z=z, h_ckpt=hck, workspace=wsb, out=grads,
@@ -641,7 +643,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{w.name}: {w.label}", "batch": w.batch, "seqlen": w.seqlen,
                    "dim": w.dim, "dstate": w.dstate, "in_dtype": w.dtype, "gate": w.gate,
-                   "plan": args.plan, "layout": args.layout,
+                   "plan": args.plan, "chunk": args.chunk, "layout": args.layout,
                    "disc": "zoh" if args.disc else "first-order",
                    "cache_flush_mib": args.flush_mib if flush is not None else 0,
                    "order": "BLD" if args.order else "BDL",
