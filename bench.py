@@ -539,7 +539,11 @@ def main():
     hck = None
     if w.backward:
         dy = t32(np.ascontiguousarray(lay(inp.dy)))
-        wsb = torch.empty(ss.workspace_size(dims, backward=True), dtype=torch.uint8, device=dev)
+        # the backward keeps its own chunk length (--chunk sets the forward's)
+        bdims = ss.make_dims(w.batch, w.seqlen, w.dim, w.dstate,
+                             ss.SS_BF16 if w.dtype == "bf16" else ss.SS_F32, 0, 0, 0, args.disc,
+                             args.order, ss.SS_DT_SHARED if args.dt_shared else ss.SS_DT_FULL)
+        wsb = torch.empty(ss.workspace_size(bdims, backward=True), dtype=torch.uint8, device=dev)
         grads = ss.ss_bwd(x, dtr, dtb, A, Bm, Cm, Dk, dy, z=z, order=args.order, disc=args.disc)
         # training use: the forward keeps its 16-step state checkpoints for the backward
         if not args.no_ckpt:

@@ -224,7 +224,7 @@ int ss_block_fwd(const ss_block_dims* dims, const void* u, const void* W_in, con
  * streams, or several host threads) race on it and give undefined results; calls ordered on
  * one stream are safe.  Nothing in the array needs to start at zero (each call writes every
  * value it reads), so the previous call's contents do no harm. */
-#define SS_NOALLOC_SCRATCH_MIB 32
+#define SS_NOALLOC_SCRATCH_MIB 64
 int ss_fwd_noalloc(const ss_dims* dims,
                    const void* x, const void* dt_raw, const float* dt_bias, const float* A,
                    const void* Bm, const void* Cm, const float* Dskip, const void* z,
