@@ -47,12 +47,12 @@ STEP_SOURCES = ["ss_step.hip", "ss_device.h", "ss_plan.h", "ss_api.cpp", "ss_ker
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 MEASURED_TRAFFIC = {
     # (workload, disc): first-order (0) or exact zero-order hold (1)
-    ("c2", 0): {"sources": FWD_SOURCES, "fetch_kib": 318863, "write_kib": 399174,
-                "sources_sha256": "0ea80df27192f7fcc1fc6ce8393157fa34700a8252c7f4bc8122077e84877175"},
-    ("c2", 1): {"sources": FWD_SOURCES, "fetch_kib": 336294, "write_kib": 415446,
-                "sources_sha256": "0ea80df27192f7fcc1fc6ce8393157fa34700a8252c7f4bc8122077e84877175"},
-    ("d1", 0): {"sources": STEP_SOURCES, "fetch_kib": 45068, "write_kib": 87040,
-                "sources_sha256": "fb704a2f5e74dc3510a1b8b4d9350cdbb9fe0159c47a80c5718f05dc8357e747"},
+    ("c2", 0): {"sources": FWD_SOURCES, "fetch_kib": 338786, "write_kib": 402506,
+                "sources_sha256": "1886fa5fe3a488c6f4fbbdf97f4c4934f26af0798262799a524a4256b5a81a93"},
+    ("c2", 1): {"sources": FWD_SOURCES, "fetch_kib": 362738, "write_kib": 400812,
+                "sources_sha256": "1886fa5fe3a488c6f4fbbdf97f4c4934f26af0798262799a524a4256b5a81a93"},
+    ("d1", 0): {"sources": STEP_SOURCES, "fetch_kib": 45069, "write_kib": 87040,
+                "sources_sha256": "450fdbf9aa09ccccb4f2de494aa94e655b524ae1d714af9917a7ae57032b0ae4"},
 }
 
 
@@ -174,6 +174,8 @@ def cpu_baseline(w, inp, budget_s=4.0, disc=0):
     one run takes about budget_s seconds of wall time on all host threads."""
     from oracle import cref
     threads = cref.threads(0)
+    if w.backward:
+        return cpu_baseline_fwd_bwd(w, inp, budget_s, disc, threads)
     C = w.batch * w.dim
     n = max(1, min(C, 64))
     rng = np.random.default_rng(0)
@@ -192,6 +194,32 @@ def cpu_baseline(w, inp, budget_s=4.0, disc=0):
     return {"value": elems / dt, "unit": "elem/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{n} of {C} channels x full L={w.seqlen} (B*L*D elements {elems}), "
                       f"{dt:.2f} s wall on {threads} OpenMP threads"}
+
+
+def cpu_baseline_fwd_bwd(w, inp, budget_s, disc, threads):
+    """Forward + backward workloads: time the oracle's forward and then its backward (which
+    recomputes the states itself, as the GPU backward does) on the first n channels of every
+    batch row, n growing until one fwd+bwd takes about budget_s / 4 seconds."""
+    from oracle import cref
+    n = max(1, min(w.dim, 64))
+    while True:
+        sl = lambda a: np.ascontiguousarray(a[:, :n])
+        x, dtr, Bm, Cm, dy = sl(inp.x), sl(inp.dt_raw), inp.Bm, inp.Cm, sl(inp.dy)
+        z = sl(inp.z) if w.gate else None
+        par = (inp.dt_bias[:n], inp.A[:n], Bm, Cm, inp.Dskip[:n])
+        t0 = time.perf_counter()
+        cref.fwd(x, dtr, par[0], par[1], par[2], par[3], par[4], z=z, want_h_final=False,
+                 zoh=bool(disc))
+        cref.bwd(x, dtr, par[0], par[1], par[2], par[3], par[4], dy, z=z, zoh=bool(disc))
+        dt = time.perf_counter() - t0
+        if dt >= budget_s / 4 or n == w.dim:
+            break
+        n = min(w.dim, int(n * max(2.0, budget_s / max(dt, 1e-3) / 2)))
+    elems = w.batch * n * w.seqlen
+    return {"value": elems / dt, "unit": "elem/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"fwd + bwd on {w.batch} x {n} of {w.batch} x {w.dim} channels x full "
+                      f"L={w.seqlen} (B*L*D elements {elems}), {dt:.2f} s wall on {threads} "
+                      f"OpenMP threads"}
 
 
 def step_min_bytes(w, s_in, dt_shared=False):
