@@ -388,19 +388,44 @@ __global__ __launch_bounds__(kBThreads) void bwd_agg_kernel(
     // step's e^{-δ} (or e^{-Σδ})
     constexpr bool kMayPow = !kZoh && S >= 2;
     const bool pow_path = kMayPow && __builtin_amdgcn_readfirstlane(int(__all(pow_lane))) != 0;
+    // Without the forward pair a step needs only Σδ up to it: dl[i] becomes that running sum
+    // (this lane's prefix plus the totals of the quad's lower lanes, which own the earlier
+    // steps of the chunk), and the lane that owns a step forms its e^{-Σδ} once for the quad
+    // (the forward pair, which needs e^{-δ} and more registers, forms it per step)
+    constexpr bool kRho = kMayPow && !kFwd;
+    float rho[kRho ? kBT : 1];
+    if constexpr (!kFwd) {
+        float run = 0.0f;
+#pragma unroll
+        for (int i = 0; i < kBT; ++i) { run += dl[i]; dl[i] = run; }
+        float incl = run;
+        const float up1 = qperm<0x90>(incl);             // quad lane j - 1
+        incl += j >= 1 ? up1 : 0.0f;
+        const float up2 = qperm<0x40>(incl);             // quad lane j - 2
+        incl += j >= 2 ? up2 : 0.0f;
+        const float below = incl - run;
+#pragma unroll
+        for (int i = 0; i < kBT; ++i) dl[i] += below;
+        if constexpr (kRho) {
+            if (pow_path) {
+#pragma unroll
+                for (int i = 0; i < kBT; ++i) rho[i] = exp2_hw(-dl[i] * kLog2e);
+            }
+        }
+    }
     __syncthreads();
 
     // tile T's steps sit in lane T of each quad: broadcast each step's values to the quad.
     // Without the forward pair no step needs its own Ā: the cumulative product is taken as
     // 2^(A·log2(e)·Σδ) from the running sum of δ, one exponential and no product per state.
-    float cum = 0.0f;
     auto tile = [&](auto tc, auto pw) {
         constexpr int T = decltype(tc)::value;
         constexpr bool kPow = decltype(pw)::value && kMayPow;
         const float* bt = bc_lds + T * kBT * R;
 #pragma unroll
         for (int i = 0; i < kBT; ++i) {
-            const float dlt = quad_bcast<T>(dl[i]);
+            // δ of the step (forward pair) or Σδ up to it (reverse pair only)
+            const float arg = quad_bcast<T>(dl[i]);
             const float dst = quad_bcast<T>(dsv[i]);
             Vec<S> bc, cc;
             cc.load(bt + i * R + NP + n0);
@@ -409,17 +434,17 @@ __global__ __launch_bounds__(kBThreads) void bwd_agg_kernel(
                 xt = quad_bcast<T>(xin[i]);
                 bc.load(bt + i * R + n0);
             }
-            if constexpr (!kFwd) cum += dlt;
             // power path: the first state's factor and the ratio to the next state's
             float pp = 1.0f, rt = 1.0f;
             if constexpr (kPow) {
-                const float arg = kFwd ? dlt : cum;
                 pp = exp2_hw(arg * A2[0]);
-                rt = exp2_hw(-arg * kLog2e);
+                if constexpr (kRho) rt = quad_bcast<T>(rho[i]);
+                else rt = exp2_hw(-arg * kLog2e);
             }
 #pragma unroll
             for (int s = 0; s < S; ++s) {
                 if constexpr (kFwd) {
+                    const float dlt = arg;
                     const float t2 = dlt * A2[s];
                     float a;
                     if constexpr (kPow) {
@@ -436,7 +461,7 @@ __global__ __launch_bounds__(kBThreads) void bwd_agg_kernel(
                     P[s] = pp;
                     if (s + 1 < S) pp *= rt;
                 } else {
-                    P[s] = exp2_hw(cum * A2[s]);
+                    P[s] = exp2_hw(arg * A2[s]);
                 }
                 Rv[s] = fmaf(P[s], dst * cc.v[s], Rv[s]);
             }
