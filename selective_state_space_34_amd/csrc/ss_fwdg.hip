@@ -228,7 +228,8 @@ struct GroupLds {
 // below d_hi), chunk k.  lds: GroupLds<G, S>::FLOATS floats, 16-byte aligned.  Requires
 // L % 8 == 0 and chunk % 32 == 0 (or K == 1) for the tiled part; the last < 32 steps of a
 // chunk run a per-step tail.
-template <typename Tin, int G, int S, bool kGate, bool kAgg, bool kZoh, bool kTok, bool kMayPow = true>
+template <typename Tin, int G, int S, bool kGate, bool kAgg, bool kZoh, bool kTok, bool kMayPow = true,
+          bool kWiden = false>
 __device__ __forceinline__ void scang_body(
     float* __restrict__ lds, int64_t blk, int k, int b, int64_t d_lo, int64_t d_hi,
     const Tin* __restrict__ x, const Tin* __restrict__ dt_raw, const Tin* __restrict__ z,
@@ -492,6 +493,20 @@ __device__ __forceinline__ void scang_body(
                     dn[hh].decode(dv[hh]);
                     if (kGate && !kAgg) zn[hh].decode(zv[hh]);
                 }
+                // kWiden: widen here, before the next tile's loads reuse the raw registers (left
+                // to itself the compiler widens at the first use and keeps a copy of every raw
+                // register across the loads: two moves per raw register per tile).  The widened
+                // values take more registers until they are used, so only where that leaves the
+                // occupancy as it was.
+                if constexpr (kWiden) {
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                        for (int i = 0; i < kH; ++i) {
+                            asm volatile("" : "+v"(xv[hh][i]), "+v"(dv[hh][i]));
+                            if (kGate && !kAgg) asm volatile("" : "+v"(zv[hh][i]));
+                        }
+                }
             }
             if (it + 1 < n_tiles) issue_loads(t0 + kTile);
             __syncthreads();
@@ -696,13 +711,16 @@ __global__ __launch_bounds__(kThreads) void scang_mixed_kernel(
     __shared__ __align__(16) float lds[F4 > F8 ? F4 : F8];
     const int64_t f = blockIdx.x;
     const int64_t n4 = int64_t(B) * nb4;
+    // early widening of the raw inputs keeps both layouts' occupancy at N = 16 with the
+    // first-order hold (measured resource use; other shapes would lose a wave per SIMD)
+    constexpr bool kWiden = N == 16 && !kZoh;
     if (f < n4) {
-        scang_body<Tin, 4, N / 4, kGate, false, kZoh, kTok, false>(
+        scang_body<Tin, 4, N / 4, kGate, false, kZoh, kTok, false, kWiden>(
             lds, f % nb4, 0, int(f / nb4), 0, d4, x, dt_raw, z, dt_bias, A, Dskip, Bm, Cm, h_init,
             y, h_last, h_ckpt, nullptr, L, D, L, 1, dtr);
     } else {
         const int64_t g = f - n4;
-        scang_body<Tin, 8, N / 8, kGate, false, kZoh, kTok>(
+        scang_body<Tin, 8, N / 8, kGate, false, kZoh, kTok, true, kWiden>(
             lds, g % nb8, 0, int(g / nb8), d4, D, x, dt_raw, z, dt_bias, A, Dskip, Bm, Cm, h_init,
             y, h_last, h_ckpt, nullptr, L, D, L, 1, dtr);
     }
