@@ -226,6 +226,35 @@ __device__ __forceinline__ void load4(const bf16_t* __restrict__ p, int64_t t, i
         for (int i = 0; i < 4; ++i) o[i] = (t + i < t_end) ? to_f32(p[(t + i) * ts]) : 0.0f;
     }
 }
+// 8 consecutive elements [t, t+8) of a row, zero past t_end: one 16-byte load of bf16 (two of
+// float32) when the run is whole and aligned (vec: L % 8 == 0, so t % 8 == 0 rows start on
+// 16 bytes), else two 4-element loads
+__device__ __forceinline__ void load8(const bf16_t* __restrict__ p, int64_t t, int64_t t_end, int vec,
+                                      int64_t ts, float (&o)[8]) {
+    if (vec && ts == 1 && t + 8 <= t_end) {
+        const uint4 v = *reinterpret_cast<const uint4*>(p + t);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            o[2 * i] = __uint_as_float(w[i] << 16);
+            o[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    } else {
+        float a[4], b[4];
+        load4(p, t, t_end, vec, ts, a);
+        load4(p, t + 4, t_end, vec, ts, b);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { o[i] = a[i]; o[4 + i] = b[i]; }
+    }
+}
+__device__ __forceinline__ void load8(const float* __restrict__ p, int64_t t, int64_t t_end, int vec,
+                                      int64_t ts, float (&o)[8]) {
+    float a[4], b[4];
+    load4(p, t, t_end, vec, ts, a);
+    load4(p, t + 4, t_end, vec, ts, b);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { o[i] = a[i]; o[4 + i] = b[i]; }
+}
 __device__ __forceinline__ void store4(float* __restrict__ p, int64_t t, int64_t t_end, int vec,
                                        int64_t ts, const float (&v)[4]) {
     if (vec && ts == 1 && t + 4 <= t_end) {
@@ -340,24 +369,25 @@ __global__ __launch_bounds__(kBThreads) void bwd_agg_kernel(
     float dsum = 0.0f;
     {
         float xv[kBT], dv[kBT], gv[kBT], zv[kBT];
+        // 16-byte loads: each instruction of a quad covers half of a bf16 line
 #pragma unroll
-        for (int q = 0; q < kBT / 4; ++q) {
-            float t4[4];
-            load4(drr, tl + 4 * q, t1c, vec, dtr.ts, t4);
+        for (int q = 0; q < kBT / 8; ++q) {
+            float t8[8];
+            load8(drr, tl + 8 * q, t1c, vec, dtr.ts, t8);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dv[4 * q + i] = t4[i];
-            load4(dy + row, tl + 4 * q, t1c, vec, ts, t4);
+            for (int i = 0; i < 8; ++i) dv[8 * q + i] = t8[i];
+            load8(dy + row, tl + 8 * q, t1c, vec, ts, t8);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) gv[4 * q + i] = t4[i];
+            for (int i = 0; i < 8; ++i) gv[8 * q + i] = t8[i];
             if (kGate) {
-                load4(z + row, tl + 4 * q, t1c, vec, ts, t4);
+                load8(z + row, tl + 8 * q, t1c, vec, ts, t8);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) zv[4 * q + i] = t4[i];
+                for (int i = 0; i < 8; ++i) zv[8 * q + i] = t8[i];
             }
             if (kFwd) {
-                load4(x + row, tl + 4 * q, t1c, vec, ts, t4);
+                load8(x + row, tl + 8 * q, t1c, vec, ts, t8);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) xv[4 * q + i] = t4[i];
+                for (int i = 0; i < 8; ++i) xv[8 * q + i] = t8[i];
             }
         }
         load_chunk_bc<Tin, NP>(bc_lds, Bm, Cm, b, Nr, L, t0c, nsteps, tid, tok);

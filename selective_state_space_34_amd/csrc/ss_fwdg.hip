@@ -688,7 +688,10 @@ __global__ __launch_bounds__(kThreads) void scang_kernel(
     float* __restrict__ h_ckpt, float* __restrict__ dsum_out, int64_t L, int64_t D,
     int64_t chunk, int K, DtRows dtr) {
     __shared__ __align__(16) float lds[GroupLds<G, S, Tin, kTok>::FLOATS];
-    scang_body<Tin, G, S, kGate, kAgg, kZoh, kTok>(lds, blockIdx.x, blockIdx.y, blockIdx.z, 0, D, x,
+    // early widening (see scang_body) except in the gated bf16 output pass, where it would
+    // cost a wave per SIMD
+    constexpr bool kWiden = kAgg || !kGate || sizeof(Tin) == 4;
+    scang_body<Tin, G, S, kGate, kAgg, kZoh, kTok, true, kWiden>(lds, blockIdx.x, blockIdx.y, blockIdx.z, 0, D, x,
                                                    dt_raw, z, dt_bias, A, Dskip, Bm, Cm, h_init, y,
                                                    h_last, h_ckpt, dsum_out, L, D, chunk, K, dtr);
 }
