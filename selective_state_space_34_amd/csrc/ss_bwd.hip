@@ -1029,51 +1029,70 @@ __global__ __launch_bounds__(256) void bwd_reduce_dt_kernel(const float* __restr
 __global__ __launch_bounds__(256) void bwd_reduce_params_kernel(
     const float* __restrict__ dA_part, const float* __restrict__ ddt_part, float* __restrict__ dA,
     float* __restrict__ dD, float* __restrict__ ddt_bias, int64_t D, int Nr, int Bn, int K) {
-    __shared__ float red[256];
+    __shared__ float red[1024];
+    __shared__ float wsum[2][4];
     const int64_t d = blockIdx.x;
     const int tid = threadIdx.x;
     const int KN = K * Nr;
-    // thread tid accumulates entries e = tid + 256 i of the K*N block; Nr divides 256,
-    // so every entry a thread touches has state n = tid % Nr
-    // four independent partial sums (loads in flight instead of a chain); every entry a
-    // thread touches still has state n = tid % Nr
+    // dA: entry e of a (b, d) block of K*N partials has state e % Nr.  With Nr >= 4 (so
+    // KN % 4 == 0 and every block starts on 16 bytes) thread tid reads 16-byte runs 4 tid + 1024 i,
+    // whose four entries have states (4 tid + q) % Nr, since Nr divides 1024, and keeps its sum
+    // q in red[4 tid + q]; otherwise it reads single entries tid + 256 i, state tid % Nr, and
+    // keeps the sum in red[tid] (slots 256.. hold zeros).  Either way every red[f] belongs to
+    // state f % Nr.
     float ac[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    const bool vec4 = Nr >= 4;
     for (int b = 0; b < Bn; ++b) {
         const float* p = dA_part + (int64_t(b) * D + d) * KN;
-        int e = tid;
-        for (; e + 3 * 256 < KN; e += 4 * 256) {
-#pragma unroll
-            for (int u = 0; u < 4; ++u) ac[u] += p[e + 256 * u];
+        if (vec4) {
+            const float4* p4 = reinterpret_cast<const float4*>(p);
+            for (int e = tid; e < KN / 4; e += 256) {
+                const float4 v = p4[e];
+                ac[0] += v.x; ac[1] += v.y; ac[2] += v.z; ac[3] += v.w;
+            }
+        } else {
+            for (int e = tid; e < KN; e += 256) ac[0] += p[e];
         }
-        for (; e < KN; e += 256) ac[0] += p[e];
     }
-    red[tid] = (ac[0] + ac[1]) + (ac[2] + ac[3]);
+    if (vec4) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) red[4 * tid + q] = ac[q];
+    } else {
+        red[tid] = ac[0];
+#pragma unroll
+        for (int q = 0; q < 3; ++q) red[256 + 3 * tid + q] = 0.0f;
+    }
+    __syncthreads();
+    // fold the 1024 slots to 256 (f, f + 256, f + 512, f + 768 share a state), then each
+    // state's 256 / Nr slots
+    const float f4 = (red[tid] + red[tid + 256]) + (red[tid + 512] + red[tid + 768]);
+    __syncthreads();
+    red[tid] = f4;
     __syncthreads();
     if (tid < Nr) {
         float t = 0.0f;
         for (int i = tid; i < 256; i += Nr) t += red[i];
         dA[d * Nr + tid] = t;
     }
-    __syncthreads();
+    // dD and ddt_bias: Σ over batch rows and chunks of the (dD, ddt) pairs
     float a0 = 0.0f, a1 = 0.0f;
     for (int b = 0; b < Bn; ++b) {
-        const float* q = ddt_part + (int64_t(b) * D + d) * K * 2;
-        for (int k = tid; k < K; k += 256) { a0 += q[2 * k]; a1 += q[2 * k + 1]; }
+        const float2* q = reinterpret_cast<const float2*>(ddt_part + (int64_t(b) * D + d) * K * 2);
+        for (int k = tid; k < K; k += 256) {
+            const float2 v = q[k];
+            a0 += v.x; a1 += v.y;
+        }
     }
-    red[tid] = a0;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        a0 += __shfl_xor(a0, o);
+        a1 += __shfl_xor(a1, o);
+    }
+    if ((tid & 63) == 0) { wsum[0][tid >> 6] = a0; wsum[1][tid >> 6] = a1; }
     __syncthreads();
     if (tid == 0) {
-        float t = 0.0f;
-        for (int i = 0; i < 256; ++i) t += red[i];
-        dD[d] = t;
-    }
-    __syncthreads();
-    red[tid] = a1;
-    __syncthreads();
-    if (tid == 0) {
-        float t = 0.0f;
-        for (int i = 0; i < 256; ++i) t += red[i];
-        ddt_bias[d] = t;
+        dD[d] = (wsum[0][0] + wsum[0][1]) + (wsum[0][2] + wsum[0][3]);
+        ddt_bias[d] = (wsum[1][0] + wsum[1][1]) + (wsum[1][2] + wsum[1][3]);
     }
 }
 
