@@ -705,7 +705,8 @@ def main():
                      "traffic": (None if args.order or args.dt_shared
                                  else measured_traffic(w, args.disc)),
                      "kernel": ("ss_fwd + ss_bwd step (every kernel of both calls)" if w.backward
-                                else "ss_fwd (scang_kernel, one launch per call)"
+                                else "ss_fwd (one group-scan launch per call: scang_kernel, or "
+                                     "scang_mixed_kernel for the four/eight-lane mixed layout)"
                                 if dims_plan_single(ss, dims) else "ss_fwd (all passes)"),
                      "launch_us": t_avg * 1e6, "launch_us_median": float(np.median(per)) * 1e6,
                      "slots_per_elem": slots_pe,
