@@ -979,32 +979,63 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(S >= 
 // 4. reductions
 // ---------------------------------------------------------------------------------------
 // dB | dC: part [B, NB, L, 2N] summed over NB -> dB, dC [B, N, L] (token-major: [B, L, N]).
-// One thread per (t, v) of a batch row: reads are coalesced across threads, the sum runs over
-// the channel blocks.
+// One thread per four consecutive (t, v) entries of a batch row (one per entry when L·2N is
+// not a multiple of 4): reads are coalesced across threads, the sum runs over the channel
+// blocks.
 __global__ __launch_bounds__(256) void bwd_reduce_bc_kernel(const float* __restrict__ part,
                                                             float* __restrict__ dB,
                                                             float* __restrict__ dC, int64_t L,
                                                             int NB, int Nr, int tok) {
     const int R = 2 * Nr;
     const int b = blockIdx.y;
-    const int64_t f = int64_t(blockIdx.x) * 256 + threadIdx.x;
     const int64_t LR = L * R;
-    if (f >= LR) return;
-    const float* p = part + int64_t(b) * NB * LR + f;
-    // eight independent partial sums: eight loads in flight per thread instead of a chain
-    float a[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-    int gi = 0;
-    for (; gi + 8 <= NB; gi += 8) {
+    // four consecutive (t, v) entries per thread when LR % 4 == 0 (each block row then starts
+    // on 16 bytes): 16-byte loads, sixteen blocks' loads in flight at a time
+    const bool v4 = (LR & 3) == 0;
+    const int64_t f0 = (int64_t(blockIdx.x) * 256 + threadIdx.x) * (v4 ? 4 : 1);
+    if (f0 >= LR) return;
+    const float* p = part + int64_t(b) * NB * LR + f0;
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (v4) {
+        float4 a[4] = {};
+        int gi = 0;
+        for (; gi + 16 <= NB; gi += 16) {
+            float4 q[16];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) a[u] += p[int64_t(gi + u) * LR];
+            for (int u = 0; u < 16; ++u) q[u] = *reinterpret_cast<const float4*>(p + int64_t(gi + u) * LR);
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                a[u & 3].x += q[u].x; a[u & 3].y += q[u].y; a[u & 3].z += q[u].z; a[u & 3].w += q[u].w;
+            }
+        }
+        for (; gi < NB; ++gi) {
+            const float4 q = *reinterpret_cast<const float4*>(p + int64_t(gi) * LR);
+            a[0].x += q.x; a[0].y += q.y; a[0].z += q.z; a[0].w += q.w;
+        }
+        acc[0] = (a[0].x + a[1].x) + (a[2].x + a[3].x);
+        acc[1] = (a[0].y + a[1].y) + (a[2].y + a[3].y);
+        acc[2] = (a[0].z + a[1].z) + (a[2].z + a[3].z);
+        acc[3] = (a[0].w + a[1].w) + (a[2].w + a[3].w);
+    } else {
+        // eight independent partial sums: eight loads in flight instead of a chain
+        float a[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+        int gi = 0;
+        for (; gi + 8 <= NB; gi += 8) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) a[u] += p[int64_t(gi + u) * LR];
+        }
+        for (; gi < NB; ++gi) a[0] += p[int64_t(gi) * LR];
+        acc[0] = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
     }
-    for (; gi < NB; ++gi) a[0] += p[int64_t(gi) * LR];
-    const float acc = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
-    const int64_t t = f / R;
-    const int v = int(f % R);
-    const int n = v < Nr ? v : v - Nr;
-    float* out = v < Nr ? dB : dC;
-    out[tok ? (int64_t(b) * L + t) * Nr + n : (int64_t(b) * Nr + n) * L + t] = acc;
+    const int nf = v4 ? 4 : 1;
+    for (int i = 0; i < nf; ++i) {
+        const int64_t f = f0 + i;
+        const int64_t t = f / R;
+        const int v = int(f % R);
+        const int n = v < Nr ? v : v - Nr;
+        float* out = v < Nr ? dB : dC;
+        out[tok ? (int64_t(b) * L + t) * Nr + n : (int64_t(b) * Nr + n) * L + t] = acc[i];
+    }
 }
 
 // Δraw shared by the channels (one value per token): its gradient [B, L] is the sum over
@@ -1156,7 +1187,8 @@ hipError_t launch_bwd(int bf16, const BwdLaunch& p, hipStream_t s) {
 hipError_t launch_bwd_reduce(const BwdLaunch& p, hipStream_t s) {
     const int NB = int((p.D + kBChan - 1) / kBChan);
     const int64_t LR = p.L * 2 * p.N;
-    hipLaunchKernelGGL(bwd_reduce_bc_kernel, dim3(unsigned((LR + 255) / 256), unsigned(p.B)), dim3(256),
+    const int64_t per = (LR % 4 == 0) ? 4 : 1;   // entries per thread (bwd_reduce_bc_kernel)
+    hipLaunchKernelGGL(bwd_reduce_bc_kernel, dim3(unsigned((LR / per + 255) / 256), unsigned(p.B)), dim3(256),
                        0, s, p.dbc_part, p.dB, p.dC, p.L, NB, int(p.N), p.tok);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
