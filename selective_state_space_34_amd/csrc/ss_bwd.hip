@@ -312,9 +312,42 @@ template <> struct In4<float> {
 template <typename Tin, int NP>
 __device__ __forceinline__ void load_chunk_bc(float* __restrict__ lds, const Tin* __restrict__ Bm,
                                               const Tin* __restrict__ Cm, int b, int Nr, int64_t L,
-                                              int64_t t0, int nsteps, int tid, int tok) {
+                                              int64_t t0, int nsteps, int tid, int tok, int vec) {
     constexpr int R = 2 * NP + 4;
     constexpr int total = 2 * NP * kBMaxSteps;
+    if (!tok && vec && Nr == NP) {
+        // channel-major rows whose runs start on 16 bytes (L % 8 == 0 and t0 % 16 == 0): each
+        // thread copies 16-byte pieces (PE steps of one B or C row), states fastest across lanes;
+        // a piece reaching past the chunk's steps is read element by element, zero past them
+        constexpr int PE = 16 / int(sizeof(Tin));
+        constexpr int PPR = kBMaxSteps / PE;          // pieces per 64-step row
+        constexpr int units = 2 * NP * PPR;
+        for (int e = tid; e < units; e += kBThreads) {
+            const int n = e % NP, q = (e / NP) % PPR, m = e / (NP * PPR);
+            const Tin* src = (m ? Cm : Bm) + (int64_t(b) * NP + n) * L + t0 + PE * q;
+            float v[PE];
+            if (PE * q + PE <= nsteps) {
+                const uint4 w = *reinterpret_cast<const uint4*>(src);
+                const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+                if constexpr (sizeof(Tin) == 2) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        v[2 * i] = __uint_as_float(ww[i] << 16);
+                        v[2 * i + 1] = __uint_as_float(ww[i] & 0xffff0000u);
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) v[i] = __uint_as_float(ww[i]);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < PE; ++i) v[i] = (PE * q + i < nsteps) ? to_f32(src[i]) : 0.0f;
+            }
+#pragma unroll
+            for (int i = 0; i < PE; ++i) lds[(PE * q + i) * R + m * NP + n] = v[i];
+        }
+        return;
+    }
     for (int e = tid; e < total; e += kBThreads) {
         const int t = tok ? (e / NP) % kBMaxSteps : e % kBMaxSteps;
         const int n = tok ? e % NP : (e / kBMaxSteps) % NP;
@@ -390,12 +423,15 @@ __global__ __launch_bounds__(kBThreads) void bwd_agg_kernel(
                 for (int i = 0; i < 8; ++i) xv[8 * q + i] = t8[i];
             }
         }
-        load_chunk_bc<Tin, NP>(bc_lds, Bm, Cm, b, Nr, L, t0c, nsteps, tid, tok);
+        load_chunk_bc<Tin, NP>(bc_lds, Bm, Cm, b, Nr, L, t0c, nsteps, tid, tok, vec);
+        const int rem = nsteps - kBT * j;             // this lane's steps inside the chunk
 #pragma unroll
         for (int i = 0; i < kBT; ++i) {
-            const bool ok = tl + i < t1c;
-            dl[i] = ok ? softplus(bias + dv[i]) : 0.0f;
-            dsv[i] = ok ? (kGate ? gv[i] * silu(zv[i]) : gv[i]) : 0.0f;
+            // past the chunk's end the loads gave zeros, so ds is zero there already; δ is
+            // formed everywhere and selected (no branch around the transcendentals)
+            const float sp = softplus(bias + dv[i]);
+            dl[i] = (i < rem) ? sp : 0.0f;
+            dsv[i] = kGate ? gv[i] * silu(zv[i]) : gv[i];
             dsum += dl[i];
             // δ·x, or x with the exact hold (its gain depends on the state)
             if (kFwd) xin[i] = kZoh ? xv[i] : dl[i] * xv[i];
@@ -488,8 +524,11 @@ __global__ __launch_bounds__(kBThreads) void bwd_agg_kernel(
                     h[s] = fmaf(a, h[s], bx);
                     P[s] *= a;
                 } else if constexpr (kPow) {
-                    P[s] = pp;
+                    // pp carries the step's ds: one product per state for the chain, one FMA
+                    if (s == 0) pp *= dst;
+                    Rv[s] = fmaf(pp, cc.v[s], Rv[s]);
                     if (s + 1 < S) pp *= rt;
+                    continue;
                 } else {
                     P[s] = exp2_hw(arg * A2[s]);
                 }
@@ -607,7 +646,7 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(S >= 
         }
     };
     if (kCk) load_tile(ntiles - 1);
-    load_chunk_bc<Tin, NP>(bc_lds, Bm, Cm, b, Nr, L, t0c, nsteps, tid, tok);
+    load_chunk_bc<Tin, NP>(bc_lds, Bm, Cm, b, Nr, L, t0c, nsteps, tid, tok, vec);
     float A2[S], An[S], iA[S], g[S], dA[S];
     float ck[kCk ? 1 : kBMaxTiles][S];          // state entering each tile (uniform index)
 #pragma unroll
@@ -691,6 +730,7 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(S >= 
         for (int tt = ntiles - 1; tt >= 0; --tt) {
             const int tb = tt * kBT;
             const int64_t te = t0c + tb + kBPer * j;
+            const int rem = nsteps - (tb + kBPer * j);      // this lane's steps inside the chunk
             if (!kCk) load_tile(tt);
             float xv[4], dv[4], zv[4], gv[4];
             bx.decode(xv);
@@ -708,16 +748,18 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(S >= 
             float rdl[kBPer], rx[kBPer], rds[kBPer], rr[kBPer];
 #pragma unroll
             for (int i = 0; i < kBPer; ++i) {
-                const bool ok = te + i < t1c;
+                // past the sequence's end the loads gave zeros, so ds is zero there already; δ
+                // is formed everywhere and selected (no branch around the transcendentals)
                 const float u = bias + dv[i];
-                const float dl = ok ? softplus(u) : 0.0f;
+                const float sp = softplus(u);
+                const float dl = (i < rem) ? sp : 0.0f;
                 if constexpr (kPow) rr[i] = exp2_hw(-dl * kLog2e);   // e^{-δ}
                 float ds;
                 if (kGate) {
                     sz[i] = sigmoid(zv[i]);
-                    ds = ok ? gv[i] * zv[i] * sz[i] : 0.0f;
+                    ds = gv[i] * zv[i] * sz[i];
                 } else {
-                    ds = ok ? gv[i] : 0.0f;
+                    ds = gv[i];
                 }
                 // channels past D compute on a clamped copy and must add nothing to dB, dC:
                 // their x and ds are zero
