@@ -169,7 +169,12 @@ __device__ __forceinline__ void chan_sum(const float (&cB)[S], const float (&cC)
         w[0] = swap_sum16(u[0], u[0]);
     }
 #pragma unroll
-    for (int k = 0; k < (S + 1) / 2; ++k) w[k] = row4_sum(w[k]);
+    for (int k = 0; k < (S + 1) / 2; ++k) {
+        w[k] = row4_sum(w[k]);
+        // the sums are formed here, for every lane: left alone, the compiler sinks the last add
+        // into the caller's masked store, where the row rotation no longer folds into it
+        asm volatile("" : "+v"(w[k]));
+    }
 }
 
 __device__ __forceinline__ void wave_sync() {

@@ -182,6 +182,12 @@ __device__ __forceinline__ float quad_step(const float (&v)[K], int t) {
     }
 }
 
+// v from quad lane quad_perm(Ctrl) of this lane's quad (same folding form as quad_step)
+template <int Ctrl>
+__device__ __forceinline__ float qperm(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), Ctrl, 0xf, 0xf, true));
+}
+
 // order LDS traffic of one wave: everything before is visible to the wave's lanes after
 __device__ __forceinline__ void wave_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -418,6 +424,12 @@ __device__ __forceinline__ void scang_body(
     // (separate copies keep either one's registers to what it needs alone)
     auto run_tiles = [&](auto pw) {
         constexpr bool kPow = decltype(pw)::value && kDpp;
+        // the aggregate pass on the power path sums weighted inputs instead of running the
+        // recurrence: over a 16-step half, h_n ← e^{-(n+1)Δ}·h_n + Σ_t e^{-(n+1)R_t}·δ_t x_t·B_{t,n},
+        // Δ the half's Σδ and R_t the Σδ of the half's steps after t (the products of Ā over
+        // the steps after t, §2.2's pair composed over the half): the weight of a lane's next
+        // state is the previous one times e^{-R_t}, so a state costs one product and one FMA
+        constexpr bool kRev = kPow && kAgg;
         for (int64_t it = 0; it < n_tiles; ++it) {
             const int64_t t0 = t_begin + it * kTile;
             float* buf = lds + (it & 1) * TILE_F;
@@ -527,7 +539,32 @@ __device__ __forceinline__ void scang_body(
                         *reinterpret_cast<float2*>(dd_row + 2 * (kH * l + i)) =
                             make_float2(dl, kZoh ? xv[hh][i] : qdx[i]);
                 }
-                if constexpr (kPow) {
+                float qR[kRev ? kH : 1];
+                if constexpr (kRev) {
+                    // R of this lane's steps: its own later steps, then the later lanes' totals
+                    // (quad lanes l+1.., which own the half's later steps)
+                    float e = 0.0f;
+#pragma unroll
+                    for (int i = kH - 1; i >= 0; --i) { qR[i] = e; e += qdl[i]; }
+                    const float n1 = qperm<0xF9>(e);                 // quad lane l + 1
+                    const float s1 = (l < 3) ? n1 : 0.0f;
+                    const float n2 = qperm<0xFE>(e + s1);            // quad lanes l + 2, l + 3
+                    const float later = s1 + ((l < 2) ? n2 : 0.0f);
+#pragma unroll
+                    for (int i = 0; i < kH; ++i) {
+                        qR[i] += later;
+                        qr[i] = exp2_hw(-qR[i] * kLog2e);   // e^{-R}
+                    }
+                    // the state entering the half decays by e^{-(n+1)Δ}
+                    const float tot = qperm<0x00>(e + later);        // Δ, from quad lane 0
+                    float E = exp2_hw(tot * A2[0]);
+                    const float eD = exp2_hw(-tot * kLog2e);
+#pragma unroll
+                    for (int s2 = 0; s2 < S; ++s2) {
+                        h[s2] *= E;
+                        if (s2 + 1 < S) E *= eD;
+                    }
+                } else if constexpr (kPow) {
 #pragma unroll
                     for (int i = 0; i < kH; ++i) qr[i] = exp2_hw(-qdl[i] * kLog2e);   // e^{-δ}
                 }
@@ -560,7 +597,16 @@ __device__ __forceinline__ void scang_body(
                         // the next step's LDS reads stay issued here; arithmetic may move across
                         __builtin_amdgcn_sched_barrier(0x7);
                         float acc = 0.0f;
-                        if constexpr (kPow) {
+                        if constexpr (kRev) {
+                            // δ_t x_t·e^{-(n0+1)R_t}, then one product per next state
+                            const float qt = quad_step(qr, t);
+                            float p = exp2_hw(quad_step(qR, t) * A2[0]) * dcur.y;
+#pragma unroll
+                            for (int s = 0; s < S; ++s) {
+                                h[s] = fmaf(p, bcur.v[s], h[s]);
+                                if (s + 1 < S) p *= qt;
+                            }
+                        } else if constexpr (kPow) {
                             const float rt = quad_step(qr, t);
                             float abar = exp2_hw(dcur.x * A2[0]);     // r^(n0+1)
 #pragma unroll
