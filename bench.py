@@ -47,10 +47,10 @@ STEP_SOURCES = ["ss_step.hip", "ss_device.h", "ss_plan.h", "ss_api.cpp", "ss_ker
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 MEASURED_TRAFFIC = {
     # (workload, disc): first-order (0) or exact zero-order hold (1)
-    ("c2", 0): {"sources": FWD_SOURCES, "fetch_kib": 321213, "write_kib": 398652,
-                "sources_sha256": "6f95532a8288a655cc5d07b47582dc2dc3abb9e55a4672c92085199c6ffec216"},
-    ("c2", 1): {"sources": FWD_SOURCES, "fetch_kib": 336709, "write_kib": 416247,
-                "sources_sha256": "6f95532a8288a655cc5d07b47582dc2dc3abb9e55a4672c92085199c6ffec216"},
+    ("c2", 0): {"sources": FWD_SOURCES, "fetch_kib": 336256, "write_kib": 400152,
+                "sources_sha256": "c40b06c7bcb4217afb7d5fafdf1bedf826f1e5e7ab38e00b8fc475d68368e828"},
+    ("c2", 1): {"sources": FWD_SOURCES, "fetch_kib": 350292, "write_kib": 414831,
+                "sources_sha256": "c40b06c7bcb4217afb7d5fafdf1bedf826f1e5e7ab38e00b8fc475d68368e828"},
     ("d1", 0): {"sources": STEP_SOURCES, "fetch_kib": 45069, "write_kib": 87040,
                 "sources_sha256": "450fdbf9aa09ccccb4f2de494aa94e655b524ae1d714af9917a7ae57032b0ae4"},
 }
