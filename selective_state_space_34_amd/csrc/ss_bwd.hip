@@ -151,12 +151,15 @@ __device__ __forceinline__ float row4_sum(float v) {
     return v;
 }
 
-// Σ over the wave's 16 channels (lane bits 2-5) of one step's dB|dC terms of the lane's S
-// states (cB, cC).  Lane bit 5 picks the type (dB for 0, dC for 1); with S >= 2, bit 4 picks
-// the half of the states, so a lane ends with W = max(S / 2, 1) complete sums: states
-// j·S + (S / 2)·bit4 + [0, W) of the type bit5, the same in the four lanes that differ in bits
-// 2 and 3 (and, for S = 1, in bit 4).
-template <int S>
+// Σ over channels of the wave of one step's dB|dC terms of the lane's S states (cB, cC).
+// Lane bit 5 picks the type (dB for 0, dC for 1); with S >= 2, bit 4 picks the half of the
+// states, so a lane ends with W = max(S / 2, 1) sums: states j·S + (S / 2)·bit4 + [0, W) of the
+// type bit5 (for S = 1 the same in both values of bit 4).  kRows = false: the sums cover the
+// four channels that differ in lane bits 4 and 5, and the four lanes that differ in bits 2 and
+// 3 hold the other channel groups' sums (they meet once per tile through LDS, for fewer
+// instructions per step than two more lane exchanges); kRows = true: DPP row rotations add
+// those too, so each sum covers all 16 channels, the same in the four lanes.
+template <int S, bool kRows>
 __device__ __forceinline__ void chan_sum(const float (&cB)[S], const float (&cC)[S],
                                          float (&w)[(S + 1) / 2]) {
     float u[S];
@@ -170,9 +173,9 @@ __device__ __forceinline__ void chan_sum(const float (&cB)[S], const float (&cC)
     }
 #pragma unroll
     for (int k = 0; k < (S + 1) / 2; ++k) {
-        w[k] = row4_sum(w[k]);
-        // the sums are formed here, for every lane: left alone, the compiler sinks the last add
-        // into the caller's masked store, where the row rotation no longer folds into it
+        if constexpr (kRows) w[k] = row4_sum(w[k]);
+        // formed here, for every lane: left alone, the compiler sinks the last add into the
+        // caller's masked store, where the row rotation no longer folds into it
         asm volatile("" : "+v"(w[k]));
     }
 }
@@ -594,13 +597,19 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(S >= 
     // lane that owns a batch's elements finishes their gradients right after the batch
     constexpr int kBB = kBPer;
     constexpr int kNBat = kBT / kBB;
-    constexpr int OUTW = kBT * 2 * NP;          // dB|dC sums of one tile for one wave
+    constexpr int OUTW = kBT * 2 * NP;          // dB|dC sums of one tile for one partial plane
+    constexpr int PS = OUTW + 4;                // stride of the planes (floats, 16-byte aligned)
+    // partial planes per wave: with the gate, four (the channel sums skip lane bits 2 and 3);
+    // without it the full butterfly, one plane (the ungated kernels, scheduled without the dz
+    // section between the sweeps, spilled registers with four)
+    constexpr int kPl = kGate ? 4 : 1;
     constexpr int CW = (S + 1) / 2;             // channel sums a lane holds per step
     __shared__ __align__(16) float bc_lds[kBMaxSteps * R];
     __shared__ __align__(16) float rows[4 * 16 * kRW];
     // a shared Δraw's gradient of a tile: [wave][channel][step], summed over the block
     __shared__ __align__(16) float dtx[4 * 16 * kBT];
-    __shared__ __align__(16) float comb[4 * OUTW];   // the wave sums of a tile
+    // a tile's dB|dC partial sums, [wave][plane][step][type][state]
+    __shared__ __align__(16) float comb[4 * kPl * PS];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -850,11 +859,11 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(S >= 
             // reverse sweep over the tile, in batches of kBB steps.  B and C of the step after
             // are read one step ahead (issued before this step's LDS stores of channel sums, which
             // the compiler cannot prove disjoint from them and would otherwise wait behind)
-            float* cbuf = comb + wave * OUTW;
+            float* cbuf = comb + (wave * kPl + (kPl > 1 ? (lane >> 2) & 3 : 0)) * PS;
             // which channel sums this lane holds after chan_sum, and whether it stores them
             const int cs_type = (lane >> 5) & 1, cs_half = (lane >> 4) & 1;
             const int cs_off = cs_type * NP + n0 + (S >= 2 ? (S / 2) * cs_half : 0);
-            const bool cs_store = (lane & 12) == 0 && (S >= 2 || cs_half == 0);
+            const bool cs_store = (kPl > 1 || (lane & 12) == 0) && (S >= 2 || cs_half == 0);
 #pragma unroll
             for (int bi = kNBat - 1; bi >= 0; --bi) {
                 float pxb[kBB], pdb[kBB];
@@ -923,10 +932,11 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(S >= 
                     }
                     pxb[i] = pxa;
                     pdb[i] = pda;
-                    // this step's dB|dC terms summed over the wave's 16 channels in registers; one
-                    // lane of each four holding the same sums stores them as [step][type][state]
+                    // this step's dB|dC terms summed over channels in registers; the lanes store
+                    // their sums in their plane as [step][type][state] (one lane of the four
+                    // holding the same sums with a single plane)
                     float cs[CW];
-                    chan_sum<S>(cB, cC, cs);
+                    chan_sum<S, kPl == 1>(cB, cC, cs);
                     if (cs_store) {
                         float* dst = cbuf + t * 2 * NP + cs_off;
                         if constexpr (CW == 4) {
@@ -977,7 +987,7 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(S >= 
                 }
             }
 
-            // dB|dC of the tile: the four waves' sums meet once per tile
+            // dB|dC of the tile: the waves' planes meet once per tile, summed in a fixed order
             __syncthreads();
             if (ddt_blk && tid < kBT) {
                 // Σ over the block's 64 channels of dΔraw at step tb + tid
@@ -991,7 +1001,15 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(S >= 
                 const int st = e / (2 * NP);
                 const int v = e % (2 * NP);
                 const int ty = v / NP, n = v % NP;
-                const float tot = (comb[e] + comb[OUTW + e]) + (comb[2 * OUTW + e] + comb[3 * OUTW + e]);
+                float tot = 0.0f;
+#pragma unroll
+                for (int w2 = 0; w2 < 4; ++w2) {
+                    const float* c = comb + w2 * kPl * PS + e;   // wave w2's planes
+                    float tw = c[0];
+#pragma unroll
+                    for (int q = 1; q < kPl; ++q) tw += c[q * PS];
+                    tot = w2 ? tot + tw : tw;
+                }
                 const int64_t t = t0c + tb + st;
                 if (n < Nr && t < t1c)
                     dbc_part[((int64_t(b) * NB + blockIdx.x) * L + t) * (2 * Nr) + ty * Nr + n] = tot;
