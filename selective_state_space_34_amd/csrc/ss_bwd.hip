@@ -598,12 +598,14 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(S >= 
     constexpr int kBB = kBPer;
     constexpr int kNBat = kBT / kBB;
     constexpr int OUTW = kBT * 2 * NP;          // dB|dC sums of one tile for one partial plane
-    constexpr int PS = OUTW + 4;                // stride of the planes (floats, 16-byte aligned)
+    constexpr int CW = (S + 1) / 2;             // channel sums a lane holds per step
+    // planes sit PS floats apart (a multiple of 32) plus an offset of {0, CW, 16, 16 + CW} floats
+    // for plane p = lane bits 2-3: the lanes of one store then hit disjoint LDS banks
+    constexpr int PS = OUTW + 32;
     // partial planes per wave: with the gate, four (the channel sums skip lane bits 2 and 3);
     // without it the full butterfly, one plane (the ungated kernels, scheduled without the dz
     // section between the sweeps, spilled registers with four)
     constexpr int kPl = kGate ? 4 : 1;
-    constexpr int CW = (S + 1) / 2;             // channel sums a lane holds per step
     __shared__ __align__(16) float bc_lds[kBMaxSteps * R];
     __shared__ __align__(16) float rows[4 * 16 * kRW];
     // a shared Δraw's gradient of a tile: [wave][channel][step], summed over the block
@@ -859,7 +861,8 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(S >= 
             // reverse sweep over the tile, in batches of kBB steps.  B and C of the step after
             // are read one step ahead (issued before this step's LDS stores of channel sums, which
             // the compiler cannot prove disjoint from them and would otherwise wait behind)
-            float* cbuf = comb + (wave * kPl + (kPl > 1 ? (lane >> 2) & 3 : 0)) * PS;
+            const int cpl = kPl > 1 ? (lane >> 2) & 3 : 0;
+            float* cbuf = comb + (wave * kPl + cpl) * PS + (cpl & 1) * CW + (cpl >> 1) * 16;
             // which channel sums this lane holds after chan_sum, and whether it stores them
             const int cs_type = (lane >> 5) & 1, cs_half = (lane >> 4) & 1;
             const int cs_off = cs_type * NP + n0 + (S >= 2 ? (S / 2) * cs_half : 0);
@@ -1007,7 +1010,7 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(S >= 
                     const float* c = comb + w2 * kPl * PS + e;   // wave w2's planes
                     float tw = c[0];
 #pragma unroll
-                    for (int q = 1; q < kPl; ++q) tw += c[q * PS];
+                    for (int q = 1; q < kPl; ++q) tw += c[q * PS + (q & 1) * CW + (q >> 1) * 16];
                     tot = w2 ? tot + tw : tw;
                 }
                 const int64_t t = t0c + tb + st;
