@@ -247,3 +247,22 @@ def test_checkpoints(gpu, case):
                          inp.Dskip, z=cut(inp.z) if gate else None, h0=inp.h0 if h0 else None)
         exp[:, :, i] = hp
     assert_close(ck, exp, tol_for(inp), "h_ckpt")
+
+
+# per-channel dt_bias cycling through Δ→0, small, moderate and Δ→∞ regimes, so every wave of
+# 16 channels mixes them
+MIXED_BIAS = np.array([-60.0, -9.5, -2.0, 0.5, 3.0, 50.0], np.float32)
+
+
+@pytest.mark.parametrize("chunk", [96, 256])
+def test_chunked_power_aggregate_mixed_steps(gpu, chunk):
+    """Chunked plan with A = -(n+1): the aggregate pass's suffix-weighted sums (per 16-step half,
+    the entering state decayed by e^{-(n+1)Δ} plus inputs weighted by e^{-(n+1)R_t}) with step
+    sizes from 1e-26 to 50 in the same wave, a chunk of three tiles and one of eight."""
+    inp = make_inputs(2, 1024, 64, 16, seed=91, gate=True, with_h0=True)
+    inp.dt_bias[:] = np.resize(MIXED_BIAS, inp.dt_bias.shape)
+    note(f"chunked power aggregate, mixed step sizes, chunk={chunk}")
+    y, hf = gpu_fwd(gpu, inp, plan=2, chunk=chunk)
+    yr, hr = oracle_fwd(inp)
+    assert_close(y, yr, 1e-4, "y")
+    assert_close(hf, hr, 1e-4, "h_final")
